@@ -1,0 +1,429 @@
+"""Benchmark of the 4-bit GEMV / GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections decode,gemm,affine,llama]
+
+A step is one decode token through the decode-GEMV workload (Q4_0 W
+[12288, 4096], one bf16 activation [1, 4096] ~ N(0,1)): quantise the
+activation to Q8_1 once, run q4_gemv on W and q4_gemv_fused2 on a (gate, up)
+pair of the same shape.  The weights rotate through enough distinct copies
+(>= 538 MB) that every step streams them from HBM, not from the 256 MB
+last-level cache.  `value` is the step's algorithmic bytes over its
+wall-clock time (GB/s); the roofline object is q4_gemv's, timed per launch
+with HIP events on the stream the kernels run on.
+
+The other sections add, under "extra": the prefill GEMM (Q4_0, M=2048,
+TFLOP/s) against dequantise-then-GEMM, the affine-4 group-64 sweep over
+M in {1, 32, 512, 2048, 8192} with its crossover, and the Llama-3.2-1B-shaped
+16-layer stack (aggregate tokens/s).  The CPU oracle is timed on the host
+cores on a bounded sample of the decode workload (rank 0, N=1 only).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from gemv_q4_affine_amd import binding as B  # noqa: E402
+from gemv_q4_affine_amd import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bf16_dev(x_f32: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(synth.bf16_bits(x_f32).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class EventTimer:
+    """Per-launch durations from HIP events recorded on the launching stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def launch(self, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.append((s, e))
+        return out
+
+    def mean_ms(self) -> float:
+        torch.cuda.synchronize()
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+
+def time_region(fn, iters: int, warmup: int = 3) -> float:
+    """Mean ms per call of fn over `iters` back-to-back calls (events around the region)."""
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+# ---------------------------------------------------------------------------
+# decode step (the headline workload)
+# ---------------------------------------------------------------------------
+
+def decode_section(steps: int, warmup: int, copies: int):
+    wl = synth.DECODE
+    N, K = wl.N, wl.K
+    log(f"[decode] generating W [{N},{K}] x3 and x [1,{K}]")
+    rng = np.random.default_rng(wl.seed)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, 1, K)
+    Wg = synth.weights(rng, N, K)
+    Wu = synth.weights(rng, N, K)
+    x = bf16_dev(X)
+    mats = []
+    for Wm in (W, Wg, Wu):
+        qs, d = B.q4_quantize(torch.from_numpy(Wm).cuda())
+        mats.append((qs, d))
+    del W, Wg, Wu
+    # distinct copies so every step streams its weights from HBM
+    rot = [[(qs.clone(), d.clone()) for (qs, d) in mats] for _ in range(copies)]
+    torch.cuda.synchronize()
+    xq = torch.empty((1, K), dtype=torch.int8, device="cuda")
+    xd = torch.empty((1, K // 32, 2), dtype=torch.int16, device="cuda")
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    y0 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+
+    bytes_q8 = K * 2 + K + (K // 32) * 4
+    bytes_gemv = N * K // 2 + N * (K // 32) * 2 + K + (K // 32) * 4 + N * 4
+    bytes_f2 = 2 * (N * K // 2 + N * (K // 32) * 2) + K + (K // 32) * 4 + 2 * N * 4
+    bytes_step = bytes_q8 + bytes_gemv + bytes_f2
+
+    def step(i, timers=None):
+        (wq, wd), (gq, gd), (uq, ud) = rot[i % copies]
+        if timers is None:
+            B.q8_1_quantize_act(x, xq, xd)
+            B.q4_gemv(wq, wd, xq, xd, y)
+            B.q4_gemv_fused2(gq, gd, uq, ud, xq, xd, y0, y1)
+        else:
+            timers[0].launch(lambda: B.q8_1_quantize_act(x, xq, xd))
+            timers[1].launch(lambda: B.q4_gemv(wq, wd, xq, xd, y))
+            timers[2].launch(lambda: B.q4_gemv_fused2(gq, gd, uq, ud, xq, xd, y0, y1))
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-job timing: exactly `steps` steps between synchronisations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+
+    # per-kernel durations from events on the launching stream
+    timers = [EventTimer(), EventTimer(), EventTimer()]
+    for i in range(steps):
+        step(i, timers)
+    ms_q8, ms_gemv, ms_f2 = (t.mean_ms() for t in timers)
+    log(f"[decode] step {ms_per_step * 1e3:.2f} us wall; kernels: q8 {ms_q8 * 1e3:.2f} us, "
+        f"gemv {ms_gemv * 1e3:.2f} us, fused2 {ms_f2 * 1e3:.2f} us")
+    return {
+        "ms_per_step": ms_per_step,
+        "bytes_step": bytes_step,
+        "gbs_step": bytes_step / (ms_per_step * 1e-3) / 1e9,
+        "gemv": {"us": ms_gemv * 1e3, "bytes": bytes_gemv, "gbs": bytes_gemv / (ms_gemv * 1e-3) / 1e9},
+        "fused2": {"us": ms_f2 * 1e3, "bytes": bytes_f2, "gbs": bytes_f2 / (ms_f2 * 1e-3) / 1e9},
+        "q8_1_quantize_act": {"us": ms_q8 * 1e3},
+        "copies": copies,
+        "rotated_bytes": copies * 3 * (N * K // 2 + N * (K // 32) * 2),
+    }
+
+
+# ---------------------------------------------------------------------------
+# prefill GEMM (Q4_0, M = 2048) and dequantise-then-GEMM
+# ---------------------------------------------------------------------------
+
+def gemm_section(iters: int):
+    wl = synth.PREFILL
+    M, N, K = wl.M, wl.N, wl.K
+    log(f"[gemm] M={M} N={N} K={K}")
+    W, X = synth.workload_inputs(wl)
+    qs, d = B.q4_quantize(torch.from_numpy(W).cuda())
+    x = bf16_dev(X)
+    del W, X
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    flop = 2.0 * M * N * K
+    fused_ms = time_region(lambda i: B.q4_gemm(qs, d, x, y=y), iters)
+    # dequantise-then-GEMM: our dequantiser, then (a) the library's dense MFMA
+    # GEMM on fp16 W, (b) hipBLASLt through torch on bf16 W (the pages' "jit")
+    w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    deq16_ms = time_region(lambda i: B.q4_dequantize(qs, d, out=w16), iters)
+    deqbf_ms = time_region(lambda i: B.q4_dequantize(qs, d, out_dtype=torch.bfloat16, out=wbf), iters)
+    dense_ms = time_region(lambda i: B.dense_gemm(x, w16, y=y), iters)
+    blas_bf16_ms = time_region(lambda i: torch.matmul(x, wbf.t(), out=y), iters)
+    x16 = x.to(torch.float16)
+    y16 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    blas_f16_ms = time_region(lambda i: torch.matmul(x16, w16.t(), out=y16), iters)
+    best_deq = deq16_ms + min(dense_ms, blas_f16_ms)
+    res = {
+        "fused_us": fused_ms * 1e3,
+        "fused_tflops": flop / (fused_ms * 1e-3) / 1e12,
+        "dequant_f16_us": deq16_ms * 1e3,
+        "dequant_bf16_us": deqbf_ms * 1e3,
+        "dense_gemm_f16_us": dense_ms * 1e3,
+        "hipblaslt_bf16_us": blas_bf16_ms * 1e3,
+        "hipblaslt_f16_us": blas_f16_ms * 1e3,
+        "jit_bf16_us": (deqbf_ms + blas_bf16_ms) * 1e3,
+        "dequant_then_gemm_best_us": best_deq * 1e3,
+        "fused_vs_dequant_then_gemm": best_deq / fused_ms,
+        "flop": flop,
+    }
+    log(f"[gemm] fused {res['fused_us']:.1f} us = {res['fused_tflops']:.0f} TFLOP/s; "
+        f"dequant f16 {res['dequant_f16_us']:.1f} us; dense {res['dense_gemm_f16_us']:.1f} us; "
+        f"hipBLASLt bf16 {res['hipblaslt_bf16_us']:.1f} us, f16 {res['hipblaslt_f16_us']:.1f} us")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# affine 4-bit sweep
+# ---------------------------------------------------------------------------
+
+def affine_section(iters: int):
+    wl = synth.AFFINE
+    N, K = wl.N, wl.K
+    rng = np.random.default_rng(wl.seed)
+    W = synth.weights(rng, N, K)
+    q, s, b = B.affine4_quantize(bf16_dev(W))
+    del W
+    wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
+    B.affine4_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf)
+    out = []
+    for M in synth.AFFINE_MS:
+        W_, X = synth.workload_inputs(wl, M=M)
+        del W_
+        x = bf16_dev(X)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        it = max(5, min(iters, int(2000 / max(1, M // 32))))
+        fused = time_region(lambda i: B.affine4_gemm(q, s, b, x, y=y), it)
+        deq16 = time_region(lambda i: B.affine4_dequantize(q, s, b, out=w16), it)
+        deqbf = time_region(lambda i: B.affine4_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf), it)
+        ref = time_region(lambda i: torch.matmul(x, wbf.t(), out=y), it)
+        dense = time_region(lambda i: B.dense_gemm(x, w16, y=y), it)
+        flop = 2.0 * M * N * K
+        byts = N * K // 2 + 2 * N * (K // 64) * 2 + M * K * 2 + M * N * 2
+        t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flop / (F16_MFMA_PEAK_TFLOPS * 1e12))
+        rec = {
+            "M": M,
+            "fused_us": fused * 1e3,
+            "jit_us": (deqbf + ref) * 1e3,            # dequantise to bf16 + hipBLASLt bf16
+            "ref_us": ref * 1e3,                       # hipBLASLt on pre-dequantised bf16 W
+            "dequant_dense_f16_us": (deq16 + dense) * 1e3,
+            "tflops": flop / (fused * 1e-3) / 1e12,
+            "gbs": byts / (fused * 1e-3) / 1e9,
+            "roofline_frac": t_roof / (fused * 1e-3),
+            "fused_beats_jit": fused < deqbf + ref,
+        }
+        out.append(rec)
+        log(f"[affine] M={M}: fused {rec['fused_us']:.1f} us, jit {rec['jit_us']:.1f} us, "
+            f"ref {rec['ref_us']:.1f} us, roofline {rec['roofline_frac']:.2f}")
+    crossover = None
+    for rec in out:
+        if not rec["fused_beats_jit"]:
+            crossover = rec["M"]
+            break
+    return {"sweep": out, "first_M_where_dequant_then_gemm_wins": crossover}
+
+
+# ---------------------------------------------------------------------------
+# Llama-3.2-1B-shaped 16-layer stack
+# ---------------------------------------------------------------------------
+
+def llama_section(iters: int):
+    rng = np.random.default_rng(0)
+    L = synth.LLAMA1B_LAYERS
+    layers = []
+    total_bytes = 0
+    flop512 = 0.0
+    for _ in range(L):
+        lw = {}
+        for name, (n, k) in synth.LLAMA1B_SHAPES.items():
+            qs, d = B.q4_quantize(torch.from_numpy(synth.weights(rng, n, k)).cuda())
+            lw[name] = (qs, d)
+            total_bytes += n * k // 2 + n * (k // 32) * 2
+            flop512 += 2.0 * 512 * n * k
+        layers.append(lw)
+    torch.cuda.synchronize()
+    H, F = 2048, 8192
+    xs = {k: bf16_dev(synth.activations(rng, 1, k)) for k in (H, F)}
+    qbuf = {k: (torch.empty((1, k), dtype=torch.int8, device="cuda"),
+                torch.empty((1, k // 32, 2), dtype=torch.int16, device="cuda")) for k in (H, F)}
+    yb = {n: torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (512, 2048, 8192)}
+    yb2 = {n: torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (512, 8192)}
+
+    def decode_token(_i):
+        for lw in layers:
+            xq, xd = B.q8_1_quantize_act(xs[H], *qbuf[H])
+            B.q4_gemv(*lw["q"], xq, xd, yb[2048])
+            B.q4_gemv_fused2(*lw["k"], *lw["v"], xq, xd, yb[512], yb2[512])
+            xq, xd = B.q8_1_quantize_act(xs[H], *qbuf[H])
+            B.q4_gemv(*lw["o"], xq, xd, yb[2048])
+            xq, xd = B.q8_1_quantize_act(xs[H], *qbuf[H])
+            B.q4_gemv_fused2(*lw["gate"], *lw["up"], xq, xd, yb[8192], yb2[8192])
+            xq, xd = B.q8_1_quantize_act(xs[F], *qbuf[F])
+            B.q4_gemv(*lw["down"], xq, xd, yb[2048])
+
+    decode_ms = time_region(decode_token, iters)
+    # prefill, M = 512
+    Mp = 512
+    xp = {k: bf16_dev(synth.activations(rng, Mp, k)) for k in (H, F)}
+    yp = {n: torch.empty((Mp, n), dtype=torch.bfloat16, device="cuda") for n in (512, 2048, 8192)}
+
+    def prefill(_i):
+        for lw in layers:
+            for name in ("q", "k", "v", "o", "gate", "up", "down"):
+                qs, d = lw[name]
+                n = d.shape[0]
+                k = d.shape[1] * 32
+                B.q4_gemm(qs, d, xp[k], y=yp[n])
+
+    prefill_ms = time_region(prefill, max(3, iters // 4))
+    res = {
+        "decode_tokens_per_s": 1e3 / decode_ms,
+        "decode_us_per_token": decode_ms * 1e3,
+        "decode_weight_gbs": total_bytes / (decode_ms * 1e-3) / 1e9,
+        "prefill_tokens_per_s": Mp * 1e3 / prefill_ms,
+        "prefill_tflops": flop512 / (prefill_ms * 1e-3) / 1e12,
+        "weights_bytes": total_bytes,
+        "launches": "plain stream",
+    }
+    log(f"[llama] decode {res['decode_tokens_per_s']:.0f} tok/s ({res['decode_weight_gbs']:.0f} GB/s); "
+        f"prefill {res['prefill_tokens_per_s']:.0f} tok/s ({res['prefill_tflops']:.0f} TFLOP/s)")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores, bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(budget_s: float):
+    import oracle
+    wl = synth.DECODE
+    N, K = wl.N, wl.K
+    W, X = synth.workload_inputs(wl)
+    Xb = synth.bf16_bits_to_f32(synth.bf16_bits(X))
+    wqs, wd = oracle.q4_0_quantize(W)
+    bytes_gemv = N * K // 2 + N * (K // 32) * 2 + K + (K // 32) * 4 + N * 4
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        xqs, xds = oracle.q8_1_quantize(Xb)
+        oracle.q4q8_gemv(wqs, wd, xqs, xds)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": bytes_gemv * reps / el / 1e9,
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"decode GEMV M=1 N={N} K={K} (Q8_1 quantise + int32 block dots + fp64 accumulate), "
+                  f"{reps} repetitions in {el:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=20,
+                    help="distinct weight copies rotated through (>= 19 keeps the 256 MB cache out)")
+    ap.add_argument("--sections", default="decode,gemm,affine,llama,cpu")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    sections = set(args.sections.split(","))
+    torch.cuda.init()
+    log(f"[bench] {torch.cuda.get_device_name(0)}; {B.version()}")
+
+    dec = decode_section(args.steps, args.warmup, args.copies)
+    extra = {"decode": dec}
+    if "gemm" in sections:
+        extra["gemm_m2048"] = gemm_section(20)
+    if "affine" in sections:
+        extra["affine4_sweep"] = affine_section(20)
+    if "llama" in sections:
+        extra["llama1b_stack"] = llama_section(20)
+    cpu = cpu_baseline(args.cpu_seconds) if "cpu" in sections else None
+
+    g = dec["gemv"]
+    line = {
+        "metric": "Q4 GEMV GB/s (M=1) and Q4 GEMM TFLOP/s (M=2048), N=12288 K=4096",
+        "value": round(dec["gbs_step"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4_0 x q8_1 (int32 block dots, f32 accumulate)",
+        "data": "synthetic (seeded numpy PCG64: W ~ N(0, 0.02^2), x ~ N(0, 1) as bf16)",
+        "config": {
+            "workload": "decode GEMV Q4_0 N=12288 K=4096 M=1: q8_1_quantize_act + q4_gemv + q4_gemv_fused2 "
+                        "(gate, up), weights rotated over %d copies" % args.copies,
+            "M": 1, "N": 12288, "K": 4096,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "q4_gemv (k_q4_gemv<1,4>)",
+            "achieved": round(g["gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(g["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": g["bytes"],
+            "avg_launch_us": round(g["us"], 3),
+        },
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    if "gemm_m2048" in extra:
+        gm = extra["gemm_m2048"]
+        line["extra"]["gemm_roofline"] = {
+            "bound": "mfma", "achieved": round(gm["fused_tflops"], 1), "peak": F16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(gm["fused_tflops"] / F16_MFMA_PEAK_TFLOPS, 4),
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

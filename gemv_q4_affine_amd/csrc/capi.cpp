@@ -1,0 +1,298 @@
+// capi.cpp -- the exported C ABI (include/q4.h): argument validation, the
+// M-threshold dispatch and the kernel launches.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// enqueues nothing and the checks work on a machine without a GPU.
+#include "q4.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+// ---- dispatch settings -----------------------------------------------------
+// Defaults come from the measured crossovers of this library on MI355X.
+constexpr int64_t kSkinnyLimit = 64;          // the skinny kernel's largest M
+std::atomic<int64_t> g_skinny_max_m{32};
+std::atomic<int64_t> g_dequant_min_m{kMaxDim + 1};   // dequantise-then-GEMM never wins by default
+std::atomic<int64_t> g_force_path{-1};
+std::once_flag g_env_once;
+
+int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+bool env_int(const char* name, int64_t* out) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return false;
+    char* end = nullptr;
+    long long v = std::strtoll(s, &end, 10);
+    if (end == s) return false;
+    *out = (int64_t)v;
+    return true;
+}
+
+// Environment overrides, read once per process and clamped (the clamped
+// token-count gate pattern of vllm.cpp issue #838, Scope).
+void read_env() {
+    std::call_once(g_env_once, [] {
+        int64_t v;
+        if (env_int("Q4_SKINNY_MAX_M", &v)) g_skinny_max_m = clamp64(v, 0, kSkinnyLimit);
+        if (env_int("Q4_DEQUANT_MIN_M", &v)) g_dequant_min_m = clamp64(v, 1, kMaxDim + 1);
+        if (env_int("Q4_FORCE_PATH", &v)) g_force_path = clamp64(v, -1, Q4_PATH_DEQUANT_GEMM);
+    });
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptrs_aligned(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p) return Q4_ERR_NULL;
+    for (const void* p : ps)
+        if (!aligned16(p)) return Q4_ERR_ALIGN;
+    return Q4_OK;
+}
+
+int check_dims(int64_t M, int64_t N, int64_t K, int64_t kmult) {
+    if (M < 0 || N < 0 || K <= 0) return Q4_ERR_SHAPE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return Q4_ERR_SHAPE;
+    if (K % kmult != 0) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* q4_status_string(int status) {
+    switch (status) {
+        case Q4_OK: return "ok";
+        case Q4_ERR_NULL: return "a required pointer is NULL";
+        case Q4_ERR_SHAPE: return "M, N or K out of range or not a multiple of the block/group size";
+        case Q4_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+        case Q4_ERR_DTYPE: return "unsupported dtype";
+        case Q4_ERR_HIP: return "HIP launch or runtime error";
+        case Q4_ERR_ARG: return "invalid argument";
+        case Q4_ERR_WORKSPACE: return "the dequantise-then-GEMM path needs a workspace of q4_gemm_workspace_size bytes";
+        default: return "unknown status";
+    }
+}
+
+const char* q4_version(void) { return "gemv_q4_affine_amd 0.1.0 (gfx950)"; }
+
+// ---- dispatch ------------------------------------------------------------------
+
+int q4_set_dispatch(int key, int64_t value) {
+    read_env();
+    switch (key) {
+        case Q4_KEY_SKINNY_MAX_M: g_skinny_max_m = clamp64(value, 0, kSkinnyLimit); return Q4_OK;
+        case Q4_KEY_DEQUANT_MIN_M: g_dequant_min_m = clamp64(value, 1, kMaxDim + 1); return Q4_OK;
+        case Q4_KEY_FORCE_PATH:
+            if (value < -1 || value > Q4_PATH_DEQUANT_GEMM || value == Q4_PATH_GEMV) return Q4_ERR_ARG;
+            g_force_path = value;
+            return Q4_OK;
+        default: return Q4_ERR_ARG;
+    }
+}
+
+int q4_get_dispatch(int key, int64_t* value) {
+    read_env();
+    if (!value) return Q4_ERR_NULL;
+    switch (key) {
+        case Q4_KEY_SKINNY_MAX_M: *value = g_skinny_max_m; return Q4_OK;
+        case Q4_KEY_DEQUANT_MIN_M: *value = g_dequant_min_m; return Q4_OK;
+        case Q4_KEY_FORCE_PATH: *value = g_force_path; return Q4_OK;
+        default: return Q4_ERR_ARG;
+    }
+}
+
+int q4_dispatch_path(int64_t M, int64_t N, int64_t K, int fmt, int have_workspace) {
+    read_env();
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE4) return Q4_ERR_ARG;
+    const int rc = check_dims(M, N, K, fmt == Q4_FMT_Q4_0 ? 32 : 64);
+    if (rc) return rc;
+    const int64_t forced = g_force_path;
+    if (forced >= 0) return (int)forced;
+    if (M <= g_skinny_max_m) return Q4_PATH_SKINNY;
+    if (have_workspace && M >= g_dequant_min_m) return Q4_PATH_DEQUANT_GEMM;
+    return Q4_PATH_MFMA;
+}
+
+int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt) {
+    (void)M;
+    (void)fmt;
+    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim) return 0;
+    return N * K * 2;
+}
+
+// ---- quantisers ------------------------------------------------------------------
+
+int q4_quantize(const void* w, int w_dtype, int64_t N, int64_t K, uint8_t* w_qs, uint16_t* w_d, void* stream) {
+    if (w_dtype != Q4_F32 && w_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    int rc = check_dims(0, N, K, 32);
+    if (rc) return rc;
+    if (N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w, w_qs, w_d}))) return rc;
+    return hip_status(q4::launch_q4_quantize(w, w_dtype, N, K, w_qs, w_d, as_stream(stream)));
+}
+
+int q8_1_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* x_qs, uint16_t* x_ds, void* stream) {
+    if (x_dtype != Q4_F32 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    int rc = check_dims(M, 0, K, 32);
+    if (rc) return rc;
+    if (M == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({x, x_qs, x_ds}))) return rc;
+    return hip_status(q4::launch_q8_1_quantize(x, x_dtype, M, K, x_qs, x_ds, as_stream(stream)));
+}
+
+int affine4_quantize(const void* w, int w_dtype, int64_t N, int64_t K, int64_t group_size, uint8_t* w_q,
+                     uint16_t* scales, uint16_t* biases, void* stream) {
+    if (w_dtype != Q4_F32 && w_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (group_size != 64) return Q4_ERR_SHAPE;
+    int rc = check_dims(0, N, K, 64);
+    if (rc) return rc;
+    if (N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w, w_q, scales, biases}))) return rc;
+    return hip_status(q4::launch_affine4_quantize(w, w_dtype, N, K, group_size, w_q, scales, biases, as_stream(stream)));
+}
+
+int q4_dequantize(const uint8_t* w_qs, const uint16_t* w_d, int64_t N, int64_t K, void* out, int out_dtype,
+                  void* stream) {
+    if (out_dtype != Q4_F32 && out_dtype != Q4_BF16 && out_dtype != Q4_F16) return Q4_ERR_DTYPE;
+    int rc = check_dims(0, N, K, 32);
+    if (rc) return rc;
+    if (N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_qs, w_d, out}))) return rc;
+    return hip_status(q4::launch_q4_dequantize(w_qs, w_d, N, K, out, out_dtype, as_stream(stream)));
+}
+
+int affine4_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases, int64_t group_size,
+                       int64_t N, int64_t K, void* out, int out_dtype, void* stream) {
+    if (out_dtype != Q4_F32 && out_dtype != Q4_BF16 && out_dtype != Q4_F16) return Q4_ERR_DTYPE;
+    if (group_size != 64) return Q4_ERR_SHAPE;
+    int rc = check_dims(0, N, K, 64);
+    if (rc) return rc;
+    if (N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_q, scales, biases, out}))) return rc;
+    return hip_status(
+        q4::launch_affine4_dequantize(w_q, scales, biases, group_size, N, K, out, out_dtype, as_stream(stream)));
+}
+
+// ---- decode GEMV -------------------------------------------------------------------
+
+int q4_gemv(const uint8_t* w_qs, const uint16_t* w_d, const int8_t* x_qs, const uint16_t* x_ds, float* y,
+            int64_t M, int64_t N, int64_t K, void* stream) {
+    int rc = check_dims(M, N, K, 32);
+    if (rc) return rc;
+    if (M > Q4_GEMV_MAX_M) return Q4_ERR_SHAPE;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_qs, w_d, x_qs, x_ds, y}))) return rc;
+    return hip_status(q4::launch_q4_gemv(w_qs, w_d, y, N, nullptr, nullptr, nullptr, 0, x_qs, x_ds, M, K,
+                                         as_stream(stream)));
+}
+
+int q4_gemv_fused2(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0, const uint8_t* w1_qs,
+                   const uint16_t* w1_d, int64_t N1, const int8_t* x_qs, const uint16_t* x_ds, float* y0, float* y1,
+                   int64_t M, int64_t K, void* stream) {
+    int rc = check_dims(M, N0, K, 32);
+    if (rc) return rc;
+    if ((rc = check_dims(M, N1, K, 32))) return rc;
+    if (M > Q4_GEMV_MAX_M) return Q4_ERR_SHAPE;
+    if (N0 + N1 > int64_t(0x7FFFFFFF)) return Q4_ERR_SHAPE;
+    if (M == 0 || N0 + N1 == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({x_qs, x_ds}))) return rc;
+    if (N0 > 0 && (rc = check_ptrs_aligned({w0_qs, w0_d, y0}))) return rc;
+    if (N1 > 0 && (rc = check_ptrs_aligned({w1_qs, w1_d, y1}))) return rc;
+    return hip_status(
+        q4::launch_q4_gemv(w0_qs, w0_d, y0, N0, w1_qs, w1_d, y1, N1, x_qs, x_ds, M, K, as_stream(stream)));
+}
+
+// ---- GEMM ----------------------------------------------------------------------------
+
+static int gemm_common(int wf, const void* a, const void* b, const void* c, const void* x, int x_dtype, void* y,
+                       int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                       void* stream) {
+    const int fmt = (wf == q4::WF_Q4_0) ? Q4_FMT_Q4_0 : Q4_FMT_AFFINE4;
+    const bool have_ws = workspace != nullptr && workspace_bytes >= q4_gemm_workspace_size(M, N, K, fmt);
+    const int path = q4_dispatch_path(M, N, K, fmt, have_ws ? 1 : 0);
+    if (path < 0) return path;
+    if (M == 0 || N == 0) return Q4_OK;
+    hipStream_t s = as_stream(stream);
+    switch (path) {
+        case Q4_PATH_SKINNY:
+            if (M > kSkinnyLimit) return Q4_ERR_ARG;
+            return hip_status(q4::launch_gemm_skinny(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
+        case Q4_PATH_MFMA:
+            return hip_status(q4::launch_gemm_mfma(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
+        case Q4_PATH_DEQUANT_GEMM: {
+            if (!have_ws) return Q4_ERR_WORKSPACE;
+            if (!aligned16(workspace)) return Q4_ERR_ALIGN;
+            hipError_t e = (wf == q4::WF_Q4_0)
+                               ? q4::launch_q4_dequantize(static_cast<const uint8_t*>(a),
+                                                          static_cast<const uint16_t*>(b), N, K, workspace,
+                                                          q4::DT_F16, s)
+                               : q4::launch_affine4_dequantize(static_cast<const uint8_t*>(a),
+                                                               static_cast<const uint16_t*>(b),
+                                                               static_cast<const uint16_t*>(c), 64, N, K, workspace,
+                                                               q4::DT_F16, s);
+            if (e != hipSuccess) return Q4_ERR_HIP;
+            if (M <= kSkinnyLimit && M <= g_skinny_max_m)
+                return hip_status(q4::launch_gemm_skinny(q4::WF_DENSE16, workspace, nullptr, nullptr, x, x_dtype, y,
+                                                         y_dtype, M, N, K, s));
+            return hip_status(q4::launch_gemm_mfma(q4::WF_DENSE16, workspace, nullptr, nullptr, x, x_dtype, y,
+                                                   y_dtype, M, N, K, s));
+        }
+        default: return Q4_ERR_ARG;
+    }
+}
+
+int q4_gemm(const uint8_t* w_qs, const uint16_t* w_d, const void* x, int x_dtype, void* y, int y_dtype, int64_t M,
+            int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+    if ((x_dtype != Q4_BF16 && x_dtype != Q4_F32) || (y_dtype != Q4_BF16 && y_dtype != Q4_F32)) return Q4_ERR_DTYPE;
+    int rc = check_dims(M, N, K, 32);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_qs, w_d, x, y}))) return rc;
+    return gemm_common(q4::WF_Q4_0, w_qs, w_d, nullptr, x, x_dtype, y, y_dtype, M, N, K, workspace, workspace_bytes,
+                       stream);
+}
+
+int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases, int64_t group_size,
+                 const void* x, int x_dtype, void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+    if ((x_dtype != Q4_BF16 && x_dtype != Q4_F32) || (y_dtype != Q4_BF16 && y_dtype != Q4_F32)) return Q4_ERR_DTYPE;
+    if (group_size != 64) return Q4_ERR_SHAPE;
+    int rc = check_dims(M, N, K, 64);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_q, scales, biases, x, y}))) return rc;
+    return gemm_common(q4::WF_AFFINE4, w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, workspace,
+                       workspace_bytes, stream);
+}
+
+int dense_gemm(const void* x, int x_dtype, const uint16_t* w_f16, void* y, int y_dtype, int64_t M, int64_t N,
+               int64_t K, void* stream) {
+    if ((x_dtype != Q4_BF16 && x_dtype != Q4_F32) || (y_dtype != Q4_BF16 && y_dtype != Q4_F32)) return Q4_ERR_DTYPE;
+    int rc = check_dims(M, N, K, 32);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({x, w_f16, y}))) return rc;
+    read_env();
+    hipStream_t s = as_stream(stream);
+    if (M <= g_skinny_max_m)
+        return hip_status(
+            q4::launch_gemm_skinny(q4::WF_DENSE16, w_f16, nullptr, nullptr, x, x_dtype, y, y_dtype, M, N, K, s));
+    return hip_status(q4::launch_gemm_mfma(q4::WF_DENSE16, w_f16, nullptr, nullptr, x, x_dtype, y, y_dtype, M, N, K, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,650 @@
+// gemm.hip -- fused dequantise + matrix-core GEMM on gfx950.
+//
+//   Y[M,N] = X[M,K] . dequant(Wq)[N,K]^T,  fp32 accumulation.
+//
+// The prefill kernel of the pages: dequantised weight tiles are made once
+// and reused across every token row of the tile, the K loop is software
+// pipelined (next tiles fetched while the current one is multiplied), and the
+// matrix engine does the contraction (llama.cpp PR "et-backend: Q4_0
+// matrix-engine GEMM rewrite for prefill", Overview; MLX issue #4621 for the
+// affine format and the dequantise-then-matmul alternative).
+//
+// gfx950 design
+//  * Operand precision.  The MFMA runs in binary16 (v_mfma_f32_32x32x16_f16
+//    and v_mfma_f32_16x16x32_f16): X (bfloat16) converts to binary16 exactly
+//    in binary16's normal range, and a dequantised weight (q-8)*d is rounded
+//    once to binary16 (relative error <= 2^-11).  Rounding the weights to
+//    bfloat16 instead (what a bf16 MFMA would need) costs about 1.6e-3
+//    relative error on top of the 1.6e-3 of the bf16 output, which together
+//    exceed the 2e-3 error bar; binary16 weights stay well inside it.
+//  * Weights never touch LDS.  Each wave owns distinct output columns, so it
+//    dequantises its B fragments straight from global memory into registers:
+//    the nibbles become binary16 1024+q with one AND-OR against 0x6400 (the
+//    binary16 exponent at which the unit in the last place is 1), then one
+//    packed subtract of 1032 and one packed multiply by d give (q-8)*d
+//    rounded to nearest even.  A weight is dequantised once per M tile of
+//    the workgroup -- the "static reuse across token tiles" of the ET-SoC-1
+//    rewrite -- and is never written back.
+//  * X goes global -> registers -> (convert to binary16) -> LDS once per
+//    workgroup and K step, double buffered, one barrier per K step.  Rows are
+//    padded to 40 halves (80 bytes) so the 128-bit fragment reads of eight
+//    consecutive lanes fall in distinct banks.
+//  * Each MFMA sums over 16 (or 32) K slots; the slot -> k assignment only has
+//    to agree between the A and B operands, so it is chosen to match each
+//    weight format's nibble order and the B loader needs no byte shuffles
+//    beyond one v_perm per pair.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace q4 {
+
+// ---------------------------------------------------------------------------
+// Weight fragment loaders.
+//
+// A fragment covers one 32-column tile and one 32-wide K step (two 32x32x16
+// MFMAs, s = 0, 1).  Lane l owns column j = l % 32 and lane group g = l / 32;
+// in MFMA s it supplies the 8 halves for K slots 8g..8g+7, which stand for
+// k = kofs(s, g) + v, v = 0..7, of the 32-wide step.  The X fragment read
+// from LDS uses the same kofs.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t perm(uint32_t a, uint32_t sel) { return __builtin_amdgcn_perm(a, a, sel); }
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Two nibble codes (in bits 0-3 and 16-19 after masking) -> binary16 (q-8)*d.
+__device__ __forceinline__ uint32_t q4_pair(uint32_t t, half2_t dd) {
+    const half2_t v = as_h2((t & 0x000F000Fu) | 0x64006400u);      // 1024 + q
+    const half2_t c = as_h2(0xE408E408u);                             // -1032
+    return h2_bits((v + c) * dd);                                     // (q - 8) * d, RNE
+}
+
+struct RawQ4 {      // raw Q4_0 data of one fragment: 8 nibble bytes and the scale
+    u32x2_t q;
+    uint32_t d;
+};
+
+struct Frag16 {     // 8 halves for each of the two 16-wide K halves
+    u32x4_t s[2];
+};
+
+// Q4_0: lane group g takes bytes 8g..8g+7 of the block: low nibbles are
+// elements 8g+v (MFMA s = 0), high nibbles 16+8g+v (s = 1): kofs = 16s + 8g.
+__device__ __forceinline__ Frag16 q4_0_frag(const RawQ4& r) {
+    const half2_t dd = as_h2(r.d | (r.d << 16));
+    Frag16 f;
+#pragma unroll
+    for (int w = 0; w < 2; w++) {
+        const uint32_t word = r.q[w];
+        const uint32_t t01 = perm(word, 0x0C010C00u);   // byte0 | byte1 << 16
+        const uint32_t t23 = perm(word, 0x0C030C02u);   // byte2 | byte3 << 16
+        f.s[0][2 * w + 0] = q4_pair(t01, dd);
+        f.s[0][2 * w + 1] = q4_pair(t23, dd);
+        f.s[1][2 * w + 0] = q4_pair(t01 >> 4, dd);
+        f.s[1][2 * w + 1] = q4_pair(t23 >> 4, dd);
+    }
+    return f;
+}
+
+struct RawAff {     // raw affine data: 8 nibble bytes, scale and bias (bf16 bits)
+    u32x2_t q;
+    uint32_t s, b;
+};
+
+// binary32 -> binary16 bits (RNE), for the affine scale and bias.
+__device__ __forceinline__ uint32_t f16b(float f) { return f32_to_f16(f); }
+
+// Affine: byte i holds elements 2i (low) and 2i+1 (high).  Lane group g takes
+// bytes 8g..8g+7 = elements 16g..16g+15: s = 0 gets 16g+v, s = 1 gets
+// 16g+8+v: kofs = 16g + 8s.  Value q*s + b, one binary16 fma (one rounding).
+__device__ __forceinline__ Frag16 affine_frag(const RawAff& r) {
+    const uint32_t s16 = f16b(bf16_to_f32(r.s));
+    const uint32_t b16 = f16b(bf16_to_f32(r.b));
+    // lane 0 of a pair holds q_lo (unit 1), lane 1 holds 16*q_hi (unit 16):
+    // scale the high lane by 1/16 (exact) folded into its scale.
+    const half2_t sc = as_h2(s16 | (f16b(bf16_to_f32(r.s) * 0.0625f) << 16));
+    const half2_t bb = as_h2(b16 | (b16 << 16));
+    const half2_t c = as_h2(0xE400E400u);   // -1024
+    Frag16 f;
+#pragma unroll
+    for (int w = 0; w < 2; w++) {
+        const uint32_t word = r.q[w];
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            // byte p -> (low nibble in bits 0-3, high nibble kept in bits 20-23)
+            const uint32_t t = perm(word, 0x0C000C00u + (uint32_t)p * 0x00010001u);
+            const half2_t v = as_h2((t & 0x00F0000Fu) | 0x64006400u);   // 1024+q_lo, 1024+16 q_hi
+            const half2_t q = v + c;                                     // q_lo, 16 q_hi (exact)
+            const half2_t y = __builtin_elementwise_fma(q, sc, bb);     // q*s + b
+            f.s[w][p] = h2_bits(y);
+        }
+    }
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// Large-M kernel: workgroup = 4 waves side by side along N; each wave owns
+// NT 32-column tiles and all MT 32-row tiles of the workgroup's M range.
+// ---------------------------------------------------------------------------
+constexpr int kLdsStride = 40;   // halves per staged X row (32 + 8 padding)
+
+struct GemmArgs {
+    const void* a;     // Q4_0 qs / affine q / dense binary16 W
+    const void* b;     // Q4_0 d / affine scales
+    const void* c;     // affine biases
+    const void* x;
+    void* y;
+    int M, N, K;
+    int m_tiles;       // workgroup tiles along M
+    int n_tiles;       // workgroup tiles along N
+};
+
+__device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
+    return h2_bits(__builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(lo, hi)));
+}
+
+// 8 consecutive X values of row m (bf16 or f32) -> 8 binary16 values.
+template <int XDT>
+__device__ __forceinline__ u32x4_t load_x8(const void* x, int64_t off, bool ok) {
+    u32x4_t r = {0u, 0u, 0u, 0u};
+    if (!ok) return r;
+    if (XDT == DT_BF16) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + off);
+#pragma unroll
+        for (int i = 0; i < 4; i++) r[i] = cvt_pk(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xFFFF0000u));
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
+        const float4 v0 = p[0], v1 = p[1];
+        r[0] = cvt_pk(v0.x, v0.y); r[1] = cvt_pk(v0.z, v0.w);
+        r[2] = cvt_pk(v1.x, v1.y); r[3] = cvt_pk(v1.z, v1.w);
+    }
+    return r;
+}
+
+template <int XDT>
+__device__ __forceinline__ u32x4_t load_x8_raw(const void* x, int64_t off, bool ok, u32x4_t& hi) {
+    // raw load only (conversion later), to keep the loads in flight across the MFMAs
+    u32x4_t r = {0u, 0u, 0u, 0u};
+    hi = r;
+    if (!ok) return r;
+    if (XDT == DT_BF16) {
+        r = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + off);
+    } else {
+        const u32x4_t* p = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(x) + off);
+        r = p[0];
+        hi = p[1];
+    }
+    return r;
+}
+
+template <int XDT>
+__device__ __forceinline__ u32x4_t convert_x8(const u32x4_t v, const u32x4_t hi) {
+    u32x4_t r;
+    if (XDT == DT_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) r[i] = cvt_pk(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xFFFF0000u));
+    } else {
+        r[0] = cvt_pk(__uint_as_float(v[0]), __uint_as_float(v[1]));
+        r[1] = cvt_pk(__uint_as_float(v[2]), __uint_as_float(v[3]));
+        r[2] = cvt_pk(__uint_as_float(hi[0]), __uint_as_float(hi[1]));
+        r[3] = cvt_pk(__uint_as_float(hi[2]), __uint_as_float(hi[3]));
+    }
+    return r;
+}
+
+__device__ __forceinline__ void store_y(void* y, int ydt, int64_t off, float v) {
+    if (ydt == DT_F32) reinterpret_cast<float*>(y)[off] = v;
+    else reinterpret_cast<uint16_t*>(y)[off] = (uint16_t)f32_to_bf16(v);
+}
+
+template <int WF>
+struct RawW;
+template <>
+struct RawW<WF_Q4_0> { RawQ4 r; };
+template <>
+struct RawW<WF_AFFINE4> { RawAff r; };
+template <>
+struct RawW<WF_DENSE16> { u32x4_t h[2]; };
+
+template <int WF>
+__device__ __forceinline__ int kofs(int s, int g) {
+    return WF == WF_AFFINE4 ? 16 * g + 8 * s : 16 * s + 8 * g;
+}
+
+// Load the raw weight data of one fragment: column n, K step kb (32 wide).
+template <int WF>
+__device__ __forceinline__ RawW<WF> load_w(const GemmArgs& a, int n, int kb, int g, bool ok) {
+    RawW<WF> r;
+    const int nb = a.K / 32;
+    if constexpr (WF == WF_Q4_0) {
+        if (ok) {
+            const uint8_t* qs = reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + kb) * 16 + 8 * g;
+            r.r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(qs));
+            r.r.d = reinterpret_cast<const uint16_t*>(a.b)[(int64_t)n * nb + kb];
+        } else {
+            r.r.q = u32x2_t{0x88888888u, 0x88888888u};
+            r.r.d = 0;
+        }
+    } else if constexpr (WF == WF_AFFINE4) {
+        if (ok) {
+            const uint8_t* q = reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + kb * 16 + 8 * g;
+            r.r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(q));
+            const int64_t gi = (int64_t)n * (a.K / 64) + (kb >> 1);
+            r.r.s = reinterpret_cast<const uint16_t*>(a.b)[gi];
+            r.r.b = reinterpret_cast<const uint16_t*>(a.c)[gi];
+        } else {
+            r.r.q = u32x2_t{0u, 0u};
+            r.r.s = 0;
+            r.r.b = 0;
+        }
+    } else {
+        if (ok) {
+            const uint16_t* w = reinterpret_cast<const uint16_t*>(a.a) + (int64_t)n * a.K + kb * 32;
+            r.h[0] = *reinterpret_cast<const u32x4_t*>(w + kofs<WF>(0, g));
+            r.h[1] = *reinterpret_cast<const u32x4_t*>(w + kofs<WF>(1, g));
+        } else {
+            r.h[0] = u32x4_t{0u, 0u, 0u, 0u};
+            r.h[1] = r.h[0];
+        }
+    }
+    return r;
+}
+
+template <int WF>
+__device__ __forceinline__ Frag16 make_frag(const RawW<WF>& r) {
+    if constexpr (WF == WF_Q4_0) return q4_0_frag(r.r);
+    else if constexpr (WF == WF_AFFINE4) return affine_frag(r.r);
+    else {
+        Frag16 f;
+        f.s[0] = r.h[0];
+        f.s[1] = r.h[1];
+        return f;
+    }
+}
+
+template <int WF, int MT, int NT, int XDT, int YDT>
+__global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][MT * 32 * kLdsStride];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane & 31;
+    const int g = lane >> 5;
+
+    // workgroup -> (m tile, n tile); consecutive workgroups share an N tile
+    const int wg = blockIdx.x;
+    const int mt_idx = wg % a.m_tiles;
+    const int nt_idx = wg / a.m_tiles;
+    const int m0 = mt_idx * MT * 32;
+    const int n0 = nt_idx * (4 * NT * 32) + wave * NT * 32;
+
+    const int nb = a.K / 32;
+
+    // X staging: units of 8 values; unit u -> row u / 4, k offset (u % 4) * 8
+    constexpr int kUnits = MT * 32 * 4;
+    constexpr int kUnitsPerThread = (kUnits + 255) / 256;
+
+    floatx16_t acc[MT][NT];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mi][ni][v] = 0.0f;
+
+    auto x_unit_ok = [&](int u, int& row, int& kq) {
+        row = u >> 2;
+        kq = (u & 3) * 8;
+        return u < kUnits && (m0 + row) < a.M;
+    };
+
+    // prologue: stage step 0
+    RawW<WF> w_next[NT];
+    {
+#pragma unroll
+        for (int t = 0; t < kUnitsPerThread; t++) {
+            const int u = tid + t * 256;
+            int row, kq;
+            const bool ok = x_unit_ok(u, row, kq);
+            const u32x4_t v = load_x8<XDT>(a.x, (int64_t)(m0 + row) * a.K + kq, ok);
+            if (u < kUnits) *reinterpret_cast<u32x4_t*>(&lds[0][row * kLdsStride + kq]) = v;
+        }
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) {
+            const int n = n0 + ni * 32 + j;
+            w_next[ni] = load_w<WF>(a, n, 0, g, n < a.N);
+        }
+    }
+    __syncthreads();
+
+    for (int kb = 0; kb < nb; kb++) {
+        const int buf = kb & 1;
+        Frag16 bf[NT];
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) bf[ni] = make_frag<WF>(w_next[ni]);
+
+        // issue the next step's global loads before the MFMAs
+        const bool more = (kb + 1) < nb;
+        u32x4_t xr[kUnitsPerThread], xh[kUnitsPerThread];
+        if (more) {
+#pragma unroll
+            for (int t = 0; t < kUnitsPerThread; t++) {
+                const int u = tid + t * 256;
+                int row, kq;
+                const bool ok = x_unit_ok(u, row, kq);
+                xr[t] = load_x8_raw<XDT>(a.x, (int64_t)(m0 + row) * a.K + (int64_t)(kb + 1) * 32 + kq, ok, xh[t]);
+            }
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) {
+                const int n = n0 + ni * 32 + j;
+                w_next[ni] = load_w<WF>(a, n, kb + 1, g, n < a.N);
+            }
+        }
+
+        // MFMAs on the current step
+        const uint16_t* la = lds[buf];
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+#pragma unroll
+            for (int mi = 0; mi < MT; mi++) {
+                const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
+                    &la[(mi * 32 + j) * kLdsStride + kofs<WF>(s, g)]);
+                const half8_t ah = __builtin_bit_cast(half8_t, av);
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++) {
+                    const half8_t bh = __builtin_bit_cast(half8_t, bf[ni].s[s]);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[mi][ni], 0, 0, 0);
+                }
+            }
+        }
+
+        if (more) {
+#pragma unroll
+            for (int t = 0; t < kUnitsPerThread; t++) {
+                const int u = tid + t * 256;
+                int row, kq;
+                x_unit_ok(u, row, kq);
+                if (u < kUnits)
+                    *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][row * kLdsStride + kq]) = convert_x8<XDT>(xr[t], xh[t]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds column j of each tile, rows 8*(v/4) + 4*g + v%4
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) {
+            const int n = n0 + ni * 32 + j;
+            if (n >= a.N) continue;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int m = m0 + mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+                if (m < a.M) store_y(a.y, YDT, (int64_t)m * a.N + n, acc[mi][ni][v]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny kernel (small M): weights streamed once at HBM rate.
+//
+// Workgroup = 4 waves on the same 16*NT columns, splitting K four ways (the
+// K-splitting of the ET-SoC-1 rewrite) and summing their partial tiles through
+// LDS in a fixed order.  MFMA 16x16x32: lane l owns column j = l % 16 and lane
+// group g = l / 16, and loads one whole 32-weight block -- block kb+g of a
+// 4-block chunk -- with one 128-bit load; in MFMA t (t = 0..3) it supplies
+// elements 8t..8t+7 of that block, and the X fragment it pairs with is
+// X[i][32 (kb+g) + 8t .. +8].  Every lane scales by its own block's d.
+// ---------------------------------------------------------------------------
+struct SkinnyRawQ4 { u32x4_t q; uint32_t d; };
+struct SkinnyRawAff { u32x4_t q; uint32_t s, b; };
+
+template <int WF>
+struct SkRaw;
+template <> struct SkRaw<WF_Q4_0> { SkinnyRawQ4 r; };
+template <> struct SkRaw<WF_AFFINE4> { SkinnyRawAff r; };
+template <> struct SkRaw<WF_DENSE16> { u32x4_t h[4]; };
+
+template <int WF>
+__device__ __forceinline__ SkRaw<WF> sk_load(const GemmArgs& a, int n, int kblk, bool ok) {
+    SkRaw<WF> r;
+    const int nb = a.K / 32;
+    if constexpr (WF == WF_Q4_0) {
+        if (ok) {
+            r.r.q = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + kblk) * 16));
+            r.r.d = reinterpret_cast<const uint16_t*>(a.b)[(int64_t)n * nb + kblk];
+        } else {
+            r.r.q = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+            r.r.d = 0;
+        }
+    } else if constexpr (WF == WF_AFFINE4) {
+        if (ok) {
+            r.r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + (int64_t)kblk * 16));
+            const int64_t gi = (int64_t)n * (a.K / 64) + (kblk >> 1);
+            r.r.s = reinterpret_cast<const uint16_t*>(a.b)[gi];
+            r.r.b = reinterpret_cast<const uint16_t*>(a.c)[gi];
+        } else {
+            r.r.q = u32x4_t{0u, 0u, 0u, 0u};
+            r.r.s = 0;
+            r.r.b = 0;
+        }
+    } else {
+        if (ok) {
+            const u32x4_t* w = reinterpret_cast<const u32x4_t*>(
+                reinterpret_cast<const uint16_t*>(a.a) + (int64_t)n * a.K + (int64_t)kblk * 32);
+#pragma unroll
+            for (int t = 0; t < 4; t++) r.h[t] = w[t];
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; t++) r.h[t] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+    }
+    return r;
+}
+
+// Elements 8t..8t+7 of the lane's block as 8 binary16 values, t = 0..3.
+template <int WF>
+__device__ __forceinline__ void sk_frag(const SkRaw<WF>& r, u32x4_t (&out)[4]) {
+    if constexpr (WF == WF_Q4_0) {
+        const half2_t dd = as_h2(r.r.d | (r.r.d << 16));
+        // t = 0: low nibbles of bytes 0..7, t = 1: low of 8..15,
+        // t = 2: high nibbles of bytes 0..7, t = 3: high of 8..15
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int w = 0; w < 2; w++) {
+                const uint32_t word = r.r.q[2 * h + w];
+                const uint32_t t01 = perm(word, 0x0C010C00u);
+                const uint32_t t23 = perm(word, 0x0C030C02u);
+                out[h][2 * w + 0] = q4_pair(t01, dd);
+                out[h][2 * w + 1] = q4_pair(t23, dd);
+                out[2 + h][2 * w + 0] = q4_pair(t01 >> 4, dd);
+                out[2 + h][2 * w + 1] = q4_pair(t23 >> 4, dd);
+            }
+        }
+    } else if constexpr (WF == WF_AFFINE4) {
+        // element 8t+v sits in word t: byte v/2, low nibble for even v
+        RawAff lo, hi;
+        lo.s = hi.s = r.r.s;
+        lo.b = hi.b = r.r.b;
+        lo.q = u32x2_t{r.r.q[0], r.r.q[1]};
+        hi.q = u32x2_t{r.r.q[2], r.r.q[3]};
+        const Frag16 f0 = affine_frag(lo);   // s[0] = word 0, s[1] = word 1
+        const Frag16 f1 = affine_frag(hi);
+        out[0] = f0.s[0];
+        out[1] = f0.s[1];
+        out[2] = f1.s[0];
+        out[3] = f1.s[1];
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; t++) out[t] = r.h[t];
+    }
+}
+
+template <int WF, int MT, int NT, int XDT, int YDT>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const GemmArgs a) {
+    __shared__ float red[3][MT * 16 * NT * 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int n0 = blockIdx.x * (NT * 16);
+    const int nb = a.K / 32;
+    const int nchunks = (nb + 3) / 4;
+
+    floatx4_t acc[MT][NT];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) acc[mi][ni] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int c = wave; c < nchunks; c += 4) {
+        const int kblk = c * 4 + g;
+        const bool kok = kblk < nb;
+        SkRaw<WF> raw[NT];
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) {
+            const int n = n0 + ni * 16 + j;
+            raw[ni] = sk_load<WF>(a, n, kblk, kok && n < a.N);
+        }
+        // X fragments: row i = mi*16 + j, 32 values of block kblk
+        u32x4_t xa[MT][4];
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++) {
+            const int m = mi * 16 + j;
+            const bool ok = kok && m < a.M;
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+                xa[mi][t] = load_x8<XDT>(a.x, (int64_t)m * a.K + (int64_t)kblk * 32 + 8 * t, ok);
+        }
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) {
+            u32x4_t bfr[4];
+            sk_frag<WF>(raw[ni], bfr);
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+#pragma unroll
+                for (int mi = 0; mi < MT; mi++)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(half8_t, xa[mi][t]), __builtin_bit_cast(half8_t, bfr[t]), acc[mi][ni], 0, 0,
+                        0);
+        }
+    }
+
+    // fixed-order reduction over the 4 K-splitting waves: out = w0 + w1 + w2 + w3
+    // lane holds column j, rows 4*g + v of each 16x16 tile
+    if (wave > 0) {
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+                for (int v = 0; v < 4; v++)
+                    red[wave - 1][((mi * 16 + 4 * g + v) * NT + ni) * 16 + j] = acc[mi][ni][v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) {
+                const int n = n0 + ni * 16 + j;
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const int r = mi * 16 + 4 * g + v;
+                    const int idx = (r * NT + ni) * 16 + j;
+                    float t = acc[mi][ni][v];
+                    t += red[0][idx];
+                    t += red[1][idx];
+                    t += red[2][idx];
+                    if (n < a.N && r < a.M) store_y(a.y, YDT, (int64_t)r * a.N + n, t);
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int WF, int MT, int NT, int XDT, int YDT>
+static void launch_mfma_t(GemmArgs ga, hipStream_t s) {
+    ga.m_tiles = (ga.M + MT * 32 - 1) / (MT * 32);
+    ga.n_tiles = (ga.N + 4 * NT * 32 - 1) / (4 * NT * 32);
+    const dim3 grid((unsigned)(ga.m_tiles * ga.n_tiles)), block(256);
+    hipLaunchKernelGGL((k_gemm_mfma<WF, MT, NT, XDT, YDT>), grid, block, 0, s, ga);
+}
+
+template <int WF, int XDT, int YDT>
+static void launch_mfma_m(GemmArgs ga, hipStream_t s) {
+    // fewer rows per tile at moderate M keeps the grid above the CU count
+    if (ga.M <= 32) launch_mfma_t<WF, 1, 2, XDT, YDT>(ga, s);
+    else if (ga.M <= 1024) launch_mfma_t<WF, 2, 2, XDT, YDT>(ga, s);
+    else launch_mfma_t<WF, 4, 2, XDT, YDT>(ga, s);
+}
+
+template <int WF>
+static void launch_mfma_w(GemmArgs ga, int xdt, int ydt, hipStream_t s) {
+    if (xdt == DT_BF16) {
+        if (ydt == DT_BF16) launch_mfma_m<WF, DT_BF16, DT_BF16>(ga, s);
+        else launch_mfma_m<WF, DT_BF16, DT_F32>(ga, s);
+    } else {
+        if (ydt == DT_BF16) launch_mfma_m<WF, DT_F32, DT_BF16>(ga, s);
+        else launch_mfma_m<WF, DT_F32, DT_F32>(ga, s);
+    }
+}
+
+hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
+                            int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    GemmArgs ga{};
+    ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
+    ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
+    if (wfmt == WF_Q4_0) launch_mfma_w<WF_Q4_0>(ga, xdt, ydt, s);
+    else if (wfmt == WF_AFFINE4) launch_mfma_w<WF_AFFINE4>(ga, xdt, ydt, s);
+    else launch_mfma_w<WF_DENSE16>(ga, xdt, ydt, s);
+    return hipGetLastError();
+}
+
+template <int WF, int MT, int NT, int XDT, int YDT>
+static void launch_skinny_t(GemmArgs ga, hipStream_t s) {
+    const dim3 grid((unsigned)((ga.N + NT * 16 - 1) / (NT * 16))), block(256);
+    hipLaunchKernelGGL((k_gemm_skinny<WF, MT, NT, XDT, YDT>), grid, block, 0, s, ga);
+}
+
+template <int WF, int XDT, int YDT>
+static void launch_skinny_m(GemmArgs ga, hipStream_t s) {
+    if (ga.M <= 16) launch_skinny_t<WF, 1, 2, XDT, YDT>(ga, s);
+    else if (ga.M <= 32) launch_skinny_t<WF, 2, 2, XDT, YDT>(ga, s);
+    else launch_skinny_t<WF, 4, 1, XDT, YDT>(ga, s);
+}
+
+template <int WF>
+static void launch_skinny_w(GemmArgs ga, int xdt, int ydt, hipStream_t s) {
+    if (xdt == DT_BF16) {
+        if (ydt == DT_BF16) launch_skinny_m<WF, DT_BF16, DT_BF16>(ga, s);
+        else launch_skinny_m<WF, DT_BF16, DT_F32>(ga, s);
+    } else {
+        if (ydt == DT_BF16) launch_skinny_m<WF, DT_F32, DT_BF16>(ga, s);
+        else launch_skinny_m<WF, DT_F32, DT_F32>(ga, s);
+    }
+}
+
+hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
+                              int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    if (M > 64) return hipErrorInvalidValue;
+    GemmArgs ga{};
+    ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
+    ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
+    if (wfmt == WF_Q4_0) launch_skinny_w<WF_Q4_0>(ga, xdt, ydt, s);
+    else if (wfmt == WF_AFFINE4) launch_skinny_w<WF_AFFINE4>(ga, xdt, ydt, s);
+    else launch_skinny_w<WF_DENSE16>(ga, xdt, ydt, s);
+    return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,40 @@
+// kernels.hpp -- launchers of the gfx950 kernels, called by the C ABI layer
+// (capi.cpp) after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+// dtype codes (same values as Q4_F32 / Q4_BF16 / Q4_F16 in include/q4.h)
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+hipError_t launch_q4_quantize(const void* w, int wdt, int64_t N, int64_t K, uint8_t* qs, uint16_t* d,
+                              hipStream_t s);
+hipError_t launch_q8_1_quantize(const void* x, int xdt, int64_t M, int64_t K, int8_t* qs, uint16_t* ds,
+                                hipStream_t s);
+hipError_t launch_affine4_quantize(const void* w, int wdt, int64_t N, int64_t K, int64_t G, uint8_t* wq,
+                                   uint16_t* sc, uint16_t* bi, hipStream_t s);
+hipError_t launch_q4_dequantize(const uint8_t* qs, const uint16_t* d, int64_t N, int64_t K, void* out, int odt,
+                                hipStream_t s);
+hipError_t launch_affine4_dequantize(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, int64_t G,
+                                     int64_t N, int64_t K, void* out, int odt, hipStream_t s);
+
+// Decode GEMV over one or two weight matrices sharing a Q8_1 activation.
+hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
+                          const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
+                          const int8_t* x_qs, const uint16_t* x_ds, int64_t M, int64_t K, hipStream_t s);
+
+// GEMM paths.  fmt: 0 = Q4_0 planes (a = qs, b = d), 1 = affine (a = q,
+// b = scales, c = biases), 2 = dense binary16 W (a = w).
+enum : int { WF_Q4_0 = 0, WF_AFFINE4 = 1, WF_DENSE16 = 2 };
+
+hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* c,
+                            const void* x, int xdt, void* y, int ydt,
+                            int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void* c,
+                              const void* x, int xdt, void* y, int ydt,
+                              int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+}  // namespace q4

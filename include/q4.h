@@ -1,0 +1,276 @@
+/*
+ * q4.h -- C ABI of the MI355X (gfx950) library for matrix multiply against
+ * 4-bit block-quantised weights:
+ *
+ *     Y[M,N] = X[M,K] . dequant(Wq)[N,K]^T
+ *
+ * W is stored [N,K] (rows are output features), the transpose=True
+ * convention of MLX's quantized_matmul (MLX issue #4621 "quantized_matmul
+ * takes 14-41% longer than dequantize + bf16 matmul at prefill sizes",
+ * Repro).  Two weight formats:
+ *
+ *   Q4_0 (GGUF block; named by llama.cpp PR "et-backend: Q4_0 matrix-engine
+ *   GEMM rewrite for prefill", Overview, and by "2026-05-06 Q4 sync-after
+ *   focused repro", Important source touch points):
+ *     blocks of 32 weights along K; a binary16 scale d and 16 bytes of
+ *     nibbles; w^ = (q - 8) * d.  Passed as two planes (structure of arrays):
+ *       w_qs : uint8  [N][K/32][16]   byte i = q_i | q_{i+16} << 4
+ *       w_d  : uint16 [N][K/32]       binary16 bit patterns
+ *
+ *   Affine 4-bit, group 64 (MLX quantize / dequantize, same MLX page, Repro):
+ *     w^ = q * s + b, q unsigned 4-bit, s and b bfloat16, one pair per group.
+ *       w_q    : uint8  [N][K/2]       byte i = q_{2i} | q_{2i+1} << 4
+ *       scales : uint16 [N][K/G]       bfloat16 bit patterns
+ *       biases : uint16 [N][K/G]       bfloat16 bit patterns
+ *
+ *   Q8_1 activations (the q4_0 x q8_1 decode kernels and Q8 cache of the
+ *   repro page, Important source touch points / Quality-cleared launch
+ *   recipe): blocks of 32 along K, d = max|x|/127, q = round(x/d),
+ *   s = d * sum(q), as two planes:
+ *       x_qs : int8   [M][K]
+ *       x_ds : uint16 [M][K/32][2]    {binary16 d, binary16 s}
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are DEVICE pointers owned by the caller (hipMalloc'd
+ *     or framework-allocated), contiguous row-major, no strides.  The library
+ *     never frees, keeps or allocates them.
+ *   - Plane pointers must be 16-byte aligned (Q4_ERR_ALIGN otherwise).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue kernels on it: no device synchronisation, no host<->device
+ *     copy and no allocation, so they may be captured into a HIP graph.
+ *   - Every argument is validated on the host before any HIP call; a failed
+ *     check returns its status code and enqueues nothing.
+ *   - M == 0 or N == 0 is a no-op that returns Q4_OK once the sizes and dtype
+ *     codes are valid; the pointers are not looked at then (empty tensors may
+ *     have NULL data pointers).
+ *   - K must be a positive multiple of 32 (Q4_0 / Q8_1) or of the group size
+ *     (affine).  N and K are limited to 2^30, M to 2^30.
+ *   - Outputs of float type are not bit-reproducible against other
+ *     summation orders, but every call is deterministic: the same inputs
+ *     give the same bits (no atomics, fixed reduction order).
+ *   - Thread-safety: calls on different streams may run concurrently; the
+ *     dispatch settings (q4_set_dispatch) are process-wide.
+ */
+#ifndef GEMV_Q4_AFFINE_AMD_Q4_H
+#define GEMV_Q4_AFFINE_AMD_Q4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+#define Q4_OK            0
+#define Q4_ERR_NULL     -1   /* a required pointer is NULL                     */
+#define Q4_ERR_SHAPE    -2   /* M/N/K out of range or not a block multiple      */
+#define Q4_ERR_ALIGN    -3   /* a plane pointer is not 16-byte aligned          */
+#define Q4_ERR_DTYPE    -4   /* unsupported dtype code                          */
+#define Q4_ERR_HIP      -5   /* a HIP launch or runtime call failed             */
+#define Q4_ERR_ARG      -6   /* other invalid argument (dispatch key, path...)  */
+#define Q4_ERR_WORKSPACE -7  /* forced dequantise path without enough workspace */
+
+/* ---- dtype codes ---------------------------------------------------------- */
+#define Q4_F32   0
+#define Q4_BF16  1
+#define Q4_F16   2
+
+/* ---- formats and dispatch paths ------------------------------------------- */
+#define Q4_FMT_Q4_0     0
+#define Q4_FMT_AFFINE4  1
+
+#define Q4_PATH_GEMV          0  /* integer-dot GEMV on Q8_1 activations (q4_gemv)     */
+#define Q4_PATH_SKINNY        1  /* fused, weights streamed once, small M              */
+#define Q4_PATH_MFMA          2  /* fused dequant-in-LDS MFMA GEMM, large M             */
+#define Q4_PATH_DEQUANT_GEMM  3  /* dequantise to a dense fp16 W, then dense MFMA GEMM  */
+
+/* dispatch keys for q4_set_dispatch / q4_get_dispatch */
+#define Q4_KEY_SKINNY_MAX_M    0  /* q4_gemm/affine4_gemm: M <= this -> SKINNY          */
+#define Q4_KEY_DEQUANT_MIN_M   1  /* M >= this (and workspace given) -> DEQUANT_GEMM    */
+#define Q4_KEY_FORCE_PATH      2  /* -1 = automatic, else a Q4_PATH_* for q4_gemm etc.  */
+
+/* Largest M that q4_gemv / q4_gemv_fused2 accept. */
+#define Q4_GEMV_MAX_M 16
+
+/* ======================================================================== */
+/* Quantisers                                                                */
+/* ======================================================================== */
+
+/*
+ * q4_quantize -- Q4_0-quantise a weight matrix (one-time weight preparation).
+ * Defines (reading of the GGUF Q4_0 block; the pages name the format but do
+ * not print the rule): per block of 32 weights along K, max = the first
+ * weight of largest magnitude (signed), d = max / -8 (binary32),
+ * q_j = min(15, floor(w_j * (1/d) + 8.5)) with separate binary32 multiply and
+ * add (q = 8 for an all-zero block), stored d = binary16(d) (RNE; an
+ * all-zero block stores -0.0).  Bit-exact, deterministic.
+ *   w       : device, [N][K] of w_dtype (Q4_F32 or Q4_BF16)
+ *   w_qs    : device out, uint8 [N][K/32][16]
+ *   w_d     : device out, uint16 [N][K/32]
+ * Errors: NULL, SHAPE (K % 32, sizes), ALIGN, DTYPE, HIP.
+ * Inputs must be finite; blocks whose largest magnitude lies in (0, 2^-125)
+ * are outside the domain (1/d overflows binary32).
+ */
+int q4_quantize(const void* w, int w_dtype, int64_t N, int64_t K,
+                uint8_t* w_qs, uint16_t* w_d, void* stream);
+
+/*
+ * q8_1_quantize_act -- quantise activations to Q8_1 once per token, for reuse
+ * by every GEMV that reads them (the Q8 cache of the repro page,
+ * Quality-cleared launch recipe).  Per block of 32: amax = max|x|,
+ * d = amax/127, q = round-half-away(x * (1/d)), s = binary16(d * sum q),
+ * d stored as binary16 (binary32 arithmetic throughout).  Bit-exact.
+ *   x       : device, [M][K] of x_dtype (Q4_F32 or Q4_BF16)
+ *   x_qs    : device out, int8 [M][K]
+ *   x_ds    : device out, uint16 [M][K/32][2] = {d, s}
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ */
+int q8_1_quantize_act(const void* x, int x_dtype, int64_t M, int64_t K,
+                      int8_t* x_qs, uint16_t* x_ds, void* stream);
+
+/*
+ * affine4_quantize -- affine 4-bit quantisation (MLX quantize with bits=4;
+ * the page shows the API only, the rule is the min/max reading): per group of
+ * G weights (bfloat16, or binary32 first rounded to bfloat16): mn/mx = group
+ * min/max (a zero extreme taken as +0), s = bfloat16((mx - mn)/15),
+ * b = bfloat16(mn), q = clamp(floor((w - b)/s + 0.5), 0, 15) in binary32
+ * (q = 0 when s == 0).  Bit-exact.
+ *   w          : device, [N][K] of w_dtype (Q4_BF16 or Q4_F32)
+ *   group_size : 64 (other values: Q4_ERR_SHAPE)
+ *   w_q        : device out, uint8 [N][K/2]
+ *   scales, biases : device out, uint16 [N][K/group_size] (bfloat16 bits)
+ */
+int affine4_quantize(const void* w, int w_dtype, int64_t N, int64_t K, int64_t group_size,
+                     uint8_t* w_q, uint16_t* scales, uint16_t* biases, void* stream);
+
+/* ======================================================================== */
+/* Dequantisers (the dequantise-then-GEMM path of the MLX page, Summary and  */
+/* Effect on a model)                                                        */
+/* ======================================================================== */
+
+/*
+ * q4_dequantize -- dense W^ [N][K] = (q - 8) * d rounded to out_dtype:
+ * binary16 or bfloat16 (RNE of the exact binary32 value), or binary32 (exact).
+ *   out : device out, [N][K] of out_dtype (Q4_F16, Q4_BF16 or Q4_F32)
+ */
+int q4_dequantize(const uint8_t* w_qs, const uint16_t* w_d, int64_t N, int64_t K,
+                  void* out, int out_dtype, void* stream);
+
+/*
+ * affine4_dequantize -- dense W^ = q*s + b: the binary32 value nearest the
+ * exact one, then RNE into out_dtype (Q4_F16, Q4_BF16 or Q4_F32).
+ */
+int affine4_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases,
+                       int64_t group_size, int64_t N, int64_t K,
+                       void* out, int out_dtype, void* stream);
+
+/* ======================================================================== */
+/* Decode GEMV (M small): integer block dots on Q8_1 activations             */
+/* ======================================================================== */
+
+/*
+ * q4_gemv -- y[m][n] = sum_b d4[n][b] * d8[m][b] * isum[m][n][b], with the
+ * exact int32 block dot isum = sum_{j<32} (q4_j - 8) * q8_j, scaled and
+ * accumulated in binary32 (the decode "vecdot" route of the ET-SoC-1 PR,
+ * Overview; the q4_0 x q8_1 mul_mat_vec_q kernel of the repro page,
+ * Important source touch points).
+ *   w_qs, w_d : device, Q4_0 planes of W [N][K]
+ *   x_qs, x_ds: device, Q8_1 planes of X [M][K] (from q8_1_quantize_act)
+ *   y         : device out, float [M][N]
+ *   1 <= M <= Q4_GEMV_MAX_M (else Q4_ERR_SHAPE; M == 0 is a no-op).
+ */
+int q4_gemv(const uint8_t* w_qs, const uint16_t* w_d,
+            const int8_t* x_qs, const uint16_t* x_ds,
+            float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * q4_gemv_fused2 -- two GEMVs that share one Q8_1 activation (gate+up, or
+ * K+V), in one launch that reads the activation once (the fused2 MMVQ kernel
+ * of the repro page, Important source touch points).  N0 != N1 is allowed.
+ * Results are bit-identical to two q4_gemv calls.
+ *   y0 : device out, float [M][N0];  y1 : device out, float [M][N1]
+ */
+int q4_gemv_fused2(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0,
+                   const uint8_t* w1_qs, const uint16_t* w1_d, int64_t N1,
+                   const int8_t* x_qs, const uint16_t* x_ds,
+                   float* y0, float* y1, int64_t M, int64_t K, void* stream);
+
+/* ======================================================================== */
+/* GEMM (any M): bf16 / f32 activations                                      */
+/* ======================================================================== */
+
+/*
+ * q4_gemm -- Y = X . dequant(Wq)^T for Q4_0 weights, fp32 accumulation
+ * (the prefill matrix-engine GEMM of the ET-SoC-1 PR, Overview).  The M
+ * dispatch (q4_dispatch_path) picks SKINNY, MFMA or DEQUANT_GEMM.  The fused
+ * paths multiply on the matrix cores in binary16: X is converted to binary16
+ * (exact for bfloat16 values with 2^-24 <= |x| <= 65504 at 8-bit precision)
+ * and the weights are dequantised to binary16 (relative rounding <= 2^-11);
+ * inputs outside binary16 range are outside the fused paths' domain.
+ *   x         : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32)
+ *   y         : device out, [M][N] of y_dtype (Q4_BF16 RNE, or Q4_F32)
+ *   workspace : device scratch for the DEQUANT_GEMM path only
+ *               (q4_gemm_workspace_size bytes), or NULL; without it the
+ *               automatic dispatch never picks DEQUANT_GEMM, and forcing that
+ *               path returns Q4_ERR_WORKSPACE.
+ */
+int q4_gemm(const uint8_t* w_qs, const uint16_t* w_d,
+            const void* x, int x_dtype, void* y, int y_dtype,
+            int64_t M, int64_t N, int64_t K,
+            void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * affine4_gemm -- Y = X . dequant(Wq)^T for affine 4-bit group-64 weights
+ * (MLX quantized_matmul with transpose=True, bits=4, group_size=64; MLX page,
+ * Repro).  Same dispatch, precision and workspace rules as q4_gemm.
+ *   group_size : 64 only (else Q4_ERR_SHAPE)
+ */
+int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases,
+                 int64_t group_size, const void* x, int x_dtype, void* y, int y_dtype,
+                 int64_t M, int64_t N, int64_t K,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace the DEQUANT_GEMM path needs: N*K*2 (a dense binary16 W). */
+int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt);
+
+/*
+ * dense_gemm -- Y = X . W^T with a dense binary16 W [N][K] (the GEMM half of
+ * dequantise-then-GEMM; MLX page, Repro "jit"/"ref" timings).  Same MFMA
+ * tiles and X conversion as the fused paths.
+ *   w_f16 : device, uint16 [N][K] binary16 bits
+ */
+int dense_gemm(const void* x, int x_dtype, const uint16_t* w_f16, void* y, int y_dtype,
+               int64_t M, int64_t N, int64_t K, void* stream);
+
+/* ======================================================================== */
+/* Dispatch and housekeeping (host only, no HIP calls)                       */
+/* ======================================================================== */
+
+/*
+ * q4_dispatch_path -- the path q4_gemm (fmt Q4_FMT_Q4_0) or affine4_gemm
+ * (Q4_FMT_AFFINE4) takes for this shape, given whether a large enough
+ * workspace is supplied: Q4_PATH_SKINNY / Q4_PATH_MFMA / Q4_PATH_DEQUANT_GEMM,
+ * or a negative status for invalid arguments.  Token-count thresholds follow
+ * the pages' pattern (ET-SoC-1 PR Overview: one token goes to the vector-dot
+ * kernel; MLX page, Effect on a model: dequantise-then-matmul only from a
+ * token count up; vllm.cpp issue #838, Scope: a clamped token-count gate).
+ * Defaults come from measurement; the environment variables
+ * Q4_SKINNY_MAX_M, Q4_DEQUANT_MIN_M and Q4_FORCE_PATH, read once, override
+ * them (clamped), and q4_set_dispatch overrides both.
+ */
+int q4_dispatch_path(int64_t M, int64_t N, int64_t K, int fmt, int have_workspace);
+
+int q4_set_dispatch(int key, int64_t value);
+int q4_get_dispatch(int key, int64_t* value);
+
+/* Static text for a status code. */
+const char* q4_status_string(int status);
+
+/* Library version string. */
+const char* q4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMV_Q4_AFFINE_AMD_Q4_H */

@@ -1,0 +1,201 @@
+"""Host-only checks of the C ABI: they run without a GPU.
+
+* libq4.so loads and exports every function include/q4.h declares;
+* every validation error is returned before any HIP call (fake, never
+  dereferenced pointers are enough to reach them);
+* the M-threshold dispatch predicate at its boundaries, through the API and
+  through the environment overrides (read once per process, clamped).
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from gemv_q4_affine_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4.h")
+
+# fake device pointers: 16-byte aligned, never dereferenced by these tests
+P = 0x10000
+P2 = 0x20000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) == 16, names
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in q4.h but not exported"
+    # and the binding covers them all with a signature
+    assert set(names) == set(B.SIGNATURES), set(names) ^ set(B.SIGNATURES)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\S+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in B.version()
+    for code in range(-7, 1):
+        assert B.status_string(code) and B.status_string(code) != "unknown status"
+    assert B.status_string(-99) == "unknown status"
+
+
+L = None
+
+
+def lib():
+    global L
+    if L is None:
+        L = B.lib()
+    return L
+
+
+def test_quantize_validation():
+    q = lib().q4_quantize
+    assert q(None, B.Q4_F32, 4, 64, P, P, None) == B.Q4_ERR_NULL
+    assert q(P, B.Q4_F32, 4, 64, None, P, None) == B.Q4_ERR_NULL
+    assert q(P, B.Q4_F32, 4, 48, P, P, None) == B.Q4_ERR_SHAPE
+    assert q(P, B.Q4_F32, 4, 0, P, P, None) == B.Q4_ERR_SHAPE
+    assert q(P, B.Q4_F32, -1, 64, P, P, None) == B.Q4_ERR_SHAPE
+    assert q(P, B.Q4_F32, 1 << 31, 64, P, P, None) == B.Q4_ERR_SHAPE
+    assert q(P, B.Q4_F16, 4, 64, P, P, None) == B.Q4_ERR_DTYPE
+    assert q(P, 7, 4, 64, P, P, None) == B.Q4_ERR_DTYPE
+    assert q(MIS, B.Q4_F32, 4, 64, P, P, None) == B.Q4_ERR_ALIGN
+    assert q(P, B.Q4_F32, 0, 64, P, P, None) == B.Q4_OK          # N == 0: no-op, no HIP call
+    a = lib().q8_1_quantize_act
+    assert a(P, B.Q4_BF16, 1, 40, P, P, None) == B.Q4_ERR_SHAPE
+    assert a(P, B.Q4_BF16, 1, 64, P, MIS, None) == B.Q4_ERR_ALIGN
+    assert a(P, B.Q4_F16, 1, 64, P, P, None) == B.Q4_ERR_DTYPE
+    assert a(P, B.Q4_BF16, 0, 64, P, P, None) == B.Q4_OK
+    f = lib().affine4_quantize
+    assert f(P, B.Q4_BF16, 4, 64, 32, P, P, P, None) == B.Q4_ERR_SHAPE
+    assert f(P, B.Q4_BF16, 4, 96, 64, P, P, P, None) == B.Q4_ERR_SHAPE
+    assert f(P, B.Q4_BF16, 4, 128, 64, P, P, None, None) == B.Q4_ERR_NULL
+    d = lib().q4_dequantize
+    assert d(P, P, 4, 64, P, 9, None) == B.Q4_ERR_DTYPE
+    assert d(P, P, 4, 65, P, B.Q4_F16, None) == B.Q4_ERR_SHAPE
+    e = lib().affine4_dequantize
+    assert e(P, P, P, 128, 4, 128, P, B.Q4_F16, None) == B.Q4_ERR_SHAPE
+
+
+def test_gemv_validation():
+    g = lib().q4_gemv
+    assert g(P, P, P, P, P, 17, 8, 64, None) == B.Q4_ERR_SHAPE            # M above the GEMV limit
+    assert g(P, P, P, P, P, 1, 8, 50, None) == B.Q4_ERR_SHAPE
+    assert g(P, P, P, P, None, 1, 8, 64, None) == B.Q4_ERR_NULL
+    assert g(P, P, MIS, P, P, 1, 8, 64, None) == B.Q4_ERR_ALIGN
+    assert g(P, P, P, P, P, 0, 8, 64, None) == B.Q4_OK                  # M == 0
+    assert g(P, P, P, P, P, 3, 0, 64, None) == B.Q4_OK                  # N == 0
+    f = lib().q4_gemv_fused2
+    assert f(P, P, 8, P, P, 8, P, P, P, P, 17, 64, None) == B.Q4_ERR_SHAPE
+    assert f(P, P, 8, P, P, -8, P, P, P, P, 1, 64, None) == B.Q4_ERR_SHAPE
+    assert f(P, P, 8, None, P, 8, P, P, P, P, 1, 64, None) == B.Q4_ERR_NULL
+    assert f(P, P, 8, P, P, 8, P, P, P, P, 0, 64, None) == B.Q4_OK
+
+
+def test_gemm_validation():
+    g = lib().q4_gemm
+    assert g(P, P, P, B.Q4_F16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_DTYPE
+    assert g(P, P, P, B.Q4_BF16, P, B.Q4_F16, 4, 8, 64, None, 0, None) == B.Q4_ERR_DTYPE
+    assert g(P, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 60, None, 0, None) == B.Q4_ERR_SHAPE
+    assert g(P, P, None, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_NULL
+    assert g(P, P, P, B.Q4_BF16, MIS, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_ALIGN
+    assert g(P, P, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None, 0, None) == B.Q4_OK
+    a = lib().affine4_gemm
+    assert a(P, P, P, 32, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_SHAPE
+    assert a(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, None, 0, None) == B.Q4_ERR_SHAPE
+    assert a(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 4, 0, 128, None, 0, None) == B.Q4_OK
+    assert lib().q4_gemm_workspace_size(2048, 12288, 4096, 0) == 12288 * 4096 * 2
+    d = lib().dense_gemm
+    assert d(P, B.Q4_BF16, P, P, B.Q4_BF16, 4, 8, 48, None) == B.Q4_ERR_SHAPE
+    assert d(P, B.Q4_BF16, None, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_NULL
+
+
+def test_forced_dequant_path_without_workspace_is_an_error():
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+    try:
+        g = lib().q4_gemm
+        assert g(P, P, P, B.Q4_BF16, P, B.Q4_BF16, 512, 256, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
+        assert g(P, P, P, B.Q4_BF16, P, B.Q4_BF16, 512, 256, 64, P2, 100, None) == B.Q4_ERR_WORKSPACE
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+
+
+def test_dispatch_predicate_boundaries():
+    skinny = B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M)
+    assert 1 <= skinny <= 64
+    for fmt, K in ((B.Q4_FMT_Q4_0, 4096), (B.Q4_FMT_AFFINE4, 4096)):
+        assert B.q4_dispatch_path(1, 12288, K, fmt) == B.Q4_PATH_SKINNY
+        assert B.q4_dispatch_path(skinny, 12288, K, fmt) == B.Q4_PATH_SKINNY
+        assert B.q4_dispatch_path(skinny + 1, 12288, K, fmt) == B.Q4_PATH_MFMA
+        assert B.q4_dispatch_path(8192, 12288, K, fmt) == B.Q4_PATH_MFMA
+    assert B.q4_dispatch_path(4, 8, 48, B.Q4_FMT_Q4_0) == B.Q4_ERR_SHAPE
+    assert B.q4_dispatch_path(4, 8, 96, B.Q4_FMT_AFFINE4) == B.Q4_ERR_SHAPE
+    assert B.q4_dispatch_path(4, 8, 64, 5) == B.Q4_ERR_ARG
+    # a dequantise threshold only applies with a workspace
+    old = B.q4_get_dispatch(B.Q4_KEY_DEQUANT_MIN_M)
+    try:
+        B.q4_set_dispatch(B.Q4_KEY_DEQUANT_MIN_M, 512)
+        assert B.q4_dispatch_path(511, 12288, 4096, have_workspace=True) == B.Q4_PATH_MFMA
+        assert B.q4_dispatch_path(512, 12288, 4096, have_workspace=True) == B.Q4_PATH_DEQUANT_GEMM
+        assert B.q4_dispatch_path(513, 12288, 4096, have_workspace=False) == B.Q4_PATH_MFMA
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_DEQUANT_MIN_M, old)
+    # set/get clamp and reject
+    B.q4_set_dispatch(B.Q4_KEY_SKINNY_MAX_M, 1000)
+    assert B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M) == 64
+    B.q4_set_dispatch(B.Q4_KEY_SKINNY_MAX_M, skinny)
+    with pytest.raises(B.Q4Error):
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, 9)
+    with pytest.raises(B.Q4Error):
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_GEMV)
+    with pytest.raises(B.Q4Error):
+        B.q4_set_dispatch(77, 1)
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
+    try:
+        assert B.q4_dispatch_path(1, 64, 64) == B.Q4_PATH_MFMA
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+
+
+_ENV_PROBE = r"""
+import sys
+sys.path.insert(0, {root!r})
+from gemv_q4_affine_amd import binding as B
+print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUANT_MIN_M),
+      B.q4_get_dispatch(B.Q4_KEY_FORCE_PATH),
+      B.q4_dispatch_path(19, 4096, 4096), B.q4_dispatch_path(64, 4096, 4096, have_workspace=True))
+"""
+
+
+@pytest.mark.parametrize("env,expect", [
+    ({"Q4_SKINNY_MAX_M": "1"}, (1, None, -1, B.Q4_PATH_MFMA, B.Q4_PATH_MFMA)),
+    ({"Q4_SKINNY_MAX_M": "500"}, (64, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_SKINNY)),
+    ({"Q4_SKINNY_MAX_M": "-3"}, (0, None, -1, B.Q4_PATH_MFMA, B.Q4_PATH_MFMA)),
+    ({"Q4_SKINNY_MAX_M": "8", "Q4_DEQUANT_MIN_M": "64"}, (8, 64, -1, B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM)),
+    ({"Q4_FORCE_PATH": "3"}, (None, None, 3, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM)),
+    ({"Q4_FORCE_PATH": "17"}, (None, None, 3, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM)),
+    ({"Q4_FORCE_PATH": "junk"}, (None, None, -1, None, None)),
+])
+def test_dispatch_environment_overrides(env, expect):
+    full = dict(os.environ)
+    for k in ("Q4_SKINNY_MAX_M", "Q4_DEQUANT_MIN_M", "Q4_FORCE_PATH"):
+        full.pop(k, None)
+    full.update(env)
+    out = subprocess.run([sys.executable, "-c", _ENV_PROBE.format(root=ROOT)], env=full, capture_output=True,
+                         text=True, check=True).stdout.split()
+    got = tuple(int(v) for v in out)
+    for g, e in zip(got, expect):
+        if e is not None:
+            assert g == e, (env, got, expect)

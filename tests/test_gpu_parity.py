@@ -1,0 +1,459 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: bit-exact for codes, packing, dequantised values and integer block dots;
+relative Frobenius error <= 2e-3 against the binary64 oracle for float
+outputs (bf16 or fp32 output).  GEMV outputs are fp32 and are also held to a
+tighter 1e-5, derived from fp32 accumulation of K/32 exact block terms.
+
+Inputs come from gemv_q4_affine_amd.synth (seeded); every expected value is
+computed by oracle/ on the same host arrays.  Full-size configurations are
+checked on sampled outputs the oracle computes one by one.
+"""
+import hashlib
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemv_q4_affine_amd import binding as B
+from gemv_q4_affine_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BAR = 2e-3          # relative Frobenius bar for float outputs
+GEMV_TIGHT = 1e-5   # fp32 GEMV against binary64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor, dtype=None) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.view(torch.int16)
+    a = t.numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+def bf16_dev(x_f32: np.ndarray) -> torch.Tensor:
+    return dev(synth.bf16_bits(x_f32)).view(torch.bfloat16)
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel(y, ref):
+    return oracle.rel_frobenius(y, ref)
+
+
+# ---------------------------------------------------------------------------
+# quantisers and dequantisers: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(256, 512), (37, 96), (1, 32), (12288, 4096)])
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+def test_q4_quantize_bitexact(N, K, wdt):
+    say(f"q4_quantize N={N} K={K} {wdt}")
+    rng = np.random.default_rng(N + K)
+    W = synth.weights(rng, N, K)
+    W[0, :8] = 0.0                      # a partly zero block
+    if N > 1:
+        W[1, :32] = 0.0                 # an all-zero block (d = -0)
+    if wdt == "bf16":
+        Wb = synth.bf16_bits(W)
+        Wref = synth.bf16_bits_to_f32(Wb)
+        wt = dev(Wb).view(torch.bfloat16)
+    else:
+        Wref = W
+        wt = dev(W)
+    qs, d = B.q4_quantize(wt)
+    torch.cuda.synchronize()
+    rqs, rd = oracle.q4_0_quantize(Wref)
+    assert np.array_equal(host(qs), rqs)
+    assert np.array_equal(host(d, np.uint16), rd)
+
+
+def _golden_q4_matrix():
+    path = os.path.join(os.path.dirname(__file__), "golden", "q4_0_blocks.txt")
+    cases = []
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        name, ws, dhex, qhex = [p.strip() for p in line.split("|")]
+        w = np.zeros(32, np.float32)
+        if ws:
+            for item in ws.split(","):
+                i, v = item.split("=")
+                w[int(i)] = np.float32(float(v))
+        cases.append((w, int(dhex, 16), bytes.fromhex(qhex.replace(" ", ""))))
+    return cases
+
+
+def test_q4_quantize_golden_blocks_on_gpu():
+    cases = _golden_q4_matrix()
+    W = np.concatenate([c[0] for c in cases]).reshape(1, -1)
+    qs, d = B.q4_quantize(dev(W))
+    torch.cuda.synchronize()
+    qs, d = host(qs), host(d, np.uint16)
+    for b, (_, dbits, qbytes) in enumerate(cases):
+        assert int(d[0, b]) == dbits
+        assert bytes(qs[0, b]) == qbytes
+
+
+@pytest.mark.parametrize("M,K", [(1, 4096), (7, 544), (16, 2048), (3, 32)])
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+def test_q8_1_quantize_bitexact(M, K, xdt):
+    say(f"q8_1 M={M} K={K} {xdt}")
+    rng = np.random.default_rng(M * 7 + K)
+    X = synth.activations(rng, M, K)
+    X[0, :32] = 0.0
+    X[-1, 32 % K:64 % K or K] *= 1e-3
+    if xdt == "bf16":
+        Xb = synth.bf16_bits(X)
+        Xref = synth.bf16_bits_to_f32(Xb)
+        xt = dev(Xb).view(torch.bfloat16)
+    else:
+        Xref, xt = X, dev(X)
+    qs, ds = B.q8_1_quantize_act(xt)
+    torch.cuda.synchronize()
+    rqs, rds = oracle.q8_1_quantize(Xref)
+    assert np.array_equal(host(qs), rqs)
+    assert np.array_equal(host(ds, np.uint16), rds)
+
+
+def test_q8_1_golden_halves():
+    # values with exact .5 products: d = 1 (amax 127) -> round half away from zero
+    x = np.zeros((1, 32), np.float32)
+    x[0, :6] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5]
+    qs, ds = B.q8_1_quantize_act(dev(x))
+    torch.cuda.synchronize()
+    assert host(qs)[0, :6].tolist() == [127, 3, -3, 1, -1, 2]
+    assert host(ds, np.uint16)[0, 0].tolist() == [0x3C00, 0x5808]
+
+
+@pytest.mark.parametrize("N,K", [(64, 128), (33, 192), (12288, 4096)])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_affine4_quantize_bitexact(N, K, wdt):
+    say(f"affine4_quantize N={N} K={K} {wdt}")
+    rng = np.random.default_rng(N * 3 + K)
+    W = synth.weights(rng, N, K)
+    W[0, :64] = 0.25                    # constant group: s = 0
+    Wb = synth.bf16_bits(W)
+    wt = dev(Wb).view(torch.bfloat16) if wdt == "bf16" else dev(W)
+    q, s, b = B.affine4_quantize(wt)
+    torch.cuda.synchronize()
+    # the f32 entry point first rounds to bf16 with the same RNE the oracle uses
+    rq, rs, rb = oracle.affine4_quantize(oracle.f32_to_bf16_bits(W), 64)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s, np.uint16), rs)
+    assert np.array_equal(host(b, np.uint16), rb)
+
+
+@pytest.mark.parametrize("N,K", [(37, 96), (12288, 4096)])
+def test_dequantize_bitexact(N, K):
+    say(f"dequantize N={N} K={K}")
+    rng = np.random.default_rng(5)
+    W = synth.weights(rng, N, K)
+    qs, d = oracle.q4_0_quantize(W)
+    tq, td = dev(qs), dev(d)
+    for kind, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        got = host(B.q4_dequantize(tq, td, out_dtype=dt), np.uint16)
+        assert np.array_equal(got, oracle.q4_0_dequantize_half(qs, d, kind)), kind
+    got32 = host(B.q4_dequantize(tq, td, out_dtype=torch.float32)).astype(np.float64)
+    assert np.array_equal(got32, oracle.q4_0_dequantize(qs, d))
+    if K % 64 == 0:
+        q, s, b = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+        aq, as_, ab = dev(q), dev(s), dev(b)
+        for kind, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+            got = host(B.affine4_dequantize(aq, as_, ab, out_dtype=dt), np.uint16)
+            assert np.array_equal(got, oracle.affine4_dequantize_half(q, s, b, kind)), kind
+        got32 = host(B.affine4_dequantize(aq, as_, ab, out_dtype=torch.float32))
+        assert np.array_equal(got32, oracle.affine4_dequantize(q, s, b).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# decode GEMV
+# ---------------------------------------------------------------------------
+
+def test_gemv_unit_scales_are_exact_integer_sums():
+    """d4 = d8 = 1: the fp32 output is the integer sum of block dots, bit-exact."""
+    rng = np.random.default_rng(31)
+    for (M, N, K) in [(1, 300, 4096), (3, 65, 32), (2, 129, 4128), (16, 17, 544)]:
+        say(f"gemv unit scales M={M} N={N} K={K}")
+        wqs = rng.integers(0, 256, (N, K // 32, 16), dtype=np.uint8)
+        wd = np.full((N, K // 32), 0x3C00, np.uint16)
+        xqs = rng.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+        xds = np.zeros((M, K // 32, 2), np.uint16)
+        xds[..., 0] = 0x3C00
+        y = B.q4_gemv(dev(wqs), dev(wd), dev(xqs), dev(xds))
+        torch.cuda.synchronize()
+        isum = oracle.q4q8_block_dots(wqs, xqs).astype(np.int64).sum(axis=2)   # [M, N]
+        assert np.array_equal(host(y).astype(np.int64), isum)
+        assert np.array_equal(host(y), isum.astype(np.float32))
+
+
+def test_gemv_block_dot_extremes():
+    N, K = 2, 32
+    wqs = np.zeros((N, 1, 16), np.uint8)
+    wqs[1] = 0xFF
+    wd = np.full((N, 1), 0x3C00, np.uint16)
+    for v, want in ((-127, [32512, -28448]), (127, [-32512, 28448])):
+        xqs = np.full((1, K), v, np.int8)
+        xds = np.array([[[0x3C00, 0]]], np.uint16)
+        y = host(B.q4_gemv(dev(wqs), dev(wd), dev(xqs), dev(xds)))
+        assert y[0].tolist() == want
+
+
+def _gemv_case(M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    wqs, wd = oracle.q4_0_quantize(W)
+    xqs, xds = oracle.q8_1_quantize(X)
+    return wqs, wd, xqs, xds
+
+
+def test_gemv_decode_config():
+    wl = synth.DECODE
+    say(f"gemv decode config N={wl.N} K={wl.K}")
+    W, X = synth.workload_inputs(wl)
+    wqs, wd = oracle.q4_0_quantize(W)
+    # the activation is quantised on the GPU (bit-checked) and fed to the GEMV
+    xq, xd = B.q8_1_quantize_act(dev(X))
+    xqs, xds = oracle.q8_1_quantize(X)
+    assert np.array_equal(host(xq), xqs) and np.array_equal(host(xd, np.uint16), xds)
+    y = B.q4_gemv(dev(wqs), dev(wd), xq, xd)
+    ref = oracle.q4q8_gemv(wqs, wd, xqs, xds)
+    e = rel(host(y).astype(np.float64), ref)
+    say(f"  rel err {e:.3e}")
+    assert e <= BAR and e <= GEMV_TIGHT
+
+
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_gemv_all_m_ragged(M):
+    for (N, K) in [(257, 544), (1000, 4128)]:
+        wqs, wd, xqs, xds = _gemv_case(M, N, K, seed=M * 1000 + N)
+        y = host(B.q4_gemv(dev(wqs), dev(wd), dev(xqs), dev(xds))).astype(np.float64)
+        ref = oracle.q4q8_gemv(wqs, wd, xqs, xds)
+        assert rel(y, ref) <= GEMV_TIGHT, (M, N, K)
+
+
+@pytest.mark.parametrize("M,N0,N1,K", [(1, 12288, 12288, 4096), (3, 512, 300, 2048), (1, 1, 17, 64), (16, 64, 8192, 2048)])
+def test_fused2_bit_identical_to_two_gemvs(M, N0, N1, K):
+    say(f"fused2 M={M} N0={N0} N1={N1} K={K}")
+    w0qs, w0d, xqs, xds = _gemv_case(M, N0, K, seed=N0)
+    rng = np.random.default_rng(N1 + 1)
+    w1qs, w1d = oracle.q4_0_quantize(synth.weights(rng, N1, K))
+    t = [dev(a) for a in (w0qs, w0d, w1qs, w1d, xqs, xds)]
+    y0, y1 = B.q4_gemv_fused2(t[0], t[1], t[2], t[3], t[4], t[5])
+    z0 = B.q4_gemv(t[0], t[1], t[4], t[5])
+    z1 = B.q4_gemv(t[2], t[3], t[4], t[5])
+    assert torch.equal(y0, z0) and torch.equal(y1, z1)
+    assert rel(host(y1).astype(np.float64), oracle.q4q8_gemv(w1qs, w1d, xqs, xds)) <= GEMV_TIGHT
+
+
+def test_gemv_deterministic_and_row_permutation():
+    wqs, wd, xqs, xds = _gemv_case(2, 3000, 4096, seed=77)
+    t = [dev(a) for a in (wqs, wd, xqs, xds)]
+    hashes = set()
+    for _ in range(20):
+        y = B.q4_gemv(*t)
+        hashes.add(hashlib.sha256(host(y).tobytes()).hexdigest())
+    assert len(hashes) == 1
+    perm = np.random.default_rng(3).permutation(3000)
+    yp = B.q4_gemv(dev(wqs[perm]), dev(wd[perm]), t[2], t[3])
+    assert np.array_equal(host(yp), host(y)[:, perm])
+
+
+# ---------------------------------------------------------------------------
+# GEMM paths
+# ---------------------------------------------------------------------------
+
+def _q4_gemm_ref(qs, d, Xf64):
+    return oracle.matmul_f64(Xf64, oracle.q4_0_dequantize(qs, d))
+
+
+def test_gemm_tiny_config_f32():
+    """The tiny configuration: W f32 [256,512] -> Q4_0, X f32 [4,512], fp32 output."""
+    wl = synth.TINY
+    W, X = synth.workload_inputs(wl)
+    qs, d = oracle.q4_0_quantize(W)
+    gq, gd = B.q4_quantize(dev(W))
+    assert np.array_equal(host(gq), qs) and np.array_equal(host(gd, np.uint16), d)
+    ref = _q4_gemm_ref(qs, d, X.astype(np.float64))
+    for path in (-1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA):
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, path)
+        try:
+            y = B.q4_gemm(gq, gd, dev(X), y_dtype=torch.float32)
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+        e = rel(out_f64(y), ref)
+        say(f"tiny path {path}: rel {e:.3e}")
+        assert e <= BAR
+    # and through the integer-dot GEMV on Q8_1 activations (M = 4)
+    xq, xd = B.q8_1_quantize_act(dev(X))
+    y = B.q4_gemv(gq, gd, xq, xd)
+    xqs, xds = oracle.q8_1_quantize(X)
+    assert rel(host(y).astype(np.float64), oracle.q4q8_gemv(qs, d, xqs, xds)) <= GEMV_TIGHT
+
+
+_BOUNDARY_M = [1, 2, 3, 4, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513]
+
+
+@pytest.mark.parametrize("M", _BOUNDARY_M)
+def test_q4_gemm_every_path_boundary_m(M):
+    N, K = 300, 2048
+    rng = np.random.default_rng(M + 11)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    qs, d = oracle.q4_0_quantize(W)
+    xb = synth.bf16_bits(X)
+    ref = _q4_gemm_ref(qs, d, synth.bf16_bits_to_f32(xb).astype(np.float64))
+    tq, td, tx = dev(qs), dev(d), dev(xb).view(torch.bfloat16)
+    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+    paths = [B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM] + ([B.Q4_PATH_SKINNY] if M <= 64 else [])
+    auto = B.q4_gemm(tq, td, tx, y_dtype=torch.bfloat16, workspace=ws)
+    assert rel(out_f64(auto), ref) <= BAR
+    for path in paths:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, path)
+        try:
+            for ydt in (torch.bfloat16, torch.float32):
+                y = B.q4_gemm(tq, td, tx, y_dtype=ydt, workspace=ws)
+                e = rel(out_f64(y), ref)
+                assert e <= BAR, (M, path, ydt, e)
+                if ydt == torch.float32:
+                    assert e <= 1e-3, (M, path, e)   # fp16 operands, fp32 output
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+
+
+@pytest.mark.parametrize("M", [1, 17, 64, 65, 300])
+def test_affine4_gemm_every_path(M):
+    N, K = 257, 1024
+    rng = np.random.default_rng(M + 99)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    q, s, b = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+    xb = synth.bf16_bits(X)
+    ref = oracle.matmul_f64(synth.bf16_bits_to_f32(xb).astype(np.float64), oracle.affine4_dequantize(q, s, b))
+    t = [dev(a) for a in (q, s, b)]
+    tx = dev(xb).view(torch.bfloat16)
+    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, B.Q4_FMT_AFFINE4), dtype=torch.uint8, device="cuda")
+    paths = [B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM] + ([B.Q4_PATH_SKINNY] if M <= 64 else [])
+    for path in paths:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, path)
+        try:
+            y = B.affine4_gemm(t[0], t[1], t[2], tx, y_dtype=torch.bfloat16, workspace=ws)
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+        e = rel(out_f64(y), ref)
+        assert e <= BAR, (M, path, e)
+
+
+def test_dequant_path_equals_dequantize_plus_dense_gemm():
+    M, N, K = 200, 384, 1024
+    rng = np.random.default_rng(8)
+    qs, d = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    tx = bf16_dev(synth.activations(rng, M, K))
+    tq, td = dev(qs), dev(d)
+    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+    try:
+        y = B.q4_gemm(tq, td, tx, workspace=ws)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+    z = B.dense_gemm(tx, B.q4_dequantize(tq, td, out_dtype=torch.float16))
+    assert torch.equal(y, z)
+
+
+def _sampled_check(y_dev, Xf64, What, seed, count=6000):
+    M, N = y_dev.shape
+    rng = np.random.default_rng(seed)
+    ms = np.concatenate([rng.integers(0, M, count), np.zeros(N, np.int64), np.arange(M) % M])
+    ns = np.concatenate([rng.integers(0, N, count), np.arange(N), np.full(M, N - 1)])
+    ref = oracle.matmul_f64_sampled(Xf64, What, ms, ns)
+    got = out_f64(y_dev)[ms, ns]
+    return rel(got, ref)
+
+
+def test_q4_gemm_prefill_config_sampled():
+    wl = synth.PREFILL
+    say(f"prefill config M={wl.M} N={wl.N} K={wl.K}")
+    W, X = synth.workload_inputs(wl)
+    qs, d = oracle.q4_0_quantize(W)
+    xb = synth.bf16_bits(X)
+    y = B.q4_gemm(dev(qs), dev(d), dev(xb).view(torch.bfloat16), y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    e = _sampled_check(y, synth.bf16_bits_to_f32(xb).astype(np.float64), oracle.q4_0_dequantize(qs, d), 1)
+    say(f"  sampled rel err {e:.3e}")
+    assert e <= BAR
+
+
+@pytest.mark.parametrize("M", synth.AFFINE_MS)
+def test_affine4_gemm_sweep_sampled(M):
+    wl = synth.AFFINE
+    say(f"affine sweep M={M}")
+    W, X = synth.workload_inputs(wl, M=M)
+    q, s, b = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+    xb = synth.bf16_bits(X)
+    y = B.affine4_gemm(dev(q), dev(s), dev(b), dev(xb).view(torch.bfloat16), y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    e = _sampled_check(y, synth.bf16_bits_to_f32(xb).astype(np.float64), oracle.affine4_dequantize(q, s, b), M)
+    say(f"  sampled rel err {e:.3e}")
+    assert e <= BAR
+
+
+def test_gemm_deterministic_and_row_permutation():
+    M, N, K = 600, 512, 2048
+    rng = np.random.default_rng(44)
+    qs, d = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    tx = bf16_dev(synth.activations(rng, M, K))
+    tq, td = dev(qs), dev(d)
+    ys = [B.q4_gemm(tq, td, tx) for _ in range(5)]
+    assert all(torch.equal(ys[0], y) for y in ys[1:])
+    perm = np.random.default_rng(1).permutation(N)
+    yp = B.q4_gemm(dev(qs[perm]), dev(d[perm]), tx)
+    assert torch.equal(yp, ys[0][:, torch.from_numpy(perm).cuda()])
+
+
+def test_empty_inputs_are_noops():
+    """M == 0 or N == 0 launches nothing and leaves the outputs alone."""
+    K = 64
+    qs, d = B.q4_quantize(torch.ones((4, K), dtype=torch.float32, device="cuda"))
+    xq, xd = B.q8_1_quantize_act(torch.ones((2, K), dtype=torch.float32, device="cuda"))
+    y = torch.full((2, 4), 7.0, device="cuda")
+    assert B.lib().q4_gemv(B._p(qs), B._p(d), B._p(xq), B._p(xd), B._p(y), 0, 4, K, None) == B.Q4_OK
+    assert B.lib().q4_gemv(B._p(qs), B._p(d), B._p(xq), B._p(xd), B._p(y), 2, 0, K, None) == B.Q4_OK
+    e = B.q4_gemv(qs, d, xq[:0], xd[:0])
+    assert e.shape == (0, 4)
+    y0, y1 = B.q4_gemv_fused2(qs, d, qs[:0], d[:0], xq, xd)
+    assert y1.shape == (2, 0)
+    assert torch.equal(y0, B.q4_gemv(qs, d, xq, xd))
+    xb = torch.zeros((3, K), dtype=torch.bfloat16, device="cuda")
+    assert B.q4_gemm(qs[:0], d[:0], xb).shape == (3, 0)
+    assert B.q4_gemm(qs, d, xb[:0]).shape == (0, 4)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
