@@ -10,10 +10,18 @@
 // sync-after focused repro", Important source touch points: gate+up, K+V).
 //
 // Design (HBM-bound: 4.5 bits per weight streamed once, ~3.5 flop/byte):
-//  * one wave owns RW consecutive output rows; its 64 lanes split K by
-//    32-weight blocks (lane l takes blocks l, l+64, ...), so every weight load
-//    is a coalesced 128-bit load of one block's 16 nibble bytes and a wave
-//    instruction reads 1 KiB of contiguous nibbles;
+//  * a workgroup of NW waves (NW = min(16, ceil(K/256))) splits K into 8*NW
+//    "block lanes": lane l of wave w owns 32-weight block column
+//    b = 8w + (l & 7) (and b + 8*NW, ... for longer rows) and row lane
+//    l >> 3, so it loads its activation block once (32 int8 + d8) and reuses
+//    it for every weight row it visits;
+//  * each lane streams RI weight rows (rows r0 + (l >> 3) + 8i): per row one
+//    128-bit load of the block's 16 nibble bytes and its binary16 d; the 8
+//    lanes of a row read 128 contiguous bytes, whole cache lines.  The
+//    (cache-resident) activation is fetched first and the weight rows in
+//    order, all before any arithmetic, so the loads are in flight together
+//    and row i's arithmetic overlaps the arrival of rows i+1.. (loads return
+//    in order);
 //  * nibbles are unpacked in registers: the low nibbles of a 32-bit word are
 //    elements i..i+3, the high nibbles elements i+16..i+19 of the block, so
 //    (word & 0x0F0F0F0F) and ((word >> 4) & 0x0F0F0F0F) feed v_dot4_i32_i8
@@ -21,9 +29,10 @@
 //    removed once per block as 8 * sum(q8), giving the exact int32 isum;
 //  * the int32 sum is scaled by d4*d8 (exact binary32 product of two binary16
 //    values) and accumulated with one fma per block in binary32;
-//  * each row's 64 lane partials are summed by a fixed butterfly, so the
-//    result is deterministic and independent of which matrix or wave the row
-//    sits in: the fused two-matrix launch is bit-identical to two launches.
+//  * partial sums meet in a fixed order: an 8-lane butterfly inside the wave,
+//    then the NW wave partials added in wave order through LDS.  The order
+//    depends on K only, never on the row's position, so the fused
+//    two-matrix launch is bit-identical to two single launches.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -55,108 +64,163 @@ __device__ __forceinline__ int block_isum(const u32x4_t w, const int (&a)[8], in
     return s;
 }
 
-template <int M, int RW>
-__global__ __launch_bounds__(256) void k_q4_gemv(const GemvArgs args) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int gw = (int)blockIdx.x * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
-    const int row0 = gw * RW;
-    if (row0 >= args.total_rows) return;  // whole wave idle (uniform branch)
+constexpr int kMaxWaves = 16;   // 1024-thread workgroups
 
+// Sum over the 8 lanes of each aligned group of 8, same value on all 8 lanes,
+// in a fixed order: swap within pairs, then pairs within quads (DPP
+// quad_perm), then the two quads of the group (DPP row_half_mirror).
+__device__ __forceinline__ float sum8(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    return v;
+}
+
+template <int M, int RI>
+__global__ __launch_bounds__(1024) void k_q4_gemv(const GemvArgs args) {
+    static_assert(RI * M <= 16, "partials per lane");
+    __shared__ float red[kMaxWaves][8 * RI * M];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int bl = w * 8 + (lane & 7);          // block lane: first block column
+    const int rl = lane >> 3;                   // row lane: 0..7
+    const int stride = nw * 8;
     const int nb = args.nb;
-    const u32x4_t* rqs[RW];
-    const uint16_t* rd[RW];
-    bool rv[RW];
+    const int r0 = blockIdx.x * 8 * RI;
+
+    // Rows past the end read row 0 of the last matrix (valid memory) and are
+    // never written: every load is unconditional.
+    const u32x4_t* rqs[RI];
+    const uint16_t* rd[RI];
 #pragma unroll
-    for (int r = 0; r < RW; r++) {
-        const int R = row0 + r;
-        rv[r] = R < args.total_rows;
-        const int mat = (R >= args.n[0]) ? 1 : 0;
-        const int rr = rv[r] ? R - (mat ? args.n[0] : 0) : 0;
-        rqs[r] = reinterpret_cast<const u32x4_t*>(args.qs[mat] + (int64_t)rr * nb * 16);
-        rd[r] = args.d[mat] + (int64_t)rr * nb;
+    for (int i = 0; i < RI; i++) {
+        const int R = r0 + rl + 8 * i;
+        const bool second = R >= args.n[0];
+        const int rr = (R < args.total_rows) ? R - (second ? args.n[0] : 0) : 0;
+        const uint8_t* qbase = second ? args.qs[1] : args.qs[0];
+        const uint16_t* dbase = second ? args.d[1] : args.d[0];
+        rqs[i] = reinterpret_cast<const u32x4_t*>(qbase + (int64_t)rr * nb * 16);
+        rd[i] = dbase + (int64_t)rr * nb;
     }
 
-    float acc[RW][M];
+    float acc[RI][M];
 #pragma unroll
-    for (int r = 0; r < RW; r++)
+    for (int i = 0; i < RI; i++)
 #pragma unroll
-        for (int m = 0; m < M; m++) acc[r][m] = 0.0f;
+        for (int m = 0; m < M; m++) acc[i][m] = 0.0f;
 
-#pragma unroll 2
-    for (int c0 = 0; c0 < nb; c0 += kWave) {
-        const int b = c0 + lane;
-        const bool act = b < nb;
-        u32x4_t wv[RW];
-        float dv[RW];
+    constexpr int MP = M < 4 ? M : 4;   // activation rows fetched ahead of the weights
+    for (int b = bl; b < nb; b += stride) {
+        // loads: activation (cache-resident) first, then the weight rows in order
+        u32x4_t xa[MP][2];
+        uint32_t d8r[MP];
 #pragma unroll
-        for (int r = 0; r < RW; r++) {
-            if (act && rv[r]) {
-                wv[r] = __builtin_nontemporal_load(rqs[r] + b);
-                dv[r] = f16_to_f32(rd[r][b]);
-            } else {
-                wv[r] = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-                dv[r] = 0.0f;
-            }
+        for (int m = 0; m < MP; m++) {
+            const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(args.xqs + (int64_t)m * args.K + (int64_t)b * 32);
+            xa[m][0] = xp[0];
+            xa[m][1] = xp[1];
+            d8r[m] = args.xds[((int64_t)m * nb + b) * 2];
         }
+        u32x4_t wv[RI];
+        uint32_t dr[RI];
+#pragma unroll
+        for (int i = 0; i < RI; i++) {
+            dr[i] = rd[i][b];
+            wv[i] = __builtin_nontemporal_load(rqs[i] + b);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        int neg8sum[M];
+        int av[M][8];
+        float d8[M];
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            int a[8];
-            float d8 = 0.0f;
-            if (act) {
-                const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(args.xqs + (int64_t)m * args.K + (int64_t)b * 32);
-                const u32x4_t x0 = xp[0], x1 = xp[1];
-                a[0] = (int)x0[0]; a[1] = (int)x0[1]; a[2] = (int)x0[2]; a[3] = (int)x0[3];
-                a[4] = (int)x1[0]; a[5] = (int)x1[1]; a[6] = (int)x1[2]; a[7] = (int)x1[3];
-                d8 = f16_to_f32(args.xds[((int64_t)m * nb + b) * 2]);
+            u32x4_t x0, x1;
+            uint32_t d8bits;
+            if (m < MP) {
+                x0 = xa[m < MP ? m : 0][0];
+                x1 = xa[m < MP ? m : 0][1];
+                d8bits = d8r[m < MP ? m : 0];
             } else {
-#pragma unroll
-                for (int i = 0; i < 8; i++) a[i] = 0;
+                const u32x4_t* xp =
+                    reinterpret_cast<const u32x4_t*>(args.xqs + (int64_t)m * args.K + (int64_t)b * 32);
+                x0 = xp[0];
+                x1 = xp[1];
+                d8bits = args.xds[((int64_t)m * nb + b) * 2];
             }
+            av[m][0] = (int)x0[0]; av[m][1] = (int)x0[1]; av[m][2] = (int)x0[2]; av[m][3] = (int)x0[3];
+            av[m][4] = (int)x1[0]; av[m][5] = (int)x1[1]; av[m][6] = (int)x1[2]; av[m][7] = (int)x1[3];
+            d8[m] = f16_to_f32(d8bits);
             int sq = 0;
 #pragma unroll
-            for (int i = 0; i < 8; i++) sq = __builtin_amdgcn_sdot4(a[i], 0x01010101, sq, false);
-            const int neg8sum = -8 * sq;
+            for (int t = 0; t < 8; t++) sq = __builtin_amdgcn_sdot4(av[m][t], 0x01010101, sq, false);
+            neg8sum[m] = -8 * sq;
+        }
 #pragma unroll
-            for (int r = 0; r < RW; r++) {
-                const int isum = block_isum(wv[r], a, neg8sum);
-                acc[r][m] = fmaf((float)isum, dv[r] * d8, acc[r][m]);
+        for (int i = 0; i < RI; i++) {
+            const float d4 = f16_to_f32(dr[i]);
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const int isum = block_isum(wv[i], av[m], neg8sum[m]);
+                acc[i][m] = fmaf((float)isum, d4 * d8[m], acc[i][m]);
             }
         }
     }
 
+    // 8 block lanes of a row -> one partial per wave, then wave partials in
+    // wave order
 #pragma unroll
-    for (int r = 0; r < RW; r++) {
-        if (!rv[r]) continue;
-        const int R = row0 + r;
-        const int mat = (R >= args.n[0]) ? 1 : 0;
-        const int rr = R - (mat ? args.n[0] : 0);
-        float* yp = args.y[mat];
-        const int nrows = args.n[mat];
+    for (int i = 0; i < RI; i++)
 #pragma unroll
         for (int m = 0; m < M; m++) {
-            const float t = wave_sum(acc[r][m]);
-            if (lane == 0) yp[(int64_t)m * nrows + rr] = t;
+            const float v = sum8(acc[i][m]);
+            if ((lane & 7) == 0) red[w][(i * 8 + rl) * M + m] = v;
         }
+    __syncthreads();
+    for (int t = threadIdx.x; t < 8 * RI * M; t += blockDim.x) {
+        const int m = t % M;
+        const int slot = t / M;                 // i * 8 + rl
+        const int R = r0 + (slot & 7) + 8 * (slot >> 3);
+        if (R >= args.total_rows) continue;
+        float v = red[0][t];
+        for (int ww = 1; ww < nw; ww++) v += red[ww][t];
+        const bool second = R >= args.n[0];
+        float* yp = second ? args.y[1] : args.y[0];
+        const int64_t rows = second ? args.n[1] : args.n[0];
+        yp[(int64_t)m * rows + (R - (second ? args.n[0] : 0))] = v;
     }
 }
 
 template <int M>
-static void launch_m(const GemvArgs& a, int rw, hipStream_t s) {
-    const int waves_per_block = 4;
-    const int waves = (a.total_rows + rw - 1) / rw;
-    const dim3 grid((waves + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
-    if (rw == 4) hipLaunchKernelGGL((k_q4_gemv<M, 4>), grid, block, 0, s, a);
-    else if (rw == 2) hipLaunchKernelGGL((k_q4_gemv<M, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_q4_gemv<M, 1>), grid, block, 0, s, a);
+static void launch_m(const GemvArgs& a, int ri, int nw, hipStream_t s) {
+    const dim3 block(nw * kWave);
+    const int rows_per_wg = 8 * ri;
+    const dim3 grid((a.total_rows + rows_per_wg - 1) / rows_per_wg);
+    if constexpr (M <= 4) {
+        if (ri == 4) { hipLaunchKernelGGL((k_q4_gemv<M, 4>), grid, block, 0, s, a); return; }
+        if (ri == 3) { hipLaunchKernelGGL((k_q4_gemv<M, 3>), grid, block, 0, s, a); return; }
+    }
+    if constexpr (M <= 8) {
+        if (ri == 2) { hipLaunchKernelGGL((k_q4_gemv<M, 2>), grid, block, 0, s, a); return; }
+    }
+    hipLaunchKernelGGL((k_q4_gemv<M, 1>), grid, block, 0, s, a);
 }
 
-// Rows per wave: enough waves to fill 256 CUs several times over, fewer
-// rows per wave as M (and with it the register footprint) grows.
-static int pick_rows_per_wave(int64_t rows, int64_t M) {
-    int rw = rows >= 8192 ? 4 : (rows >= 4096 ? 2 : 1);
-    if (M > 8) rw = 1;
-    else if (M > 4 && rw > 2) rw = 2;
-    return rw;
+// Waves per workgroup: one block lane per 32-weight block of a row, up to 16
+// waves.  Rows per lane: enough workgroups to fill the 256 CUs twice, fewer
+// rows per lane as M (and with it the register footprint) grows.
+static int pick_waves(int64_t nb) {
+    int64_t nw = (nb + 7) / 8;
+    return (int)(nw < 1 ? 1 : (nw > kMaxWaves ? kMaxWaves : nw));
+}
+
+static int pick_rows_per_lane(int64_t rows, int64_t M) {
+    int64_t ri = rows / (8 * 512);
+    ri = ri < 1 ? 1 : (ri > 4 ? 4 : ri);
+    if (M > 8) ri = 1;
+    else if (M > 4 && ri > 2) ri = 2;
+    return (int)ri;
 }
 
 hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
@@ -167,24 +231,15 @@ hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0,
     a.qs[1] = w1_qs ? w1_qs : w0_qs; a.d[1] = w1_d ? w1_d : w0_d; a.y[1] = y1 ? y1 : y0; a.n[1] = (int)N1;
     a.xqs = x_qs; a.xds = x_ds; a.K = (int)K; a.nb = (int)(K / 32);
     a.total_rows = (int)(N0 + N1);
-    const int rw = pick_rows_per_wave(N0 + N1, M);
+    const int ri = pick_rows_per_lane(N0 + N1, M);
+    const int nw = pick_waves(K / 32);
     switch (M) {
-        case 1: launch_m<1>(a, rw, s); break;
-        case 2: launch_m<2>(a, rw, s); break;
-        case 3: launch_m<3>(a, rw, s); break;
-        case 4: launch_m<4>(a, rw, s); break;
-        case 5: launch_m<5>(a, rw, s); break;
-        case 6: launch_m<6>(a, rw, s); break;
-        case 7: launch_m<7>(a, rw, s); break;
-        case 8: launch_m<8>(a, rw, s); break;
-        case 9: launch_m<9>(a, rw, s); break;
-        case 10: launch_m<10>(a, rw, s); break;
-        case 11: launch_m<11>(a, rw, s); break;
-        case 12: launch_m<12>(a, rw, s); break;
-        case 13: launch_m<13>(a, rw, s); break;
-        case 14: launch_m<14>(a, rw, s); break;
-        case 15: launch_m<15>(a, rw, s); break;
-        case 16: launch_m<16>(a, rw, s); break;
+#define Q4_GEMV_CASE(m) case m: launch_m<m>(a, ri, nw, s); break;
+        Q4_GEMV_CASE(1) Q4_GEMV_CASE(2) Q4_GEMV_CASE(3) Q4_GEMV_CASE(4)
+        Q4_GEMV_CASE(5) Q4_GEMV_CASE(6) Q4_GEMV_CASE(7) Q4_GEMV_CASE(8)
+        Q4_GEMV_CASE(9) Q4_GEMV_CASE(10) Q4_GEMV_CASE(11) Q4_GEMV_CASE(12)
+        Q4_GEMV_CASE(13) Q4_GEMV_CASE(14) Q4_GEMV_CASE(15) Q4_GEMV_CASE(16)
+#undef Q4_GEMV_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
