@@ -126,8 +126,15 @@ __device__ __forceinline__ Frag16 affine_frag(const RawAff& r) {
 // ---------------------------------------------------------------------------
 // Large-M kernel: workgroup = 4 waves side by side along N; each wave owns
 // NT 32-column tiles and all MT 32-row tiles of the workgroup's M range.
+//
+// K advances 64 per iteration (two 32-weight blocks).  In the four
+// 32x32x16 MFMAs of an iteration (s = 0..3), lane (j = l % 32, g = l / 32)
+// supplies elements 8s..8s+7 of block 2k+g of column j: one 128-bit load
+// brings the lane its whole block, and the X fragment it pairs with is
+// X[i][64k + 32g + 8s .. +8].
 // ---------------------------------------------------------------------------
-constexpr int kLdsStride = 40;   // halves per staged X row (32 + 8 padding)
+constexpr int kStep = 64;            // K per iteration
+constexpr int kLdsStride = 72;       // halves per staged X row (64 + 8 padding)
 
 struct GemmArgs {
     const void* a;     // Q4_0 qs / affine q / dense binary16 W
@@ -144,7 +151,7 @@ __device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
     return h2_bits(__builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(lo, hi)));
 }
 
-// 8 consecutive X values of row m (bf16 or f32) -> 8 binary16 values.
+// 8 consecutive X values (bf16 or f32) -> 8 binary16 values (skinny kernel).
 template <int XDT>
 __device__ __forceinline__ u32x4_t load_x8(const void* x, int64_t off, bool ok) {
     u32x4_t r = {0u, 0u, 0u, 0u};
@@ -162,33 +169,36 @@ __device__ __forceinline__ u32x4_t load_x8(const void* x, int64_t off, bool ok) 
     return r;
 }
 
+// Raw X loads for the staging pipeline (converted later): 8 values per unit.
 template <int XDT>
-__device__ __forceinline__ u32x4_t load_x8_raw(const void* x, int64_t off, bool ok, u32x4_t& hi) {
-    // raw load only (conversion later), to keep the loads in flight across the MFMAs
-    u32x4_t r = {0u, 0u, 0u, 0u};
-    hi = r;
-    if (!ok) return r;
-    if (XDT == DT_BF16) {
-        r = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + off);
+struct RawX8 { u32x4_t lo, hi; };   // bf16: lo only; f32: lo = values 0..3, hi = 4..7
+
+template <int XDT>
+__device__ __forceinline__ RawX8<XDT> load_x8_raw(const void* x, int64_t off) {
+    RawX8<XDT> r;
+    if constexpr (XDT == DT_BF16) {
+        r.lo = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + off);
+        r.hi = r.lo;
     } else {
         const u32x4_t* p = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const float*>(x) + off);
-        r = p[0];
-        hi = p[1];
+        r.lo = p[0];
+        r.hi = p[1];
     }
     return r;
 }
 
 template <int XDT>
-__device__ __forceinline__ u32x4_t convert_x8(const u32x4_t v, const u32x4_t hi) {
+__device__ __forceinline__ u32x4_t convert_x8(const RawX8<XDT>& v) {
     u32x4_t r;
-    if (XDT == DT_BF16) {
+    if constexpr (XDT == DT_BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) r[i] = cvt_pk(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xFFFF0000u));
+        for (int i = 0; i < 4; i++)
+            r[i] = cvt_pk(__uint_as_float(v.lo[i] << 16), __uint_as_float(v.lo[i] & 0xFFFF0000u));
     } else {
-        r[0] = cvt_pk(__uint_as_float(v[0]), __uint_as_float(v[1]));
-        r[1] = cvt_pk(__uint_as_float(v[2]), __uint_as_float(v[3]));
-        r[2] = cvt_pk(__uint_as_float(hi[0]), __uint_as_float(hi[1]));
-        r[3] = cvt_pk(__uint_as_float(hi[2]), __uint_as_float(hi[3]));
+        r[0] = cvt_pk(__uint_as_float(v.lo[0]), __uint_as_float(v.lo[1]));
+        r[1] = cvt_pk(__uint_as_float(v.lo[2]), __uint_as_float(v.lo[3]));
+        r[2] = cvt_pk(__uint_as_float(v.hi[0]), __uint_as_float(v.hi[1]));
+        r[3] = cvt_pk(__uint_as_float(v.hi[2]), __uint_as_float(v.hi[3]));
     }
     return r;
 }
@@ -198,74 +208,158 @@ __device__ __forceinline__ void store_y(void* y, int ydt, int64_t off, float v) 
     else reinterpret_cast<uint16_t*>(y)[off] = (uint16_t)f32_to_bf16(v);
 }
 
-template <int WF>
-struct RawW;
-template <>
-struct RawW<WF_Q4_0> { RawQ4 r; };
-template <>
-struct RawW<WF_AFFINE4> { RawAff r; };
-template <>
-struct RawW<WF_DENSE16> { u32x4_t h[2]; };
+// Raw weight data of one whole 32-weight block of one column.
+struct BlkQ4 { u32x4_t q; uint32_t d; };
+struct BlkAff { u32x4_t q; uint32_t s, b; };
+struct BlkF16 { u32x4_t h[4]; };
 
-template <int WF>
-__device__ __forceinline__ int kofs(int s, int g) {
-    return WF == WF_AFFINE4 ? 16 * g + 8 * s : 16 * s + 8 * g;
-}
+template <int WF> struct BlkOf;
+template <> struct BlkOf<WF_Q4_0> { using T = BlkQ4; };
+template <> struct BlkOf<WF_AFFINE4> { using T = BlkAff; };
+template <> struct BlkOf<WF_DENSE16> { using T = BlkF16; };
 
-// Load the raw weight data of one fragment: column n, K step kb (32 wide).
+// Block kblk of column n.  Callers pass a clamped, valid (n, kblk): the load
+// is unconditional so that it never waits inside a branch.
 template <int WF>
-__device__ __forceinline__ RawW<WF> load_w(const GemmArgs& a, int n, int kb, int g, bool ok) {
-    RawW<WF> r;
+__device__ __forceinline__ typename BlkOf<WF>::T load_blk(const GemmArgs& a, int n, int kblk) {
+    typename BlkOf<WF>::T r;
     const int nb = a.K / 32;
     if constexpr (WF == WF_Q4_0) {
-        if (ok) {
-            const uint8_t* qs = reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + kb) * 16 + 8 * g;
-            r.r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(qs));
-            r.r.d = reinterpret_cast<const uint16_t*>(a.b)[(int64_t)n * nb + kb];
-        } else {
-            r.r.q = u32x2_t{0x88888888u, 0x88888888u};
-            r.r.d = 0;
-        }
+        r.q = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + kblk) * 16));
+        r.d = reinterpret_cast<const uint16_t*>(a.b)[(int64_t)n * nb + kblk];
     } else if constexpr (WF == WF_AFFINE4) {
-        if (ok) {
-            const uint8_t* q = reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + kb * 16 + 8 * g;
-            r.r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(q));
-            const int64_t gi = (int64_t)n * (a.K / 64) + (kb >> 1);
-            r.r.s = reinterpret_cast<const uint16_t*>(a.b)[gi];
-            r.r.b = reinterpret_cast<const uint16_t*>(a.c)[gi];
-        } else {
-            r.r.q = u32x2_t{0u, 0u};
-            r.r.s = 0;
-            r.r.b = 0;
-        }
+        r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + (int64_t)kblk * 16));
+        const int64_t gi = (int64_t)n * (a.K / 64) + (kblk >> 1);
+        r.s = reinterpret_cast<const uint16_t*>(a.b)[gi];
+        r.b = reinterpret_cast<const uint16_t*>(a.c)[gi];
     } else {
-        if (ok) {
-            const uint16_t* w = reinterpret_cast<const uint16_t*>(a.a) + (int64_t)n * a.K + kb * 32;
-            r.h[0] = *reinterpret_cast<const u32x4_t*>(w + kofs<WF>(0, g));
-            r.h[1] = *reinterpret_cast<const u32x4_t*>(w + kofs<WF>(1, g));
-        } else {
-            r.h[0] = u32x4_t{0u, 0u, 0u, 0u};
-            r.h[1] = r.h[0];
-        }
+        const u32x4_t* w = reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const uint16_t*>(a.a) + (int64_t)n * a.K + (int64_t)kblk * 32);
+#pragma unroll
+        for (int t = 0; t < 4; t++) r.h[t] = w[t];
     }
     return r;
 }
 
+// A block past the end of K (K = 32 mod 64) contributes zeros.
 template <int WF>
-__device__ __forceinline__ Frag16 make_frag(const RawW<WF>& r) {
-    if constexpr (WF == WF_Q4_0) return q4_0_frag(r.r);
-    else if constexpr (WF == WF_AFFINE4) return affine_frag(r.r);
-    else {
-        Frag16 f;
-        f.s[0] = r.h[0];
-        f.s[1] = r.h[1];
-        return f;
+__device__ __forceinline__ void zero_blk(typename BlkOf<WF>::T& r, bool keep) {
+    if constexpr (WF == WF_Q4_0) {
+        r.d = keep ? r.d : 0u;
+    } else if constexpr (WF == WF_AFFINE4) {
+        r.s = keep ? r.s : 0u;
+        r.b = keep ? r.b : 0u;
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) r.h[t][e] = keep ? r.h[t][e] : 0u;
     }
+}
+
+// Elements 8t..8t+7 of a block as 8 binary16 values, t = 0..3.
+template <int WF>
+__device__ __forceinline__ void blk_frags(const typename BlkOf<WF>::T& r, u32x4_t (&out)[4]) {
+    if constexpr (WF == WF_Q4_0) {
+        const half2_t dd = as_h2(r.d | (r.d << 16));
+        // t = 0: low nibbles of bytes 0..7, t = 1: low of 8..15,
+        // t = 2: high nibbles of bytes 0..7, t = 3: high of 8..15
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+#pragma unroll
+            for (int w = 0; w < 2; w++) {
+                const uint32_t word = r.q[2 * h + w];
+                const uint32_t t01 = perm(word, 0x0C010C00u);
+                const uint32_t t23 = perm(word, 0x0C030C02u);
+                out[h][2 * w + 0] = q4_pair(t01, dd);
+                out[h][2 * w + 1] = q4_pair(t23, dd);
+                out[2 + h][2 * w + 0] = q4_pair(t01 >> 4, dd);
+                out[2 + h][2 * w + 1] = q4_pair(t23 >> 4, dd);
+            }
+        }
+    } else if constexpr (WF == WF_AFFINE4) {
+        // element 8t+v sits in word t: byte v/2, low nibble for even v
+        RawAff lo, hi;
+        lo.s = hi.s = r.s;
+        lo.b = hi.b = r.b;
+        lo.q = u32x2_t{r.q[0], r.q[1]};
+        hi.q = u32x2_t{r.q[2], r.q[3]};
+        const Frag16 f0 = affine_frag(lo);   // s[0] = word 0, s[1] = word 1
+        const Frag16 f1 = affine_frag(hi);
+        out[0] = f0.s[0];
+        out[1] = f0.s[1];
+        out[2] = f1.s[0];
+        out[3] = f1.s[1];
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; t++) out[t] = r.h[t];
+    }
+}
+
+// Quantised weights reach the workgroup through LDS: direct-to-LDS loads
+// (global_load_lds: no registers held while in flight) copy the raw blocks
+// of the workgroup's 4*NT*32 columns for one K step (2 blocks per column)
+// into one of 4 slots, three steps before the step is multiplied.  Every
+// load instruction reads 32 columns x 32 contiguous bytes.
+constexpr int kSlots = 4;
+
+template <int WF, int NT>
+struct WStage;
+// A 2-byte direct-to-LDS load puts each lane's value in a 4-byte slot (lane i
+// at byte 4i, zero-extended), so the 16-bit scales occupy one dword each.
+template <int NT>
+struct WStage<WF_Q4_0, NT> {
+    static constexpr int kCols = 4 * NT * 32;
+    uint8_t q[kSlots][kCols][2][16];      // raw nibble blocks
+    uint32_t d[kSlots][kCols][2];         // binary16 scales
+};
+template <int NT>
+struct WStage<WF_AFFINE4, NT> {
+    static constexpr int kCols = 4 * NT * 32;
+    uint8_t q[kSlots][kCols][2][16];      // raw nibbles (2 blocks = one group)
+    uint32_t s[kSlots][kCols];            // bfloat16 scale of the group
+    uint32_t b[kSlots][kCols];            // bfloat16 bias of the group
+};
+template <int NT>
+struct WStage<WF_DENSE16, NT> {
+    uint32_t unused;
+};
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma2(const void* src, void* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 2, 0, 0);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+#define Q4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
+
+// Workgroup barrier for the main loop: this wave's LDS writes are complete
+// (lgkmcnt 0) and all but the newest `vm` vector-memory loads have landed,
+// which covers the direct-to-LDS copies the next step reads.  Unlike
+// __syncthreads() it does not wait for every outstanding load (the release
+// fence there would, because a direct-to-LDS copy counts as a pending LDS
+// store).  The signal fences stop the compiler from moving memory accesses
+// across the barrier; they emit no instructions.
+template <int VM>
+__device__ __forceinline__ void step_barrier() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0070 | (VM & 0xF) | (((VM >> 4) & 3) << 14));   // lgkmcnt(0), vmcnt(VM)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <int WF, int MT, int NT, int XDT, int YDT>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][MT * 32 * kLdsStride];
+    constexpr bool kStaged = WF != WF_DENSE16;
+    __shared__ __attribute__((aligned(16))) WStage<WF, NT> ws;
+    using Blk = typename BlkOf<WF>::T;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -273,18 +367,35 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
     const int j = lane & 31;
     const int g = lane >> 5;
 
-    // workgroup -> (m tile, n tile); consecutive workgroups share an N tile
     const int wg = blockIdx.x;
     const int mt_idx = wg % a.m_tiles;
     const int nt_idx = wg / a.m_tiles;
     const int m0 = mt_idx * MT * 32;
-    const int n0 = nt_idx * (4 * NT * 32) + wave * NT * 32;
-
+    const int nwg0 = nt_idx * (4 * NT * 32);
+    const int n0 = nwg0 + wave * NT * 32;
     const int nb = a.K / 32;
+    const int nsteps = (nb + 1) / 2;                 // a last step may hold one block only
 
-    // X staging: units of 8 values; unit u -> row u / 4, k offset (u % 4) * 8
-    constexpr int kUnits = MT * 32 * 4;
+    // X staging: units of 8 values; unit u -> row u / 8, column (u % 8) * 8
+    constexpr int kUnits = MT * 32 * 8;
     constexpr int kUnitsPerThread = (kUnits + 255) / 256;
+    int xrow[kUnitsPerThread], xcol[kUnitsPerThread];
+    int64_t xoff[kUnitsPerThread];
+#pragma unroll
+    for (int t = 0; t < kUnitsPerThread; t++) {
+        const int u = tid + t * 256;
+        xrow[t] = u >> 3;
+        xcol[t] = (u & 7) * 8;
+        const int m = m0 + xrow[t];
+        xoff[t] = (int64_t)(m < a.M ? m : a.M - 1) * a.K;   // clamped: padded rows are never stored
+    }
+    // weight columns (clamped: padded columns are never stored)
+    int wn[NT];
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) {
+        const int n = n0 + ni * 32 + j;
+        wn[ni] = n < a.N ? n : a.N - 1;
+    }
 
     floatx16_t acc[MT][NT];
 #pragma unroll
@@ -294,81 +405,154 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mi][ni][v] = 0.0f;
 
-    auto x_unit_ok = [&](int u, int& row, int& kq) {
-        row = u >> 2;
-        kq = (u & 3) * 8;
-        return u < kUnits && (m0 + row) < a.M;
-    };
+    RawX8<XDT> xr[kUnitsPerThread];
+    Blk wr[NT];
+    u32x4_t bf[NT][4];
 
-    // prologue: stage step 0
-    RawW<WF> w_next[NT];
-    {
+    auto load_x = [&](int k) {
 #pragma unroll
         for (int t = 0; t < kUnitsPerThread; t++) {
-            const int u = tid + t * 256;
-            int row, kq;
-            const bool ok = x_unit_ok(u, row, kq);
-            const u32x4_t v = load_x8<XDT>(a.x, (int64_t)(m0 + row) * a.K + kq, ok);
-            if (u < kUnits) *reinterpret_cast<u32x4_t*>(&lds[0][row * kLdsStride + kq]) = v;
+            const int col = k * kStep + xcol[t];
+            xr[t] = load_x8_raw<XDT>(a.x, xoff[t] + (col < a.K ? col : a.K - 8));
         }
+    };
+    // raw weights of step k (blocks 2k, 2k+1 of the workgroup's columns) -> slot k % 4
+    constexpr int kCols = 4 * NT * 32;
+    constexpr int kDmaQ = kCols * 2 / 256;                 // 16-byte block loads per wave
+    constexpr int kDmaS = (WF == WF_Q4_0) ? kCols * 2 / 256 : 2 * kCols / 256;   // 2-byte loads per wave
+    constexpr int kDmaPerStep = kStaged ? kDmaQ + kDmaS : 0;
+    auto dma_step = [&](int k) {
+        if constexpr (kStaged) {
+            const int slot = k & (kSlots - 1);
 #pragma unroll
-        for (int ni = 0; ni < NT; ni++) {
-            const int n = n0 + ni * 32 + j;
-            w_next[ni] = load_w<WF>(a, n, 0, g, n < a.N);
-        }
-    }
-    __syncthreads();
-
-    for (int kb = 0; kb < nb; kb++) {
-        const int buf = kb & 1;
-        Frag16 bf[NT];
-#pragma unroll
-        for (int ni = 0; ni < NT; ni++) bf[ni] = make_frag<WF>(w_next[ni]);
-
-        // issue the next step's global loads before the MFMAs
-        const bool more = (kb + 1) < nb;
-        u32x4_t xr[kUnitsPerThread], xh[kUnitsPerThread];
-        if (more) {
-#pragma unroll
-            for (int t = 0; t < kUnitsPerThread; t++) {
-                const int u = tid + t * 256;
-                int row, kq;
-                const bool ok = x_unit_ok(u, row, kq);
-                xr[t] = load_x8_raw<XDT>(a.x, (int64_t)(m0 + row) * a.K + (int64_t)(kb + 1) * 32 + kq, ok, xh[t]);
+            for (int i = 0; i < kDmaQ; i++) {
+                const int q = wave * kDmaQ + i;             // 32 columns x 2 blocks
+                int n = nwg0 + q * 32 + (lane >> 1);
+                n = n < a.N ? n : a.N - 1;
+                int blk = 2 * k + (lane & 1);
+                blk = blk < nb ? blk : nb - 1;
+                const uint8_t* src = (WF == WF_Q4_0)
+                    ? reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + blk) * 16
+                    : reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + (int64_t)blk * 16;
+                dma16(src, &ws.q[slot][q * 32][0][0]);
             }
+            if constexpr (WF == WF_Q4_0) {
 #pragma unroll
-            for (int ni = 0; ni < NT; ni++) {
-                const int n = n0 + ni * 32 + j;
-                w_next[ni] = load_w<WF>(a, n, kb + 1, g, n < a.N);
-            }
-        }
-
-        // MFMAs on the current step
-        const uint16_t* la = lds[buf];
+                for (int i = 0; i < kDmaS; i++) {
+                    const int q = wave * kDmaS + i;         // 64 scale entries
+                    int n = nwg0 + q * 32 + (lane >> 1);
+                    n = n < a.N ? n : a.N - 1;
+                    int blk = 2 * k + (lane & 1);
+                    blk = blk < nb ? blk : nb - 1;
+                    dma2(reinterpret_cast<const uint16_t*>(a.b) + (int64_t)n * nb + blk, &ws.d[slot][q * 32][0]);
+                }
+            } else {
+                const int ng = a.K / 64;
+                int gi = k < ng ? k : ng - 1;
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-#pragma unroll
-            for (int mi = 0; mi < MT; mi++) {
-                const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
-                    &la[(mi * 32 + j) * kLdsStride + kofs<WF>(s, g)]);
-                const half8_t ah = __builtin_bit_cast(half8_t, av);
-#pragma unroll
-                for (int ni = 0; ni < NT; ni++) {
-                    const half8_t bh = __builtin_bit_cast(half8_t, bf[ni].s[s]);
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[mi][ni], 0, 0, 0);
+                for (int i = 0; i < kDmaS / 2; i++) {
+                    const int q = wave * (kDmaS / 2) + i;   // 64 columns
+                    int n = nwg0 + q * 64 + lane;
+                    n = n < a.N ? n : a.N - 1;
+                    dma2(reinterpret_cast<const uint16_t*>(a.b) + (int64_t)n * ng + gi, &ws.s[slot][q * 64]);
+                    dma2(reinterpret_cast<const uint16_t*>(a.c) + (int64_t)n * ng + gi, &ws.b[slot][q * 64]);
                 }
             }
         }
-
-        if (more) {
+    };
+    // registers for the weights of step k: from the LDS slot, or from global (dense)
+    auto fetch_w = [&](int k) {
+        if constexpr (kStaged) {
+            const int slot = k & (kSlots - 1);
 #pragma unroll
-            for (int t = 0; t < kUnitsPerThread; t++) {
-                const int u = tid + t * 256;
-                int row, kq;
-                x_unit_ok(u, row, kq);
-                if (u < kUnits)
-                    *reinterpret_cast<u32x4_t*>(&lds[buf ^ 1][row * kLdsStride + kq]) = convert_x8<XDT>(xr[t], xh[t]);
+            for (int ni = 0; ni < NT; ni++) {
+                const int cw = wave * NT * 32 + ni * 32 + j;
+                wr[ni].q = *reinterpret_cast<const u32x4_t*>(&ws.q[slot][cw][g][0]);
+                if constexpr (WF == WF_Q4_0) {
+                    wr[ni].d = ws.d[slot][cw][g] & 0xFFFFu;
+                } else {
+                    wr[ni].s = ws.s[slot][cw] & 0xFFFFu;
+                    wr[ni].b = ws.b[slot][cw] & 0xFFFFu;
+                }
             }
+        } else {
+            const int kblk = 2 * k + g;
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) wr[ni] = load_blk<WF>(a, wn[ni], kblk < nb ? kblk : nb - 1);
+        }
+    };
+    auto stage_step = [&](int k, int dst) {
+#pragma unroll
+        for (int t = 0; t < kUnitsPerThread; t++) {
+            if (tid + t * 256 < kUnits) {
+                u32x4_t v = convert_x8<XDT>(xr[t]);
+                const bool ok = k * kStep + xcol[t] < a.K;
+#pragma unroll
+                for (int e = 0; e < 4; e++) v[e] = ok ? v[e] : 0u;
+                *reinterpret_cast<u32x4_t*>(&lds[dst][xrow[t] * kLdsStride + xcol[t]]) = v;
+            }
+        }
+        if constexpr (kStaged) fetch_w(k);
+        const bool bok = 2 * k + g < nb;
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) {
+            zero_blk<WF>(wr[ni], bok);
+            blk_frags<WF>(wr[ni], bf[ni]);
+        }
+    };
+    auto mfmas = [&](int k) {
+        const uint16_t* la = lds[k & 1];
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+#pragma unroll
+            for (int mi = 0; mi < MT; mi++) {
+                const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&la[(mi * 32 + j) * kLdsStride + 32 * g + 8 * s]);
+                const half8_t ah = __builtin_bit_cast(half8_t, av);
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        ah, __builtin_bit_cast(half8_t, bf[ni][s]), acc[mi][ni], 0, 0, 0);
+            }
+        }
+    };
+
+    // prologue: raw weights of steps 0 and 1 requested and step 0 staged; then
+    // step 1's X and step 2's weights go in flight in the same order as in
+    // the main loop (X, then weights), so that the loop's waits are exact
+    dma_step(0);
+    if (nsteps > 1) dma_step(1);
+    load_x(0);
+    if constexpr (!kStaged) fetch_w(0);
+    Q4_WAIT_VMCNT(0);
+    __syncthreads();
+    stage_step(0, 0);
+    if (nsteps > 1) {
+        load_x(1);
+        if constexpr (!kStaged) fetch_w(1);
+    }
+    if (nsteps > 2) dma_step(2);
+    __syncthreads();
+
+    // main loop: every iteration requests the raw weights of step k+3
+    int k = 0;
+    for (; k + 3 < nsteps; k++) {
+        mfmas(k);
+        stage_step(k + 1, (k + 1) & 1);               // X loaded during the previous iteration
+        load_x(k + 2);                                // the next X goes in flight
+        if constexpr (!kStaged) fetch_w(k + 2);
+        dma_step(k + 3);
+        // step k+2's weights (requested one iteration ago) must have landed:
+        // only this iteration's X loads and weight requests may be in flight
+        if constexpr (kStaged) step_barrier<kUnitsPerThread + kDmaPerStep>();
+        else __syncthreads();
+    }
+    // last iterations: nothing left to request
+    for (; k < nsteps; k++) {
+        mfmas(k);
+        if (k + 1 < nsteps) stage_step(k + 1, (k + 1) & 1);
+        if (k + 2 < nsteps) {
+            load_x(k + 2);
+            if constexpr (!kStaged) fetch_w(k + 2);
         }
         __syncthreads();
     }
