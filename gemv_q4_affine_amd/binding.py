@@ -187,21 +187,34 @@ def q4_gemv_fused2(w0_qs, w0_d, w1_qs, w1_d, x_qs, x_ds, y0=None, y1=None, strea
 
 # ---- GEMM -----------------------------------------------------------------------------
 
-def q4_gemm(w_qs, w_d, x, y_dtype=torch.bfloat16, y=None, workspace=None, stream=None):
+def _workspace(workspace, M, N, K, fmt, like):
+    """"auto": a fresh scratch tensor of q4_gemm_workspace_size bytes (None if
+    that is 0); None: no workspace; else the caller's tensor."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+        n = q4_gemm_workspace_size(M, N, K, fmt)
+        return torch.empty(n, dtype=torch.uint8, device=like.device) if n > 0 else None
+    return workspace
+
+
+def q4_gemm(w_qs, w_d, x, y_dtype=torch.bfloat16, y=None, workspace="auto", stream=None):
     N = w_d.shape[0]
     M, K = x.shape
     y = _empty((M, N), y_dtype, x) if y is None else y
+    workspace = _workspace(workspace, M, N, K, Q4_FMT_Q4_0, x)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("q4_gemm", lib().q4_gemm(_p(w_qs), _p(w_d), _p(x), _dt(x), _p(y), _dt(y), M, N, K, _p(workspace),
                                     ws_bytes, _stream(stream)))
     return y
 
 
-def affine4_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, y=None, workspace=None,
+def affine4_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, y=None, workspace="auto",
                  stream=None):
     N = w_q.shape[0]
     M, K = x.shape
     y = _empty((M, N), y_dtype, x) if y is None else y
+    workspace = _workspace(workspace, M, N, K, Q4_FMT_AFFINE4, x)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("affine4_gemm", lib().affine4_gemm(_p(w_q), _p(scales), _p(biases), group_size, _p(x), _dt(x), _p(y),
                                               _dt(y), M, N, K, _p(workspace), ws_bytes, _stream(stream)))

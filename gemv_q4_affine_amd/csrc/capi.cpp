@@ -83,7 +83,7 @@ const char* q4_status_string(int status) {
         case Q4_ERR_DTYPE: return "unsupported dtype";
         case Q4_ERR_HIP: return "HIP launch or runtime error";
         case Q4_ERR_ARG: return "invalid argument";
-        case Q4_ERR_WORKSPACE: return "the dequantise-then-GEMM path needs a workspace of q4_gemm_workspace_size bytes";
+        case Q4_ERR_WORKSPACE: return "the dequantise-then-GEMM path needs a workspace of N*K*2 bytes";
         default: return "unknown status";
     }
 }
@@ -129,10 +129,10 @@ int q4_dispatch_path(int64_t M, int64_t N, int64_t K, int fmt, int have_workspac
 }
 
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt) {
-    (void)M;
-    (void)fmt;
-    if (N < 0 || K < 0 || N > kMaxDim || K > kMaxDim) return 0;
-    return N * K * 2;
+    const int path = q4_dispatch_path(M, N, K, fmt, 1);
+    if (path == Q4_PATH_MFMA) return q4::packed_x_bytes(M, K);
+    if (path == Q4_PATH_DEQUANT_GEMM) return N * K * 2;
+    return 0;
 }
 
 // ---- quantisers ------------------------------------------------------------------
@@ -223,7 +223,8 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
                        int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                        void* stream) {
     const int fmt = (wf == q4::WF_Q4_0) ? Q4_FMT_Q4_0 : Q4_FMT_AFFINE4;
-    const bool have_ws = workspace != nullptr && workspace_bytes >= q4_gemm_workspace_size(M, N, K, fmt);
+    // "have workspace" for the dispatch: enough for the dequantised weights
+    const bool have_ws = workspace != nullptr && workspace_bytes >= N * K * 2;
     const int path = q4_dispatch_path(M, N, K, fmt, have_ws ? 1 : 0);
     if (path < 0) return path;
     if (M == 0 || N == 0) return Q4_OK;
@@ -233,6 +234,10 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
             if (M > kSkinnyLimit) return Q4_ERR_ARG;
             return hip_status(q4::launch_gemm_skinny(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
         case Q4_PATH_MFMA:
+            if (workspace != nullptr && workspace_bytes >= q4::packed_x_bytes(M, K)) {
+                if (!aligned16(workspace)) return Q4_ERR_ALIGN;
+                return hip_status(q4::launch_gemm_packed(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, workspace, s));
+            }
             return hip_status(q4::launch_gemm_mfma(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
         case Q4_PATH_DEQUANT_GEMM: {
             if (!have_ws) return Q4_ERR_WORKSPACE;

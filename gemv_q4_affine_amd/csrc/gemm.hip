@@ -17,22 +17,26 @@
 //    bfloat16 instead (what a bf16 MFMA would need) costs about 1.6e-3
 //    relative error on top of the 1.6e-3 of the bf16 output, which together
 //    exceed the 2e-3 error bar; binary16 weights stay well inside it.
-//  * Weights never touch LDS.  Each wave owns distinct output columns, so it
-//    dequantises its B fragments straight from global memory into registers:
-//    the nibbles become binary16 1024+q with one AND-OR against 0x6400 (the
-//    binary16 exponent at which the unit in the last place is 1), then one
-//    packed subtract of 1032 and one packed multiply by d give (q-8)*d
-//    rounded to nearest even.  A weight is dequantised once per M tile of
-//    the workgroup -- the "static reuse across token tiles" of the ET-SoC-1
-//    rewrite -- and is never written back.
-//  * X goes global -> registers -> (convert to binary16) -> LDS once per
-//    workgroup and K step, double buffered, one barrier per K step.  Rows are
-//    padded to 40 halves (80 bytes) so the 128-bit fragment reads of eight
-//    consecutive lanes fall in distinct banks.
+//  * Weights are dequantised in registers, never written back: the nibbles
+//    become binary16 1024+q (or 64+q) with one AND-OR against a binary16
+//    exponent at which the nibble's unit in the last place is 1, then one
+//    packed subtract and one packed multiply (Q4_0) or fma (affine) give the
+//    weight, rounded once.  A weight is dequantised once per M tile of the
+//    workgroup -- the "static reuse across token tiles" of the ET-SoC-1
+//    rewrite.
+//  * Large M (k_gemm_pk): X is converted once into a binary16 tile image that
+//    direct-to-LDS copies move straight into a 4-deep LDS ring together with
+//    the raw weight blocks; compute waves overlap each K step's MFMAs with the
+//    next step's dequantisation, one barrier per K step.  Without a workspace
+//    for the image, k_gemm_mfma converts X on the way into LDS instead.
+//  * Small M (k_gemm_skinny): weights stream once from HBM at full rate and
+//    four waves split K.
 //  * Each MFMA sums over 16 (or 32) K slots; the slot -> k assignment only has
 //    to agree between the A and B operands, so it is chosen to match each
 //    weight format's nibble order and the B loader needs no byte shuffles
-//    beyond one v_perm per pair.
+//    beyond one v_perm or shift per pair.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -347,7 +351,7 @@ __device__ __forceinline__ void dma2(const void* src, void* lds_wave_base) {
 // across the barrier; they emit no instructions.
 template <int VM>
 __device__ __forceinline__ void step_barrier() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    static_assert(VM >= 0 && VM < 64, "vmcnt range (63 = no constraint)");
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x0070 | (VM & 0xF) | (((VM >> 4) & 3) << 14));   // lgkmcnt(0), vmcnt(VM)
     __builtin_amdgcn_s_barrier();
@@ -573,6 +577,485 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Packed-X large-M kernel.
+//
+// X is first converted once to a binary16 "LDS image" (k_pack_x): for each
+// 128-row M tile and 64-wide K step a 16 KiB tile laid out exactly as the
+// GEMM keeps it in LDS.  Inside a tile row r (128 bytes) stores its 16-byte
+// chunk c (k = 8c..8c+7) at chunk position c ^ img_swz(r) -- an XOR swizzle
+// that puts the 128-bit fragment reads of 8 consecutive rows (one 128-byte
+// bank sweep) and of 16 consecutive rows (256 bytes) in distinct banks
+// without padding -- and the halves of a chunk follow the fragment order of
+// blk_frags_perm.  Rows past M and steps past K are zero.  The GEMM then never
+// converts X: its producer waves only issue direct-to-LDS copies.
+//
+// Workgroup: 6 waves, one per CU.
+//  * waves 0-3 (consumers) own NT 32-column tiles each and all MT 32-row tiles
+//    of the workgroup's 128 x 256 output tile; per K step they run the MFMAs
+//    of step k while dequantising the weights of step k+1 into registers,
+//    interleaved instruction by instruction (one basic block per step);
+//  * waves 4-5 (producers) copy the X tile and the raw weight blocks (and
+//    scales) of step k+3 into a 4-deep ring with direct-to-LDS loads and, before
+//    each barrier, wait until step k+2 has landed.  They issue no other memory
+//    operation, so the count in that wait is exact.
+// One barrier per K step.  After the loop the LDS is reused to stage the
+// output tile, which is written back with 16-byte stores.
+// ---------------------------------------------------------------------------
+constexpr int kPkSlots = 4;              // ring depth: steps k..k+3 resident
+constexpr int kImgRows = 128;            // rows of an image tile
+constexpr int kImgTile = kImgRows * 64;  // halves of an image tile (16 KiB)
+constexpr int kOutStride = 72;           // floats per staged output row (64 + 8 padding)
+
+// Row r of an image tile: chunk c sits at c ^ img_swz(r).  A permutation of
+// rows 0..7 and, separately, of the even and of the odd rows among 0..15.
+__device__ __forceinline__ int img_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Shift-free dequantiser of the packed-X kernel.
+//
+// A nibble in bits 0-3 of a binary16 with exponent field 0x64 (value 1024,
+// unit 1) reads as 1024+q; a nibble in bits 4-7 of a binary16 with exponent
+// field 0x54 (value 64, unit 1/16) reads as 64+q.  So the four nibble pairs
+// of a 32-bit word come out of word & 0x000F000F, word & 0x00F000F0 and the
+// same two masks on word >> 8, each with one AND-OR, one packed subtract
+// (exact) and one packed multiply (Q4_0, one rounding) or fma (affine, one
+// rounding): 13 instructions per 8 weights.  The price is the order of the
+// halves inside each 8-weight fragment, which the X tile in LDS copies:
+//   Q4_0   (bytes carry elements b and b+16): positions hold k = 0,2,1,3,4,6,5,7
+//   affine (bytes carry elements 2b, 2b+1):  positions hold k = 0,4,1,5,2,6,3,7
+// The two masks live in VGPRs (NibMasks, made opaque once per kernel) so that
+// each AND-OR is one v_and_or_b32 (a gfx9 VOP3 takes no literal and one SGPR).
+struct NibMasks {
+    uint32_t lo, hi;
+    __device__ __forceinline__ static NibMasks make() {
+        NibMasks m{0x000F000Fu, 0x00F000F0u};
+        asm volatile("" : "+v"(m.lo), "+v"(m.hi));
+        return m;
+    }
+};
+__device__ __forceinline__ uint32_t nib_lo(uint32_t w, const NibMasks& m) { return (w & m.lo) | 0x64006400u; }   // 1024+q
+__device__ __forceinline__ uint32_t nib_hi(uint32_t w, const NibMasks& m) { return (w & m.hi) | 0x54005400u; }   // 64+q
+
+// Per-block constants of the dequantiser: Q4_0 d in both halves; affine
+// scale and bias in both halves (binary16).
+struct BlkConst {
+    half2_t c0, c1;
+};
+template <int WF>
+__device__ __forceinline__ BlkConst blk_const(const typename BlkOf<WF>::T& r) {
+    if constexpr (WF == WF_Q4_0) {
+        const half2_t dd = as_h2(__builtin_amdgcn_perm(r.d, r.d, 0x01000100u));
+        return {dd, dd};
+    } else {
+        static_assert(WF == WF_AFFINE4, "quantised formats only");
+        const uint32_t s16 = f16b(bf16_to_f32(r.s));
+        const uint32_t b16 = f16b(bf16_to_f32(r.b));
+        return {as_h2(s16 | (s16 << 16)), as_h2(b16 | (b16 << 16))};
+    }
+}
+
+// The 8 weights of 32-bit word w of a block, into their fragment slots.
+//  Q4_0: word w holds the low nibbles of elements 4w..4w+3 (fragment w/2,
+//        pairs 2(w%2), 2(w%2)+1) and the high nibbles 16+4w.. (fragment
+//        2 + w/2, same pairs).
+//  affine: word w holds elements 8w..8w+7 (fragment w, all four pairs).
+template <int WF>
+__device__ __forceinline__ void blk_word(const typename BlkOf<WF>::T& r, const BlkConst& c, int w, const NibMasks& m,
+                                         u32x4_t (&out)[4]) {
+    const uint32_t word = r.q[w];
+    const uint32_t sh = word >> 8;
+    if constexpr (WF == WF_Q4_0) {
+        const half2_t clo = as_h2(0xE408E408u);   // -1032
+        const half2_t chi = as_h2(0xD480D480u);   // -72
+        const int h = w >> 1, p = 2 * (w & 1);
+        out[h][p + 0] = h2_bits((as_h2(nib_lo(word, m)) + clo) * c.c0);
+        out[h][p + 1] = h2_bits((as_h2(nib_lo(sh, m)) + clo) * c.c0);
+        out[2 + h][p + 0] = h2_bits((as_h2(nib_hi(word, m)) + chi) * c.c0);
+        out[2 + h][p + 1] = h2_bits((as_h2(nib_hi(sh, m)) + chi) * c.c0);
+    } else {
+        const half2_t clo = as_h2(0xE400E400u);   // -1024
+        const half2_t chi = as_h2(0xD400D400u);   // -64
+        out[w][0] = h2_bits(__builtin_elementwise_fma(as_h2(nib_lo(word, m)) + clo, c.c0, c.c1));
+        out[w][1] = h2_bits(__builtin_elementwise_fma(as_h2(nib_hi(word, m)) + chi, c.c0, c.c1));
+        out[w][2] = h2_bits(__builtin_elementwise_fma(as_h2(nib_lo(sh, m)) + clo, c.c0, c.c1));
+        out[w][3] = h2_bits(__builtin_elementwise_fma(as_h2(nib_hi(sh, m)) + chi, c.c0, c.c1));
+    }
+}
+
+template <int WF>
+__device__ __forceinline__ void blk_frags_perm(const typename BlkOf<WF>::T& r, const NibMasks& m, u32x4_t (&out)[4]) {
+    const BlkConst c = blk_const<WF>(r);
+#pragma unroll
+    for (int w = 0; w < 4; w++) blk_word<WF>(r, c, w, m, out);
+}
+
+// X -> image (see above).  One thread per 16-byte image chunk.  binary16
+// values are rounded to nearest even (exact for bfloat16 input in binary16's
+// normal range).
+template <int WF, int XDT>
+__global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint16_t* __restrict__ img, int M, int K,
+                                                int ksteps, int64_t nchunks) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= nchunks) return;
+    const int pc = (int)(t & 7);
+    const int r = (int)((t >> 3) & (kImgRows - 1));
+    const int64_t tile = t >> 10;
+    const int ks = (int)(tile % ksteps);
+    const int mt = (int)(tile / ksteps);
+    const int c = pc ^ img_swz(r);
+    const int m = mt * kImgRows + r;
+    const int k0 = ks * 64 + c * 8;
+    u32x4_t o = {0u, 0u, 0u, 0u};
+    if (m < M && k0 < K) {                       // K % 32 == 0: a chunk is wholly inside or outside
+        float f[8];
+        if constexpr (XDT == DT_BF16) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + (int64_t)m * K + k0);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                f[2 * i] = __uint_as_float(v[i] << 16);
+                f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+            }
+        } else {
+            const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + (int64_t)m * K + k0);
+            const float4 v0 = p[0], v1 = p[1];
+            f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
+            f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
+        }
+        // position p of the chunk holds k = perm[p]
+        constexpr int kPermQ[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+        constexpr int kPermA[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int p0 = (WF == WF_Q4_0) ? kPermQ[2 * i] : kPermA[2 * i];
+            const int p1 = (WF == WF_Q4_0) ? kPermQ[2 * i + 1] : kPermA[2 * i + 1];
+            o[i] = f32_to_f16(f[p0]) | (f32_to_f16(f[p1]) << 16);
+        }
+    }
+    *reinterpret_cast<u32x4_t*>(img + t * 8) = o;
+}
+
+// Raw weights of one K step for the workgroup's 256 columns, as the
+// direct-to-LDS copies lay them out (a 2-byte copy puts each lane's value in
+// its own dword).
+template <int WF>
+struct PkW;
+template <>
+struct PkW<WF_Q4_0> {
+    uint8_t q[256][2][16];
+    uint32_t d[256][2];
+};
+template <>
+struct PkW<WF_AFFINE4> {
+    uint8_t q[256][2][16];
+    uint32_t s[256];
+    uint32_t b[256];
+};
+
+template <int WF>
+union PkLds {
+    struct {
+        uint16_t x[kPkSlots][kImgTile];
+        PkW<WF> w[kPkSlots];
+    } loop;
+    float out[4][32 * kOutStride];
+};
+
+template <int WF, int YDT>
+__global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
+    static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
+    constexpr int MT = 4, NT = 2;
+    constexpr int kCols = 4 * NT * 32;
+    constexpr int kRows = MT * 32;
+    static_assert(kRows == kImgRows && kCols == 256, "tile shape");
+    __shared__ __attribute__((aligned(16))) PkLds<WF> lds;
+    using Blk = typename BlkOf<WF>::T;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    const int wg = blockIdx.x;
+    const int mt_idx = wg % a.m_tiles;
+    const int nt_idx = wg / a.m_tiles;
+    const int m0 = mt_idx * kRows;
+    const int nwg0 = nt_idx * kCols;
+    const int nb = a.K / 32;
+    const int nsteps = (nb + 1) / 2;
+
+    if (wave < 4) {
+        // ------------------------------ consumer ------------------------------
+        const int j = lane & 31;
+        const int g = lane >> 5;
+        const int n0 = nwg0 + wave * NT * 32;
+        floatx16_t acc[MT][NT];
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[mi][ni][v] = 0.0f;
+        u32x4_t bfA[NT][4], bfB[NT][4];
+        const NibMasks masks = NibMasks::make();
+
+        // raw weight blocks of step k from its ring slot
+        auto read_w = [&](int k, Blk (&r)[NT]) {
+            const PkW<WF>& w = lds.loop.w[k & (kPkSlots - 1)];
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) {
+                const int cw = wave * NT * 32 + ni * 32 + j;
+                r[ni].q = *reinterpret_cast<const u32x4_t*>(&w.q[cw][g][0]);
+                if constexpr (WF == WF_Q4_0) {
+                    r[ni].d = w.d[cw][g];
+                } else {
+                    r[ni].s = w.s[cw];
+                    r[ni].b = w.b[cw];
+                }
+            }
+        };
+        // a block past the end of K (K = 32 mod 64) gets a zero scale; the
+        // image holds zeros there as well
+        auto dequant = [&](int k, Blk (&r)[NT], u32x4_t (&bf)[NT][4]) {
+            const bool bok = 2 * k + g < nb;
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) {
+                zero_blk<WF>(r[ni], bok);
+                blk_frags_perm<WF>(r[ni], masks, bf[ni]);
+            }
+        };
+        // X fragment (mi, s) of this lane: row mi*32 + j, chunk 4g + s
+        // (kofs = 32g + 8s), swizzled by the row
+        int aofs[4];
+#pragma unroll
+        for (int s = 0; s < 4; s++) aofs[s] = j * 64 + (((4 * g + s) ^ img_swz(j)) * 8);   // rows mi*32 + j
+        auto read_a = [&](int k, int s, u32x4_t (&av)[MT]) {
+            const uint16_t* la = lds.loop.x[k & (kPkSlots - 1)];
+#pragma unroll
+            for (int mi = 0; mi < MT; mi++)
+                av[mi] = *reinterpret_cast<const u32x4_t*>(&la[mi * 32 * 64 + aofs[s]]);
+        };
+        // MFMA (mi, ni) of K slice s; `first` selects (0, 0), else the others
+        auto mfma_slice = [&](int s, const u32x4_t (&av)[MT], const u32x4_t (&bf)[NT][4], bool first) {
+#pragma unroll
+            for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++)
+                    if ((mi == 0 && ni == 0) == first)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(half8_t, av[mi]), __builtin_bit_cast(half8_t, bf[ni][s]),
+                            acc[mi][ni], 0, 0, 0);
+        };
+        // Instruction order inside one segment: the first MFMA (its operands
+        // were loaded during the previous segment), the segment's LDS reads,
+        // then each remaining MFMA followed by up to `valu` vector
+        // instructions.  The compiler waits for all outstanding LDS reads at
+        // the first MFMA (it does not count LDS returns as ordered here), so
+        // the reads issued after it get a whole segment to land.
+        auto segment_order = [&](auto nreads, auto valu) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, decltype(nreads)::value, 0);
+#pragma unroll
+            for (int i = 1; i < MT * NT; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, decltype(valu)::value, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        constexpr int kWReads = NT * (WF == WF_Q4_0 ? 2 : 3);
+        // One K step in four segments (K slices s = 0..3) fenced by
+        // sched_barrier, so that every LDS read is issued one segment ahead of
+        // its use: the slice s+1 X fragments during slice s, the next step's
+        // slice 0 during slice 3 (that tile landed one barrier ago), and the
+        // raw weights of step k+1 in segment 0 for the dequantisation, which
+        // runs word by word under the MFMAs of segments 1-3.  `a0` holds this
+        // step's slice 0 on entry and the next step's on return.  Past the
+        // last step the k+1 slots hold older data that is never used.
+        auto body = [&](int k, const u32x4_t (&cur)[NT][4], u32x4_t (&nxt)[NT][4], u32x4_t (&a0)[MT]) {
+            Blk r[NT];
+            u32x4_t a1[MT], a2[MT], a3[MT];
+            mfma_slice(0, a0, cur, true);
+            read_a(k, 1, a1);
+            read_w(k + 1, r);
+            mfma_slice(0, a0, cur, false);
+            segment_order(std::integral_constant<int, kWReads + MT>{}, std::integral_constant<int, 2>{});
+
+            mfma_slice(1, a1, cur, true);
+            read_a(k, 2, a2);
+            mfma_slice(1, a1, cur, false);
+            const bool bok = 2 * (k + 1) + g < nb;
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) zero_blk<WF>(r[ni], bok);
+            const BlkConst c0 = blk_const<WF>(r[0]);
+            blk_word<WF>(r[0], c0, 0, masks, nxt[0]);
+            blk_word<WF>(r[0], c0, 1, masks, nxt[0]);
+            blk_word<WF>(r[0], c0, 2, masks, nxt[0]);
+            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 7>{});
+
+            mfma_slice(2, a2, cur, true);
+            read_a(k, 3, a3);
+            mfma_slice(2, a2, cur, false);
+            const BlkConst c1 = blk_const<WF>(r[1]);
+            blk_word<WF>(r[0], c0, 3, masks, nxt[0]);
+            blk_word<WF>(r[1], c1, 0, masks, nxt[1]);
+            blk_word<WF>(r[1], c1, 1, masks, nxt[1]);
+            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 7>{});
+
+            mfma_slice(3, a3, cur, true);
+            read_a(k + 1, 0, a0);
+            mfma_slice(3, a3, cur, false);
+            blk_word<WF>(r[1], c1, 2, masks, nxt[1]);
+            blk_word<WF>(r[1], c1, 3, masks, nxt[1]);
+            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 5>{});
+        };
+        static_assert(NT == 2, "the dequantisation split assumes two blocks per step");
+
+        step_barrier<63>();                    // prologue: steps 0 and 1 landed
+        u32x4_t a0[MT];
+        {
+            Blk r[NT];
+            read_w(0, r);
+            dequant(0, r, bfA);
+            read_a(0, 0, a0);
+        }
+        // no condition inside an iteration: a conditional use of the next
+        // step's fragments would let the compiler sink their dequantisation
+        // out of the block of MFMAs it is meant to overlap
+        int k = 0;
+        for (; k + 1 < nsteps; k += 2) {
+            body(k, bfA, bfB, a0);
+            step_barrier<63>();
+            body(k + 1, bfB, bfA, a0);
+            step_barrier<63>();
+        }
+        if (k < nsteps) {
+            body(k, bfA, bfB, a0);
+            step_barrier<63>();
+        }
+
+        // Epilogue.  The last barrier above is also the producers' last (their
+        // copies have all landed), so the ring is free.  Each wave stages one
+        // 32-row slice of its tiles as f32 (lane: column j, rows 8*(v/4) +
+        // 4*g + v%4) and writes it back with 16-byte row stores.
+        float* st = lds.out[wave];
+        constexpr int kVec = (YDT == DT_BF16) ? 8 : 4;        // values per 16-byte store
+        constexpr int kUnitsRow = NT * 32 / kVec;
+        const bool vec_ok = (a.N % kVec) == 0;                // y itself is 16-byte aligned
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++) {
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+                for (int v = 0; v < 16; v++)
+                    st[(8 * (v >> 2) + 4 * g + (v & 3)) * kOutStride + ni * 32 + j] = acc[mi][ni][v];
+#pragma unroll
+            for (int t = 0; t < 32 * kUnitsRow / 64; t++) {
+                const int u = lane + 64 * t;
+                const int row = u / kUnitsRow;
+                const int col = (u % kUnitsRow) * kVec;
+                const int m = m0 + mi * 32 + row;
+                const int n = n0 + col;
+                if (m >= a.M) continue;
+                const float* src = st + row * kOutStride + col;
+                if constexpr (YDT == DT_BF16) {
+                    const float4 f0 = *reinterpret_cast<const float4*>(src);
+                    const float4 f1 = *reinterpret_cast<const float4*>(src + 4);
+                    const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                    uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + (int64_t)m * a.N + n;
+                    if (vec_ok && n + 8 <= a.N) {
+                        u32x4_t o;
+#pragma unroll
+                        for (int e = 0; e < 4; e++) o[e] = f32_to_bf16(f[2 * e]) | (f32_to_bf16(f[2 * e + 1]) << 16);
+                        *reinterpret_cast<u32x4_t*>(yp) = o;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; e++)
+                            if (n + e < a.N) yp[e] = (uint16_t)f32_to_bf16(f[e]);
+                    }
+                } else {
+                    const float4 f0 = *reinterpret_cast<const float4*>(src);
+                    float* yp = reinterpret_cast<float*>(a.y) + (int64_t)m * a.N + n;
+                    if (vec_ok && n + 4 <= a.N) {
+                        *reinterpret_cast<float4*>(yp) = f0;
+                    } else {
+                        const float f[4] = {f0.x, f0.y, f0.z, f0.w};
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (n + e < a.N) yp[e] = f[e];
+                    }
+                }
+            }
+        }
+    } else {
+        // ------------------------------ producer ------------------------------
+        // 2 waves; per step each copies half the X tile (8 x 1 KiB), half the
+        // weight blocks (4 x 32 columns x 2 blocks) and half the scales.
+        const int pw = wave - 4;
+        const uint16_t* ximg = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)mt_idx * nsteps * kImgTile;
+        constexpr int kXDma = 8, kQDma = 4, kSDma = 4;
+        constexpr int kPerStep = kXDma + kQDma + kSDma;
+        auto copy_step = [&](int k) {
+            const int slot = k & (kPkSlots - 1);
+            const uint16_t* xs = ximg + (int64_t)k * kImgTile;
+#pragma unroll
+            for (int i = 0; i < kXDma; i++) {
+                const int c = pw * kXDma + i;                     // 1 KiB chunk of the tile
+                dma16(xs + c * 512 + lane * 8, &lds.loop.x[slot][c * 512]);
+            }
+            PkW<WF>& w = lds.loop.w[slot];
+#pragma unroll
+            for (int i = 0; i < kQDma; i++) {
+                const int q = pw * kQDma + i;                     // 32 columns x 2 blocks
+                int n = nwg0 + q * 32 + (lane >> 1);
+                n = n < a.N ? n : a.N - 1;
+                int blk = 2 * k + (lane & 1);
+                blk = blk < nb ? blk : nb - 1;
+                const uint8_t* src = (WF == WF_Q4_0)
+                    ? reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + blk) * 16
+                    : reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + (int64_t)blk * 16;
+                dma16(src, &w.q[q * 32][0][0]);
+            }
+            if constexpr (WF == WF_Q4_0) {
+#pragma unroll
+                for (int i = 0; i < kSDma; i++) {
+                    const int q = pw * kSDma + i;                 // 32 columns x 2 blocks
+                    int n = nwg0 + q * 32 + (lane >> 1);
+                    n = n < a.N ? n : a.N - 1;
+                    int blk = 2 * k + (lane & 1);
+                    blk = blk < nb ? blk : nb - 1;
+                    dma2(reinterpret_cast<const uint16_t*>(a.b) + (int64_t)n * nb + blk, &w.d[q * 32][0]);
+                }
+            } else {
+                const int ngr = a.K / 64;                         // == nsteps
+#pragma unroll
+                for (int i = 0; i < kSDma / 2; i++) {
+                    const int q = pw * (kSDma / 2) + i;           // 64 columns
+                    int n = nwg0 + q * 64 + lane;
+                    n = n < a.N ? n : a.N - 1;
+                    dma2(reinterpret_cast<const uint16_t*>(a.b) + (int64_t)n * ngr + k, &w.s[q * 64]);
+                    dma2(reinterpret_cast<const uint16_t*>(a.c) + (int64_t)n * ngr + k, &w.b[q * 64]);
+                }
+            }
+        };
+        // prologue: steps 0 and 1 landed, step 2 in flight
+        copy_step(0);
+        if (nsteps > 1) copy_step(1);
+        if (nsteps > 2) {
+            copy_step(2);
+            step_barrier<kPerStep>();
+        } else {
+            step_barrier<0>();
+        }
+        // during step k: request step k+3, then make sure step k+2 has landed
+        for (int k = 0; k < nsteps; k++) {
+            if (k + 3 < nsteps) {
+                copy_step(k + 3);
+                step_barrier<kPerStep>();
+            } else {
+                step_barrier<0>();
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Skinny kernel (small M): weights streamed once at HBM rate.
 //
 // Workgroup = 4 waves on the same 16*NT columns, splitting K four ways (the
@@ -792,6 +1275,43 @@ hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* 
     if (wfmt == WF_Q4_0) launch_mfma_w<WF_Q4_0>(ga, xdt, ydt, s);
     else if (wfmt == WF_AFFINE4) launch_mfma_w<WF_AFFINE4>(ga, xdt, ydt, s);
     else launch_mfma_w<WF_DENSE16>(ga, xdt, ydt, s);
+    return hipGetLastError();
+}
+
+int64_t packed_x_bytes(int64_t M, int64_t K) {
+    const int64_t m_tiles = (M + kImgRows - 1) / kImgRows;
+    const int64_t ksteps = (K + 63) / 64;
+    return m_tiles * ksteps * (int64_t)kImgTile * 2;
+}
+
+template <int WF, int XDT>
+static void launch_pack_t(const GemmArgs& ga, uint16_t* img, hipStream_t s) {
+    const int ksteps = (ga.K + 63) / 64;
+    const int64_t nchunks = (int64_t)ga.m_tiles * ksteps * (kImgTile / 8);
+    const dim3 grid((unsigned)((nchunks + 255) / 256)), block(256);
+    hipLaunchKernelGGL((k_pack_x<WF, XDT>), grid, block, 0, s, ga.x, img, ga.M, ga.K, ksteps, nchunks);
+}
+
+template <int WF>
+static void launch_packed_w(GemmArgs ga, int xdt, int ydt, uint16_t* img, hipStream_t s) {
+    ga.m_tiles = (ga.M + kImgRows - 1) / kImgRows;
+    ga.n_tiles = (ga.N + 255) / 256;
+    if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, img, s);
+    else launch_pack_t<WF, DT_F32>(ga, img, s);
+    ga.x = img;
+    const dim3 grid((unsigned)(ga.m_tiles * ga.n_tiles)), block(384);
+    if (ydt == DT_BF16) hipLaunchKernelGGL((k_gemm_pk<WF, DT_BF16>), grid, block, 0, s, ga);
+    else hipLaunchKernelGGL((k_gemm_pk<WF, DT_F32>), grid, block, 0, s, ga);
+}
+
+hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
+                              int ydt, int64_t M, int64_t N, int64_t K, void* img, hipStream_t s) {
+    if (wfmt != WF_Q4_0 && wfmt != WF_AFFINE4) return hipErrorInvalidValue;
+    GemmArgs ga{};
+    ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
+    ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
+    if (wfmt == WF_Q4_0) launch_packed_w<WF_Q4_0>(ga, xdt, ydt, static_cast<uint16_t*>(img), s);
+    else launch_packed_w<WF_AFFINE4>(ga, xdt, ydt, static_cast<uint16_t*>(img), s);
     return hipGetLastError();
 }
 

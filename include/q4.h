@@ -209,10 +209,17 @@ int q4_gemv_fused2(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0,
  * inputs outside binary16 range are outside the fused paths' domain.
  *   x         : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32)
  *   y         : device out, [M][N] of y_dtype (Q4_BF16 RNE, or Q4_F32)
- *   workspace : device scratch for the DEQUANT_GEMM path only
- *               (q4_gemm_workspace_size bytes), or NULL; without it the
- *               automatic dispatch never picks DEQUANT_GEMM, and forcing that
- *               path returns Q4_ERR_WORKSPACE.
+ *   workspace : device scratch owned by the caller (16-byte aligned), or
+ *               NULL.  q4_gemm_workspace_size bytes let the call take its
+ *               fastest path.  The MFMA path uses packed_x bytes (see
+ *               q4_gemm_workspace_size) to convert X once into the binary16
+ *               tile image its matrix-core kernel copies straight into LDS;
+ *               with less it converts X inside the GEMM (slower, same
+ *               results).  The DEQUANT_GEMM path needs N*K*2 bytes for the
+ *               dequantised weights: the automatic dispatch picks it only
+ *               with that much, and forcing it without returns
+ *               Q4_ERR_WORKSPACE.  Calls that share a workspace must not run
+ *               concurrently.
  */
 int q4_gemm(const uint8_t* w_qs, const uint16_t* w_d,
             const void* x, int x_dtype, void* y, int y_dtype,
@@ -230,7 +237,12 @@ int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
                  int64_t M, int64_t N, int64_t K,
                  void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Bytes of workspace the DEQUANT_GEMM path needs: N*K*2 (a dense binary16 W). */
+/*
+ * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
+ * 0 for SKINNY; for MFMA the packed X image, ceil(M/128)*128 *
+ * ceil(K/64)*64 * 2 bytes; for DEQUANT_GEMM N*K*2 (a dense binary16 W).
+ * Returns 0 for invalid arguments.
+ */
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt);
 
 /*

@@ -323,6 +323,18 @@ def test_gemm_tiny_config_f32():
 _BOUNDARY_M = [1, 2, 3, 4, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 511, 512, 513]
 
 
+def _workspace_every_path(M, N, K, fmt=B.Q4_FMT_Q4_0):
+    """A workspace large enough for the forced MFMA and DEQUANT_GEMM paths."""
+    sizes = []
+    for path in (B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM):
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, path)
+        try:
+            sizes.append(B.q4_gemm_workspace_size(M, N, K, fmt))
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+    return torch.empty(max(sizes), dtype=torch.uint8, device="cuda")
+
+
 @pytest.mark.parametrize("M", _BOUNDARY_M)
 def test_q4_gemm_every_path_boundary_m(M):
     N, K = 300, 2048
@@ -333,19 +345,22 @@ def test_q4_gemm_every_path_boundary_m(M):
     xb = synth.bf16_bits(X)
     ref = _q4_gemm_ref(qs, d, synth.bf16_bits_to_f32(xb).astype(np.float64))
     tq, td, tx = dev(qs), dev(d), dev(xb).view(torch.bfloat16)
-    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
-    paths = [B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM] + ([B.Q4_PATH_SKINNY] if M <= 64 else [])
-    auto = B.q4_gemm(tq, td, tx, y_dtype=torch.bfloat16, workspace=ws)
+    ws = _workspace_every_path(M, N, K)
+    auto = B.q4_gemm(tq, td, tx, y_dtype=torch.bfloat16)
     assert rel(out_f64(auto), ref) <= BAR
-    for path in paths:
+    # (path, workspace): the MFMA path runs on the packed X image with a
+    # workspace and converts X in the GEMM without one
+    cases = [(B.Q4_PATH_MFMA, ws), (B.Q4_PATH_MFMA, None), (B.Q4_PATH_DEQUANT_GEMM, ws)]
+    cases += [(B.Q4_PATH_SKINNY, None)] if M <= 64 else []
+    for path, w in cases:
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, path)
         try:
             for ydt in (torch.bfloat16, torch.float32):
-                y = B.q4_gemm(tq, td, tx, y_dtype=ydt, workspace=ws)
+                y = B.q4_gemm(tq, td, tx, y_dtype=ydt, workspace=w)
                 e = rel(out_f64(y), ref)
-                assert e <= BAR, (M, path, ydt, e)
+                assert e <= BAR, (M, path, w is None, ydt, e)
                 if ydt == torch.float32:
-                    assert e <= 1e-3, (M, path, e)   # fp16 operands, fp32 output
+                    assert e <= 1e-3, (M, path, w is None, e)   # fp16 operands, fp32 output
         finally:
             B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
 
@@ -361,16 +376,18 @@ def test_affine4_gemm_every_path(M):
     ref = oracle.matmul_f64(synth.bf16_bits_to_f32(xb).astype(np.float64), oracle.affine4_dequantize(q, s, b))
     t = [dev(a) for a in (q, s, b)]
     tx = dev(xb).view(torch.bfloat16)
-    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, B.Q4_FMT_AFFINE4), dtype=torch.uint8, device="cuda")
-    paths = [B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM] + ([B.Q4_PATH_SKINNY] if M <= 64 else [])
-    for path in paths:
+    ws = _workspace_every_path(M, N, K, B.Q4_FMT_AFFINE4)
+    cases = [(B.Q4_PATH_MFMA, ws), (B.Q4_PATH_MFMA, None), (B.Q4_PATH_DEQUANT_GEMM, ws)]
+    cases += [(B.Q4_PATH_SKINNY, None)] if M <= 64 else []
+    for path, w in cases:
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, path)
         try:
-            y = B.affine4_gemm(t[0], t[1], t[2], tx, y_dtype=torch.bfloat16, workspace=ws)
+            for ydt in (torch.bfloat16, torch.float32):
+                y = B.affine4_gemm(t[0], t[1], t[2], tx, y_dtype=ydt, workspace=w)
+                e = rel(out_f64(y), ref)
+                assert e <= BAR, (M, path, w is None, ydt, e)
         finally:
             B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
-        e = rel(out_f64(y), ref)
-        assert e <= BAR, (M, path, e)
 
 
 def test_dequant_path_equals_dequantize_plus_dense_gemm():
@@ -379,7 +396,7 @@ def test_dequant_path_equals_dequantize_plus_dense_gemm():
     qs, d = oracle.q4_0_quantize(synth.weights(rng, N, K))
     tx = bf16_dev(synth.activations(rng, M, K))
     tq, td = dev(qs), dev(d)
-    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+    ws = _workspace_every_path(M, N, K)
     B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
     try:
         y = B.q4_gemm(tq, td, tx, workspace=ws)
