@@ -76,7 +76,9 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
-template <int M, int RI>
+// NMAT: 1 for q4_gemv, 2 for q4_gemv_fused2 (rows past n[0] belong to the
+// second matrix).  Per-row arithmetic does not depend on RI or NMAT.
+template <int M, int RI, int NMAT>
 __global__ __launch_bounds__(1024) void k_q4_gemv(const GemvArgs args) {
     static_assert(RI * M <= 16, "partials per lane");
     __shared__ float red[kMaxWaves][8 * RI * M];
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(1024) void k_q4_gemv(const GemvArgs args) {
 #pragma unroll
     for (int i = 0; i < RI; i++) {
         const int R = r0 + rl + 8 * i;
-        const bool second = R >= args.n[0];
+        const bool second = NMAT == 2 && R >= args.n[0];
         const int rr = (R < args.total_rows) ? R - (second ? args.n[0] : 0) : 0;
         const uint8_t* qbase = second ? args.qs[1] : args.qs[0];
         const uint16_t* dbase = second ? args.d[1] : args.d[0];
@@ -185,26 +187,32 @@ __global__ __launch_bounds__(1024) void k_q4_gemv(const GemvArgs args) {
         if (R >= args.total_rows) continue;
         float v = red[0][t];
         for (int ww = 1; ww < nw; ww++) v += red[ww][t];
-        const bool second = R >= args.n[0];
+        const bool second = NMAT == 2 && R >= args.n[0];
         float* yp = second ? args.y[1] : args.y[0];
         const int64_t rows = second ? args.n[1] : args.n[0];
         yp[(int64_t)m * rows + (R - (second ? args.n[0] : 0))] = v;
     }
 }
 
-template <int M>
+template <int M, int NMAT>
 static void launch_m(const GemvArgs& a, int ri, int nw, hipStream_t s) {
     const dim3 block(nw * kWave);
     const int rows_per_wg = 8 * ri;
     const dim3 grid((a.total_rows + rows_per_wg - 1) / rows_per_wg);
     if constexpr (M <= 4) {
-        if (ri == 4) { hipLaunchKernelGGL((k_q4_gemv<M, 4>), grid, block, 0, s, a); return; }
-        if (ri == 3) { hipLaunchKernelGGL((k_q4_gemv<M, 3>), grid, block, 0, s, a); return; }
+        if (ri == 4) { hipLaunchKernelGGL((k_q4_gemv<M, 4, NMAT>), grid, block, 0, s, a); return; }
+        if (ri == 3) { hipLaunchKernelGGL((k_q4_gemv<M, 3, NMAT>), grid, block, 0, s, a); return; }
     }
     if constexpr (M <= 8) {
-        if (ri == 2) { hipLaunchKernelGGL((k_q4_gemv<M, 2>), grid, block, 0, s, a); return; }
+        if (ri == 2) { hipLaunchKernelGGL((k_q4_gemv<M, 2, NMAT>), grid, block, 0, s, a); return; }
     }
-    hipLaunchKernelGGL((k_q4_gemv<M, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_q4_gemv<M, 1, NMAT>), grid, block, 0, s, a);
+}
+
+template <int M>
+static void launch_m(const GemvArgs& a, int ri, int nw, hipStream_t s) {
+    if (a.n[1] > 0) launch_m<M, 2>(a, ri, nw, s);
+    else launch_m<M, 1>(a, ri, nw, s);
 }
 
 // Waves per workgroup: one block lane per 32-weight block of a row, up to 16

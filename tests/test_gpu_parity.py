@@ -474,3 +474,51 @@ def test_empty_inputs_are_noops():
     assert B.q4_gemm(qs, d, xb[:0]).shape == (0, 4)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# HIP graph replay: the decode step and the packed prefill GEMM
+# ---------------------------------------------------------------------------
+
+def test_graph_replays_match_eager():
+    """Capture q8_1_quantize_act + q4_gemv + q4_gemv_fused2 + q4_gemm (packed
+    path, caller workspace) in one graph; every replay, with eager work and
+    synchronisations between replays, reproduces the eager results exactly."""
+    rng = np.random.default_rng(21)
+    N, K, M = 640, 1024, 160
+    w = [oracle.q4_0_quantize(synth.weights(rng, N, K)) for _ in range(3)]
+    t = [(dev(q), dev(d)) for q, d in w]
+    x1 = bf16_dev(synth.activations(rng, 1, K))
+    xm = bf16_dev(synth.activations(rng, M, K))
+    xq = torch.empty((1, K), dtype=torch.int8, device="cuda")
+    xd = torch.empty((1, K // 32, 2), dtype=torch.int16, device="cuda")
+    y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    y0 = torch.empty_like(y)
+    y1 = torch.empty_like(y)
+    yg = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+
+    def work():
+        B.q8_1_quantize_act(x1, xq, xd)
+        B.q4_gemv(*t[0], xq, xd, y)
+        B.q4_gemv_fused2(*t[1], *t[2], xq, xd, y0, y1)
+        B.q4_gemm(*t[0], xm, y=yg, workspace=ws)
+
+    work()
+    torch.cuda.synchronize()
+    ref = [a.clone() for a in (xq, xd, y, y0, y1, yg)]
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        work()
+    for rep in range(4):
+        for a in (xq, xd, y, y0, y1, yg):
+            a.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, r in zip((xq, xd, y, y0, y1, yg), ref):
+            assert torch.equal(a, r), f"replay {rep} differs"
+        work()                                   # eager work between replays
+        torch.cuda.synchronize()
