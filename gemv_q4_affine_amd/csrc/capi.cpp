@@ -130,7 +130,7 @@ int q4_dispatch_path(int64_t M, int64_t N, int64_t K, int fmt, int have_workspac
 
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt) {
     const int path = q4_dispatch_path(M, N, K, fmt, 1);
-    if (path == Q4_PATH_MFMA) return q4::packed_x_bytes(M, K);
+    if (path == Q4_PATH_MFMA) return q4::packed_x_bytes(M, N, K);
     if (path == Q4_PATH_DEQUANT_GEMM) return N * K * 2;
     return 0;
 }
@@ -234,7 +234,7 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
             if (M > kSkinnyLimit) return Q4_ERR_ARG;
             return hip_status(q4::launch_gemm_skinny(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
         case Q4_PATH_MFMA:
-            if (workspace != nullptr && workspace_bytes >= q4::packed_x_bytes(M, K)) {
+            if (workspace != nullptr && workspace_bytes >= q4::packed_x_bytes(M, N, K)) {
                 if (!aligned16(workspace)) return Q4_ERR_ALIGN;
                 return hip_status(q4::launch_gemm_packed(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, workspace, s));
             }

@@ -589,22 +589,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 // blk_frags_perm.  Rows past M and steps past K are zero.  The GEMM then never
 // converts X: its producer waves only issue direct-to-LDS copies.
 //
-// Workgroup: 6 waves, one per CU.
+// Persistent workgroups of 8 waves, one per CU, each running a stream of
+// 128 x 256 output tiles:
 //  * waves 0-3 (consumers) own NT 32-column tiles each and all MT 32-row tiles
-//    of the workgroup's 128 x 256 output tile; per K step they run the MFMAs
-//    of step k while dequantising the weights of step k+1 into registers,
-//    interleaved instruction by instruction (one basic block per step);
-//  * waves 4-5 (producers) copy the X tile and the raw weight blocks (and
-//    scales) of step k+3 into a 4-deep ring with direct-to-LDS loads and, before
-//    each barrier, wait until step k+2 has landed.  They issue no other memory
-//    operation, so the count in that wait is exact.
-// One barrier per K step.  After the loop the LDS is reused to stage the
-// output tile, which is written back with 16-byte stores.
+//    of the current output tile; per K step they run the MFMAs of step k while
+//    dequantising the weights of step k+1 into registers, interleaved
+//    instruction by instruction (one basic block per step);
+//  * waves 4-7 (producers, one per SIMD) copy the X tile and the raw weight
+//    blocks (and scales) of step k+5 into a 6-deep LDS ring with
+//    direct-to-LDS loads and, before each barrier, wait until step k+2 has
+//    landed.  They issue no other memory operation, so the count in that
+//    wait is exact.  Their stream runs on across tile boundaries.
+// One barrier per K step.  At the end of each tile the consumers write the
+// output straight from the accumulators (pairs of columns per store) and
+// go on with the next tile, whose first steps are already in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kPkSlots = 4;              // ring depth: steps k..k+3 resident
+constexpr int kPkSlots = 6;              // ring depth: steps k..k+5 resident
+constexpr int kPkAhead = kPkSlots - 1;   // producers request step k+5 during step k
+constexpr int kPkProducers = 4;          // producer waves, one per SIMD
 constexpr int kImgRows = 128;            // rows of an image tile
 constexpr int kImgTile = kImgRows * 64;  // halves of an image tile (16 KiB)
-constexpr int kOutStride = 72;           // floats per staged output row (64 + 8 padding)
 
 // Row r of an image tile: chunk c sits at c ^ img_swz(r).  A permutation of
 // rows 0..7 and, separately, of the even and of the odd rows among 0..15.
@@ -733,59 +737,124 @@ __global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint
     *reinterpret_cast<u32x4_t*>(img + t * 8) = o;
 }
 
-// Raw weights of one K step for the workgroup's 256 columns, as the
-// direct-to-LDS copies lay them out (a 2-byte copy puts each lane's value in
-// its own dword).
-template <int WF>
-struct PkW;
-template <>
-struct PkW<WF_Q4_0> {
-    uint8_t q[256][2][16];
-    uint32_t d[256][2];
-};
-template <>
-struct PkW<WF_AFFINE4> {
-    uint8_t q[256][2][16];
-    uint32_t s[256];
-    uint32_t b[256];
-};
+// Weight image for k_gemm_pk: for every 256-column tile and 64-wide K step a
+// contiguous 9 KiB chunk, ((nt * ksteps) + k) * kWChunk bytes in,
+//   bytes    0..8191  nibble blocks, block-plane major: [blk 0..1][col 0..255][16 B]
+//   bytes 8192..9215  Q4_0:   d  as binary16 [blk 0..1][col 0..255]
+//                     affine: s  as bfloat16 [col 0..255], then b [col 0..255]
+// Columns past N and blocks past K are zero (scale 0: the weights are 0).
+// The block-plane order puts the 16-byte block reads of consecutive columns in
+// consecutive LDS units (no bank conflicts), and a chunk travels as nine
+// contiguous 1 KiB direct-to-LDS copies.
+constexpr int kWChunk = 9216;
 
+// planar weights -> image, one workgroup per (256-column tile, 4 K steps).
+// Loads go row by row (8 lanes read a row's 128 contiguous bytes of nibble
+// blocks) into an LDS tile swizzled by row; stores go plane by plane (each
+// thread writes one column's 16-byte block), so both sides are coalesced.
 template <int WF>
-union PkLds {
-    struct {
-        uint16_t x[kPkSlots][kImgTile];
-        PkW<WF> w[kPkSlots];
-    } loop;
-    float out[4][32 * kOutStride];
+__global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsc,
+                                                const uint16_t* __restrict__ wbias, uint8_t* __restrict__ img,
+                                                int N, int K, int n_tiles, int ksteps) {
+    __shared__ u32x4_t lq[256 * 8];            // [column][8 blocks], block slot b ^ (column & 7)
+    const int tid = threadIdx.x;
+    const int kq = (ksteps + 3) / 4;
+    const int grp = blockIdx.x % kq;
+    const int nt = blockIdx.x / kq;
+    const int nb = K / 32;
+    // nibble blocks 8*grp .. 8*grp+7 of the tile's columns
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int u = tid + 256 * i;
+        const int row = u >> 3, b8 = u & 7;
+        const int n = nt * 256 + row;
+        const int b = grp * 8 + b8;
+        u32x4_t q = {0u, 0u, 0u, 0u};
+        if (n < N && b < nb) {
+            if constexpr (WF == WF_Q4_0) q = *reinterpret_cast<const u32x4_t*>(wq + ((int64_t)n * nb + b) * 16);
+            else q = *reinterpret_cast<const u32x4_t*>(wq + (int64_t)n * (K / 2) + (int64_t)b * 16);
+        }
+        lq[row * 8 + (b8 ^ (row & 7))] = q;
+    }
+    // this thread's column's scales (Q4_0: 8 blocks; affine: 4 groups)
+    const int n = nt * 256 + tid;
+    uint16_t sc[8], bi[4];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int b = grp * 8 + i;
+        sc[i] = 0;
+        if constexpr (WF == WF_Q4_0) {
+            if (n < N && b < nb) sc[i] = wsc[(int64_t)n * nb + b];
+        }
+    }
+    if constexpr (WF == WF_AFFINE4) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int gi = grp * 4 + i;
+            const bool ok = n < N && gi < K / 64;
+            sc[i] = ok ? wsc[(int64_t)n * (K / 64) + gi] : (uint16_t)0;
+            bi[i] = ok ? wbias[(int64_t)n * (K / 64) + gi] : (uint16_t)0;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+        const int k = grp * 4 + st;
+        if (k >= ksteps) break;
+        uint8_t* chunk = img + ((int64_t)nt * ksteps + k) * kWChunk;
+#pragma unroll
+        for (int blk = 0; blk < 2; blk++) {
+            const int b8 = 2 * st + blk;
+            *reinterpret_cast<u32x4_t*>(chunk + (blk * 256 + tid) * 16) = lq[tid * 8 + (b8 ^ (tid & 7))];
+            if constexpr (WF == WF_Q4_0) reinterpret_cast<uint16_t*>(chunk + 8192)[blk * 256 + tid] = sc[b8];
+        }
+        if constexpr (WF == WF_AFFINE4) {
+            reinterpret_cast<uint16_t*>(chunk + 8192)[tid] = sc[st];
+            reinterpret_cast<uint16_t*>(chunk + 8704)[tid] = bi[st];
+        }
+    }
+}
+
+// One ring slot: the X tile (16 KiB) and the weight chunk (9 KiB) of a step.
+struct PkSlot {
+    uint16_t x[kImgTile];
+    uint8_t w[kWChunk];
+};
+struct PkLds {
+    PkSlot slot[kPkSlots];
 };
 
 template <int WF, int YDT>
-__global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
+__global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const GemmArgs a) {
     static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
     constexpr int MT = 4, NT = 2;
     constexpr int kCols = 4 * NT * 32;
     constexpr int kRows = MT * 32;
     static_assert(kRows == kImgRows && kCols == 256, "tile shape");
-    __shared__ __attribute__((aligned(16))) PkLds<WF> lds;
+    __shared__ __attribute__((aligned(16))) PkLds lds;
     using Blk = typename BlkOf<WF>::T;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    const int wg = blockIdx.x;
-    const int mt_idx = wg % a.m_tiles;
-    const int nt_idx = wg / a.m_tiles;
-    const int m0 = mt_idx * kRows;
-    const int nwg0 = nt_idx * kCols;
+    // Persistent: workgroup b runs tiles b, b + G, b + 2G, ... (G = gridDim.x)
+    // as one stream of K steps: global step s is step s % nsteps of the
+    // workgroup's tile s / nsteps.  Tile t covers rows (t % m_tiles) * 128 and
+    // columns (t / m_tiles) * 256.
+    const int G = gridDim.x;
+    const int ntiles = a.m_tiles * a.n_tiles;
+    const int my_tiles = (ntiles - (int)blockIdx.x + G - 1) / G;
     const int nb = a.K / 32;
     const int nsteps = (nb + 1) / 2;
+    const int S = my_tiles * nsteps;
+    auto tile_m0 = [&](int i) { return ((int)blockIdx.x + i * G) % a.m_tiles * kRows; };
+    auto tile_n0 = [&](int i) { return ((int)blockIdx.x + i * G) / a.m_tiles * kCols; };
 
     if (wave < 4) {
         // ------------------------------ consumer ------------------------------
         const int j = lane & 31;
         const int g = lane >> 5;
-        const int n0 = nwg0 + wave * NT * 32;
         floatx16_t acc[MT][NT];
 #pragma unroll
         for (int mi = 0; mi < MT; mi++)
@@ -798,21 +867,21 @@ __global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
 
         // raw weight blocks of step k from its ring slot
         auto read_w = [&](int k, Blk (&r)[NT]) {
-            const PkW<WF>& w = lds.loop.w[k & (kPkSlots - 1)];
+            const uint8_t* wb = lds.slot[k % kPkSlots].w;
 #pragma unroll
             for (int ni = 0; ni < NT; ni++) {
                 const int cw = wave * NT * 32 + ni * 32 + j;
-                r[ni].q = *reinterpret_cast<const u32x4_t*>(&w.q[cw][g][0]);
+                r[ni].q = *reinterpret_cast<const u32x4_t*>(wb + (g * 256 + cw) * 16);
                 if constexpr (WF == WF_Q4_0) {
-                    r[ni].d = w.d[cw][g];
+                    r[ni].d = reinterpret_cast<const uint16_t*>(wb + 8192)[g * 256 + cw];
                 } else {
-                    r[ni].s = w.s[cw];
-                    r[ni].b = w.b[cw];
+                    r[ni].s = reinterpret_cast<const uint16_t*>(wb + 8192)[cw];
+                    r[ni].b = reinterpret_cast<const uint16_t*>(wb + 8704)[cw];
                 }
             }
         };
-        // a block past the end of K (K = 32 mod 64) gets a zero scale; the
-        // image holds zeros there as well
+        // blocks past the end of K (K = 32 mod 64) have a zero scale in the
+        // weight image (and zero X in the X image)
         auto dequant = [&](int k, Blk (&r)[NT], u32x4_t (&bf)[NT][4]) {
             const bool bok = 2 * k + g < nb;
 #pragma unroll
@@ -827,7 +896,7 @@ __global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; s++) aofs[s] = j * 64 + (((4 * g + s) ^ img_swz(j)) * 8);   // rows mi*32 + j
         auto read_a = [&](int k, int s, u32x4_t (&av)[MT]) {
-            const uint16_t* la = lds.loop.x[k & (kPkSlots - 1)];
+            const uint16_t* la = lds.slot[k % kPkSlots].x;
 #pragma unroll
             for (int mi = 0; mi < MT; mi++)
                 av[mi] = *reinterpret_cast<const u32x4_t*>(&la[mi * 32 * 64 + aofs[s]]);
@@ -866,8 +935,9 @@ __global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
         // slice 0 during slice 3 (that tile landed one barrier ago), and the
         // raw weights of step k+1 in segment 0 for the dequantisation, which
         // runs word by word under the MFMAs of segments 1-3.  `a0` holds this
-        // step's slice 0 on entry and the next step's on return.  Past the
-        // last step the k+1 slots hold older data that is never used.
+        // step's slice 0 on entry and the next step's on return.  k is the
+        // global step; the next one may start the next tile.  Past the last
+        // step the k+1 slots hold older data that is never used.
         auto body = [&](int k, const u32x4_t (&cur)[NT][4], u32x4_t (&nxt)[NT][4], u32x4_t (&a0)[MT]) {
             Blk r[NT];
             u32x4_t a1[MT], a2[MT], a3[MT];
@@ -880,9 +950,6 @@ __global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
             mfma_slice(1, a1, cur, true);
             read_a(k, 2, a2);
             mfma_slice(1, a1, cur, false);
-            const bool bok = 2 * (k + 1) + g < nb;
-#pragma unroll
-            for (int ni = 0; ni < NT; ni++) zero_blk<WF>(r[ni], bok);
             const BlkConst c0 = blk_const<WF>(r[0]);
             blk_word<WF>(r[0], c0, 0, masks, nxt[0]);
             blk_word<WF>(r[0], c0, 1, masks, nxt[0]);
@@ -904,8 +971,72 @@ __global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
             blk_word<WF>(r[1], c1, 2, masks, nxt[1]);
             blk_word<WF>(r[1], c1, 3, masks, nxt[1]);
             segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 5>{});
+            // the fragments must be complete here: without this the compiler
+            // may sink their dequantisation past the barrier into the next step
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) asm volatile("" : "+v"(nxt[ni][t]));
         };
         static_assert(NT == 2, "the dequantisation split assumes two blocks per step");
+
+        // Epilogue of local tile i, straight from the accumulators (lane:
+        // column j, rows 8*(v/4) + 4*g + v%4).  A DPP swap of neighbouring
+        // lanes hands each lane two adjacent columns of one row -- the even
+        // lane row r, the odd lane row r+1 -- so every store writes a pair
+        // (two bf16 in 4 bytes, or two f32 in 8).  No LDS is involved: the
+        // stores drain while the next tile's MFMAs run.  Then the accumulators
+        // restart.
+        const bool odd = (lane & 1) != 0;
+        const bool pair_ok = (a.N & 1) == 0;                  // pair stores stay aligned
+        auto swap_pair = [](float v) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+        };
+        auto epilogue = [&](int i) {
+            const int m0 = tile_m0(i);
+            const int nw0 = tile_n0(i) + wave * NT * 32;
+#pragma unroll
+            for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++) {
+                    const int col = nw0 + ni * 32 + (j & ~1);    // even column of the pair
+#pragma unroll
+                    for (int v = 0; v < 16; v += 2) {
+                        const float a0v = acc[mi][ni][v], a1v = acc[mi][ni][v + 1];
+                        const float d0 = swap_pair(a0v), d1 = swap_pair(a1v);
+                        const float lo = odd ? d1 : a0v;         // column col
+                        const float hi = odd ? a1v : d0;         // column col + 1
+                        const int row = m0 + mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3) + (odd ? 1 : 0);
+                        if (row >= a.M || col >= a.N) continue;
+                        const int64_t off = (int64_t)row * a.N + col;
+                        if constexpr (YDT == DT_BF16) {
+                            uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + off;
+                            if (pair_ok && col + 1 < a.N) {
+                                const f32x2_t f = {lo, hi};
+                                *reinterpret_cast<uint32_t*>(yp) =
+                                    __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+                            } else {
+                                yp[0] = (uint16_t)f32_to_bf16(lo);
+                                if (col + 1 < a.N) yp[1] = (uint16_t)f32_to_bf16(hi);
+                            }
+                        } else {
+                            float* yp = reinterpret_cast<float*>(a.y) + off;
+                            if (pair_ok && col + 1 < a.N) {
+                                *reinterpret_cast<f32x2_t*>(yp) = f32x2_t{lo, hi};
+                            } else {
+                                yp[0] = lo;
+                                if (col + 1 < a.N) yp[1] = hi;
+                            }
+                        }
+                    }
+                }
+#pragma unroll
+            for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) acc[mi][ni][v] = 0.0f;
+        };
 
         step_barrier<63>();                    // prologue: steps 0 and 1 landed
         u32x4_t a0[MT];
@@ -915,139 +1046,80 @@ __global__ __launch_bounds__(384, 1) void k_gemm_pk(const GemmArgs a) {
             dequant(0, r, bfA);
             read_a(0, 0, a0);
         }
-        // no condition inside an iteration: a conditional use of the next
-        // step's fragments would let the compiler sink their dequantisation
-        // out of the block of MFMAs it is meant to overlap
+        // kl: local index of the current step in its tile, ti: local tile
+        int kl = 0, ti = 0;
+        auto end_step = [&]() {
+            if (kl + 1 == nsteps) {
+                epilogue(ti);
+                ti++;
+                kl = 0;
+            } else {
+                kl++;
+            }
+        };
+        // no condition inside a step's block of MFMAs: a conditional use of the
+        // next step's fragments would let the compiler sink their
+        // dequantisation out of the block it is meant to overlap
         int k = 0;
-        for (; k + 1 < nsteps; k += 2) {
+        for (; k + 1 < S; k += 2) {
             body(k, bfA, bfB, a0);
             step_barrier<63>();
+            end_step();
             body(k + 1, bfB, bfA, a0);
             step_barrier<63>();
+            end_step();
         }
-        if (k < nsteps) {
+        if (k < S) {
             body(k, bfA, bfB, a0);
             step_barrier<63>();
-        }
-
-        // Epilogue.  The last barrier above is also the producers' last (their
-        // copies have all landed), so the ring is free.  Each wave stages one
-        // 32-row slice of its tiles as f32 (lane: column j, rows 8*(v/4) +
-        // 4*g + v%4) and writes it back with 16-byte row stores.
-        float* st = lds.out[wave];
-        constexpr int kVec = (YDT == DT_BF16) ? 8 : 4;        // values per 16-byte store
-        constexpr int kUnitsRow = NT * 32 / kVec;
-        const bool vec_ok = (a.N % kVec) == 0;                // y itself is 16-byte aligned
-#pragma unroll
-        for (int mi = 0; mi < MT; mi++) {
-#pragma unroll
-            for (int ni = 0; ni < NT; ni++)
-#pragma unroll
-                for (int v = 0; v < 16; v++)
-                    st[(8 * (v >> 2) + 4 * g + (v & 3)) * kOutStride + ni * 32 + j] = acc[mi][ni][v];
-#pragma unroll
-            for (int t = 0; t < 32 * kUnitsRow / 64; t++) {
-                const int u = lane + 64 * t;
-                const int row = u / kUnitsRow;
-                const int col = (u % kUnitsRow) * kVec;
-                const int m = m0 + mi * 32 + row;
-                const int n = n0 + col;
-                if (m >= a.M) continue;
-                const float* src = st + row * kOutStride + col;
-                if constexpr (YDT == DT_BF16) {
-                    const float4 f0 = *reinterpret_cast<const float4*>(src);
-                    const float4 f1 = *reinterpret_cast<const float4*>(src + 4);
-                    const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                    uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + (int64_t)m * a.N + n;
-                    if (vec_ok && n + 8 <= a.N) {
-                        u32x4_t o;
-#pragma unroll
-                        for (int e = 0; e < 4; e++) o[e] = f32_to_bf16(f[2 * e]) | (f32_to_bf16(f[2 * e + 1]) << 16);
-                        *reinterpret_cast<u32x4_t*>(yp) = o;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; e++)
-                            if (n + e < a.N) yp[e] = (uint16_t)f32_to_bf16(f[e]);
-                    }
-                } else {
-                    const float4 f0 = *reinterpret_cast<const float4*>(src);
-                    float* yp = reinterpret_cast<float*>(a.y) + (int64_t)m * a.N + n;
-                    if (vec_ok && n + 4 <= a.N) {
-                        *reinterpret_cast<float4*>(yp) = f0;
-                    } else {
-                        const float f[4] = {f0.x, f0.y, f0.z, f0.w};
-#pragma unroll
-                        for (int e = 0; e < 4; e++)
-                            if (n + e < a.N) yp[e] = f[e];
-                    }
-                }
-            }
+            end_step();
         }
     } else {
         // ------------------------------ producer ------------------------------
-        // 2 waves; per step each copies half the X tile (8 x 1 KiB), half the
-        // weight blocks (4 x 32 columns x 2 blocks) and half the scales.
+        // kPkProducers waves; per step each copies its share of the X tile
+        // (1 KiB copies), of the weight blocks (32 columns x 2 blocks per copy)
+        // and of the scales.
         const int pw = wave - 4;
-        const uint16_t* ximg = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)mt_idx * nsteps * kImgTile;
-        constexpr int kXDma = 8, kQDma = 4, kSDma = 4;
-        constexpr int kPerStep = kXDma + kQDma + kSDma;
-        auto copy_step = [&](int k) {
-            const int slot = k & (kPkSlots - 1);
-            const uint16_t* xs = ximg + (int64_t)k * kImgTile;
+        // per step 25 copies of 1 KiB (16 of X, 9 of weights); wave pw takes
+        // copies pw, pw + 4, ...: 7 for wave 0, 6 for the others
+        constexpr int kCopies = 16 + kWChunk / 1024;
+        const int my_copies = (kCopies - pw + kPkProducers - 1) / kPkProducers;
+        // the next step to request: global index rs = ri * nsteps + rk
+        int rs = 0, ri = 0, rk = 0;
+        auto copy_next = [&]() {
+            PkSlot& sl = lds.slot[rs % kPkSlots];
+            const int mt_idx = tile_m0(ri) / kRows;
+            const int nt_idx = tile_n0(ri) / kCols;
+            const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)mt_idx * nsteps + rk) * (kImgTile * 2);
+            const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)nt_idx * nsteps + rk) * kWChunk;
 #pragma unroll
-            for (int i = 0; i < kXDma; i++) {
-                const int c = pw * kXDma + i;                     // 1 KiB chunk of the tile
-                dma16(xs + c * 512 + lane * 8, &lds.loop.x[slot][c * 512]);
+            for (int i = 0; i < (kCopies + kPkProducers - 1) / kPkProducers; i++) {
+                const int c = pw + kPkProducers * i;
+                if (c < 16) dma16(xs + c * 1024 + lane * 16, reinterpret_cast<uint8_t*>(sl.x) + c * 1024);
+                else if (c < kCopies) dma16(wsrc + (c - 16) * 1024 + lane * 16, sl.w + (c - 16) * 1024);
             }
-            PkW<WF>& w = lds.loop.w[slot];
-#pragma unroll
-            for (int i = 0; i < kQDma; i++) {
-                const int q = pw * kQDma + i;                     // 32 columns x 2 blocks
-                int n = nwg0 + q * 32 + (lane >> 1);
-                n = n < a.N ? n : a.N - 1;
-                int blk = 2 * k + (lane & 1);
-                blk = blk < nb ? blk : nb - 1;
-                const uint8_t* src = (WF == WF_Q4_0)
-                    ? reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + blk) * 16
-                    : reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + (int64_t)blk * 16;
-                dma16(src, &w.q[q * 32][0][0]);
-            }
-            if constexpr (WF == WF_Q4_0) {
-#pragma unroll
-                for (int i = 0; i < kSDma; i++) {
-                    const int q = pw * kSDma + i;                 // 32 columns x 2 blocks
-                    int n = nwg0 + q * 32 + (lane >> 1);
-                    n = n < a.N ? n : a.N - 1;
-                    int blk = 2 * k + (lane & 1);
-                    blk = blk < nb ? blk : nb - 1;
-                    dma2(reinterpret_cast<const uint16_t*>(a.b) + (int64_t)n * nb + blk, &w.d[q * 32][0]);
-                }
-            } else {
-                const int ngr = a.K / 64;                         // == nsteps
-#pragma unroll
-                for (int i = 0; i < kSDma / 2; i++) {
-                    const int q = pw * (kSDma / 2) + i;           // 64 columns
-                    int n = nwg0 + q * 64 + lane;
-                    n = n < a.N ? n : a.N - 1;
-                    dma2(reinterpret_cast<const uint16_t*>(a.b) + (int64_t)n * ngr + k, &w.s[q * 64]);
-                    dma2(reinterpret_cast<const uint16_t*>(a.c) + (int64_t)n * ngr + k, &w.b[q * 64]);
-                }
+            rs++;
+            if (++rk == nsteps) {
+                rk = 0;
+                ri++;
             }
         };
-        // prologue: steps 0 and 1 landed, step 2 in flight
-        copy_step(0);
-        if (nsteps > 1) copy_step(1);
-        if (nsteps > 2) {
-            copy_step(2);
-            step_barrier<kPerStep>();
-        } else {
-            step_barrier<0>();
-        }
-        // during step k: request step k+3, then make sure step k+2 has landed
-        for (int k = 0; k < nsteps; k++) {
-            if (k + 3 < nsteps) {
-                copy_step(k + 3);
-                step_barrier<kPerStep>();
+        // prologue: steps 0..4 requested, steps 0 and 1 landed.  Steps k+3..k+5
+        // may stay in flight: 3 steps of this wave's copies.
+        static_assert(kCopies == 25 && kPkProducers == 4 && kPkAhead == 5, "wait counts below");
+        auto wait_step = [&]() {
+            if (my_copies == 7) step_barrier<3 * 7>();
+            else step_barrier<3 * 6>();
+        };
+        for (int i = 0; i < kPkAhead; i++)
+            if (i < S) copy_next();
+        if (S >= kPkAhead) wait_step();
+        else step_barrier<0>();
+        // during step k: request step k+5, then make sure step k+2 has landed
+        for (int k = 0; k < S; k++) {
+            if (k + kPkAhead < S) {
+                copy_next();
+                wait_step();
             } else {
                 step_barrier<0>();
             }
@@ -1278,10 +1350,11 @@ hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* 
     return hipGetLastError();
 }
 
-int64_t packed_x_bytes(int64_t M, int64_t K) {
+int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t m_tiles = (M + kImgRows - 1) / kImgRows;
+    const int64_t n_tiles = (N + 255) / 256;
     const int64_t ksteps = (K + 63) / 64;
-    return m_tiles * ksteps * (int64_t)kImgTile * 2;
+    return m_tiles * ksteps * (int64_t)kImgTile * 2 + n_tiles * ksteps * (int64_t)kWChunk;
 }
 
 template <int WF, int XDT>
@@ -1296,10 +1369,25 @@ template <int WF>
 static void launch_packed_w(GemmArgs ga, int xdt, int ydt, uint16_t* img, hipStream_t s) {
     ga.m_tiles = (ga.M + kImgRows - 1) / kImgRows;
     ga.n_tiles = (ga.N + 255) / 256;
+    const int ksteps = (ga.K + 63) / 64;
     if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, img, s);
     else launch_pack_t<WF, DT_F32>(ga, img, s);
+    // the weight image follows the X image in the workspace
+    uint8_t* wimg = reinterpret_cast<uint8_t*>(img) + (int64_t)ga.m_tiles * ksteps * kImgTile * 2;
+    {
+        const dim3 grid((unsigned)(ga.n_tiles * ((ksteps + 3) / 4))), block(256);
+        hipLaunchKernelGGL((k_pack_w<WF>), grid, block, 0, s, static_cast<const uint8_t*>(ga.a),
+                           static_cast<const uint16_t*>(ga.b), static_cast<const uint16_t*>(ga.c), wimg, ga.N,
+                           ga.K, ga.n_tiles, ksteps);
+    }
     ga.x = img;
-    const dim3 grid((unsigned)(ga.m_tiles * ga.n_tiles)), block(384);
+    ga.a = wimg;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const int tiles = ga.m_tiles * ga.n_tiles;
+    const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(256 + 64 * kPkProducers);
     if (ydt == DT_BF16) hipLaunchKernelGGL((k_gemm_pk<WF, DT_BF16>), grid, block, 0, s, ga);
     else hipLaunchKernelGGL((k_gemm_pk<WF, DT_F32>), grid, block, 0, s, ga);
 }

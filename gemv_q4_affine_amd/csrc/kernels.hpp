@@ -33,9 +33,10 @@ enum : int { WF_Q4_0 = 0, WF_AFFINE4 = 1, WF_DENSE16 = 2 };
 hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* c,
                             const void* x, int xdt, void* y, int ydt,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
-// Large-M quantised GEMM on a packed binary16 X image: converts X into `img`
-// (packed_x_bytes(M, K) bytes, 16-byte aligned), then multiplies.
-int64_t packed_x_bytes(int64_t M, int64_t K);
+// Large-M quantised GEMM on packed images: converts X into a binary16 tile
+// image and the weights into a tile image, both in `img` (packed_x_bytes(M,
+// N, K) bytes, 16-byte aligned), then multiplies.
+int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void* c,
                               const void* x, int xdt, void* y, int ydt,
                               int64_t M, int64_t N, int64_t K, void* img, hipStream_t s);

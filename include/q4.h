@@ -211,11 +211,11 @@ int q4_gemv_fused2(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0,
  *   y         : device out, [M][N] of y_dtype (Q4_BF16 RNE, or Q4_F32)
  *   workspace : device scratch owned by the caller (16-byte aligned), or
  *               NULL.  q4_gemm_workspace_size bytes let the call take its
- *               fastest path.  The MFMA path uses packed_x bytes (see
- *               q4_gemm_workspace_size) to convert X once into the binary16
- *               tile image its matrix-core kernel copies straight into LDS;
- *               with less it converts X inside the GEMM (slower, same
- *               results).  The DEQUANT_GEMM path needs N*K*2 bytes for the
+ *               fastest path.  The MFMA path uses them for tile images of X
+ *               (binary16) and of the weights (the same Q4_0 / affine blocks,
+ *               regrouped per 256-column tile and 64-wide K step) that its
+ *               matrix-core kernel copies straight into LDS; with less it
+ *               converts X inside the GEMM (slower, same results).  The DEQUANT_GEMM path needs N*K*2 bytes for the
  *               dequantised weights: the automatic dispatch picks it only
  *               with that much, and forcing it without returns
  *               Q4_ERR_WORKSPACE.  Calls that share a workspace must not run
@@ -239,8 +239,9 @@ int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
 
 /*
  * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
- * 0 for SKINNY; for MFMA the packed X image, ceil(M/128)*128 *
- * ceil(K/64)*64 * 2 bytes; for DEQUANT_GEMM N*K*2 (a dense binary16 W).
+ * 0 for SKINNY; for MFMA the X and weight tile images,
+ * ceil(M/128)*128 * ceil(K/64)*64 * 2 + ceil(N/256) * ceil(K/64) * 9216 bytes;
+ * for DEQUANT_GEMM N*K*2 (a dense binary16 W).
  * Returns 0 for invalid arguments.
  */
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt);

@@ -116,10 +116,11 @@ def test_gemm_validation():
     assert a(P, P, P, 32, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_SHAPE
     assert a(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, None, 0, None) == B.Q4_ERR_SHAPE
     assert a(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 4, 0, 128, None, 0, None) == B.Q4_OK
-    # the matrix-core path's workspace is the packed X image: M and K rounded
-    # up to the 128-row tile and the 64-wide K step, binary16
-    assert lib().q4_gemm_workspace_size(2048, 12288, 4096, 0) == 2048 * 4096 * 2
-    assert lib().q4_gemm_workspace_size(129, 300, 96, 0) == 256 * 128 * 2
+    # the matrix-core path's workspace holds the X image (M and K rounded up
+    # to the 128-row tile and the 64-wide K step, binary16) and the weight
+    # image (9216 bytes per 256-column tile and K step)
+    assert lib().q4_gemm_workspace_size(2048, 12288, 4096, 0) == 2048 * 4096 * 2 + 48 * 64 * 9216
+    assert lib().q4_gemm_workspace_size(129, 300, 96, 0) == 256 * 128 * 2 + 2 * 2 * 9216
     assert lib().q4_gemm_workspace_size(4, 300, 4096, 0) == 0            # skinny: none
     assert lib().q4_gemm_workspace_size(4, 300, 4000, 0) == 0            # invalid K
     B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
