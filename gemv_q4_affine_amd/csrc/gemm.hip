@@ -776,24 +776,48 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ wq, 
         }
         lq[row * 8 + (b8 ^ (row & 7))] = q;
     }
-    // this thread's column's scales (Q4_0: 8 blocks; affine: 4 groups)
+    // this thread's column's scales (Q4_0: 8 blocks; affine: 4 groups), as
+    // one vector load when K is a multiple of 256 (the run is then whole and
+    // aligned), else one by one
     const int n = nt * 256 + tid;
-    uint16_t sc[8], bi[4];
+    uint16_t sc[8] = {0, 0, 0, 0, 0, 0, 0, 0}, bi[4] = {0, 0, 0, 0};
+    const bool whole = (K % 256) == 0;
+    if constexpr (WF == WF_Q4_0) {
+        if (n < N) {
+            if (whole) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(wsc + (int64_t)n * nb + grp * 8);
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int b = grp * 8 + i;
-        sc[i] = 0;
-        if constexpr (WF == WF_Q4_0) {
-            if (n < N && b < nb) sc[i] = wsc[(int64_t)n * nb + b];
+                for (int i = 0; i < 4; i++) {
+                    sc[2 * i] = (uint16_t)(v[i] & 0xFFFFu);
+                    sc[2 * i + 1] = (uint16_t)(v[i] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    if (grp * 8 + i < nb) sc[i] = wsc[(int64_t)n * nb + grp * 8 + i];
+            }
         }
-    }
-    if constexpr (WF == WF_AFFINE4) {
+    } else {
+        const int ngr = K / 64;
+        if (n < N) {
+            if (whole) {
+                const u32x2_t vs = *reinterpret_cast<const u32x2_t*>(wsc + (int64_t)n * ngr + grp * 4);
+                const u32x2_t vb = *reinterpret_cast<const u32x2_t*>(wbias + (int64_t)n * ngr + grp * 4);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int gi = grp * 4 + i;
-            const bool ok = n < N && gi < K / 64;
-            sc[i] = ok ? wsc[(int64_t)n * (K / 64) + gi] : (uint16_t)0;
-            bi[i] = ok ? wbias[(int64_t)n * (K / 64) + gi] : (uint16_t)0;
+                for (int i = 0; i < 2; i++) {
+                    sc[2 * i] = (uint16_t)(vs[i] & 0xFFFFu);
+                    sc[2 * i + 1] = (uint16_t)(vs[i] >> 16);
+                    bi[2 * i] = (uint16_t)(vb[i] & 0xFFFFu);
+                    bi[2 * i + 1] = (uint16_t)(vb[i] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    if (grp * 4 + i < ngr) {
+                        sc[i] = wsc[(int64_t)n * ngr + grp * 4 + i];
+                        bi[i] = wbias[(int64_t)n * ngr + grp * 4 + i];
+                    }
+            }
         }
     }
     __syncthreads();
@@ -1130,14 +1154,20 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
 // ---------------------------------------------------------------------------
 // Skinny kernel (small M): weights streamed once at HBM rate.
 //
-// Workgroup = 4 waves on the same 16*NT columns, splitting K four ways (the
-// K-splitting of the ET-SoC-1 rewrite) and summing their partial tiles through
-// LDS in a fixed order.  MFMA 16x16x32: lane l owns column j = l % 16 and lane
-// group g = l / 16, and loads one whole 32-weight block -- block kb+g of a
-// 4-block chunk -- with one 128-bit load; in MFMA t (t = 0..3) it supplies
-// elements 8t..8t+7 of that block, and the X fragment it pairs with is
-// X[i][32 (kb+g) + 8t .. +8].  Every lane scales by its own block's d.
+// Workgroup = kSkWaves waves on the same 16*NT columns, splitting K by chunks
+// of 4 blocks (the K-splitting of the ET-SoC-1 rewrite) and summing their
+// partial tiles through LDS in a fixed order.  MFMA 16x16x32: lane l owns
+// column j = l % 16 and lane group g = l / 16, and loads one whole 32-weight
+// block -- block 4c+g of chunk c -- with one 128-bit load; in MFMA t
+// (t = 0..3) it supplies elements 8t..8t+7 of that block, and the X fragment
+// it pairs with is X[i][32 (4c+g) + 8t .. +8].  Every lane scales by its own
+// block's d.  Bandwidth comes from memory-level parallelism: every load is
+// unconditional (clamped addresses; a block past the end of K gets a zero
+// scale, rows past M are computed and dropped), and the next chunk's weights
+// and X fragments are in flight while the current chunk is multiplied.
 // ---------------------------------------------------------------------------
+constexpr int kSkWaves = 8;
+
 struct SkinnyRawQ4 { u32x4_t q; uint32_t d; };
 struct SkinnyRawAff { u32x4_t q; uint32_t s, b; };
 
@@ -1147,43 +1177,45 @@ template <> struct SkRaw<WF_Q4_0> { SkinnyRawQ4 r; };
 template <> struct SkRaw<WF_AFFINE4> { SkinnyRawAff r; };
 template <> struct SkRaw<WF_DENSE16> { u32x4_t h[4]; };
 
+// Raw data of block kblk of column n (both valid): one 128-bit load of the
+// nibbles (16 for dense binary16) and the scales.
 template <int WF>
-__device__ __forceinline__ SkRaw<WF> sk_load(const GemmArgs& a, int n, int kblk, bool ok) {
+__device__ __forceinline__ SkRaw<WF> sk_load(const GemmArgs& a, int n, int kblk) {
     SkRaw<WF> r;
     const int nb = a.K / 32;
     if constexpr (WF == WF_Q4_0) {
-        if (ok) {
-            r.r.q = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + kblk) * 16));
-            r.r.d = reinterpret_cast<const uint16_t*>(a.b)[(int64_t)n * nb + kblk];
-        } else {
-            r.r.q = u32x4_t{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-            r.r.d = 0;
-        }
+        r.r.q = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)n * nb + kblk) * 16));
+        r.r.d = reinterpret_cast<const uint16_t*>(a.b)[(int64_t)n * nb + kblk];
     } else if constexpr (WF == WF_AFFINE4) {
-        if (ok) {
-            r.r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + (int64_t)kblk * 16));
-            const int64_t gi = (int64_t)n * (a.K / 64) + (kblk >> 1);
-            r.r.s = reinterpret_cast<const uint16_t*>(a.b)[gi];
-            r.r.b = reinterpret_cast<const uint16_t*>(a.c)[gi];
-        } else {
-            r.r.q = u32x4_t{0u, 0u, 0u, 0u};
-            r.r.s = 0;
-            r.r.b = 0;
-        }
+        r.r.q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const uint8_t*>(a.a) + (int64_t)n * (a.K / 2) + (int64_t)kblk * 16));
+        const int64_t gi = (int64_t)n * (a.K / 64) + (kblk >> 1);
+        r.r.s = reinterpret_cast<const uint16_t*>(a.b)[gi];
+        r.r.b = reinterpret_cast<const uint16_t*>(a.c)[gi];
     } else {
-        if (ok) {
-            const u32x4_t* w = reinterpret_cast<const u32x4_t*>(
-                reinterpret_cast<const uint16_t*>(a.a) + (int64_t)n * a.K + (int64_t)kblk * 32);
+        const u32x4_t* w = reinterpret_cast<const u32x4_t*>(
+            reinterpret_cast<const uint16_t*>(a.a) + (int64_t)n * a.K + (int64_t)kblk * 32);
 #pragma unroll
-            for (int t = 0; t < 4; t++) r.h[t] = w[t];
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; t++) r.h[t] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+        for (int t = 0; t < 4; t++) r.h[t] = __builtin_nontemporal_load(w + t);
     }
     return r;
+}
+
+// A block that must not contribute: zero scale (quantised) or zero weights.
+template <int WF>
+__device__ __forceinline__ void sk_zero(SkRaw<WF>& r, bool keep) {
+    if constexpr (WF == WF_Q4_0) {
+        r.r.d = keep ? r.r.d : 0u;
+    } else if constexpr (WF == WF_AFFINE4) {
+        r.r.s = keep ? r.r.s : 0u;
+        r.r.b = keep ? r.r.b : 0u;
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) r.h[t][e] = keep ? r.h[t][e] : 0u;
+    }
 }
 
 // Elements 8t..8t+7 of the lane's block as 8 binary16 values, t = 0..3.
@@ -1226,8 +1258,8 @@ __device__ __forceinline__ void sk_frag(const SkRaw<WF>& r, u32x4_t (&out)[4]) {
 }
 
 template <int WF, int MT, int NT, int XDT, int YDT>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const GemmArgs a) {
-    __shared__ float red[3][MT * 16 * NT * 16];
+__global__ __launch_bounds__(64 * kSkWaves) void k_gemm_skinny(const GemmArgs a) {
+    __shared__ float red[kSkWaves - 1][MT * 16 * NT * 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1238,35 +1270,56 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const GemmArgs a) {
     const int nb = a.K / 32;
     const int nchunks = (nb + 3) / 4;
 
+    // clamped columns and rows (never stored when out of range)
+    int ncl[NT];
+    bool nok[NT];
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) {
+        const int n = n0 + ni * 16 + j;
+        nok[ni] = n < a.N;
+        ncl[ni] = nok[ni] ? n : a.N - 1;
+    }
+    int64_t xrow[MT];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) {
+        const int m = mi * 16 + j;
+        xrow[mi] = (int64_t)(m < a.M ? m : a.M - 1) * a.K;
+    }
+
+    struct Stage {
+        SkRaw<WF> w[NT];
+        RawX8<XDT> x[MT][4];
+        bool kok;
+    };
+    auto load = [&](int c, Stage& st) {
+        const int kblk = c * 4 + g;
+        st.kok = kblk < nb;
+        const int kb = st.kok ? kblk : nb - 1;
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) st.w[ni] = sk_load<WF>(a, ncl[ni], kb);
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+            for (int t = 0; t < 4; t++) st.x[mi][t] = load_x8_raw<XDT>(a.x, xrow[mi] + (int64_t)kb * 32 + 8 * t);
+    };
+
     floatx4_t acc[MT][NT];
 #pragma unroll
     for (int mi = 0; mi < MT; mi++)
 #pragma unroll
         for (int ni = 0; ni < NT; ni++) acc[mi][ni] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int c = wave; c < nchunks; c += 4) {
-        const int kblk = c * 4 + g;
-        const bool kok = kblk < nb;
-        SkRaw<WF> raw[NT];
-#pragma unroll
-        for (int ni = 0; ni < NT; ni++) {
-            const int n = n0 + ni * 16 + j;
-            raw[ni] = sk_load<WF>(a, n, kblk, kok && n < a.N);
-        }
-        // X fragments: row i = mi*16 + j, 32 values of block kblk
+    auto compute = [&](Stage& st) {
         u32x4_t xa[MT][4];
 #pragma unroll
-        for (int mi = 0; mi < MT; mi++) {
-            const int m = mi * 16 + j;
-            const bool ok = kok && m < a.M;
+        for (int mi = 0; mi < MT; mi++)
 #pragma unroll
-            for (int t = 0; t < 4; t++)
-                xa[mi][t] = load_x8<XDT>(a.x, (int64_t)m * a.K + (int64_t)kblk * 32 + 8 * t, ok);
-        }
+            for (int t = 0; t < 4; t++) xa[mi][t] = convert_x8<XDT>(st.x[mi][t]);
 #pragma unroll
         for (int ni = 0; ni < NT; ni++) {
+            sk_zero<WF>(st.w[ni], st.kok && nok[ni]);
             u32x4_t bfr[4];
-            sk_frag<WF>(raw[ni], bfr);
+            sk_frag<WF>(st.w[ni], bfr);
 #pragma unroll
             for (int t = 0; t < 4; t++)
 #pragma unroll
@@ -1275,9 +1328,31 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const GemmArgs a) {
                         __builtin_bit_cast(half8_t, xa[mi][t]), __builtin_bit_cast(half8_t, bfr[t]), acc[mi][ni], 0, 0,
                         0);
         }
+    };
+
+    if (wave < nchunks) {
+        // chunks wave, wave + W, ...: the next one loads while this one
+        // multiplies; two stages with fixed roles (no register copies, which
+        // would wait for the loads in flight).  A load past the end repeats
+        // the last chunk and is never used.
+        Stage s0, s1;
+        load(wave, s0);
+        for (int c = wave;;) {
+            const int c1 = c + kSkWaves;
+            load(c1 < nchunks ? c1 : c, s1);
+            __builtin_amdgcn_sched_barrier(0);     // the next chunk's loads go out before this chunk's math
+            compute(s0);
+            if (c1 >= nchunks) break;
+            const int c2 = c1 + kSkWaves;
+            load(c2 < nchunks ? c2 : c1, s0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(s1);
+            if (c2 >= nchunks) break;
+            c = c2;
+        }
     }
 
-    // fixed-order reduction over the 4 K-splitting waves: out = w0 + w1 + w2 + w3
+    // fixed-order reduction over the K-splitting waves: w0 + w1 + ...;
     // lane holds column j, rows 4*g + v of each 16x16 tile
     if (wave > 0) {
 #pragma unroll
@@ -1300,9 +1375,8 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const GemmArgs a) {
                     const int r = mi * 16 + 4 * g + v;
                     const int idx = (r * NT + ni) * 16 + j;
                     float t = acc[mi][ni][v];
-                    t += red[0][idx];
-                    t += red[1][idx];
-                    t += red[2][idx];
+#pragma unroll
+                    for (int w = 0; w < kSkWaves - 1; w++) t += red[w][idx];
                     if (n < a.N && r < a.M) store_y(a.y, YDT, (int64_t)r * a.N + n, t);
                 }
             }
@@ -1405,7 +1479,7 @@ hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void
 
 template <int WF, int MT, int NT, int XDT, int YDT>
 static void launch_skinny_t(GemmArgs ga, hipStream_t s) {
-    const dim3 grid((unsigned)((ga.N + NT * 16 - 1) / (NT * 16))), block(256);
+    const dim3 grid((unsigned)((ga.N + NT * 16 - 1) / (NT * 16))), block(64 * kSkWaves);
     hipLaunchKernelGGL((k_gemm_skinny<WF, MT, NT, XDT, YDT>), grid, block, 0, s, ga);
 }
 
