@@ -3,14 +3,15 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections decode,gemm,affine,llama,cpu]
 
 A step is one decode token through the decode-GEMV workload (Q4_0 W
-[12288, 4096], one bf16 activation [1, 4096] ~ N(0,1)): quantise the
-activation to Q8_1 once, run q4_gemv on W and q4_gemv_fused2 on a (gate, up)
-pair of the same shape.  The weights rotate through enough distinct copies
+[12288, 4096], one bf16 activation [1, 4096] ~ N(0,1)): q4_gemv_act on W and
+q4_gemv_fused2_act on a (gate, up) pair of the same shape, each quantising
+the activation to Q8_1 on chip (the same bits as q8_1_quantize_act, whose
+three-launch step is timed beside it under "extra").  The weights rotate through enough distinct copies
 (>= 538 MB) that every step streams them from HBM, not from the 256 MB
 last-level cache.  Steps run as replays of a HIP graph (as a decode loop
 would), and `value` is the step's algorithmic bytes over the wall-clock time
 of exactly K steps between two synchronisations (GB/s).  The roofline object
-is q4_gemv_fused2's, the step's longest kernel: its mean duration over
+is q4_gemv_fused2_act's, the step's longest kernel: its mean duration over
 back-to-back launches queued behind a GPU hold, bracketed by HIP events on
 the launching stream.
 
@@ -151,10 +152,18 @@ def decode_section(steps: int, warmup: int, copies: int):
     y0 = torch.empty((1, N), dtype=torch.float32, device="cuda")
     y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
 
+    ya = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    ya0 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    ya1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+
+    wbytes = N * K // 2 + N * (K // 32) * 2                 # one Q4_0 matrix: nibbles + binary16 d
     bytes_q8 = K * 2 + K + (K // 32) * 4
-    bytes_gemv = N * K // 2 + N * (K // 32) * 2 + K + (K // 32) * 4 + N * 4
-    bytes_f2 = 2 * (N * K // 2 + N * (K // 32) * 2) + K + (K // 32) * 4 + 2 * N * 4
-    bytes_step = bytes_q8 + bytes_gemv + bytes_f2
+    bytes_gemv = wbytes + K + (K // 32) * 4 + N * 4
+    bytes_f2 = 2 * wbytes + K + (K // 32) * 4 + 2 * N * 4
+    bytes_gemv_act = wbytes + K * 2 + N * 4
+    bytes_f2_act = 2 * wbytes + K * 2 + 2 * N * 4
+    bytes_step_split = bytes_q8 + bytes_gemv + bytes_f2
+    bytes_step = bytes_gemv_act + bytes_f2_act
 
     def q8(i):
         B.q8_1_quantize_act(x, xq, xd)
@@ -167,70 +176,97 @@ def decode_section(steps: int, warmup: int, copies: int):
         _, (gq, gd), (uq, ud) = rot[i % copies]
         B.q4_gemv_fused2(gq, gd, uq, ud, xq, xd, y0, y1)
 
-    def step(i):
+    def gemv_act(i):
+        (wq, wd), _, _ = rot[i % copies]
+        B.q4_gemv_act(wq, wd, x, ya)
+
+    def fused2_act(i):
+        _, (gq, gd), (uq, ud) = rot[i % copies]
+        B.q4_gemv_fused2_act(gq, gd, uq, ud, x, ya0, ya1)
+
+    def step_split(i):
         q8(i)
         gemv(i)
         fused2(i)
 
-    # eager reference results, then the step as a HIP graph over all copies
-    step(0)
-    torch.cuda.synchronize()
-    ref = (y.clone(), y0.clone(), y1.clone())
-    side = torch.cuda.Stream()
-    g_all = graph_of([(lambda i=i: step(i)) for i in range(copies)], side)
-    rem = steps % copies
-    g_rem = graph_of([(lambda i=i: step(i)) for i in range(rem)], side) if rem else None
-    for _ in range(max(1, -(-warmup // copies))):
-        g_all.replay()
-    torch.cuda.synchronize()
-    step(0)
-    torch.cuda.synchronize()
-    assert torch.equal(y, ref[0]) and torch.equal(y0, ref[1]) and torch.equal(y1, ref[2]), \
-        "graph replays changed the decode results"
+    def step(i):
+        gemv_act(i)
+        fused2_act(i)
 
-    # whole-job timing: exactly `steps` steps between synchronisations
-    n_full = steps // copies
+    # eager results: the one-launch-per-matrix step must give the bits of the
+    # quantise-then-GEMV step
+    step_split(0)
+    step(0)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(n_full):
-        g_all.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    ev1.record()
+    assert torch.equal(ya, y) and torch.equal(ya0, y0) and torch.equal(ya1, y1), \
+        "q4_gemv_act / q4_gemv_fused2_act differ from q8_1_quantize_act + q4_gemv / q4_gemv_fused2"
+    ref = (ya.clone(), ya0.clone(), ya1.clone())
+    side = torch.cuda.Stream()
+
+    def timed_steps(fn):
+        g_all = graph_of([(lambda i=i: fn(i)) for i in range(copies)], side)
+        rem = steps % copies
+        g_rem = graph_of([(lambda i=i: fn(i)) for i in range(rem)], side) if rem else None
+        for _ in range(max(1, -(-warmup // copies))):
+            g_all.replay()
+        torch.cuda.synchronize()
+        # whole-job timing: exactly `steps` steps between synchronisations
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(steps // copies):
+            g_all.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+    ms_split, gpu_ms_split = timed_steps(step_split)
+    ms_per_step, gpu_ms_per_step = timed_steps(step)
+    step(0)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / steps
-    gpu_ms_per_step = ev0.elapsed_time(ev1) / steps
+    assert torch.equal(ya, ref[0]) and torch.equal(ya0, ref[1]) and torch.equal(ya1, ref[2]), \
+        "graph replays changed the decode results"
 
     # per-kernel launch durations: back-to-back launches of one kernel,
     # (a) as a graph over the copies, (b) eagerly queued behind a hold
     reps = max(1, 200 // copies)
     per = {}
-    for name, fn in (("q8_1_quantize_act", q8), ("q4_gemv", gemv), ("q4_gemv_fused2", fused2)):
+    for name, fn in (("q8_1_quantize_act", q8), ("q4_gemv", gemv), ("q4_gemv_fused2", fused2),
+                     ("q4_gemv_act", gemv_act), ("q4_gemv_fused2_act", fused2_act)):
         g = graph_of([(lambda i=i: fn(i)) for i in range(copies)], side)
         per[name] = {"us_graph": graph_region_us(g, copies, reps),
                      "us_eager": region_us(fn, reps * copies)}
         del g
-    log(f"[decode] step {ms_per_step * 1e3:.2f} us wall ({gpu_ms_per_step * 1e3:.2f} us GPU); kernels "
+    log(f"[decode] step {ms_per_step * 1e3:.2f} us wall ({gpu_ms_per_step * 1e3:.2f} us GPU), "
+        f"quantise-then-GEMV step {ms_split * 1e3:.2f} us; kernels "
         + ", ".join(f"{k} {v['us_graph']:.2f}/{v['us_eager']:.2f} us" for k, v in per.items())
         + " (graph/eager)")
-    us_gemv = per["q4_gemv"]["us_eager"]
-    us_f2 = per["q4_gemv_fused2"]["us_eager"]
+
+    def kern(name, nbytes):
+        us = per[name]["us_eager"]
+        return {"us": us, "bytes": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9, **per[name]}
+
     return {
         "ms_per_step": ms_per_step,
         "gpu_ms_per_step": gpu_ms_per_step,
         "bytes_step": bytes_step,
         "gbs_step": bytes_step / (ms_per_step * 1e-3) / 1e9,
         "launch": "HIP graph of %d steps, replayed" % copies,
-        "gemv": {"us": us_gemv, "bytes": bytes_gemv, "gbs": bytes_gemv / (us_gemv * 1e-6) / 1e9, **per["q4_gemv"]},
-        "fused2": {"us": us_f2, "bytes": bytes_f2, "gbs": bytes_f2 / (us_f2 * 1e-6) / 1e9,
-                   **per["q4_gemv_fused2"]},
-        "q8_1_quantize_act": {"bytes": bytes_q8, **per["q8_1_quantize_act"]},
+        "gemv_act": kern("q4_gemv_act", bytes_gemv_act),
+        "fused2_act": kern("q4_gemv_fused2_act", bytes_f2_act),
+        "quantise_then_gemv_step": {
+            "ms_per_step": ms_split, "gpu_ms_per_step": gpu_ms_split, "bytes_step": bytes_step_split,
+            "gbs_step": bytes_step_split / (ms_split * 1e-3) / 1e9,
+            "gemv": kern("q4_gemv", bytes_gemv),
+            "fused2": kern("q4_gemv_fused2", bytes_f2),
+            "q8_1_quantize_act": {"bytes": bytes_q8, **per["q8_1_quantize_act"]},
+        },
         "copies": copies,
-        "rotated_bytes": copies * 3 * (N * K // 2 + N * (K // 32) * 2),
+        "rotated_bytes": copies * 3 * wbytes,
     }
 
 
@@ -355,22 +391,18 @@ def llama_section(iters: int):
     torch.cuda.synchronize()
     H, F = 2048, 8192
     xs = {k: bf16_dev(synth.activations(rng, 1, k)) for k in (H, F)}
-    qbuf = {k: (torch.empty((1, k), dtype=torch.int8, device="cuda"),
-                torch.empty((1, k // 32, 2), dtype=torch.int16, device="cuda")) for k in (H, F)}
     yb = {n: torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (512, 2048, 8192)}
     yb2 = {n: torch.empty((1, n), dtype=torch.float32, device="cuda") for n in (512, 8192)}
 
+    # per layer: q, (k, v), o, (gate, up), down; each GEMV quantises its bf16
+    # activation on chip
     def decode_token(_i):
         for lw in layers:
-            xq, xd = B.q8_1_quantize_act(xs[H], *qbuf[H])
-            B.q4_gemv(*lw["q"], xq, xd, yb[2048])
-            B.q4_gemv_fused2(*lw["k"], *lw["v"], xq, xd, yb[512], yb2[512])
-            xq, xd = B.q8_1_quantize_act(xs[H], *qbuf[H])
-            B.q4_gemv(*lw["o"], xq, xd, yb[2048])
-            xq, xd = B.q8_1_quantize_act(xs[H], *qbuf[H])
-            B.q4_gemv_fused2(*lw["gate"], *lw["up"], xq, xd, yb[8192], yb2[8192])
-            xq, xd = B.q8_1_quantize_act(xs[F], *qbuf[F])
-            B.q4_gemv(*lw["down"], xq, xd, yb[2048])
+            B.q4_gemv_act(*lw["q"], xs[H], yb[2048])
+            B.q4_gemv_fused2_act(*lw["k"], *lw["v"], xs[H], yb[512], yb2[512])
+            B.q4_gemv_act(*lw["o"], xs[H], yb[2048])
+            B.q4_gemv_fused2_act(*lw["gate"], *lw["up"], xs[H], yb[8192], yb2[8192])
+            B.q4_gemv_act(*lw["down"], xs[F], yb[2048])
 
     side = torch.cuda.Stream()
     g_tok = graph_of([lambda: decode_token(0)], side)
@@ -399,7 +431,8 @@ def llama_section(iters: int):
         "prefill_tokens_per_s": Mp * 1e3 / prefill_ms,
         "prefill_tflops": flop512 / (prefill_ms * 1e-3) / 1e12,
         "weights_bytes": total_bytes,
-        "launches": "decode: one HIP graph per token; prefill: eager launches queued back to back",
+        "launches": "decode: one HIP graph per token, 5 GEMV launches per layer (q4_gemv_act, "
+                    "q4_gemv_fused2_act); prefill: eager q4_gemm launches queued back to back",
     }
     log(f"[llama] decode {res['decode_tokens_per_s']:.0f} tok/s ({res['decode_weight_gbs']:.0f} GB/s); "
         f"prefill {res['prefill_tokens_per_s']:.0f} tok/s ({res['prefill_tflops']:.0f} TFLOP/s)")
@@ -485,7 +518,7 @@ def main():
         extra["counter_calibration"] = calib_section()
     cpu = cpu_baseline(args.cpu_seconds) if "cpu" in sections else None
 
-    g = dec["fused2"]
+    g = dec["fused2_act"]
     line = {
         "metric": "Q4 GEMV GB/s (M=1) and Q4 GEMM TFLOP/s (M=2048), N=12288 K=4096",
         "value": round(dec["gbs_step"], 2),
@@ -500,14 +533,14 @@ def main():
         "dtype": "q4_0 x q8_1 (int32 block dots, f32 accumulate)",
         "data": "synthetic (seeded numpy PCG64: W ~ N(0, 0.02^2), x ~ N(0, 1) as bf16)",
         "config": {
-            "workload": "decode GEMV Q4_0 N=12288 K=4096 M=1: q8_1_quantize_act + q4_gemv + q4_gemv_fused2 "
-                        "(gate, up) per step, weights rotated over %d copies, steps replayed as a HIP graph"
-                        % args.copies,
+            "workload": "decode GEMV Q4_0 N=12288 K=4096 M=1: q4_gemv_act + q4_gemv_fused2_act (gate, up) "
+                        "per step, each quantising the bf16 activation to Q8_1 on chip; weights rotated over "
+                        "%d copies, steps replayed as a HIP graph" % args.copies,
             "M": 1, "N": 12288, "K": 4096,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "q4_gemv_fused2 (k_q4_gemv<1,4,2>), the step's longest kernel",
+            "kernel": "q4_gemv_fused2_act (k_q4_gemv_act<1,4,2,bf16>), the step's longest kernel",
             "achieved": round(g["gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -23,6 +23,7 @@ Q4_FMT_Q4_0, Q4_FMT_AFFINE4 = 0, 1
 Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM = 0, 1, 2, 3
 Q4_KEY_SKINNY_MAX_M, Q4_KEY_DEQUANT_MIN_M, Q4_KEY_FORCE_PATH = 0, 1, 2
 Q4_GEMV_MAX_M = 16
+Q4_GEMV_ACT_MAX_M = 4
 
 # exported symbols and their ctypes signatures
 _P, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -34,6 +35,8 @@ SIGNATURES = {
     "affine4_dequantize": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _INT, _P]),
     "q4_gemv": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "q4_gemv_fused2": (_INT, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P]),
+    "q4_gemv_act": (_INT, [_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P]),
+    "q4_gemv_fused2_act": (_INT, [_P, _P, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _I64, _P]),
     "q4_gemm": (_INT, [_P, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "affine4_gemm": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "q4_gemm_workspace_size": (_I64, [_I64, _I64, _I64, _INT]),
@@ -182,6 +185,27 @@ def q4_gemv_fused2(w0_qs, w0_d, w1_qs, w1_d, x_qs, x_ds, y0=None, y1=None, strea
     y1 = _empty((M, N1), torch.float32, x_qs) if y1 is None else y1
     _check("q4_gemv_fused2", lib().q4_gemv_fused2(_p(w0_qs), _p(w0_d), N0, _p(w1_qs), _p(w1_d), N1, _p(x_qs),
                                                   _p(x_ds), _p(y0), _p(y1), M, K, _stream(stream)))
+    return y0, y1
+
+
+def q4_gemv_act(w_qs, w_d, x, y=None, stream=None):
+    """q4_gemv on a raw bf16 / f32 activation x [M, K], quantised to Q8_1 inside
+    the kernel; bit-identical to q8_1_quantize_act followed by q4_gemv."""
+    N = w_d.shape[0]
+    M, K = x.shape
+    y = _empty((M, N), torch.float32, x) if y is None else y
+    _check("q4_gemv_act", lib().q4_gemv_act(_p(w_qs), _p(w_d), _p(x), _dt(x), _p(y), M, N, K, _stream(stream)))
+    return y
+
+
+def q4_gemv_fused2_act(w0_qs, w0_d, w1_qs, w1_d, x, y0=None, y1=None, stream=None):
+    N0, N1 = w0_d.shape[0], w1_d.shape[0]
+    M, K = x.shape
+    y0 = _empty((M, N0), torch.float32, x) if y0 is None else y0
+    y1 = _empty((M, N1), torch.float32, x) if y1 is None else y1
+    _check("q4_gemv_fused2_act", lib().q4_gemv_fused2_act(_p(w0_qs), _p(w0_d), N0, _p(w1_qs), _p(w1_d), N1,
+                                                          _p(x), _dt(x), _p(y0), _p(y1), M, K,
+                                                          _stream(stream)))
     return y0, y1
 
 

@@ -72,6 +72,25 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
 
+namespace q4 {
+
+int current_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];   // 0: not yet queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+}  // namespace q4
+
 extern "C" {
 
 const char* q4_status_string(int status) {
@@ -215,6 +234,39 @@ int q4_gemv_fused2(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0, const
     if (N1 > 0 && (rc = check_ptrs_aligned({w1_qs, w1_d, y1}))) return rc;
     return hip_status(
         q4::launch_q4_gemv(w0_qs, w0_d, y0, N0, w1_qs, w1_d, y1, N1, x_qs, x_ds, M, K, as_stream(stream)));
+}
+
+static int gemv_act_shape(int x_dtype, int64_t M) {
+    if (x_dtype != Q4_F32 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (M > Q4_GEMV_ACT_MAX_M) return Q4_ERR_SHAPE;
+    return Q4_OK;
+}
+
+int q4_gemv_act(const uint8_t* w_qs, const uint16_t* w_d, const void* x, int x_dtype, float* y, int64_t M,
+                int64_t N, int64_t K, void* stream) {
+    int rc = check_dims(M, N, K, 32);
+    if (rc) return rc;
+    if ((rc = gemv_act_shape(x_dtype, M))) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_qs, w_d, x, y}))) return rc;
+    return hip_status(q4::launch_q4_gemv_act(w_qs, w_d, y, N, nullptr, nullptr, nullptr, 0, x, x_dtype, M, K,
+                                             as_stream(stream)));
+}
+
+int q4_gemv_fused2_act(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0, const uint8_t* w1_qs,
+                       const uint16_t* w1_d, int64_t N1, const void* x, int x_dtype, float* y0, float* y1,
+                       int64_t M, int64_t K, void* stream) {
+    int rc = check_dims(M, N0, K, 32);
+    if (rc) return rc;
+    if ((rc = check_dims(M, N1, K, 32))) return rc;
+    if ((rc = gemv_act_shape(x_dtype, M))) return rc;
+    if (N0 + N1 > int64_t(0x7FFFFFFF)) return Q4_ERR_SHAPE;
+    if (M == 0 || N0 + N1 == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({x}))) return rc;
+    if (N0 > 0 && (rc = check_ptrs_aligned({w0_qs, w0_d, y0}))) return rc;
+    if (N1 > 0 && (rc = check_ptrs_aligned({w1_qs, w1_d, y1}))) return rc;
+    return hip_status(
+        q4::launch_q4_gemv_act(w0_qs, w0_d, y0, N0, w1_qs, w1_d, y1, N1, x, x_dtype, M, K, as_stream(stream)));
 }
 
 // ---- GEMM ----------------------------------------------------------------------------

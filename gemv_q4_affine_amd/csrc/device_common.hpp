@@ -9,6 +9,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "kernels.hpp"   // dtype codes
+
 namespace q4 {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -74,6 +78,108 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
+}
+
+
+// Reductions over a group of 8 lanes that every lane of the group ends up
+// holding.  Only exact, order-free operations go through them (max, integer
+// sum), so the grouping does not change any result.
+//
+// Q8Adjacent: aligned groups of 8 neighbouring lanes, through DPP: 0xB1 swaps
+// neighbours, 0x4E swaps pairs within a quad, 0x141 (row_half_mirror) maps
+// lane i of the group to lane 7 - i, in the other quad.
+struct Q8Adjacent {
+    template <int CTRL>
+    __device__ static int dpp(int v) { return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false); }
+    __device__ static float max8(float a) {
+        a = fmaxf(a, __int_as_float(dpp<0xB1>(__float_as_int(a))));
+        a = fmaxf(a, __int_as_float(dpp<0x4E>(__float_as_int(a))));
+        return fmaxf(a, __int_as_float(dpp<0x141>(__float_as_int(a))));
+    }
+    __device__ static int sum8(int a) {
+        a += dpp<0xB1>(a);
+        a += dpp<0x4E>(a);
+        return a + dpp<0x141>(a);
+    }
+};
+
+// Q8Strided: the 8 lanes of a wave that agree in lane & 7 (lanes c, c+8, ...,
+// c+56): DPP row_ror:8 pairs lane i with i ^ 8 inside its row of 16, and the
+// gfx950 lane swaps pair rows (i ^ 16) and wave halves (i ^ 32); a swap of a
+// register with itself leaves the lane's own value in one result and its
+// partner's in the other.
+struct Q8Strided {
+    __device__ static int x8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
+    __device__ static float max8(float a) {
+        a = fmaxf(a, __int_as_float(x8(__float_as_int(a))));
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+        a = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+        return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    }
+    __device__ static int sum8(int a) {
+        a += x8(a);
+        auto r = __builtin_amdgcn_permlane16_swap((unsigned)a, (unsigned)a, false, false);
+        a = (int)(r[0] + r[1]);
+        auto t = __builtin_amdgcn_permlane32_swap((unsigned)a, (unsigned)a, false, false);
+        return (int)(t[0] + t[1]);
+    }
+};
+
+// Q8_1 quantisation of one 32-value block by a group of 8 lanes (all active),
+// 4 values per lane: d = amax / 127 (binary32), q = round-half-away(v / d)
+// via v * (1 / d), s = d * sum(q).  Returns the lane's 4 codes packed
+// little-endian; d (and, with WANT_S, s) comes back as binary16 bits (round
+// to nearest even), the same on all 8 lanes.  The standalone quantiser and
+// the GEMV that quantises its own activation both use it, so they give the
+// same bits.
+template <class G, bool WANT_S>
+__device__ __forceinline__ uint32_t q8_1_block(const float (&v)[4], uint32_t& d16, uint32_t& s16) {
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = G::max8(amax);
+    const float dd = amax / 127.0f;
+    const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+    int q[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const float t = v[j] * id;
+        q[j] = (int)roundf(t);  // half away from zero
+        sum += q[j];
+    }
+    d16 = f32_to_f16_rne(dd);
+    if constexpr (WANT_S) {
+        sum = G::sum8(sum);
+        s16 = f32_to_f16_rne(dd * (float)sum);
+    }
+    return (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) | ((uint32_t)(q[2] & 0xFF) << 16) |
+           ((uint32_t)(q[3] & 0xFF) << 24);
+}
+
+// 4 consecutive activation values (bf16 or f32) starting at element e0: the
+// raw load, the conversion to binary32, and both in one.
+template <int XDT>
+using act4_raw_t = std::conditional_t<XDT == DT_F32, float4, u32x2_t>;
+
+template <int XDT>
+__device__ __forceinline__ act4_raw_t<XDT> load_act4_raw(const void* x, int64_t e0) {
+    if constexpr (XDT == DT_F32) return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + e0);
+    else return *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(x) + e0);
+}
+
+template <int XDT>
+__device__ __forceinline__ void act4_to_f32(const act4_raw_t<XDT>& t, float (&v)[4]) {
+    if constexpr (XDT == DT_F32) {
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+        v[0] = bf16_to_f32(t[0] & 0xFFFFu); v[1] = bf16_to_f32(t[0] >> 16);
+        v[2] = bf16_to_f32(t[1] & 0xFFFFu); v[3] = bf16_to_f32(t[1] >> 16);
+    }
+}
+
+template <int XDT>
+__device__ __forceinline__ void load_act4(const void* x, int64_t e0, float (&v)[4]) {
+    act4_to_f32<XDT>(load_act4_raw<XDT>(x, e0), v);
 }
 
 }  // namespace q4

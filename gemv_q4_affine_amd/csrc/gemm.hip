@@ -1456,10 +1456,7 @@ static void launch_packed_w(GemmArgs ga, int xdt, int ydt, uint16_t* img, hipStr
     }
     ga.x = img;
     ga.a = wimg;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
+    const int cus = current_cu_count();
     const int tiles = ga.m_tiles * ga.n_tiles;
     const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(256 + 64 * kPkProducers);
     if (ydt == DT_BF16) hipLaunchKernelGGL((k_gemm_pk<WF, DT_BF16>), grid, block, 0, s, ga);

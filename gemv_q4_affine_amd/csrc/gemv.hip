@@ -10,18 +10,22 @@
 // sync-after focused repro", Important source touch points: gate+up, K+V).
 //
 // Design (HBM-bound: 4.5 bits per weight streamed once, ~3.5 flop/byte):
-//  * a workgroup of NW waves (NW = min(16, ceil(K/256))) splits K into 8*NW
-//    "block lanes": lane l of wave w owns 32-weight block column
-//    b = 8w + (l & 7) (and b + 8*NW, ... for longer rows) and row lane
-//    l >> 3, so it loads its activation block once (32 int8 + d8) and reuses
-//    it for every weight row it visits;
+//  * the K/32 block columns of a row are dealt to V = min(16, ceil(K/256))
+//    virtual waves of 8 block lanes: virtual lane j = 8v + c owns columns
+//    j, j + 8V, j + 16V, ... and sums them in that order.  A workgroup runs
+//    V / F physical waves; lane l of wave w plays virtual lanes
+//    8(w + f V/F) + (l & 7), f < F, which is to say that it walks columns
+//    b = 8w + (l & 7) + k 8V/F and adds column k into accumulator k mod F.
+//    Row lane l >> 3 picks the rows.  The sum order thus depends on K only,
+//    not on F, the rows per lane or the row's position, so every launch
+//    shape, and the fused two-matrix launch, gives the same bits;
 //  * each lane streams RI weight rows (rows r0 + (l >> 3) + 8i): per row one
 //    128-bit load of the block's 16 nibble bytes and its binary16 d; the 8
 //    lanes of a row read 128 contiguous bytes, whole cache lines.  The
 //    (cache-resident) activation is fetched first and the weight rows in
-//    order, all before any arithmetic, so the loads are in flight together
-//    and row i's arithmetic overlaps the arrival of rows i+1.. (loads return
-//    in order);
+//    order, U columns at a time, all before any arithmetic, so the loads are
+//    in flight together and row i's arithmetic overlaps the arrival of rows
+//    i+1.. (loads return in order);
 //  * nibbles are unpacked in registers: the low nibbles of a 32-bit word are
 //    elements i..i+3, the high nibbles elements i+16..i+19 of the block, so
 //    (word & 0x0F0F0F0F) and ((word >> 4) & 0x0F0F0F0F) feed v_dot4_i32_i8
@@ -29,10 +33,14 @@
 //    removed once per block as 8 * sum(q8), giving the exact int32 isum;
 //  * the int32 sum is scaled by d4*d8 (exact binary32 product of two binary16
 //    values) and accumulated with one fma per block in binary32;
-//  * partial sums meet in a fixed order: an 8-lane butterfly inside the wave,
-//    then the NW wave partials added in wave order through LDS.  The order
-//    depends on K only, never on the row's position, so the fused
-//    two-matrix launch is bit-identical to two single launches.
+//  * partial sums meet in a fixed order: an 8-lane butterfly inside the wave
+//    per virtual wave, then the V virtual-wave partials added in order
+//    through LDS;
+//  * the variant on a raw bf16 / f32 activation quantises each block to Q8_1
+//    where it is consumed: the 8 row lanes that share a column load 4 values
+//    each and produce the block's code words together (q8_1_block over the
+//    lanes that agree in l & 7), with the arithmetic of the standalone
+//    quantiser, and swap the words through a per-wave LDS slot.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -48,6 +56,7 @@ struct GemvArgs {
     int K;
     int nb;            // K / 32
     int total_rows;    // n[0] + n[1]
+    const void* x;     // raw activation (bf16 / f32) for the quantising variant
 };
 
 __device__ __forceinline__ int block_isum(const u32x4_t w, const int (&a)[8], int neg8sum) {
@@ -77,18 +86,29 @@ __device__ __forceinline__ float sum8(float v) {
 }
 
 // NMAT: 1 for q4_gemv, 2 for q4_gemv_fused2 (rows past n[0] belong to the
-// second matrix).  Per-row arithmetic does not depend on RI or NMAT.
-template <int M, int RI, int NMAT>
-__global__ __launch_bounds__(1024) void k_q4_gemv(const GemvArgs args) {
-    static_assert(RI * M <= 16, "partials per lane");
+// second matrix).  XIN: -1 reads Q8_1 activation planes, DT_BF16 / DT_F32 a
+// raw activation that the kernel quantises.  U columns in flight per loop
+// iteration, all loaded before any arithmetic, F virtual waves per physical
+// wave (U a multiple of F).  For
+// M == 1 the kernel keeps to 64 VGPRs, so that two 1024-thread workgroups
+// (8 waves per SIMD) share a CU and twice the loads are in flight.
+template <int M, int RI, int NMAT, int U, int F, int XIN>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(M == 1 ? 8 : 1)))
+void k_q4_gemv(const GemvArgs args) {
+    static_assert(RI * M * F <= 16, "partials per lane");
+    static_assert(U % F == 0, "each iteration covers whole virtual-wave rounds");
+    static_assert(U == 1 || M <= 4, "several columns in flight only for small M");
+    constexpr bool RAW = XIN >= 0;
+    static_assert(!RAW || M <= 4, "the quantising variant takes M <= 4");
     __shared__ float red[kMaxWaves][8 * RI * M];
+    __shared__ __attribute__((aligned(16))) uint32_t xch[RAW ? kMaxWaves : 1][RAW ? M : 1][64];
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    const int nw = blockDim.x / kWave;
-    const int bl = w * 8 + (lane & 7);          // block lane: first block column
+    const int nwp = blockDim.x / kWave;         // physical waves; V = F * nwp virtual ones
+    const int bl = w * 8 + (lane & 7);          // first block column of the lane
     const int rl = lane >> 3;                   // row lane: 0..7
-    const int stride = nw * 8;
+    const int stride = nwp * 8;
     const int nb = args.nb;
     const int r0 = blockIdx.x * 8 * RI;
 
@@ -107,86 +127,128 @@ __global__ __launch_bounds__(1024) void k_q4_gemv(const GemvArgs args) {
         rd[i] = dbase + (int64_t)rr * nb;
     }
 
-    float acc[RI][M];
+    float acc[F][RI][M];
 #pragma unroll
-    for (int i = 0; i < RI; i++)
+    for (int f = 0; f < F; f++)
 #pragma unroll
-        for (int m = 0; m < M; m++) acc[i][m] = 0.0f;
+        for (int i = 0; i < RI; i++)
+#pragma unroll
+            for (int m = 0; m < M; m++) acc[f][i][m] = 0.0f;
 
+    uint32_t* slot = &xch[RAW ? w : 0][0][(lane & 7) * 8];
     constexpr int MP = M < 4 ? M : 4;   // activation rows fetched ahead of the weights
-    for (int b = bl; b < nb; b += stride) {
-        // loads: activation (cache-resident) first, then the weight rows in order
-        u32x4_t xa[MP][2];
-        uint32_t d8r[MP];
+    // U columns per iteration (b, b + stride, ...), all loads issued before
+    // any arithmetic; a column past the end loads column b again and is not
+    // accumulated.
+    for (int b = bl; b < nb; b += U * stride) {
+        u32x4_t xa[U][RAW ? 1 : MP][2];
+        uint32_t d8r[U][RAW ? 1 : MP];
+        act4_raw_t<RAW ? XIN : DT_BF16> xr[U][RAW ? M : 1];
+        u32x4_t wv[U][RI];
+        uint32_t dr[U][RI];
+        // loads of column u: activation (cache-resident) first, then the weight
+        // rows in order
+        auto load = [&](int u, int bu) {
+            if constexpr (RAW) {
 #pragma unroll
-        for (int m = 0; m < MP; m++) {
-            const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(args.xqs + (int64_t)m * args.K + (int64_t)b * 32);
-            xa[m][0] = xp[0];
-            xa[m][1] = xp[1];
-            d8r[m] = args.xds[((int64_t)m * nb + b) * 2];
-        }
-        u32x4_t wv[RI];
-        uint32_t dr[RI];
-#pragma unroll
-        for (int i = 0; i < RI; i++) {
-            dr[i] = rd[i][b];
-            wv[i] = __builtin_nontemporal_load(rqs[i] + b);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        int neg8sum[M];
-        int av[M][8];
-        float d8[M];
-#pragma unroll
-        for (int m = 0; m < M; m++) {
-            u32x4_t x0, x1;
-            uint32_t d8bits;
-            if (m < MP) {
-                x0 = xa[m < MP ? m : 0][0];
-                x1 = xa[m < MP ? m : 0][1];
-                d8bits = d8r[m < MP ? m : 0];
+                for (int m = 0; m < M; m++)
+                    xr[u][m] = load_act4_raw<RAW ? XIN : DT_BF16>(args.x, (int64_t)m * args.K + (int64_t)bu * 32 + rl * 4);
             } else {
-                const u32x4_t* xp =
-                    reinterpret_cast<const u32x4_t*>(args.xqs + (int64_t)m * args.K + (int64_t)b * 32);
-                x0 = xp[0];
-                x1 = xp[1];
-                d8bits = args.xds[((int64_t)m * nb + b) * 2];
+#pragma unroll
+                for (int m = 0; m < MP; m++) {
+                    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(args.xqs + (int64_t)m * args.K + (int64_t)bu * 32);
+                    xa[u][m][0] = xp[0];
+                    xa[u][m][1] = xp[1];
+                    d8r[u][m] = args.xds[((int64_t)m * nb + bu) * 2];
+                }
             }
-            av[m][0] = (int)x0[0]; av[m][1] = (int)x0[1]; av[m][2] = (int)x0[2]; av[m][3] = (int)x0[3];
-            av[m][4] = (int)x1[0]; av[m][5] = (int)x1[1]; av[m][6] = (int)x1[2]; av[m][7] = (int)x1[3];
-            d8[m] = f16_to_f32(d8bits);
-            int sq = 0;
+            __builtin_amdgcn_sched_barrier(0);     // the activation loads stay ahead of the weights
 #pragma unroll
-            for (int t = 0; t < 8; t++) sq = __builtin_amdgcn_sdot4(av[m][t], 0x01010101, sq, false);
-            neg8sum[m] = -8 * sq;
-        }
+            for (int i = 0; i < RI; i++) {
+                dr[u][i] = rd[i][bu];
+                wv[u][i] = __builtin_nontemporal_load(rqs[i] + bu);
+            }
+        };
+        // arithmetic of column u (block column bu) into accumulator u mod F
+        auto compute = [&](int u, int bu) {
+            int neg8sum[M];
+            int av[M][8];
+            float d8[M];
+            if constexpr (RAW) {
 #pragma unroll
-        for (int i = 0; i < RI; i++) {
-            const float d4 = f16_to_f32(dr[i]);
+                for (int m = 0; m < M; m++) {
+                    float v[4];
+                    act4_to_f32<RAW ? XIN : DT_BF16>(xr[u][m], v);
+                    uint32_t d16, s16;
+                    slot[m * 64 + rl] = q8_1_block<Q8Strided, false>(v, d16, s16);
+                    d8[m] = f16_to_f32(d16);
+                }
+                // the wave reads back what it wrote (LDS operations of one wave
+                // are performed in order)
+            }
 #pragma unroll
             for (int m = 0; m < M; m++) {
-                const int isum = block_isum(wv[i], av[m], neg8sum[m]);
-                acc[i][m] = fmaf((float)isum, d4 * d8[m], acc[i][m]);
+                u32x4_t x0, x1;
+                if constexpr (RAW) {
+                    x0 = *reinterpret_cast<const u32x4_t*>(slot + m * 64);
+                    x1 = *reinterpret_cast<const u32x4_t*>(slot + m * 64 + 4);
+                } else if (m < MP) {
+                    x0 = xa[u][m < MP ? m : 0][0];
+                    x1 = xa[u][m < MP ? m : 0][1];
+                    d8[m] = f16_to_f32(d8r[u][m < MP ? m : 0]);
+                } else {
+                    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(args.xqs + (int64_t)m * args.K + (int64_t)bu * 32);
+                    x0 = xp[0];
+                    x1 = xp[1];
+                    d8[m] = f16_to_f32(args.xds[((int64_t)m * nb + bu) * 2]);
+                }
+                av[m][0] = (int)x0[0]; av[m][1] = (int)x0[1]; av[m][2] = (int)x0[2]; av[m][3] = (int)x0[3];
+                av[m][4] = (int)x1[0]; av[m][5] = (int)x1[1]; av[m][6] = (int)x1[2]; av[m][7] = (int)x1[3];
+                int sq = 0;
+#pragma unroll
+                for (int t = 0; t < 8; t++) sq = __builtin_amdgcn_sdot4(av[m][t], 0x01010101, sq, false);
+                neg8sum[m] = -8 * sq;
             }
+#pragma unroll
+            for (int i = 0; i < RI; i++) {
+                const float d4 = f16_to_f32(dr[u][i]);
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    const int isum = block_isum(wv[u][i], av[m], neg8sum[m]);
+                    acc[u % F][i][m] = fmaf((float)isum, d4 * d8[m], acc[u % F][i][m]);
+                }
+            }
+        };
+#pragma unroll
+        for (int u = 0; u < U; u++) load(u, (b + u * stride < nb) ? b + u * stride : b);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (u > 0 && b + u * stride >= nb) break;
+            compute(u, b + u * stride);
         }
     }
 
-    // 8 block lanes of a row -> one partial per wave, then wave partials in
-    // wave order
+    // 8 block lanes of a row -> one partial per virtual wave (w + f * nwp),
+    // then the virtual-wave partials in order
 #pragma unroll
-    for (int i = 0; i < RI; i++)
+    for (int f = 0; f < F; f++)
 #pragma unroll
-        for (int m = 0; m < M; m++) {
-            const float v = sum8(acc[i][m]);
-            if ((lane & 7) == 0) red[w][(i * 8 + rl) * M + m] = v;
-        }
+        for (int i = 0; i < RI; i++)
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                const float v = sum8(acc[f][i][m]);
+                if ((lane & 7) == 0) red[w + f * nwp][(i * 8 + rl) * M + m] = v;
+            }
     __syncthreads();
+    const int nv = F * nwp;
     for (int t = threadIdx.x; t < 8 * RI * M; t += blockDim.x) {
         const int m = t % M;
-        const int slot = t / M;                 // i * 8 + rl
-        const int R = r0 + (slot & 7) + 8 * (slot >> 3);
+        const int slot_i = t / M;               // i * 8 + rl
+        const int R = r0 + (slot_i & 7) + 8 * (slot_i >> 3);
         if (R >= args.total_rows) continue;
         float v = red[0][t];
-        for (int ww = 1; ww < nw; ww++) v += red[ww][t];
+        for (int vw = 1; vw < nv; vw++) v += red[vw][t];
         const bool second = NMAT == 2 && R >= args.n[0];
         float* yp = second ? args.y[1] : args.y[0];
         const int64_t rows = second ? args.n[1] : args.n[0];
@@ -194,41 +256,123 @@ __global__ __launch_bounds__(1024) void k_q4_gemv(const GemvArgs args) {
     }
 }
 
-template <int M, int NMAT>
-static void launch_m(const GemvArgs& a, int ri, int nw, hipStream_t s) {
-    const dim3 block(nw * kWave);
-    const int rows_per_wg = 8 * ri;
-    const dim3 grid((a.total_rows + rows_per_wg - 1) / rows_per_wg);
-    if constexpr (M <= 4) {
-        if (ri == 4) { hipLaunchKernelGGL((k_q4_gemv<M, 4, NMAT>), grid, block, 0, s, a); return; }
-        if (ri == 3) { hipLaunchKernelGGL((k_q4_gemv<M, 3, NMAT>), grid, block, 0, s, a); return; }
+// Launch shape: V virtual waves (a function of K only), F of them per
+// physical wave, ri rows per lane, u columns in flight per iteration.
+struct GemvShape {
+    int v, f, ri, u;
+};
+
+// V = min(16, ceil(K / 256)) virtual waves.  Rows per lane: the fewest that
+// let the whole grid be resident at once (32 waves per CU, the M == 1
+// occupancy), at most 4; where V physical waves would need more, V / 2 of
+// them with two virtual waves each and both columns in flight (M == 1, at
+// most 2 rows per lane, which keeps the registers under 64).  Fewer rows per lane as M (and
+// with it the register footprint) grows.  Two columns in flight when a lane
+// walks more than one and its registers allow.
+static GemvShape pick_shape(int64_t rows, int64_t nb, int64_t M) {
+    const int64_t cus = current_cu_count();
+    GemvShape g;
+    g.v = (int)(nb < 8 ? 1 : ((nb + 7) / 8 > kMaxWaves ? kMaxWaves : (nb + 7) / 8));
+    g.f = 1;
+    auto rows_per_lane = [&](int nwp) {
+        const int64_t slots = cus * 32 / nwp;
+        return (rows + 8 * slots - 1) / (8 * slots);
+    };
+    int64_t ri = rows_per_lane(g.v);
+    if (ri > 4 && M == 1 && g.v % 2 == 0) {
+        g.f = 2;                                 // two columns in flight: at most 2 rows per lane
+        ri = rows_per_lane(g.v / 2);
+        ri = ri > 2 ? 2 : ri;
     }
-    if constexpr (M <= 8) {
-        if (ri == 2) { hipLaunchKernelGGL((k_q4_gemv<M, 2, NMAT>), grid, block, 0, s, a); return; }
-    }
-    hipLaunchKernelGGL((k_q4_gemv<M, 1, NMAT>), grid, block, 0, s, a);
-}
-
-template <int M>
-static void launch_m(const GemvArgs& a, int ri, int nw, hipStream_t s) {
-    if (a.n[1] > 0) launch_m<M, 2>(a, ri, nw, s);
-    else launch_m<M, 1>(a, ri, nw, s);
-}
-
-// Waves per workgroup: one block lane per 32-weight block of a row, up to 16
-// waves.  Rows per lane: enough workgroups to fill the 256 CUs twice, fewer
-// rows per lane as M (and with it the register footprint) grows.
-static int pick_waves(int64_t nb) {
-    int64_t nw = (nb + 7) / 8;
-    return (int)(nw < 1 ? 1 : (nw > kMaxWaves ? kMaxWaves : nw));
-}
-
-static int pick_rows_per_lane(int64_t rows, int64_t M) {
-    int64_t ri = rows / (8 * 512);
     ri = ri < 1 ? 1 : (ri > 4 ? 4 : ri);
     if (M > 8) ri = 1;
     else if (M > 4 && ri > 2) ri = 2;
-    return (int)ri;
+    g.ri = (int)ri;
+    g.u = g.f == 2 ? 2 : ((nb > 8 * g.v && M * ri <= 2) ? 2 : 1);
+    return g;
+}
+
+// The quantising variant keeps to 3 rows per lane, 2 for two matrices (its
+// registers), and, with rows enough for two per lane on every CU, takes at
+// least two: its per-column quantisation is then shared by more rows.  Two
+// matrices that would want more take two virtual waves per physical wave.
+static GemvShape raw_shape(GemvShape g, int64_t rows, int64_t nb, int64_t M, bool two_mats) {
+    if (g.f == 1 && M == 1) {
+        const int64_t two = rows / (16 * (int64_t)current_cu_count());
+        const int want = (int)(two < 1 ? 1 : (two > 3 ? 3 : two));
+        if (g.ri < want) g.ri = want;
+    }
+    const int cap = two_mats ? 2 : 3;
+    if (g.ri > cap) {
+        if (g.f == 1 && M == 1 && g.v % 2 == 0) g.f = 2;
+        g.ri = cap;
+    }
+    if (g.f == 2) g.ri = g.ri > 2 ? 2 : g.ri;
+    g.u = g.f == 2 ? 2 : ((nb > 8 * g.v && M * g.ri <= 2) ? 2 : 1);
+    return g;
+}
+
+#define Q4_LAUNCH(...)                                            \
+    do {                                                          \
+        hipLaunchKernelGGL((__VA_ARGS__), grid, block, 0, s, a);  \
+        return;                                                   \
+    } while (0)
+
+template <int M, int NMAT, int XIN>
+static void launch_mx(const GemvArgs& a, const GemvShape& g, hipStream_t s) {
+    const dim3 block(g.v / g.f * kWave);
+    const dim3 grid((a.total_rows + 8 * g.ri - 1) / (8 * g.ri));
+    if constexpr (M == 1) {
+        if (g.f == 2) {
+            if (g.ri == 2) Q4_LAUNCH(k_q4_gemv<1, 2, NMAT, 2, 2, XIN>);
+            Q4_LAUNCH(k_q4_gemv<1, 1, NMAT, 2, 2, XIN>);
+        }
+        if (g.u == 2 && g.ri == 2) Q4_LAUNCH(k_q4_gemv<1, 2, NMAT, 2, 1, XIN>);
+    }
+    if constexpr (M <= 2) {
+        if (g.u == 2 && g.ri == 1) Q4_LAUNCH(k_q4_gemv<M, 1, NMAT, 2, 1, XIN>);
+    }
+    if constexpr (M <= 4 && XIN < 0) {
+        if (g.ri == 4) Q4_LAUNCH(k_q4_gemv<M, 4, NMAT, 1, 1, XIN>);
+    }
+    if constexpr (M <= 4 && (XIN < 0 || NMAT == 1)) {
+        if (g.ri == 3) Q4_LAUNCH(k_q4_gemv<M, 3, NMAT, 1, 1, XIN>);
+    }
+    if constexpr (M <= 8) {
+        if (g.ri == 2) Q4_LAUNCH(k_q4_gemv<M, 2, NMAT, 1, 1, XIN>);
+    }
+    Q4_LAUNCH(k_q4_gemv<M, 1, NMAT, 1, 1, XIN>);
+}
+
+#undef Q4_LAUNCH
+
+template <int M, int XIN>
+static void launch_m(const GemvArgs& a, const GemvShape& g, hipStream_t s) {
+    if (a.n[1] > 0) launch_mx<M, 2, XIN>(a, g, s);
+    else launch_mx<M, 1, XIN>(a, g, s);
+}
+
+hipError_t launch_q4_gemv_act(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
+                              const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
+                              const void* x, int xdt, int64_t M, int64_t K, hipStream_t s) {
+    GemvArgs a;
+    a.qs[0] = w0_qs; a.d[0] = w0_d; a.y[0] = y0; a.n[0] = (int)N0;
+    a.qs[1] = w1_qs ? w1_qs : w0_qs; a.d[1] = w1_d ? w1_d : w0_d; a.y[1] = y1 ? y1 : y0; a.n[1] = (int)N1;
+    a.xqs = nullptr; a.xds = nullptr; a.x = x;
+    a.K = (int)K; a.nb = (int)(K / 32);
+    a.total_rows = (int)(N0 + N1);
+    const GemvShape g = raw_shape(pick_shape(N0 + N1, K / 32, M), N0 + N1, K / 32, M, N1 > 0);
+    switch (M) {
+#define Q4_GEMV_ACT_CASE(m)                                                  \
+    case m:                                                                  \
+        if (xdt == DT_F32) launch_m<m, DT_F32>(a, g, s);                     \
+        else launch_m<m, DT_BF16>(a, g, s);                                  \
+        break;
+        Q4_GEMV_ACT_CASE(1) Q4_GEMV_ACT_CASE(2) Q4_GEMV_ACT_CASE(3) Q4_GEMV_ACT_CASE(4)
+#undef Q4_GEMV_ACT_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
@@ -237,12 +381,11 @@ hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0,
     GemvArgs a;
     a.qs[0] = w0_qs; a.d[0] = w0_d; a.y[0] = y0; a.n[0] = (int)N0;
     a.qs[1] = w1_qs ? w1_qs : w0_qs; a.d[1] = w1_d ? w1_d : w0_d; a.y[1] = y1 ? y1 : y0; a.n[1] = (int)N1;
-    a.xqs = x_qs; a.xds = x_ds; a.K = (int)K; a.nb = (int)(K / 32);
+    a.xqs = x_qs; a.xds = x_ds; a.x = nullptr; a.K = (int)K; a.nb = (int)(K / 32);
     a.total_rows = (int)(N0 + N1);
-    const int ri = pick_rows_per_lane(N0 + N1, M);
-    const int nw = pick_waves(K / 32);
+    const GemvShape g = pick_shape(N0 + N1, K / 32, M);
     switch (M) {
-#define Q4_GEMV_CASE(m) case m: launch_m<m>(a, ri, nw, s); break;
+#define Q4_GEMV_CASE(m) case m: launch_m<m, -1>(a, g, s); break;
         Q4_GEMV_CASE(1) Q4_GEMV_CASE(2) Q4_GEMV_CASE(3) Q4_GEMV_CASE(4)
         Q4_GEMV_CASE(5) Q4_GEMV_CASE(6) Q4_GEMV_CASE(7) Q4_GEMV_CASE(8)
         Q4_GEMV_CASE(9) Q4_GEMV_CASE(10) Q4_GEMV_CASE(11) Q4_GEMV_CASE(12)

@@ -10,6 +10,10 @@ namespace q4 {
 // dtype codes (same values as Q4_F32 / Q4_BF16 / Q4_F16 in include/q4.h)
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).
+int current_cu_count();
+
 hipError_t launch_q4_quantize(const void* w, int wdt, int64_t N, int64_t K, uint8_t* qs, uint16_t* d,
                               hipStream_t s);
 hipError_t launch_q8_1_quantize(const void* x, int xdt, int64_t M, int64_t K, int8_t* qs, uint16_t* ds,
@@ -25,6 +29,12 @@ hipError_t launch_affine4_dequantize(const uint8_t* wq, const uint16_t* sc, cons
 hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
                           const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
                           const int8_t* x_qs, const uint16_t* x_ds, int64_t M, int64_t K, hipStream_t s);
+
+// The same GEMV on a raw bf16 / f32 activation, quantised to Q8_1 inside the
+// kernel (bit-identical to launch_q8_1_quantize + launch_q4_gemv); M <= 4.
+hipError_t launch_q4_gemv_act(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
+                              const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
+                              const void* x, int xdt, int64_t M, int64_t K, hipStream_t s);
 
 // GEMM paths.  fmt: 0 = Q4_0 planes (a = qs, b = d), 1 = affine (a = q,
 // b = scales, c = biases), 2 = dense binary16 W (a = w).

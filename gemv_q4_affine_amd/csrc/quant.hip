@@ -88,39 +88,11 @@ __global__ __launch_bounds__(256) void k_q8_1_quantize(const void* __restrict__ 
          base += ((int64_t)gridDim.x * blockDim.x) >> 3) {
         const int64_t e0 = base * 32 + sub * 4;
         float v[4];
-        if (XDT == DT_F32) {
-            float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + e0);
-            v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
-        } else {
-            u32x2_t t = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint16_t*>(x) + e0);
-            v[0] = bf16_to_f32(t[0] & 0xFFFFu); v[1] = bf16_to_f32(t[0] >> 16);
-            v[2] = bf16_to_f32(t[1] & 0xFFFFu); v[3] = bf16_to_f32(t[1] >> 16);
-        }
-        float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-        amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-        amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
-        const float dd = amax / 127.0f;
-        const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
-        int q[4];
-        int sum = 0;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            float t = v[j] * id;
-            q[j] = (int)roundf(t);  // half away from zero
-            sum += q[j];
-        }
-        sum += __shfl_xor(sum, 1, 8);
-        sum += __shfl_xor(sum, 2, 8);
-        sum += __shfl_xor(sum, 4, 8);
-        uint32_t word = (uint32_t)(q[0] & 0xFF) | ((uint32_t)(q[1] & 0xFF) << 8) |
-                        ((uint32_t)(q[2] & 0xFF) << 16) | ((uint32_t)(q[3] & 0xFF) << 24);
+        load_act4<XDT>(x, e0, v);
+        uint32_t d16, s16;
+        const uint32_t word = q8_1_block<Q8Adjacent, true>(v, d16, s16);
         *reinterpret_cast<uint32_t*>(qs + e0) = word;
-        if (sub == 0) {
-            const float s = dd * (float)sum;
-            uint32_t pair = f32_to_f16_rne(dd) | (f32_to_f16_rne(s) << 16);
-            reinterpret_cast<uint32_t*>(ds)[base] = pair;
-        }
+        if (sub == 0) reinterpret_cast<uint32_t*>(ds)[base] = d16 | (s16 << 16);
     }
 }
 

@@ -195,6 +195,32 @@ int q4_gemv_fused2(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0,
                    const int8_t* x_qs, const uint16_t* x_ds,
                    float* y0, float* y1, int64_t M, int64_t K, void* stream);
 
+/*
+ * q4_gemv_act -- q4_gemv on a raw activation: the kernel quantises each X
+ * block to Q8_1 in registers where it is consumed, with the arithmetic of
+ * q8_1_quantize_act, so y is bit-identical to q8_1_quantize_act followed by
+ * q4_gemv, in one launch and without the Q8_1 planes in HBM (the decode step
+ * of the repro page, Important source touch points: quantise the activation,
+ * then the MMVQ GEMV).
+ *   x       : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32), 16-byte aligned
+ *   y       : device out, float [M][N]
+ *   1 <= M <= Q4_GEMV_ACT_MAX_M (else Q4_ERR_SHAPE; M == 0 is a no-op).
+ */
+#define Q4_GEMV_ACT_MAX_M     4
+int q4_gemv_act(const uint8_t* w_qs, const uint16_t* w_d,
+                const void* x, int x_dtype,
+                float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * q4_gemv_fused2_act -- q4_gemv_fused2 on a raw activation, quantised inside
+ * the kernel as in q4_gemv_act: bit-identical to q8_1_quantize_act followed by
+ * q4_gemv_fused2.  Same limits as q4_gemv_act.
+ */
+int q4_gemv_fused2_act(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0,
+                       const uint8_t* w1_qs, const uint16_t* w1_d, int64_t N1,
+                       const void* x, int x_dtype,
+                       float* y0, float* y1, int64_t M, int64_t K, void* stream);
+
 /* ======================================================================== */
 /* GEMM (any M): bf16 / f32 activations                                      */
 /* ======================================================================== */

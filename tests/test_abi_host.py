@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in q4.h but not exported"
@@ -102,6 +102,19 @@ def test_gemv_validation():
     assert f(P, P, 8, P, P, -8, P, P, P, P, 1, 64, None) == B.Q4_ERR_SHAPE
     assert f(P, P, 8, None, P, 8, P, P, P, P, 1, 64, None) == B.Q4_ERR_NULL
     assert f(P, P, 8, P, P, 8, P, P, P, P, 0, 64, None) == B.Q4_OK
+    a = lib().q4_gemv_act
+    assert a(P, P, P, B.Q4_BF16, P, 5, 8, 64, None) == B.Q4_ERR_SHAPE     # M above the fused-quantise limit
+    assert a(P, P, P, B.Q4_F16, P, 1, 8, 64, None) == B.Q4_ERR_DTYPE
+    assert a(P, P, P, B.Q4_BF16, P, 1, 8, 50, None) == B.Q4_ERR_SHAPE
+    assert a(P, P, MIS, B.Q4_BF16, P, 1, 8, 64, None) == B.Q4_ERR_ALIGN
+    assert a(P, P, None, B.Q4_F32, P, 1, 8, 64, None) == B.Q4_ERR_NULL
+    assert a(P, P, P, B.Q4_BF16, P, 0, 8, 64, None) == B.Q4_OK
+    assert a(P, P, P, B.Q4_BF16, P, 4, 0, 64, None) == B.Q4_OK
+    f = lib().q4_gemv_fused2_act
+    assert f(P, P, 8, P, P, 8, P, B.Q4_BF16, P, P, 5, 64, None) == B.Q4_ERR_SHAPE
+    assert f(P, P, 8, P, P, 8, P, 9, P, P, 1, 64, None) == B.Q4_ERR_DTYPE
+    assert f(P, P, 8, None, P, 8, P, B.Q4_BF16, P, P, 1, 64, None) == B.Q4_ERR_NULL
+    assert f(P, P, 8, P, P, 8, P, B.Q4_BF16, P, P, 0, 64, None) == B.Q4_OK
 
 
 def test_gemm_validation():

@@ -275,6 +275,43 @@ def test_fused2_bit_identical_to_two_gemvs(M, N0, N1, K):
     assert rel(host(y1).astype(np.float64), oracle.q4q8_gemv(w1qs, w1d, xqs, xds)) <= GEMV_TIGHT
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 12288, 4096), (1, 300, 96), (2, 1000, 4128), (3, 257, 544),
+                                   (4, 640, 14336), (1, 64, 65536), (4, 3, 32), (1, 8192, 8192)])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_gemv_act_bit_identical_to_quantise_then_gemv(M, N, K, xdt):
+    """The GEMV that quantises its own activation gives the bits of
+    q8_1_quantize_act followed by q4_gemv, and the oracle's value."""
+    say(f"gemv_act M={M} N={N} K={K} {xdt}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    wqs, wd = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    X = synth.activations(rng, M, K)
+    x = bf16_dev(X) if xdt == "bf16" else dev(X.astype(np.float32))
+    Xh = synth.bf16_bits_to_f32(synth.bf16_bits(X)) if xdt == "bf16" else X.astype(np.float32)
+    tw = (dev(wqs), dev(wd))
+    y = B.q4_gemv_act(*tw, x)
+    xq, xd = B.q8_1_quantize_act(x)
+    assert torch.equal(y, B.q4_gemv(*tw, xq, xd))
+    xqs, xds = oracle.q8_1_quantize(Xh)
+    assert rel(host(y).astype(np.float64), oracle.q4q8_gemv(wqs, wd, xqs, xds)) <= GEMV_TIGHT
+
+
+@pytest.mark.parametrize("M,N0,N1,K", [(1, 14336, 14336, 4096), (2, 512, 300, 2048), (4, 1, 17, 64)])
+def test_gemv_fused2_act_bit_identical(M, N0, N1, K):
+    say(f"fused2_act M={M} N0={N0} N1={N1} K={K}")
+    rng = np.random.default_rng(N0 + N1)
+    w0 = oracle.q4_0_quantize(synth.weights(rng, N0, K))
+    w1 = oracle.q4_0_quantize(synth.weights(rng, N1, K))
+    x = bf16_dev(synth.activations(rng, M, K))
+    t = [dev(a) for a in (*w0, *w1)]
+    y0, y1 = B.q4_gemv_fused2_act(*t, x)
+    xq, xd = B.q8_1_quantize_act(x)
+    z0, z1 = B.q4_gemv_fused2(*t, xq, xd)
+    assert torch.equal(y0, z0) and torch.equal(y1, z1)
+    # one matrix only
+    e0, e1 = B.q4_gemv_fused2_act(t[0][:0], t[1][:0], t[2], t[3], x)
+    assert e0.shape == (M, 0) and torch.equal(e1, z1)
+
+
 def test_gemv_deterministic_and_row_permutation():
     wqs, wd, xqs, xds = _gemv_case(2, 3000, 4096, seed=77)
     t = [dev(a) for a in (wqs, wd, xqs, xds)]
@@ -482,7 +519,7 @@ def test_empty_inputs_are_noops():
 
 def test_graph_replays_match_eager():
     """Capture q8_1_quantize_act + q4_gemv + q4_gemv_fused2 + q4_gemm (packed
-    path, caller workspace) in one graph; every replay, with eager work and
+    path, caller workspace) + the activation-quantising GEMVs in one graph; every replay, with eager work and
     synchronisations between replays, reproduces the eager results exactly."""
     rng = np.random.default_rng(21)
     N, K, M = 640, 1024, 160
@@ -499,26 +536,34 @@ def test_graph_replays_match_eager():
     ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
     assert ws.numel() > 0
 
+    ya = torch.empty_like(y)
+    ya0 = torch.empty_like(y)
+    ya1 = torch.empty_like(y)
+    outs = (xq, xd, y, y0, y1, yg, ya, ya0, ya1)
+
     def work():
         B.q8_1_quantize_act(x1, xq, xd)
         B.q4_gemv(*t[0], xq, xd, y)
         B.q4_gemv_fused2(*t[1], *t[2], xq, xd, y0, y1)
         B.q4_gemm(*t[0], xm, y=yg, workspace=ws)
+        B.q4_gemv_act(*t[0], x1, ya)
+        B.q4_gemv_fused2_act(*t[1], *t[2], x1, ya0, ya1)
 
     work()
     torch.cuda.synchronize()
-    ref = [a.clone() for a in (xq, xd, y, y0, y1, yg)]
+    assert torch.equal(ya, y) and torch.equal(ya0, y0) and torch.equal(ya1, y1)
+    ref = [a.clone() for a in outs]
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
         work()
     for rep in range(4):
-        for a in (xq, xd, y, y0, y1, yg):
+        for a in outs:
             a.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for a, r in zip((xq, xd, y, y0, y1, yg), ref):
+        for a, r in zip(outs, ref):
             assert torch.equal(a, r), f"replay {rep} differs"
         work()                                   # eager work between replays
         torch.cuda.synchronize()
