@@ -46,19 +46,26 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
 
-# HBM bytes per launch of the roofline kernel (k_q4_gemv<1,4,2>, decode
-# shape), from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes summarised in
-# profiles/q4_gemv_n12288_k4096_hbm_traffic.md.  They hold only for the GEMV
-# source they were taken on: with any other source the figure is reported as
-# null until the counters are taken again.
-MEASURED_TRAFFIC = {"source": "gemv_q4_affine_amd/csrc/gemv.hip", "sha256_prefix": "ead8723e950721d4",
-                    "bytes_per_launch": 56808525}
+# HBM bytes per launch of the roofline kernel (q4_gemv_fused2_act at the
+# decode shape, k_q4_gemv<1,2,2,2,2,bf16>), from the rocprofv3 FETCH_SIZE /
+# WRITE_SIZE passes summarised in profiles/q4_gemv_n12288_k4096_hbm_traffic.md.
+# They hold only for the sources they were taken on: with any other source the
+# figure is reported as null until the counters are taken again.
+MEASURED_TRAFFIC = {"sources": ["gemv_q4_affine_amd/csrc/gemv.hip", "gemv_q4_affine_amd/csrc/device_common.hpp"],
+                    "sha256_prefix": "30a19ea5ee90e418", "bytes_per_launch": 56858282}
+
+
+def sources_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
-    with open(os.path.join(ROOT, MEASURED_TRAFFIC["source"]), "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()[:16]
-    return MEASURED_TRAFFIC["bytes_per_launch"] if h == MEASURED_TRAFFIC["sha256_prefix"] else None
+    ok = sources_hash(MEASURED_TRAFFIC["sources"]) == MEASURED_TRAFFIC["sha256_prefix"]
+    return MEASURED_TRAFFIC["bytes_per_launch"] if ok else None
 
 
 def log(*a):
@@ -540,7 +547,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "q4_gemv_fused2_act (k_q4_gemv_act<1,4,2,bf16>), the step's longest kernel",
+            "kernel": "q4_gemv_fused2_act (k_q4_gemv<1,2,2,2,2,bf16>), the step's longest kernel",
             "achieved": round(g["gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
