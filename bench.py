@@ -293,6 +293,10 @@ def gemm_section(iters: int):
     ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
     flop = 2.0 * M * N * K
     fused_ms = region_us(lambda i: B.q4_gemm(qs, d, x, y=y, workspace=ws), iters) * 1e-3
+    # the same matrix-core GEMM on a weight image prepared once
+    image = B.q4_pack_weight_image(qs, d)
+    xws = torch.empty(B.lib().q4_gemm_image_workspace_size(M, K), dtype=torch.uint8, device="cuda")
+    image_ms = region_us(lambda i: B.q4_gemm_image(image, x, N, y=y, workspace=xws), iters) * 1e-3
     # dequantise-then-GEMM: our dequantiser, then (a) the library's dense MFMA
     # GEMM on fp16 W, (b) hipBLASLt through torch on bf16 W (the pages' "jit")
     w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
@@ -308,6 +312,8 @@ def gemm_section(iters: int):
     res = {
         "fused_us": fused_ms * 1e3,
         "fused_tflops": flop / (fused_ms * 1e-3) / 1e12,
+        "image_us": image_ms * 1e3,
+        "image_tflops": flop / (image_ms * 1e-3) / 1e12,
         "dequant_f16_us": deq16_ms * 1e3,
         "dequant_bf16_us": deqbf_ms * 1e3,
         "dense_gemm_f16_us": dense_ms * 1e3,
@@ -319,6 +325,7 @@ def gemm_section(iters: int):
         "flop": flop,
     }
     log(f"[gemm] fused {res['fused_us']:.1f} us = {res['fused_tflops']:.0f} TFLOP/s; "
+        f"prepacked weights {res['image_us']:.1f} us = {res['image_tflops']:.0f} TFLOP/s; "
         f"dequant f16 {res['dequant_f16_us']:.1f} us; dense {res['dense_gemm_f16_us']:.1f} us; "
         f"hipBLASLt bf16 {res['hipblaslt_bf16_us']:.1f} us, f16 {res['hipblaslt_f16_us']:.1f} us")
     return res
@@ -564,6 +571,9 @@ def main():
         line["extra"]["gemm_roofline"] = {
             "bound": "mfma", "achieved": round(gm["fused_tflops"], 1), "peak": F16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(gm["fused_tflops"] / F16_MFMA_PEAK_TFLOPS, 4),
+            "what": "q4_gemm per call: X image + weight image + matrix-core GEMM",
+            "achieved_prepacked_weights": round(gm["image_tflops"], 1),
+            "frac_prepacked_weights": round(gm["image_tflops"] / F16_MFMA_PEAK_TFLOPS, 4),
         }
     print(json.dumps(line), flush=True)
 

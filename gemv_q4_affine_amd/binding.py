@@ -41,6 +41,10 @@ SIGNATURES = {
     "affine4_gemm": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "q4_gemm_workspace_size": (_I64, [_I64, _I64, _I64, _INT]),
     "dense_gemm": (_INT, [_P, _INT, _P, _P, _INT, _I64, _I64, _I64, _P]),
+    "q4_weight_image_size": (_I64, [_I64, _I64, _INT]),
+    "q4_pack_weight_image": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P]),
+    "q4_gemm_image_workspace_size": (_I64, [_I64, _I64]),
+    "q4_gemm_image": (_INT, [_INT, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "q4_dispatch_path": (_INT, [_I64, _I64, _I64, _INT, _INT]),
     "q4_set_dispatch": (_INT, [_INT, _I64]),
     "q4_get_dispatch": (_INT, [_INT, ctypes.POINTER(ctypes.c_int64)]),
@@ -247,6 +251,33 @@ def affine4_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, 
 
 def q4_gemm_workspace_size(M, N, K, fmt=Q4_FMT_Q4_0) -> int:
     return int(lib().q4_gemm_workspace_size(M, N, K, fmt))
+
+
+def q4_pack_weight_image(w_q, w_s, w_b=None, fmt=None, image=None, stream=None):
+    """The matrix-core GEMM's weight image of Q4_0 planes (w_q = qs [N, K/32, 16],
+    w_s = d) or affine planes (w_q [N, K/2], w_s = scales, w_b = biases)."""
+    if fmt is None:
+        fmt = Q4_FMT_AFFINE4 if w_b is not None else Q4_FMT_Q4_0
+    N = w_s.shape[0]
+    K = w_s.shape[1] * (32 if fmt == Q4_FMT_Q4_0 else 64)
+    if image is None:
+        n = lib().q4_weight_image_size(N, K, fmt)
+        image = _empty((max(n, 16),), torch.uint8, w_q)
+    _check("q4_pack_weight_image", lib().q4_pack_weight_image(fmt, _p(w_q), _p(w_s), _p(w_b),
+                                                              N, K, _p(image), _stream(stream)))
+    return image
+
+
+def q4_gemm_image(image, x, N, fmt=Q4_FMT_Q4_0, y_dtype=torch.bfloat16, y=None, workspace=None, stream=None):
+    """Y [M, N] = X . dequant(W)^T from a weight image (q4_pack_weight_image)."""
+    M, K = x.shape
+    y = _empty((M, N), y_dtype, x) if y is None else y
+    if workspace is None:
+        workspace = _empty((max(lib().q4_gemm_image_workspace_size(M, K), 16),), torch.uint8, x)
+    _check("q4_gemm_image", lib().q4_gemm_image(fmt, _p(image), _p(x), _dt(x), _p(y), _dt(y), M, N, K,
+                                                _p(workspace), workspace.numel() * workspace.element_size(),
+                                                _stream(stream)))
+    return y
 
 
 def dense_gemm(x, w_f16, y_dtype=torch.bfloat16, y=None, stream=None):

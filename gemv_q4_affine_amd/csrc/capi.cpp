@@ -102,7 +102,7 @@ const char* q4_status_string(int status) {
         case Q4_ERR_DTYPE: return "unsupported dtype";
         case Q4_ERR_HIP: return "HIP launch or runtime error";
         case Q4_ERR_ARG: return "invalid argument";
-        case Q4_ERR_WORKSPACE: return "the dequantise-then-GEMM path needs a workspace of N*K*2 bytes";
+        case Q4_ERR_WORKSPACE: return "the workspace is missing or smaller than the path needs";
         default: return "unknown status";
     }
 }
@@ -335,6 +335,46 @@ int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
     if ((rc = check_ptrs_aligned({w_q, scales, biases, x, y}))) return rc;
     return gemm_common(q4::WF_AFFINE4, w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, workspace,
                        workspace_bytes, stream);
+}
+
+static int image_dims(int fmt, int64_t M, int64_t N, int64_t K) {
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE4) return Q4_ERR_ARG;
+    return check_dims(M, N, K, fmt == Q4_FMT_Q4_0 ? 32 : 64);
+}
+
+int64_t q4_weight_image_size(int64_t N, int64_t K, int fmt) {
+    if (image_dims(fmt, 0, N, K) != Q4_OK) return 0;
+    return q4::weight_image_bytes(N, K);
+}
+
+int q4_pack_weight_image(int fmt, const uint8_t* w_q, const uint16_t* w_s, const uint16_t* w_b, int64_t N,
+                         int64_t K, void* image, void* stream) {
+    int rc = image_dims(fmt, 0, N, K);
+    if (rc) return rc;
+    if (N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_q, w_s, image}))) return rc;
+    if (fmt == Q4_FMT_AFFINE4 && (rc = check_ptrs_aligned({w_b}))) return rc;
+    const int wf = fmt == Q4_FMT_Q4_0 ? q4::WF_Q4_0 : q4::WF_AFFINE4;
+    return hip_status(q4::launch_pack_weight_image(wf, w_q, w_s, fmt == Q4_FMT_Q4_0 ? nullptr : w_b, N, K, image,
+                                                   as_stream(stream)));
+}
+
+int64_t q4_gemm_image_workspace_size(int64_t M, int64_t K) {
+    if (check_dims(M, 0, K, 32) != Q4_OK) return 0;
+    return q4::x_image_bytes(M, K);
+}
+
+int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* y, int y_dtype, int64_t M,
+                  int64_t N, int64_t K, void* workspace, int64_t workspace_bytes, void* stream) {
+    if ((x_dtype != Q4_BF16 && x_dtype != Q4_F32) || (y_dtype != Q4_BF16 && y_dtype != Q4_F32)) return Q4_ERR_DTYPE;
+    int rc = image_dims(fmt, M, N, K);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({image, x, y}))) return rc;
+    if (workspace == nullptr || workspace_bytes < q4::x_image_bytes(M, K)) return Q4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return Q4_ERR_ALIGN;
+    const int wf = fmt == Q4_FMT_Q4_0 ? q4::WF_Q4_0 : q4::WF_AFFINE4;
+    return hip_status(q4::launch_gemm_image(wf, image, x, x_dtype, y, y_dtype, M, N, K, workspace, as_stream(stream)));
 }
 
 int dense_gemm(const void* x, int x_dtype, const uint16_t* w_f16, void* y, int y_dtype, int64_t M, int64_t N,

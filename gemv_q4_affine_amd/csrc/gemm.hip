@@ -1424,12 +1424,13 @@ hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* 
     return hipGetLastError();
 }
 
-int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K) {
-    const int64_t m_tiles = (M + kImgRows - 1) / kImgRows;
-    const int64_t n_tiles = (N + 255) / 256;
-    const int64_t ksteps = (K + 63) / 64;
-    return m_tiles * ksteps * (int64_t)kImgTile * 2 + n_tiles * ksteps * (int64_t)kWChunk;
+int64_t x_image_bytes(int64_t M, int64_t K) {
+    return (M + kImgRows - 1) / kImgRows * ((K + 63) / 64) * (int64_t)kImgTile * 2;
 }
+
+int64_t weight_image_bytes(int64_t N, int64_t K) { return (N + 255) / 256 * ((K + 63) / 64) * (int64_t)kWChunk; }
+
+int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K) { return x_image_bytes(M, K) + weight_image_bytes(N, K); }
 
 template <int WF, int XDT>
 static void launch_pack_t(const GemmArgs& ga, uint16_t* img, hipStream_t s) {
@@ -1440,22 +1441,22 @@ static void launch_pack_t(const GemmArgs& ga, uint16_t* img, hipStream_t s) {
 }
 
 template <int WF>
-static void launch_packed_w(GemmArgs ga, int xdt, int ydt, uint16_t* img, hipStream_t s) {
+static void launch_pack_w_t(const void* a, const void* b, const void* c, int N, int K, uint8_t* wimg, hipStream_t s) {
+    const int n_tiles = (N + 255) / 256;
+    const int ksteps = (K + 63) / 64;
+    const dim3 grid((unsigned)(n_tiles * ((ksteps + 3) / 4))), block(256);
+    hipLaunchKernelGGL((k_pack_w<WF>), grid, block, 0, s, static_cast<const uint8_t*>(a),
+                       static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(c), wimg, N, K, n_tiles, ksteps);
+}
+
+// X image into ximg, then the GEMM on it and the weight image ga.a.
+template <int WF>
+static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, hipStream_t s) {
     ga.m_tiles = (ga.M + kImgRows - 1) / kImgRows;
     ga.n_tiles = (ga.N + 255) / 256;
-    const int ksteps = (ga.K + 63) / 64;
-    if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, img, s);
-    else launch_pack_t<WF, DT_F32>(ga, img, s);
-    // the weight image follows the X image in the workspace
-    uint8_t* wimg = reinterpret_cast<uint8_t*>(img) + (int64_t)ga.m_tiles * ksteps * kImgTile * 2;
-    {
-        const dim3 grid((unsigned)(ga.n_tiles * ((ksteps + 3) / 4))), block(256);
-        hipLaunchKernelGGL((k_pack_w<WF>), grid, block, 0, s, static_cast<const uint8_t*>(ga.a),
-                           static_cast<const uint16_t*>(ga.b), static_cast<const uint16_t*>(ga.c), wimg, ga.N,
-                           ga.K, ga.n_tiles, ksteps);
-    }
-    ga.x = img;
-    ga.a = wimg;
+    if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
+    else launch_pack_t<WF, DT_F32>(ga, ximg, s);
+    ga.x = ximg;
     const int cus = current_cu_count();
     const int tiles = ga.m_tiles * ga.n_tiles;
     const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(256 + 64 * kPkProducers);
@@ -1463,15 +1464,33 @@ static void launch_packed_w(GemmArgs ga, int xdt, int ydt, uint16_t* img, hipStr
     else hipLaunchKernelGGL((k_gemm_pk<WF, DT_F32>), grid, block, 0, s, ga);
 }
 
+hipError_t launch_pack_weight_image(int wfmt, const void* a, const void* b, const void* c, int64_t N, int64_t K,
+                                    void* wimg, hipStream_t s) {
+    if (wfmt == WF_Q4_0) launch_pack_w_t<WF_Q4_0>(a, b, c, (int)N, (int)K, static_cast<uint8_t*>(wimg), s);
+    else if (wfmt == WF_AFFINE4) launch_pack_w_t<WF_AFFINE4>(a, b, c, (int)N, (int)K, static_cast<uint8_t*>(wimg), s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_image(int wfmt, const void* wimg, const void* x, int xdt, void* y, int ydt, int64_t M,
+                             int64_t N, int64_t K, void* ximg, hipStream_t s) {
+    GemmArgs ga{};
+    ga.a = wimg; ga.x = x; ga.y = y;
+    ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
+    if (wfmt == WF_Q4_0) launch_on_images<WF_Q4_0>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), s);
+    else if (wfmt == WF_AFFINE4) launch_on_images<WF_AFFINE4>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Both images in one workspace: the X image first, the weight image after it.
 hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
                               int ydt, int64_t M, int64_t N, int64_t K, void* img, hipStream_t s) {
     if (wfmt != WF_Q4_0 && wfmt != WF_AFFINE4) return hipErrorInvalidValue;
-    GemmArgs ga{};
-    ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
-    ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
-    if (wfmt == WF_Q4_0) launch_packed_w<WF_Q4_0>(ga, xdt, ydt, static_cast<uint16_t*>(img), s);
-    else launch_packed_w<WF_AFFINE4>(ga, xdt, ydt, static_cast<uint16_t*>(img), s);
-    return hipGetLastError();
+    uint8_t* wimg = static_cast<uint8_t*>(img) + x_image_bytes(M, K);
+    hipError_t e = launch_pack_weight_image(wfmt, a, b, c, N, K, wimg, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_image(wfmt, wimg, x, xdt, y, ydt, M, N, K, img, s);
 }
 
 template <int WF, int MT, int NT, int XDT, int YDT>

@@ -173,71 +173,62 @@ __device__ __forceinline__ uint32_t pack_out(float v, int odt) {
     return odt == DT_F16 ? f32_to_f16_rne(v) : f32_to_bf16(v);
 }
 
+// Each 32-weight block (Q4_0) or half group (affine) is written by 4 lanes,
+// 8 consecutive outputs each, so that the lanes of a wave store one
+// contiguous run (1 KiB of binary16 per store instruction).
 template <int ODT>
-__global__ __launch_bounds__(256) void k_q4_dequantize(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
-                                                       int64_t nblocks, void* __restrict__ out) {
-    for (int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nblocks;
-         blk += (int64_t)gridDim.x * blockDim.x) {
-        const u32x4_t w = reinterpret_cast<const u32x4_t*>(qs)[blk];
-        const float dd = f16_to_f32(d[blk]);
-        float v[32];
+__device__ __forceinline__ void store8(void* out, int64_t e0, const float (&v)[8]) {
+    if constexpr (ODT == DT_F32) {
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + e0);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        u32x4_t t;
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-            v[i] = (float)((int)(byte & 0xF) - 8) * dd;        // exact in binary32
-            v[i + 16] = (float)((int)(byte >> 4) - 8) * dd;
-        }
-        if (ODT == DT_F32) {
-            float4* o = reinterpret_cast<float4*>(out) + blk * 8;
-#pragma unroll
-            for (int i = 0; i < 8; i++) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-        } else {
-            u32x4_t* o = reinterpret_cast<u32x4_t*>(out) + blk * 4;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                u32x4_t t;
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    t[j] = pack_out(v[8 * i + 2 * j], ODT) | (pack_out(v[8 * i + 2 * j + 1], ODT) << 16);
-                o[i] = t;
-            }
-        }
+        for (int j = 0; j < 4; j++) t[j] = pack_out(v[2 * j], ODT) | (pack_out(v[2 * j + 1], ODT) << 16);
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(out) + e0) = t;
     }
 }
 
-// One thread per 32 weights (half a group of 64).
+// Part p of a block holds elements 8p..8p+7: the low nibbles of bytes
+// 8(p & 1)..+7 for p < 2, their high nibbles for p >= 2.
+template <int ODT>
+__global__ __launch_bounds__(256) void k_q4_dequantize(const uint8_t* __restrict__ qs, const uint16_t* __restrict__ d,
+                                                       int64_t nparts, void* __restrict__ out) {
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nparts;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t blk = t >> 2;
+        const int p = (int)(t & 3);
+        const u32x2_t w = *reinterpret_cast<const u32x2_t*>(qs + blk * 16 + 8 * (p & 1));
+        const float dd = f16_to_f32(d[blk]);
+        const int sh = 4 * (p >> 1);
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t nib = (w[i >> 2] >> (8 * (i & 3) + sh)) & 0xFu;
+            v[i] = (float)((int)nib - 8) * dd;        // exact in binary32
+        }
+        store8<ODT>(out, t * 8, v);
+    }
+}
+
+// Part p of a 32-weight half group holds elements 8p..8p+7, the nibbles of
+// bytes 4p..4p+3 (element 2i in the low nibble of byte i).
 template <int ODT>
 __global__ __launch_bounds__(256) void k_affine4_dequantize(const uint8_t* __restrict__ wq,
                                                             const uint16_t* __restrict__ scales,
-                                                            const uint16_t* __restrict__ biases, int64_t nchunks,
+                                                            const uint16_t* __restrict__ biases, int64_t nparts,
                                                             int group_shift, void* __restrict__ out) {
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const u32x4_t w = reinterpret_cast<const u32x4_t*>(wq)[c];
-        const int64_t g = (c * 32) >> group_shift;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nparts;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(wq + t * 4);
+        const int64_t g = (t * 8) >> group_shift;
         const float s = bf16_to_f32(scales[g]);
         const float b = bf16_to_f32(biases[g]);
-        float v[32];
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-            uint32_t code = (w[i >> 3] >> (4 * (i & 7))) & 0xFu;
-            v[i] = fmaf((float)code, s, b);  // nearest binary32 to q*s + b
-        }
-        if (ODT == DT_F32) {
-            float4* o = reinterpret_cast<float4*>(out) + c * 8;
-#pragma unroll
-            for (int i = 0; i < 8; i++) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-        } else {
-            u32x4_t* o = reinterpret_cast<u32x4_t*>(out) + c * 4;
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                u32x4_t t;
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    t[j] = pack_out(v[8 * i + 2 * j], ODT) | (pack_out(v[8 * i + 2 * j + 1], ODT) << 16);
-                o[i] = t;
-            }
-        }
+        for (int i = 0; i < 8; i++) v[i] = fmaf((float)((w >> (4 * i)) & 0xFu), s, b);  // nearest binary32 to q*s + b
+        store8<ODT>(out, t * 8, v);
     }
 }
 
@@ -283,22 +274,22 @@ hipError_t launch_affine4_quantize(const void* w, int wdt, int64_t N, int64_t K,
 
 hipError_t launch_q4_dequantize(const uint8_t* qs, const uint16_t* d, int64_t N, int64_t K, void* out, int odt,
                                 hipStream_t s) {
-    const int64_t nb = N * (K / 32);
-    const dim3 g(grid_for(nb, 256)), b(256);
-    if (odt == DT_F16) hipLaunchKernelGGL(k_q4_dequantize<DT_F16>, g, b, 0, s, qs, d, nb, out);
-    else if (odt == DT_BF16) hipLaunchKernelGGL(k_q4_dequantize<DT_BF16>, g, b, 0, s, qs, d, nb, out);
-    else hipLaunchKernelGGL(k_q4_dequantize<DT_F32>, g, b, 0, s, qs, d, nb, out);
+    const int64_t np = N * (K / 32) * 4;
+    const dim3 g(grid_for(np, 256)), b(256);
+    if (odt == DT_F16) hipLaunchKernelGGL(k_q4_dequantize<DT_F16>, g, b, 0, s, qs, d, np, out);
+    else if (odt == DT_BF16) hipLaunchKernelGGL(k_q4_dequantize<DT_BF16>, g, b, 0, s, qs, d, np, out);
+    else hipLaunchKernelGGL(k_q4_dequantize<DT_F32>, g, b, 0, s, qs, d, np, out);
     return hipGetLastError();
 }
 
 hipError_t launch_affine4_dequantize(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, int64_t G,
                                      int64_t N, int64_t K, void* out, int odt, hipStream_t s) {
-    const int64_t nc = N * (K / 32);
+    const int64_t np = N * (K / 8);
     const int gs = (G == 64) ? 6 : 5;
-    const dim3 g(grid_for(nc, 256)), b(256);
-    if (odt == DT_F16) hipLaunchKernelGGL(k_affine4_dequantize<DT_F16>, g, b, 0, s, wq, sc, bi, nc, gs, out);
-    else if (odt == DT_BF16) hipLaunchKernelGGL(k_affine4_dequantize<DT_BF16>, g, b, 0, s, wq, sc, bi, nc, gs, out);
-    else hipLaunchKernelGGL(k_affine4_dequantize<DT_F32>, g, b, 0, s, wq, sc, bi, nc, gs, out);
+    const dim3 g(grid_for(np, 256)), b(256);
+    if (odt == DT_F16) hipLaunchKernelGGL(k_affine4_dequantize<DT_F16>, g, b, 0, s, wq, sc, bi, np, gs, out);
+    else if (odt == DT_BF16) hipLaunchKernelGGL(k_affine4_dequantize<DT_BF16>, g, b, 0, s, wq, sc, bi, np, gs, out);
+    else hipLaunchKernelGGL(k_affine4_dequantize<DT_F32>, g, b, 0, s, wq, sc, bi, np, gs, out);
     return hipGetLastError();
 }
 

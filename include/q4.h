@@ -68,7 +68,7 @@ extern "C" {
 #define Q4_ERR_DTYPE    -4   /* unsupported dtype code                          */
 #define Q4_ERR_HIP      -5   /* a HIP launch or runtime call failed             */
 #define Q4_ERR_ARG      -6   /* other invalid argument (dispatch key, path...)  */
-#define Q4_ERR_WORKSPACE -7  /* forced dequantise path without enough workspace */
+#define Q4_ERR_WORKSPACE -7  /* a path that needs workspace got too little */
 
 /* ---- dtype codes ---------------------------------------------------------- */
 #define Q4_F32   0
@@ -271,6 +271,42 @@ int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
  * Returns 0 for invalid arguments.
  */
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt);
+
+/*
+ * Weight image for the matrix-core GEMM, prepared once per weight matrix:
+ * the MFMA path's per-call weight regrouping (q4_gemm with a workspace) moved
+ * out of the call, for callers that multiply the same weights many times
+ * (prefill over many prompts).  The dequantisation itself stays fused in the
+ * GEMM: the image holds the same 4.5 bits per weight as the planes.
+ *
+ * q4_weight_image_size -- bytes of the image of an [N][K] matrix,
+ * ceil(N/256) * ceil(K/64) * 9216; 0 for invalid arguments.
+ */
+int64_t q4_weight_image_size(int64_t N, int64_t K, int fmt);
+
+/*
+ * q4_pack_weight_image -- lay the weight planes out as that image.
+ *   fmt   : Q4_FMT_Q4_0 (w_q = qs, w_s = d, w_b unused) or Q4_FMT_AFFINE4
+ *           (w_q, w_s = scales, w_b = biases; group size 64)
+ *   image : device out, q4_weight_image_size(N, K, fmt) bytes, 16-byte aligned
+ * K % 32 == 0 (Q4_0) or K % 64 == 0 (affine), else Q4_ERR_SHAPE.
+ */
+int q4_pack_weight_image(int fmt, const uint8_t* w_q, const uint16_t* w_s, const uint16_t* w_b,
+                         int64_t N, int64_t K, void* image, void* stream);
+
+/*
+ * q4_gemm_image -- Y = X . dequant(W)^T on the matrix-core path from a
+ * weight image: the same results as q4_gemm / affine4_gemm on the MFMA path
+ * with a workspace, for any M >= 1.
+ *   workspace : device scratch for the X image, at least
+ *               q4_gemm_image_workspace_size(M, K) =
+ *               ceil(M/128)*128 * ceil(K/64)*64 * 2 bytes (else
+ *               Q4_ERR_WORKSPACE).  Calls sharing it must not overlap.
+ */
+int64_t q4_gemm_image_workspace_size(int64_t M, int64_t K);
+int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* y, int y_dtype,
+                  int64_t M, int64_t N, int64_t K,
+                  void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * dense_gemm -- Y = X . W^T with a dense binary16 W [N][K] (the GEMM half of

@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 22, names
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in q4.h but not exported"
@@ -144,6 +144,30 @@ def test_gemm_validation():
     d = lib().dense_gemm
     assert d(P, B.Q4_BF16, P, P, B.Q4_BF16, 4, 8, 48, None) == B.Q4_ERR_SHAPE
     assert d(P, B.Q4_BF16, None, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_NULL
+
+
+def test_weight_image_validation_and_sizes():
+    assert lib().q4_weight_image_size(12288, 4096, B.Q4_FMT_Q4_0) == 48 * 64 * 9216
+    assert lib().q4_weight_image_size(300, 96, B.Q4_FMT_Q4_0) == 2 * 2 * 9216
+    assert lib().q4_weight_image_size(300, 96, B.Q4_FMT_AFFINE4) == 0        # K % 64 != 0
+    assert lib().q4_weight_image_size(300, 128, 5) == 0
+    assert lib().q4_gemm_image_workspace_size(2048, 4096) == 2048 * 4096 * 2
+    assert lib().q4_gemm_image_workspace_size(129, 96) == 256 * 128 * 2
+    p = lib().q4_pack_weight_image
+    assert p(5, P, P, None, 8, 64, P, None) == B.Q4_ERR_ARG
+    assert p(B.Q4_FMT_Q4_0, P, P, None, 8, 48, P, None) == B.Q4_ERR_SHAPE
+    assert p(B.Q4_FMT_AFFINE4, P, P, P, 8, 96, P, None) == B.Q4_ERR_SHAPE
+    assert p(B.Q4_FMT_AFFINE4, P, P, None, 8, 128, P, None) == B.Q4_ERR_NULL   # affine needs biases
+    assert p(B.Q4_FMT_Q4_0, P, P, None, 8, 64, MIS, None) == B.Q4_ERR_ALIGN
+    assert p(B.Q4_FMT_Q4_0, P, P, None, 0, 64, P, None) == B.Q4_OK
+    g = lib().q4_gemm_image
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_F16, P, B.Q4_BF16, 4, 8, 64, P2, 1 << 20, None) == B.Q4_ERR_DTYPE
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, P2, 128 * 64 * 2 - 1, None) == B.Q4_ERR_WORKSPACE
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, MIS, 1 << 20, None) == B.Q4_ERR_ALIGN
+    assert g(B.Q4_FMT_Q4_0, None, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, P2, 1 << 20, None) == B.Q4_ERR_NULL
+    assert g(B.Q4_FMT_AFFINE4, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, P2, 1 << 20, None) == B.Q4_ERR_SHAPE
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None, 0, None) == B.Q4_OK
 
 
 def test_forced_dequant_path_without_workspace_is_an_error():

@@ -402,6 +402,36 @@ def test_q4_gemm_every_path_boundary_m(M):
             B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 160, 640, 1024), ("q4_0", 129, 300, 96), ("q4_0", 1, 257, 4096),
+                                       ("affine", 160, 640, 1024), ("affine", 129, 300, 128)])
+def test_gemm_image_equals_mfma_path(fmt, M, N, K):
+    """A prepacked weight image gives the bits of q4_gemm / affine4_gemm on the
+    matrix-core path with a workspace, call after call with new activations."""
+    say(f"gemm_image {fmt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    W = synth.weights(rng, N, K)
+    if fmt == "q4_0":
+        planes = [dev(a) for a in oracle.q4_0_quantize(W)]
+        run = lambda x, ws, ydt: B.q4_gemm(*planes, x, y_dtype=ydt, workspace=ws)
+        f = B.Q4_FMT_Q4_0
+    else:
+        planes = [dev(a) for a in oracle.affine4_quantize(synth.bf16_bits(W), 64)]
+        run = lambda x, ws, ydt: B.affine4_gemm(*planes, x, y_dtype=ydt, workspace=ws)
+        f = B.Q4_FMT_AFFINE4
+    image = B.q4_pack_weight_image(*planes, fmt=f)
+    ws = torch.empty(B.lib().q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
+    try:
+        for call in range(2):
+            x = bf16_dev(synth.activations(rng, M, K))
+            for ydt in (torch.bfloat16, torch.float32):
+                want = run(x, ws, ydt)
+                got = B.q4_gemm_image(image, x, N, fmt=f, y_dtype=ydt)
+                assert torch.equal(got, want), (fmt, M, N, K, call, ydt)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+
+
 @pytest.mark.parametrize("M", [1, 17, 64, 65, 300])
 def test_affine4_gemm_every_path(M):
     N, K = 257, 1024
