@@ -30,7 +30,8 @@
 //    next step's dequantisation, one barrier per K step.  Without a workspace
 //    for the image, k_gemm_mfma converts X on the way into LDS instead.
 //  * Small M (k_gemm_skinny): weights stream once from HBM at full rate and
-//    four waves split K.
+//    the waves of a workgroup split K; M == 1 (k_gemv_x) runs the decode
+//    GEMV's layout with fp32 dot2 products on bf16 / binary16 X.
 //  * Each MFMA sums over 16 (or 32) K slots; the slot -> k assignment only has
 //    to agree between the A and B operands, so it is chosen to match each
 //    weight format's nibble order and the B loader needs no byte shuffles
@@ -1517,13 +1518,256 @@ static void launch_skinny_w(GemmArgs ga, int xdt, int ydt, hipStream_t s) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Vector kernel for M == 1 on bf16 / f32 activations (the MFMA skinny kernel
+// is faster from M = 2 on).
+//
+// The layout of the decode GEMV: lane l of wave w owns 32-weight block
+// column 8w + (l & 7) (and every 8*NW-th after it) and RI rows r0 + (l >> 3)
+// + 8i; one 128-bit load brings a row's block.  The dots run two products at a
+// time in fp32 (v_dot2_f32_bf16 on bf16 X, v_dot2_f32_f16 on f32 X rounded to
+// binary16): each nibble pair becomes the 16-bit pair (B+q, B+q') with one
+// AND-OR against the exponent of B (bf16 128 or binary16 1024, where a
+// nibble's unit is 1), exact, so a block row's sum of (B+q)*x minus B times
+// the column's sum of x gives sum q*x (exact products, fp32 sums).  Q4_0 then
+// takes (q-8)*d per block, affine s*sum q*x + b*sum x per group.  The X pairs
+// are permuted once per column to match the nibble pairs and serve all RI
+// rows.  Partial sums meet in a fixed order (an 8-lane butterfly, then waves
+// in order through LDS), so results are deterministic.
+// ---------------------------------------------------------------------------
+template <int XDT>
+struct VecDot {
+    // magic exponent and value: bf16 128.0 / binary16 1024.0
+    static constexpr uint32_t kMagic = XDT == DT_BF16 ? 0x43004300u : 0x64006400u;
+    static constexpr float kBase = XDT == DT_BF16 ? 128.0f : 1024.0f;
+    static constexpr uint32_t kOne = XDT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;   // (1, 1)
+    __device__ static float dot(uint32_t a, uint32_t b, float c) {
+        if constexpr (XDT == DT_BF16)
+            return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                                   false);
+        else
+            return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+    }
+};
+
+constexpr int kVecMaxWaves = 16;
+
+// M == 1 on bf16 X keeps to 64 VGPRs (8 waves per SIMD, 2 workgroups per
+// CU); larger M and f32 X take 512-thread workgroups and more registers.
+template <int WF, int M, int RI, int XDT, int YDT>
+__global__ __launch_bounds__(M == 1 ? 1024 : 512) __attribute__((amdgpu_waves_per_eu(M == 1 && XDT == DT_BF16 ? 8 : 1)))
+void k_gemv_x(const GemmArgs a) {
+    static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
+    using D = VecDot<XDT == DT_BF16 ? DT_BF16 : DT_F16>;
+    __shared__ float red[kVecMaxWaves][8 * RI * M];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int bl = w * 8 + (lane & 7);
+    const int rl = lane >> 3;
+    const int stride = nw * 8;
+    const int nb = a.K / 32;
+    const int r0 = blockIdx.x * 8 * RI;
+
+    // rows past N read row 0 (valid memory) and are never written
+    const uint8_t* rq[RI];
+    const uint16_t* rs[RI];
+    const uint16_t* rb[RI];
+#pragma unroll
+    for (int i = 0; i < RI; i++) {
+        const int R = r0 + rl + 8 * i;
+        const int n = R < a.N ? R : 0;
+        rq[i] = static_cast<const uint8_t*>(a.a) + (int64_t)n * nb * 16;
+        if constexpr (WF == WF_Q4_0) {
+            rs[i] = static_cast<const uint16_t*>(a.b) + (int64_t)n * nb;
+            rb[i] = nullptr;
+        } else {
+            rs[i] = static_cast<const uint16_t*>(a.b) + (int64_t)n * (nb / 2);
+            rb[i] = static_cast<const uint16_t*>(a.c) + (int64_t)n * (nb / 2);
+        }
+    }
+    float acc[RI][M];
+#pragma unroll
+    for (int i = 0; i < RI; i++)
+#pragma unroll
+        for (int m = 0; m < M; m++) acc[i][m] = 0.0f;
+
+    for (int c = bl; c < nb; c += stride) {
+        // X of column c, as 16 words of two 16-bit values (elements 2j, 2j+1)
+        uint32_t xw[M][16];
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            if constexpr (XDT == DT_BF16) {
+                const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(
+                    static_cast<const uint16_t*>(a.x) + (int64_t)m * a.K + (int64_t)c * 32);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const u32x4_t v = xp[q];
+#pragma unroll
+                    for (int t = 0; t < 4; t++) xw[m][4 * q + t] = v[t];
+                }
+            } else {
+                const float4* xp = reinterpret_cast<const float4*>(
+                    static_cast<const float*>(a.x) + (int64_t)m * a.K + (int64_t)c * 32);
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    const float4 v = xp[q];
+                    xw[m][2 * q] = f32_to_f16(v.x) | (f32_to_f16(v.y) << 16);
+                    xw[m][2 * q + 1] = f32_to_f16(v.z) | (f32_to_f16(v.w) << 16);
+                }
+            }
+        }
+        u32x4_t wq[RI];
+        uint32_t sc[RI], bi[RI];
+#pragma unroll
+        for (int i = 0; i < RI; i++) {
+            wq[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rq[i] + (int64_t)c * 16));
+            if constexpr (WF == WF_Q4_0) {
+                sc[i] = rs[i][c];
+                bi[i] = 0;
+            } else {
+                sc[i] = rs[i][c >> 1];
+                bi[i] = rb[i][c >> 1];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // X pairs in the order of the nibble pairs of word t: slots 0-3 =
+        // low nibbles of bytes (0, 2), of bytes (1, 3), high nibbles of bytes
+        // (0, 2), of bytes (1, 3)
+        auto lo2 = [](uint32_t p, uint32_t q) { return (p & 0xFFFFu) | (q << 16); };
+        auto hi2 = [](uint32_t p, uint32_t q) { return (p >> 16) | (q & 0xFFFF0000u); };
+        uint32_t xp[M][16];
+        float sx[M];
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                if constexpr (WF == WF_Q4_0) {      // byte b: elements b and b + 16
+                    xp[m][4 * t + 0] = lo2(xw[m][2 * t], xw[m][2 * t + 1]);
+                    xp[m][4 * t + 1] = hi2(xw[m][2 * t], xw[m][2 * t + 1]);
+                    xp[m][4 * t + 2] = lo2(xw[m][8 + 2 * t], xw[m][9 + 2 * t]);
+                    xp[m][4 * t + 3] = hi2(xw[m][8 + 2 * t], xw[m][9 + 2 * t]);
+                } else {                             // byte b: elements 2b and 2b + 1
+                    xp[m][4 * t + 0] = lo2(xw[m][4 * t], xw[m][4 * t + 2]);
+                    xp[m][4 * t + 1] = lo2(xw[m][4 * t + 1], xw[m][4 * t + 3]);
+                    xp[m][4 * t + 2] = hi2(xw[m][4 * t], xw[m][4 * t + 2]);
+                    xp[m][4 * t + 3] = hi2(xw[m][4 * t + 1], xw[m][4 * t + 3]);
+                }
+            }
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 16; j++) s = D::dot(xw[m][j], D::kOne, s);
+            sx[m] = s;
+        }
+        const float off = D::kBase + (WF == WF_Q4_0 ? 8.0f : 0.0f);
+#pragma unroll
+        for (int i = 0; i < RI; i++) {
+            uint32_t wp[16];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t v = wq[i][t];
+                wp[4 * t + 0] = (v & 0x000F000Fu) | D::kMagic;
+                wp[4 * t + 1] = ((v >> 8) & 0x000F000Fu) | D::kMagic;
+                wp[4 * t + 2] = ((v >> 4) & 0x000F000Fu) | D::kMagic;
+                wp[4 * t + 3] = ((v >> 12) & 0x000F000Fu) | D::kMagic;
+            }
+            float scale, bias;
+            if constexpr (WF == WF_Q4_0) {
+                scale = f16_to_f32(sc[i]);
+                bias = 0.0f;
+            } else {
+                scale = bf16_to_f32(sc[i]);
+                bias = bf16_to_f32(bi[i]);
+            }
+#pragma unroll
+            for (int m = 0; m < M; m++) {
+                float d = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 16; j++) d = D::dot(wp[j], xp[m][j], d);
+                const float t = fmaf(-off, sx[m], d);          // sum of (q - 8) x, or q x
+                acc[i][m] = fmaf(scale, t, acc[i][m]);
+                if constexpr (WF == WF_AFFINE4) acc[i][m] = fmaf(bias, sx[m], acc[i][m]);
+            }
+        }
+    }
+
+    auto sum8 = [](float v) {
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+        return v;
+    };
+#pragma unroll
+    for (int i = 0; i < RI; i++)
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            const float v = sum8(acc[i][m]);
+            if ((lane & 7) == 0) red[w][(i * 8 + rl) * M + m] = v;
+        }
+    __syncthreads();
+    for (int t = threadIdx.x; t < 8 * RI * M; t += blockDim.x) {
+        const int m = t % M;
+        const int slot = t / M;
+        const int R = r0 + (slot & 7) + 8 * (slot >> 3);
+        if (R >= a.N) continue;
+        float v = red[0][t];
+        for (int ww = 1; ww < nw; ww++) v += red[ww][t];
+        const int64_t off = (int64_t)m * a.N + R;
+        if constexpr (YDT == DT_BF16) reinterpret_cast<uint16_t*>(a.y)[off] = (uint16_t)f32_to_bf16(v);
+        else reinterpret_cast<float*>(a.y)[off] = v;
+    }
+}
+
+template <int WF, int M, int XDT, int YDT>
+static void launch_vec_m(const GemmArgs& ga, hipStream_t s) {
+    const int nb = ga.K / 32;
+    const int maxw = M == 1 ? kVecMaxWaves : kVecMaxWaves / 2;
+    const int nw = nb < 8 ? 1 : ((nb + 7) / 8 > maxw ? maxw : (nb + 7) / 8);
+    // rows per lane: enough workgroups for 32 resident waves per CU at most
+    const int64_t slots = (int64_t)current_cu_count() * 32 / nw;
+    int64_t ri = (ga.N + 8 * slots - 1) / (8 * slots);
+    const int cap = M == 1 && XDT == DT_BF16 ? 2 : 1;
+    ri = ri < 1 ? 1 : (ri > cap ? cap : ri);
+    const dim3 block(nw * 64);
+    const dim3 grid((unsigned)((ga.N + 8 * ri - 1) / (8 * ri)));
+    if constexpr (M == 1 && XDT == DT_BF16) {
+        if (ri == 2) { hipLaunchKernelGGL((k_gemv_x<WF, M, 2, XDT, YDT>), grid, block, 0, s, ga); return; }
+    }
+    hipLaunchKernelGGL((k_gemv_x<WF, M, 1, XDT, YDT>), grid, block, 0, s, ga);
+}
+
+template <int WF, int XDT, int YDT>
+static void launch_vec_t(const GemmArgs& ga, hipStream_t s) {
+    switch (ga.M) {
+        case 1: launch_vec_m<WF, 1, XDT, YDT>(ga, s); break;
+        case 2: launch_vec_m<WF, 2, XDT, YDT>(ga, s); break;
+        case 3: launch_vec_m<WF, 3, XDT, YDT>(ga, s); break;
+        default: launch_vec_m<WF, 4, XDT, YDT>(ga, s); break;
+    }
+}
+
+template <int WF>
+static void launch_vec_w(const GemmArgs& ga, int xdt, int ydt, hipStream_t s) {
+    if (xdt == DT_BF16) {
+        if (ydt == DT_BF16) launch_vec_t<WF, DT_BF16, DT_BF16>(ga, s);
+        else launch_vec_t<WF, DT_BF16, DT_F32>(ga, s);
+    } else {
+        if (ydt == DT_BF16) launch_vec_t<WF, DT_F32, DT_BF16>(ga, s);
+        else launch_vec_t<WF, DT_F32, DT_F32>(ga, s);
+    }
+}
+
+constexpr int kVecMaxM = 1;   // the skinny path's vector kernel serves M == 1 (MFMA beyond)
+
 hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
                               int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
     if (M > 64) return hipErrorInvalidValue;
     GemmArgs ga{};
     ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
     ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
-    if (wfmt == WF_Q4_0) launch_skinny_w<WF_Q4_0>(ga, xdt, ydt, s);
+    if (M <= kVecMaxM && wfmt == WF_Q4_0) launch_vec_w<WF_Q4_0>(ga, xdt, ydt, s);
+    else if (M <= kVecMaxM && wfmt == WF_AFFINE4) launch_vec_w<WF_AFFINE4>(ga, xdt, ydt, s);
+    else if (wfmt == WF_Q4_0) launch_skinny_w<WF_Q4_0>(ga, xdt, ydt, s);
     else if (wfmt == WF_AFFINE4) launch_skinny_w<WF_AFFINE4>(ga, xdt, ydt, s);
     else launch_skinny_w<WF_DENSE16>(ga, xdt, ydt, s);
     return hipGetLastError();
