@@ -24,6 +24,7 @@ Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM = 0, 1, 2, 3
 Q4_KEY_SKINNY_MAX_M, Q4_KEY_DEQUANT_MIN_M, Q4_KEY_FORCE_PATH = 0, 1, 2
 Q4_GEMV_MAX_M = 16
 Q4_GEMV_ACT_MAX_M = 4
+Q4_GEMV_MAX_MATS = 4
 
 # exported symbols and their ctypes signatures
 _P, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -37,6 +38,8 @@ SIGNATURES = {
     "q4_gemv_fused2": (_INT, [_P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P]),
     "q4_gemv_act": (_INT, [_P, _P, _P, _INT, _P, _I64, _I64, _I64, _P]),
     "q4_gemv_fused2_act": (_INT, [_P, _P, _I64, _P, _P, _I64, _P, _INT, _P, _P, _I64, _I64, _P]),
+    "q4_gemv_multi": (_INT, [_INT, _P, _P, _P, _P, _P, _P, _I64, _I64, _P]),
+    "q4_gemv_multi_act": (_INT, [_INT, _P, _P, _P, _P, _INT, _P, _I64, _I64, _P]),
     "q4_gemm": (_INT, [_P, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "affine4_gemm": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "q4_gemm_workspace_size": (_I64, [_I64, _I64, _I64, _INT]),
@@ -211,6 +214,36 @@ def q4_gemv_fused2_act(w0_qs, w0_d, w1_qs, w1_d, x, y0=None, y1=None, stream=Non
                                                           _p(x), _dt(x), _p(y0), _p(y1), M, K,
                                                           _stream(stream)))
     return y0, y1
+
+
+def _mat_arrays(mats, ys):
+    n = len(mats)
+    qs = (ctypes.c_void_p * n)(*[_p(q) for q, _ in mats])
+    ds = (ctypes.c_void_p * n)(*[_p(d) for _, d in mats])
+    rows = (ctypes.c_int64 * n)(*[d.shape[0] for _, d in mats])
+    yp = (ctypes.c_void_p * n)(*[_p(y) for y in ys])
+    return qs, ds, rows, yp
+
+
+def q4_gemv_multi(mats, x_qs, x_ds, ys=None, stream=None):
+    """One launch over several Q4_0 matrices [(qs, d), ...] sharing the Q8_1
+    activation; returns a list of float32 [M, N_i]."""
+    M, K = x_qs.shape
+    ys = [_empty((M, d.shape[0]), torch.float32, x_qs) for _, d in mats] if ys is None else ys
+    qs, ds, rows, yp = _mat_arrays(mats, ys)
+    _check("q4_gemv_multi", lib().q4_gemv_multi(len(mats), qs, ds, rows, _p(x_qs), _p(x_ds), yp, M, K,
+                                                _stream(stream)))
+    return ys
+
+
+def q4_gemv_multi_act(mats, x, ys=None, stream=None):
+    """q4_gemv_multi on a raw bf16 / f32 activation, quantised to Q8_1 in the kernel."""
+    M, K = x.shape
+    ys = [_empty((M, d.shape[0]), torch.float32, x) for _, d in mats] if ys is None else ys
+    qs, ds, rows, yp = _mat_arrays(mats, ys)
+    _check("q4_gemv_multi_act", lib().q4_gemv_multi_act(len(mats), qs, ds, rows, _p(x), _dt(x), yp, M, K,
+                                                        _stream(stream)))
+    return ys
 
 
 # ---- GEMM -----------------------------------------------------------------------------

@@ -209,64 +209,99 @@ int affine4_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
 
 // ---- decode GEMV -------------------------------------------------------------------
 
+// Shared checks and launch of every GEMV entry point: nmat matrices (host
+// arrays) sharing the activation -- Q8_1 planes (x == nullptr) or the raw
+// activation x of x_dtype, quantised inside the kernel.
+static int gemv_common(int nmat, const uint8_t* const* qs, const uint16_t* const* d, const int64_t* n,
+                       float* const* y, const int8_t* x_qs, const uint16_t* x_ds, const void* x, int x_dtype,
+                       int64_t M, int64_t K, void* stream) {
+    if (nmat < 1 || nmat > Q4_GEMV_MAX_MATS) return Q4_ERR_ARG;
+    if (!qs || !d || !n || !y) return Q4_ERR_NULL;
+    int64_t total = 0;
+    for (int i = 0; i < nmat; i++) {
+        const int rc = check_dims(M, n[i], K, 32);
+        if (rc) return rc;
+        total += n[i];
+    }
+    const bool raw = x != nullptr || (x_qs == nullptr && x_ds == nullptr);
+    if (raw) {
+        if (x_dtype != Q4_F32 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+        if (M > Q4_GEMV_ACT_MAX_M) return Q4_ERR_SHAPE;
+    } else if (M > Q4_GEMV_MAX_M) {
+        return Q4_ERR_SHAPE;
+    }
+    if (total > int64_t(0x7FFFFFFF)) return Q4_ERR_SHAPE;
+    if (M == 0 || total == 0) return Q4_OK;
+    int rc = raw ? check_ptrs_aligned({x}) : check_ptrs_aligned({x_qs, x_ds});
+    if (rc) return rc;
+    for (int i = 0; i < nmat; i++)
+        if (n[i] > 0 && (rc = check_ptrs_aligned({qs[i], d[i], y[i]}))) return rc;
+    return hip_status(q4::launch_q4_gemv_multi(nmat, qs, d, n, y, raw ? nullptr : x_qs, raw ? nullptr : x_ds,
+                                               raw ? x : nullptr, x_dtype, M, K, as_stream(stream)));
+}
+
 int q4_gemv(const uint8_t* w_qs, const uint16_t* w_d, const int8_t* x_qs, const uint16_t* x_ds, float* y,
             int64_t M, int64_t N, int64_t K, void* stream) {
-    int rc = check_dims(M, N, K, 32);
-    if (rc) return rc;
-    if (M > Q4_GEMV_MAX_M) return Q4_ERR_SHAPE;
-    if (M == 0 || N == 0) return Q4_OK;
-    if ((rc = check_ptrs_aligned({w_qs, w_d, x_qs, x_ds, y}))) return rc;
-    return hip_status(q4::launch_q4_gemv(w_qs, w_d, y, N, nullptr, nullptr, nullptr, 0, x_qs, x_ds, M, K,
-                                         as_stream(stream)));
+    if (!x_qs || !x_ds) {
+        const int rc = check_dims(M, N, K, 32);
+        if (rc) return rc;
+        if (M > Q4_GEMV_MAX_M) return Q4_ERR_SHAPE;
+        if (M == 0 || N == 0) return Q4_OK;
+        return Q4_ERR_NULL;
+    }
+    const uint8_t* qs[1] = {w_qs};
+    const uint16_t* d[1] = {w_d};
+    const int64_t n[1] = {N};
+    float* ys[1] = {y};
+    return gemv_common(1, qs, d, n, ys, x_qs, x_ds, nullptr, Q4_BF16, M, K, stream);
 }
 
 int q4_gemv_fused2(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0, const uint8_t* w1_qs,
                    const uint16_t* w1_d, int64_t N1, const int8_t* x_qs, const uint16_t* x_ds, float* y0, float* y1,
                    int64_t M, int64_t K, void* stream) {
-    int rc = check_dims(M, N0, K, 32);
-    if (rc) return rc;
-    if ((rc = check_dims(M, N1, K, 32))) return rc;
-    if (M > Q4_GEMV_MAX_M) return Q4_ERR_SHAPE;
-    if (N0 + N1 > int64_t(0x7FFFFFFF)) return Q4_ERR_SHAPE;
-    if (M == 0 || N0 + N1 == 0) return Q4_OK;
-    if ((rc = check_ptrs_aligned({x_qs, x_ds}))) return rc;
-    if (N0 > 0 && (rc = check_ptrs_aligned({w0_qs, w0_d, y0}))) return rc;
-    if (N1 > 0 && (rc = check_ptrs_aligned({w1_qs, w1_d, y1}))) return rc;
-    return hip_status(
-        q4::launch_q4_gemv(w0_qs, w0_d, y0, N0, w1_qs, w1_d, y1, N1, x_qs, x_ds, M, K, as_stream(stream)));
-}
-
-static int gemv_act_shape(int x_dtype, int64_t M) {
-    if (x_dtype != Q4_F32 && x_dtype != Q4_BF16) return Q4_ERR_DTYPE;
-    if (M > Q4_GEMV_ACT_MAX_M) return Q4_ERR_SHAPE;
-    return Q4_OK;
+    if (!x_qs || !x_ds) {
+        int rc = check_dims(M, N0, K, 32);
+        if (rc || (rc = check_dims(M, N1, K, 32))) return rc;
+        if (M > Q4_GEMV_MAX_M) return Q4_ERR_SHAPE;
+        if (M == 0 || N0 + N1 == 0) return Q4_OK;
+        return Q4_ERR_NULL;
+    }
+    const uint8_t* qs[2] = {w0_qs, w1_qs};
+    const uint16_t* d[2] = {w0_d, w1_d};
+    const int64_t n[2] = {N0, N1};
+    float* ys[2] = {y0, y1};
+    return gemv_common(2, qs, d, n, ys, x_qs, x_ds, nullptr, Q4_BF16, M, K, stream);
 }
 
 int q4_gemv_act(const uint8_t* w_qs, const uint16_t* w_d, const void* x, int x_dtype, float* y, int64_t M,
                 int64_t N, int64_t K, void* stream) {
-    int rc = check_dims(M, N, K, 32);
-    if (rc) return rc;
-    if ((rc = gemv_act_shape(x_dtype, M))) return rc;
-    if (M == 0 || N == 0) return Q4_OK;
-    if ((rc = check_ptrs_aligned({w_qs, w_d, x, y}))) return rc;
-    return hip_status(q4::launch_q4_gemv_act(w_qs, w_d, y, N, nullptr, nullptr, nullptr, 0, x, x_dtype, M, K,
-                                             as_stream(stream)));
+    const uint8_t* qs[1] = {w_qs};
+    const uint16_t* d[1] = {w_d};
+    const int64_t n[1] = {N};
+    float* ys[1] = {y};
+    return gemv_common(1, qs, d, n, ys, nullptr, nullptr, x, x_dtype, M, K, stream);
 }
 
 int q4_gemv_fused2_act(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0, const uint8_t* w1_qs,
                        const uint16_t* w1_d, int64_t N1, const void* x, int x_dtype, float* y0, float* y1,
                        int64_t M, int64_t K, void* stream) {
-    int rc = check_dims(M, N0, K, 32);
-    if (rc) return rc;
-    if ((rc = check_dims(M, N1, K, 32))) return rc;
-    if ((rc = gemv_act_shape(x_dtype, M))) return rc;
-    if (N0 + N1 > int64_t(0x7FFFFFFF)) return Q4_ERR_SHAPE;
-    if (M == 0 || N0 + N1 == 0) return Q4_OK;
-    if ((rc = check_ptrs_aligned({x}))) return rc;
-    if (N0 > 0 && (rc = check_ptrs_aligned({w0_qs, w0_d, y0}))) return rc;
-    if (N1 > 0 && (rc = check_ptrs_aligned({w1_qs, w1_d, y1}))) return rc;
-    return hip_status(
-        q4::launch_q4_gemv_act(w0_qs, w0_d, y0, N0, w1_qs, w1_d, y1, N1, x, x_dtype, M, K, as_stream(stream)));
+    const uint8_t* qs[2] = {w0_qs, w1_qs};
+    const uint16_t* d[2] = {w0_d, w1_d};
+    const int64_t n[2] = {N0, N1};
+    float* ys[2] = {y0, y1};
+    return gemv_common(2, qs, d, n, ys, nullptr, nullptr, x, x_dtype, M, K, stream);
+}
+
+int q4_gemv_multi(int nmat, const uint8_t* const* w_qs, const uint16_t* const* w_d, const int64_t* n,
+                  const int8_t* x_qs, const uint16_t* x_ds, float* const* y, int64_t M, int64_t K, void* stream) {
+    if (!x_qs || !x_ds) return Q4_ERR_NULL;
+    return gemv_common(nmat, w_qs, w_d, n, y, x_qs, x_ds, nullptr, Q4_BF16, M, K, stream);
+}
+
+int q4_gemv_multi_act(int nmat, const uint8_t* const* w_qs, const uint16_t* const* w_d, const int64_t* n,
+                      const void* x, int x_dtype, float* const* y, int64_t M, int64_t K, void* stream) {
+    if (!x) return Q4_ERR_NULL;
+    return gemv_common(nmat, w_qs, w_d, n, y, nullptr, nullptr, x, x_dtype, M, K, stream);
 }
 
 // ---- GEMM ----------------------------------------------------------------------------

@@ -41,23 +41,65 @@
 //    each and produce the block's code words together (q8_1_block over the
 //    lanes that agree in l & 7), with the arithmetic of the standalone
 //    quantiser, and swap the words through a per-wave LDS slot.
+#include <climits>
+#include <cstddef>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace q4 {
 
+// Up to kGemvMats matrices share one activation.  Each workgroup serves one
+// of them: matrix 0 owns workgroups 0 .. wg0[0] - 1, matrix i > 0 owns
+// wg0[i-1] .. wg0[i] - 1, each 8*RI of its rows.  Only non-empty matrices
+// are passed; the starts of absent ones are INT_MAX.
+//
+// Every dispatch's argument block is cold in the scalar cache, and a load
+// whose address depends on an earlier argument load pays that miss twice.
+// So the first 64 bytes (one cache line) hold everything a one-matrix launch
+// reads, and a several-matrix launch reads all its fields up front and picks
+// its matrix with selects, never with an index into the block.  The waves
+// per workgroup are passed, so the hidden block-size argument is not read.
+struct GemvMat {
+    const uint8_t* qs;
+    const uint16_t* d;
+    float* y;
+};
 struct GemvArgs {
-    const uint8_t* qs[2];
-    const uint16_t* d[2];
-    float* y[2];
-    int n[2];          // rows of each matrix
+    GemvMat m0;                     // matrix 0
     const int8_t* xqs;
     const uint16_t* xds;
+    const void* x;                  // raw activation (bf16 / f32) for the quantising variant
+    int nb;                         // K / 32
+    int nwp;                        // waves per workgroup
+    int n0;                         // rows of matrix 0
     int K;
-    int nb;            // K / 32
-    int total_rows;    // n[0] + n[1]
-    const void* x;     // raw activation (bf16 / f32) for the quantising variant
+    // several-matrix launches only
+    int wg0[kGemvMats - 1];         // first workgroup of matrices 1 ..
+    int nr[kGemvMats - 1];          // rows of matrices 1 ..
+    GemvMat mr[kGemvMats - 1];      // matrices 1 ..
 };
+static_assert(offsetof(GemvArgs, wg0) == 64, "one-matrix fields in the first 64 bytes");
+
+// The matrix of workgroup b (uniform across the workgroup): its pointers,
+// rows and first workgroup.
+template <int NMAT>
+__device__ __forceinline__ void mat_of(const GemvArgs& a, int b, GemvMat& m, int& rows, int& first_wg) {
+    m = a.m0;
+    rows = a.n0;
+    first_wg = 0;
+    if constexpr (NMAT > 1) {
+#pragma unroll
+        for (int t = 1; t < kGemvMats; t++) {
+            const bool sel = b >= a.wg0[t - 1];
+            m.qs = sel ? a.mr[t - 1].qs : m.qs;
+            m.d = sel ? a.mr[t - 1].d : m.d;
+            m.y = sel ? a.mr[t - 1].y : m.y;
+            rows = sel ? a.nr[t - 1] : rows;
+            first_wg = sel ? a.wg0[t - 1] : first_wg;
+        }
+    }
+}
 
 __device__ __forceinline__ int block_isum(const u32x4_t w, const int (&a)[8], int neg8sum) {
     const uint32_t lo = 0x0F0F0F0Fu;
@@ -85,8 +127,8 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
-// NMAT: 1 for q4_gemv, 2 for q4_gemv_fused2 (rows past n[0] belong to the
-// second matrix).  XIN: -1 reads Q8_1 activation planes, DT_BF16 / DT_F32 a
+// NMAT: 1 for one matrix, kGemvMats for several (q4_gemv_fused2,
+// q4_gemv_multi: each workgroup serves one matrix, found from wg0).  XIN: -1 reads Q8_1 activation planes, DT_BF16 / DT_F32 a
 // raw activation that the kernel quantises.  U columns in flight per loop
 // iteration, all loaded before any arithmetic, F virtual waves per physical
 // wave (U a multiple of F).  For
@@ -105,26 +147,26 @@ void k_q4_gemv(const GemvArgs args) {
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;
-    const int nwp = blockDim.x / kWave;         // physical waves; V = F * nwp virtual ones
+    const int nwp = args.nwp;                   // physical waves; V = F * nwp virtual ones
+    __builtin_assume(nwp >= 1 && nwp <= kMaxWaves);   // keeps column offsets non-negative
     const int bl = w * 8 + (lane & 7);          // first block column of the lane
     const int rl = lane >> 3;                   // row lane: 0..7
     const int stride = nwp * 8;
     const int nb = args.nb;
-    const int r0 = blockIdx.x * 8 * RI;
+    GemvMat mat;
+    int nrows, first_wg;
+    mat_of<NMAT>(args, (int)blockIdx.x, mat, nrows, first_wg);
+    const int r0 = ((int)blockIdx.x - first_wg) * 8 * RI;   // first row in its matrix
 
-    // Rows past the end read row 0 of the last matrix (valid memory) and are
-    // never written: every load is unconditional.
+    // Rows past the end read the last row (valid memory) and are never
+    // written: every load is unconditional.
     const u32x4_t* rqs[RI];
     const uint16_t* rd[RI];
 #pragma unroll
     for (int i = 0; i < RI; i++) {
-        const int R = r0 + rl + 8 * i;
-        const bool second = NMAT == 2 && R >= args.n[0];
-        const int rr = (R < args.total_rows) ? R - (second ? args.n[0] : 0) : 0;
-        const uint8_t* qbase = second ? args.qs[1] : args.qs[0];
-        const uint16_t* dbase = second ? args.d[1] : args.d[0];
-        rqs[i] = reinterpret_cast<const u32x4_t*>(qbase + (int64_t)rr * nb * 16);
-        rd[i] = dbase + (int64_t)rr * nb;
+        const int rr = min(r0 + rl + 8 * i, nrows - 1);
+        rqs[i] = reinterpret_cast<const u32x4_t*>(mat.qs + (int64_t)rr * nb * 16);
+        rd[i] = mat.d + (int64_t)rr * nb;
     }
 
     float acc[F][RI][M];
@@ -242,17 +284,14 @@ void k_q4_gemv(const GemvArgs args) {
             }
     __syncthreads();
     const int nv = F * nwp;
-    for (int t = threadIdx.x; t < 8 * RI * M; t += blockDim.x) {
+    for (int t = threadIdx.x; t < 8 * RI * M; t += nwp * kWave) {
         const int m = t % M;
         const int slot_i = t / M;               // i * 8 + rl
         const int R = r0 + (slot_i & 7) + 8 * (slot_i >> 3);
-        if (R >= args.total_rows) continue;
+        if (R >= nrows) continue;
         float v = red[0][t];
         for (int vw = 1; vw < nv; vw++) v += red[vw][t];
-        const bool second = NMAT == 2 && R >= args.n[0];
-        float* yp = second ? args.y[1] : args.y[0];
-        const int64_t rows = second ? args.n[1] : args.n[0];
-        yp[(int64_t)m * rows + (R - (second ? args.n[0] : 0))] = v;
+        mat.y[(int64_t)m * nrows + R] = v;
     }
 }
 
@@ -318,10 +357,21 @@ static GemvShape raw_shape(GemvShape g, int64_t rows, int64_t nb, int64_t M, boo
         return;                                                   \
     } while (0)
 
+// Workgroups of each matrix for rows_per_wg rows per workgroup, and the total.
+static int assign_workgroups(GemvArgs& a, int rows_per_wg) {
+    int wg = (a.n0 + rows_per_wg - 1) / rows_per_wg;
+    for (int k = 0; k < kGemvMats - 1; k++) {
+        a.wg0[k] = a.nr[k] == 0 ? INT_MAX : wg;
+        wg += (a.nr[k] + rows_per_wg - 1) / rows_per_wg;
+    }
+    return wg;
+}
+
 template <int M, int NMAT, int XIN>
-static void launch_mx(const GemvArgs& a, const GemvShape& g, hipStream_t s) {
-    const dim3 block(g.v / g.f * kWave);
-    const dim3 grid((a.total_rows + 8 * g.ri - 1) / (8 * g.ri));
+static void launch_mx(GemvArgs a, const GemvShape& g, hipStream_t s) {
+    a.nwp = g.v / g.f;
+    const dim3 block(a.nwp * kWave);
+    const dim3 grid((unsigned)assign_workgroups(a, 8 * g.ri));
     if constexpr (M == 1) {
         if (g.f == 2) {
             if (g.ri == 2) Q4_LAUNCH(k_q4_gemv<1, 2, NMAT, 2, 2, XIN>);
@@ -348,50 +398,69 @@ static void launch_mx(const GemvArgs& a, const GemvShape& g, hipStream_t s) {
 
 template <int M, int XIN>
 static void launch_m(const GemvArgs& a, const GemvShape& g, hipStream_t s) {
-    if (a.n[1] > 0) launch_mx<M, 2, XIN>(a, g, s);
+    if (a.nr[0] != 0) launch_mx<M, kGemvMats, XIN>(a, g, s);
     else launch_mx<M, 1, XIN>(a, g, s);
 }
 
-hipError_t launch_q4_gemv_act(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
-                              const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
-                              const void* x, int xdt, int64_t M, int64_t K, hipStream_t s) {
+// Pack the non-empty matrices of the list into the arguments.
+static void pack_mats(GemvArgs& a, int nmat, const uint8_t* const* qs, const uint16_t* const* d, const int64_t* n,
+                      float* const* y) {
+    GemvMat ms[kGemvMats];
+    int ns[kGemvMats];
+    int k = 0;
+    for (int i = 0; i < nmat; i++) {
+        if (n[i] <= 0) continue;
+        ms[k] = GemvMat{qs[i], d[i], y[i]};
+        ns[k] = (int)n[i];
+        k++;
+    }
+    for (; k < kGemvMats; k++) {
+        ms[k] = GemvMat{nullptr, nullptr, nullptr};
+        ns[k] = 0;
+    }
+    a.m0 = ms[0];
+    a.n0 = ns[0];
+    for (k = 1; k < kGemvMats; k++) {
+        a.mr[k - 1] = ms[k];
+        a.nr[k - 1] = ns[k];
+    }
+}
+
+hipError_t launch_q4_gemv_multi(int nmat, const uint8_t* const* qs, const uint16_t* const* d, const int64_t* n,
+                                float* const* y, const int8_t* x_qs, const uint16_t* x_ds, const void* x, int xdt,
+                                int64_t M, int64_t K, hipStream_t s) {
+    if (nmat < 1 || nmat > kGemvMats) return hipErrorInvalidValue;
     GemvArgs a;
-    a.qs[0] = w0_qs; a.d[0] = w0_d; a.y[0] = y0; a.n[0] = (int)N0;
-    a.qs[1] = w1_qs ? w1_qs : w0_qs; a.d[1] = w1_d ? w1_d : w0_d; a.y[1] = y1 ? y1 : y0; a.n[1] = (int)N1;
-    a.xqs = nullptr; a.xds = nullptr; a.x = x;
+    pack_mats(a, nmat, qs, d, n, y);
+    int64_t total_rows = a.n0;
+    for (int k = 0; k < kGemvMats - 1; k++) total_rows += a.nr[k];
+    if (total_rows == 0) return hipSuccess;
+    a.xqs = x_qs; a.xds = x_ds; a.x = x;
     a.K = (int)K; a.nb = (int)(K / 32);
-    a.total_rows = (int)(N0 + N1);
-    const GemvShape g = raw_shape(pick_shape(N0 + N1, K / 32, M), N0 + N1, K / 32, M, N1 > 0);
-    switch (M) {
+    const bool several = a.nr[0] != 0;
+    if (x == nullptr) {
+        const GemvShape g = pick_shape(total_rows, K / 32, M);
+        switch (M) {
+#define Q4_GEMV_CASE(m) case m: launch_m<m, -1>(a, g, s); break;
+            Q4_GEMV_CASE(1) Q4_GEMV_CASE(2) Q4_GEMV_CASE(3) Q4_GEMV_CASE(4)
+            Q4_GEMV_CASE(5) Q4_GEMV_CASE(6) Q4_GEMV_CASE(7) Q4_GEMV_CASE(8)
+            Q4_GEMV_CASE(9) Q4_GEMV_CASE(10) Q4_GEMV_CASE(11) Q4_GEMV_CASE(12)
+            Q4_GEMV_CASE(13) Q4_GEMV_CASE(14) Q4_GEMV_CASE(15) Q4_GEMV_CASE(16)
+#undef Q4_GEMV_CASE
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        const GemvShape g = raw_shape(pick_shape(total_rows, K / 32, M), total_rows, K / 32, M, several);
+        switch (M) {
 #define Q4_GEMV_ACT_CASE(m)                                                  \
     case m:                                                                  \
         if (xdt == DT_F32) launch_m<m, DT_F32>(a, g, s);                     \
         else launch_m<m, DT_BF16>(a, g, s);                                  \
         break;
-        Q4_GEMV_ACT_CASE(1) Q4_GEMV_ACT_CASE(2) Q4_GEMV_ACT_CASE(3) Q4_GEMV_ACT_CASE(4)
+            Q4_GEMV_ACT_CASE(1) Q4_GEMV_ACT_CASE(2) Q4_GEMV_ACT_CASE(3) Q4_GEMV_ACT_CASE(4)
 #undef Q4_GEMV_ACT_CASE
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
-                          const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
-                          const int8_t* x_qs, const uint16_t* x_ds, int64_t M, int64_t K, hipStream_t s) {
-    GemvArgs a;
-    a.qs[0] = w0_qs; a.d[0] = w0_d; a.y[0] = y0; a.n[0] = (int)N0;
-    a.qs[1] = w1_qs ? w1_qs : w0_qs; a.d[1] = w1_d ? w1_d : w0_d; a.y[1] = y1 ? y1 : y0; a.n[1] = (int)N1;
-    a.xqs = x_qs; a.xds = x_ds; a.x = nullptr; a.K = (int)K; a.nb = (int)(K / 32);
-    a.total_rows = (int)(N0 + N1);
-    const GemvShape g = pick_shape(N0 + N1, K / 32, M);
-    switch (M) {
-#define Q4_GEMV_CASE(m) case m: launch_m<m, -1>(a, g, s); break;
-        Q4_GEMV_CASE(1) Q4_GEMV_CASE(2) Q4_GEMV_CASE(3) Q4_GEMV_CASE(4)
-        Q4_GEMV_CASE(5) Q4_GEMV_CASE(6) Q4_GEMV_CASE(7) Q4_GEMV_CASE(8)
-        Q4_GEMV_CASE(9) Q4_GEMV_CASE(10) Q4_GEMV_CASE(11) Q4_GEMV_CASE(12)
-        Q4_GEMV_CASE(13) Q4_GEMV_CASE(14) Q4_GEMV_CASE(15) Q4_GEMV_CASE(16)
-#undef Q4_GEMV_CASE
-        default: return hipErrorInvalidValue;
+            default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }

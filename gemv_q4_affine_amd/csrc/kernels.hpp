@@ -25,16 +25,14 @@ hipError_t launch_q4_dequantize(const uint8_t* qs, const uint16_t* d, int64_t N,
 hipError_t launch_affine4_dequantize(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, int64_t G,
                                      int64_t N, int64_t K, void* out, int odt, hipStream_t s);
 
-// Decode GEMV over one or two weight matrices sharing a Q8_1 activation.
-hipError_t launch_q4_gemv(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
-                          const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
-                          const int8_t* x_qs, const uint16_t* x_ds, int64_t M, int64_t K, hipStream_t s);
-
-// The same GEMV on a raw bf16 / f32 activation, quantised to Q8_1 inside the
-// kernel (bit-identical to launch_q8_1_quantize + launch_q4_gemv); M <= 4.
-hipError_t launch_q4_gemv_act(const uint8_t* w0_qs, const uint16_t* w0_d, float* y0, int64_t N0,
-                              const uint8_t* w1_qs, const uint16_t* w1_d, float* y1, int64_t N1,
-                              const void* x, int xdt, int64_t M, int64_t K, hipStream_t s);
+// Decode GEMV over 1..kGemvMats weight matrices sharing one activation: the
+// Q8_1 planes (x == nullptr), or a raw bf16 / f32 activation x quantised to
+// Q8_1 inside the kernel (the same bits; M <= 4).  Host arrays of nmat
+// entries; matrices with n == 0 are skipped.
+constexpr int kGemvMats = 4;
+hipError_t launch_q4_gemv_multi(int nmat, const uint8_t* const* qs, const uint16_t* const* d, const int64_t* n,
+                                float* const* y, const int8_t* x_qs, const uint16_t* x_ds, const void* x, int xdt,
+                                int64_t M, int64_t K, hipStream_t s);
 
 // GEMM paths.  fmt: 0 = Q4_0 planes (a = qs, b = d), 1 = affine (a = q,
 // b = scales, c = biases), 2 = dense binary16 W (a = w).

@@ -221,6 +221,29 @@ int q4_gemv_fused2_act(const uint8_t* w0_qs, const uint16_t* w0_d, int64_t N0,
                        const void* x, int x_dtype,
                        float* y0, float* y1, int64_t M, int64_t K, void* stream);
 
+/*
+ * q4_gemv_multi / q4_gemv_multi_act -- up to Q4_GEMV_MAX_MATS matrices (q, k
+ * and v; gate and up; or any set) that share one activation, in one launch
+ * that reads the activation once: the fused MMVQ kernel of the repro page
+ * (Important source touch points) taken from two matrices to several.
+ * Results are bit-identical to one q4_gemv (q4_gemv_act) call per matrix.
+ *   nmat        : 1 .. Q4_GEMV_MAX_MATS (else Q4_ERR_ARG)
+ *   w_qs, w_d, y: host arrays of nmat device pointers; n: host array of the
+ *                 nmat row counts (a matrix with n[i] == 0 is skipped, and its
+ *                 pointers may be NULL)
+ *   y[i]        : device out, float [M][n[i]]
+ * The activation and M limits are those of q4_gemv (Q8_1 planes) and
+ * q4_gemv_act (raw activation); the rows of all matrices together must fit
+ * in 2^31 - 1.
+ */
+#define Q4_GEMV_MAX_MATS 4
+int q4_gemv_multi(int nmat, const uint8_t* const* w_qs, const uint16_t* const* w_d, const int64_t* n,
+                  const int8_t* x_qs, const uint16_t* x_ds, float* const* y,
+                  int64_t M, int64_t K, void* stream);
+int q4_gemv_multi_act(int nmat, const uint8_t* const* w_qs, const uint16_t* const* w_d, const int64_t* n,
+                      const void* x, int x_dtype, float* const* y,
+                      int64_t M, int64_t K, void* stream);
+
 /* ======================================================================== */
 /* GEMM (any M): bf16 / f32 activations                                      */
 /* ======================================================================== */

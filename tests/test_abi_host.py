@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 24, names
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in q4.h but not exported"
@@ -144,6 +144,29 @@ def test_gemm_validation():
     d = lib().dense_gemm
     assert d(P, B.Q4_BF16, P, P, B.Q4_BF16, 4, 8, 48, None) == B.Q4_ERR_SHAPE
     assert d(P, B.Q4_BF16, None, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_NULL
+
+
+def test_gemv_multi_validation():
+    import ctypes
+    arr = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    rows = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    m = lib().q4_gemv_multi
+    a = lib().q4_gemv_multi_act
+    three = (arr(P, P, P), arr(P, P, P), rows(8, 8, 8), arr(P, P, P))
+    assert m(0, *three[:3], P, P, three[3], 1, 64, None) == B.Q4_ERR_ARG
+    assert m(5, *three[:3], P, P, three[3], 1, 64, None) == B.Q4_ERR_ARG
+    assert m(3, None, three[1], three[2], P, P, three[3], 1, 64, None) == B.Q4_ERR_NULL
+    assert m(3, *three[:3], None, P, three[3], 1, 64, None) == B.Q4_ERR_NULL
+    assert m(3, *three[:3], P, P, three[3], 17, 64, None) == B.Q4_ERR_SHAPE
+    assert m(3, three[0], three[1], rows(8, -1, 8), P, P, three[3], 1, 64, None) == B.Q4_ERR_SHAPE
+    assert m(3, arr(P, None, P), three[1], three[2], P, P, three[3], 1, 64, None) == B.Q4_ERR_NULL
+    # an empty matrix may have NULL pointers
+    assert m(3, arr(P, None, P), arr(P, None, P), rows(0, 0, 0), P, P, arr(P, None, P), 1, 64, None) == B.Q4_OK
+    assert a(3, *three[:3], P, B.Q4_F16, three[3], 1, 64, None) == B.Q4_ERR_DTYPE
+    assert a(3, *three[:3], P, B.Q4_BF16, three[3], 5, 64, None) == B.Q4_ERR_SHAPE
+    assert a(3, *three[:3], None, B.Q4_BF16, three[3], 1, 64, None) == B.Q4_ERR_NULL
+    assert a(3, *three[:3], MIS, B.Q4_BF16, three[3], 1, 64, None) == B.Q4_ERR_ALIGN
+    assert a(3, *three[:3], P, B.Q4_BF16, three[3], 0, 64, None) == B.Q4_OK
 
 
 def test_weight_image_validation_and_sizes():

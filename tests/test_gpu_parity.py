@@ -312,6 +312,28 @@ def test_gemv_fused2_act_bit_identical(M, N0, N1, K):
     assert e0.shape == (M, 0) and torch.equal(e1, z1)
 
 
+@pytest.mark.parametrize("M,rows,K", [(1, (12288, 12288, 12288), 4096), (1, (2048, 512, 512), 2048),
+                                      (2, (300, 0, 17, 1000), 4128), (4, (64, 8, 1, 520), 96)])
+def test_gemv_multi_bit_identical(M, rows, K):
+    """Several matrices in one launch give the bits of one launch per matrix,
+    on Q8_1 planes and on the raw activation."""
+    say(f"gemv_multi M={M} rows={rows} K={K}")
+    rng = np.random.default_rng(sum(rows) + K)
+    mats = [tuple(dev(a) for a in oracle.q4_0_quantize(synth.weights(rng, max(n, 1), K)))
+            for n in rows]
+    mats = [(q[:n], d[:n]) for (q, d), n in zip(mats, rows)]
+    x = bf16_dev(synth.activations(rng, M, K))
+    xq, xd = B.q8_1_quantize_act(x)
+    ys = B.q4_gemv_multi(mats, xq, xd)
+    ya = B.q4_gemv_multi_act(mats, x)
+    for (q, d), y, y2 in zip(mats, ys, ya):
+        if d.shape[0] == 0:
+            assert y.shape == (M, 0)
+            continue
+        want = B.q4_gemv(q, d, xq, xd)
+        assert torch.equal(y, want) and torch.equal(y2, want)
+
+
 def test_gemv_deterministic_and_row_permutation():
     wqs, wd, xqs, xds = _gemv_case(2, 3000, 4096, seed=77)
     t = [dev(a) for a in (wqs, wd, xqs, xds)]
