@@ -47,12 +47,12 @@ F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
 
 
 # HBM bytes per launch of the roofline kernel (q4_gemv_fused2_act at the
-# decode shape, k_q4_gemv<1,2,2,2,2,bf16>), from the rocprofv3 FETCH_SIZE /
+# decode shape, k_q4_gemv<1,2,4,2,2,bf16>), from the rocprofv3 FETCH_SIZE /
 # WRITE_SIZE passes summarised in profiles/q4_gemv_n12288_k4096_hbm_traffic.md.
 # They hold only for the sources they were taken on: with any other source the
 # figure is reported as null until the counters are taken again.
 MEASURED_TRAFFIC = {"sources": ["gemv_q4_affine_amd/csrc/gemv.hip", "gemv_q4_affine_amd/csrc/device_common.hpp"],
-                    "sha256_prefix": "30a19ea5ee90e418", "bytes_per_launch": 56858282}
+                    "sha256_prefix": "8dd04f621edf0401", "bytes_per_launch": 56861607}
 
 
 def sources_hash(paths):
@@ -555,7 +555,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "q4_gemv_fused2_act (k_q4_gemv<1,2,2,2,2,bf16>), the step's longest kernel",
+            "kernel": "q4_gemv_fused2_act (k_q4_gemv<1,2,4,2,2,bf16>), the step's longest kernel",
             "achieved": round(g["gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
