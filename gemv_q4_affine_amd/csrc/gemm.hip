@@ -1385,6 +1385,416 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemm_skinny(const GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Small-M kernel (2 <= M <= 32, bf16 X, Q4_0 or affine): X is used as it is
+// and the weights are never rounded.
+//
+// The bf16 MFMA 16x16x32 takes bf16 X directly and each weight as the exact
+// bf16 value 128 + q (the nibble ANDed into the mantissa of 128.0, whose unit
+// is 1).  One MFMA covers exactly one 32-weight block of 16 columns, so its
+// result is per block and is scaled afterwards in fp32:
+//   Q4_0:    y += d * (sum x (128 + q) - 136 sum x)            = d * sum x (q - 8)
+//   affine:  y += s * (sum x (128 + q) - 128 sum x) + b * sum x  per group of 64
+// The -136 sum x (-128 sum x) term is the MFMA's accumulator input: itself an
+// MFMA of X against a constant operand, so it arrives in the output layout
+// and serves every column tile.  Products are exact and sums fp32, so the
+// result differs from the exact one by fp32 accumulation and the output
+// rounding only.
+//
+// Lane l = 16 g + j.  The MFMA's B operand takes from lane (j, g) eight
+// weights of column j, all from one block.  Dword g of a block holds eight of
+// its weights (Q4_0: elements 4g..4g+3 and 16+4g..16+4g+3; affine: 8g..8g+7).
+// The loads are coalesced instead: lane 4j + i loads block 4c + i of column j
+// (one 128-bit load; four neighbouring lanes read a column's 64 contiguous
+// bytes).  A 4 x 4 DPP transpose inside each lane quad then gives lane 4j + i
+// dword i of each of the chunk's four blocks, and one ds_bpermute per dword
+// moves it to lane 16 i + j.  A dword's nibbles pair up as (byte 0, byte 2)
+// and (byte 1, byte 3); the X fragment is permuted into the same order.  The
+// block scales, loaded the same way, reach every lane of their column by
+// ds_bpermute.
+//
+// Workgroup: 8 waves on the same NT*16 columns.  K runs in slices of 32
+// blocks; in each slice wave w takes blocks 4w..4w+3 (one chunk).  X is the
+// costly operand here -- every workgroup needs all of it, and fragment loads
+// straight from memory would cost more vector-memory instructions than the
+// weights -- so the workgroup copies each X slice into LDS once, with 16-byte
+// loads, double-buffered: slice s+1 (and the weights of the wave's next
+// chunk) is in flight while slice s is multiplied, and one barrier per slice
+// hands the buffers over.  The partial tiles meet in LDS at the end and are
+// summed in wave order, so results are deterministic.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr int kSmWaves = 8;
+constexpr int kSmMaxM = 32;
+
+// On entry lane row g (lanes 16g..16g+15) holds item g's dwords in r[0..3];
+// on exit it holds dword g of item t in r[t].
+__device__ __forceinline__ void row_transpose4(uint32_t (&r)[4]) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+    const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    r[0] = s01[0];
+    r[1] = s01[1];
+    r[2] = s23[0];
+    r[3] = s23[1];
+}
+
+// 4 x 4 transpose of dwords inside each quad of lanes: on entry lane 4q + i
+// holds item i's dwords in r[0..3]; on exit it holds dword i of item t in
+// r[t].  Two rounds of DPP exchanges, across lane ^ 1 and lane ^ 2.
+__device__ __forceinline__ void quad_transpose4(uint32_t (&r)[4], bool odd, bool hi2) {
+    auto x1 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); };
+    auto x2 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); };
+    const uint32_t t0 = x1(r[0]), t1 = x1(r[1]), t2 = x1(r[2]), t3 = x1(r[3]);
+    const uint32_t a0 = odd ? t1 : r[0];
+    const uint32_t a1 = odd ? r[1] : t0;
+    const uint32_t a2 = odd ? t3 : r[2];
+    const uint32_t a3 = odd ? r[3] : t2;
+    const uint32_t u0 = x2(a0), u1 = x2(a1), u2 = x2(a2), u3 = x2(a3);
+    r[0] = hi2 ? u2 : a0;
+    r[1] = hi2 ? u3 : a1;
+    r[2] = hi2 ? a2 : u0;
+    r[3] = hi2 ? a3 : u1;
+}
+
+// Eight weights of dword w as bf16 128 + q, in the pair order (byte 0,
+// byte 2), (byte 1, byte 3) of the low nibbles, then of the high nibbles.
+__device__ __forceinline__ bf16x8_t sm_weights(uint32_t w, uint32_t mask) {
+    const uint32_t magic = 0x43004300u;    // bf16 (128, 128)
+    u32x4_t b;
+    b[0] = (w & mask) | magic;
+    b[1] = ((w >> 8) & mask) | magic;
+    b[2] = ((w >> 4) & mask) | magic;
+    b[3] = ((w >> 12) & mask) | magic;
+    return __builtin_bit_cast(bf16x8_t, b);
+}
+
+// X fragment for the weight order above.  Q4_0: lo = x[4g..4g+3],
+// hi = x[16+4g..16+4g+3] of the block; affine: x[8g..8g+7].
+template <int WF>
+struct SmX;
+template <> struct SmX<WF_Q4_0> { u32x2_t lo, hi; };
+template <> struct SmX<WF_AFFINE4> { u32x4_t v; };
+
+template <int WF>
+__device__ __forceinline__ bf16x8_t sm_xfrag(const SmX<WF>& x) {
+    u32x4_t r;
+    if constexpr (WF == WF_Q4_0) {
+        // bytes: (0,2) pairs elements (4g, 4g+2), (1,3) pairs (4g+1, 4g+3)
+        r[0] = __builtin_amdgcn_perm(x.lo[1], x.lo[0], 0x05040100u);
+        r[1] = __builtin_amdgcn_perm(x.lo[1], x.lo[0], 0x07060302u);
+        r[2] = __builtin_amdgcn_perm(x.hi[1], x.hi[0], 0x05040100u);
+        r[3] = __builtin_amdgcn_perm(x.hi[1], x.hi[0], 0x07060302u);
+    } else {
+        // byte i of a dword holds elements 2i (low) and 2i+1 (high): the
+        // pairs are (0,4), (2,6), (1,5), (3,7)
+        r[0] = __builtin_amdgcn_perm(x.v[2], x.v[0], 0x05040100u);
+        r[1] = __builtin_amdgcn_perm(x.v[3], x.v[1], 0x05040100u);
+        r[2] = __builtin_amdgcn_perm(x.v[2], x.v[0], 0x07060302u);
+        r[3] = __builtin_amdgcn_perm(x.v[3], x.v[1], 0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+template <int WF, int MT, int NT, int YDT, int XP, bool ONE>
+__global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs a) {
+    static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
+    constexpr int kThreads = 64 * kSmWaves;
+    constexpr int kRows = MT * 16;
+    constexpr int kSliceBlk = 4 * kSmWaves;               // blocks per K slice
+    constexpr int kRowH = kSliceBlk * 32 + 8;             // LDS row of a slice, bf16 (16 B pad)
+    constexpr int kBufH = kRows * kRowH;                  // one slice buffer, bf16
+    constexpr int kUnitsRow = kSliceBlk * 4;              // 16-byte units per row of a slice
+    static_assert(XP * kThreads / kUnitsRow <= kRows, "X rows copied fit the slice buffer");
+    constexpr int kTile = MT * NT * 4 * 64;               // partial values per wave
+    constexpr int kXBytes = 2 * kBufH * 2;
+    constexpr int kRedBytes = kSmWaves * kTile * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kXBytes > kRedBytes ? kXBytes : kRedBytes];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);     // [2][kRows][kRowH]
+    float* red = reinterpret_cast<float*>(smem);          // [kSmWaves][kTile], after the last slice
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int n0 = blockIdx.x * (NT * 16);
+    const int nb = a.K / 32;
+    const int nchunks = (nb + 3) / 4;
+    const int nslices = (nb + kSliceBlk - 1) / kSliceBlk;
+    const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
+
+    // columns this lane loads (lane 4j' + i: column j' of each tile), clamped:
+    // a column past N is computed, never stored
+    int nld[NT];
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) {
+        const int n = n0 + ni * 16 + (lane >> 2);
+        nld[ni] = n < a.N ? n : a.N - 1;
+    }
+    // LDS rows of the A fragments, clamped (rows past M are computed, never stored)
+    int xrow[MT];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) {
+        const int m = mi * 16 + j;
+        xrow[mi] = (m < a.M ? m : a.M - 1) * kRowH;
+    }
+
+    // ---- X slices: global -> registers -> LDS ----
+    // XP passes of 16-byte units cover rows 0 .. 4 XP - 1 (>= M); rows past
+    // M re-read row M-1, and a unit past K reads another unit of its row
+    // (slices past the end re-read the last one), so every load is valid,
+    // unconditional and spread over lines; a unit past K is stored as zeros,
+    // so blocks past K (and whole slices past the end) contribute nothing
+    // whatever their scale.  The steps hold no branch and no select next to a load: either
+    // makes the compiler wait for every load in flight, which would drain
+    // the weight ring below.
+    u32x4_t xr[MT == 1 ? 2 : 1][XP];      // register sets (two: slice sl lives in set sl & 1)
+    auto x_load = [&](int sl, u32x4_t (&r)[XP]) {
+        const int slc = sl < nslices ? sl : nslices - 1;     // past the end: a real slice, stored as zeros
+#pragma unroll
+        for (int i = 0; i < XP; i++) {
+            const int u = tid + i * kThreads;
+            const int row = u / kUnitsRow, cu = u % kUnitsRow;
+            const int k = slc * kSliceBlk * 32 + cu * 8;
+            r[i] = *reinterpret_cast<const u32x4_t*>(xg + (int64_t)(row < a.M ? row : a.M - 1) * a.K +
+                                                     (k < a.K ? k : k % a.K));
+        }
+    };
+    auto x_store = [&](int sl, const u32x4_t (&r)[XP]) {
+        uint16_t* buf = xs + (sl & 1) * kBufH;
+#pragma unroll
+        for (int i = 0; i < XP; i++) {
+            const int u = tid + i * kThreads;
+            const int row = u / kUnitsRow, cu = u % kUnitsRow;
+            const int k = sl * kSliceBlk * 32 + cu * 8;
+            const u32x4_t v = k < a.K ? r[i] : u32x4_t{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4_t*>(buf + row * kRowH + cu * 8) = v;
+        }
+    };
+
+    // ---- weights of one chunk: block 4c + g of each column, and its scale ----
+    struct Stage {
+        u32x4_t w[NT];
+        uint16_t s0[NT];      // Q4_0 d; affine s of its group
+        uint16_t s1[NT];      // affine b of its group
+    };
+    // Lane 4j' + i: block 4c + i of column j' of each tile.
+    auto w_load = [&](int c, Stage& st) {
+        const int kb = 4 * c + (lane & 3);
+        const int kbc = kb < nb ? kb : nb - 1;    // past K: any valid block (its X is zero)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) {
+            const int64_t n = nld[ni];
+            if constexpr (WF == WF_Q4_0) {
+                st.w[ni] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                    reinterpret_cast<const uint8_t*>(a.a) + (n * nb + kbc) * 16));
+                st.s0[ni] = reinterpret_cast<const uint16_t*>(a.b)[n * nb + kbc];
+            } else {
+                st.w[ni] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                    reinterpret_cast<const uint8_t*>(a.a) + n * (a.K / 2) + (int64_t)kbc * 16));
+                const int64_t gi = n * (a.K / 64) + (kbc >> 1);
+                st.s0[ni] = reinterpret_cast<const uint16_t*>(a.b)[gi];
+                st.s1[ni] = reinterpret_cast<const uint16_t*>(a.c)[gi];
+            }
+        }
+    };
+
+    floatx4_t acc[MT][NT];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) acc[mi][ni] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    uint32_t mask = 0x000F000Fu;
+    asm volatile("" : "+v"(mask));           // a VGPR operand: one v_and_or_b32 per pair
+    const floatx4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    // ds_bpermute byte addresses: lane 16g + j takes its weights from lane
+    // 4j + g and the scale of block t from lane 4j + t
+    const int bp_w = (4 * j + g) * 4;
+    const int bp_s = 4 * j * 4;
+
+    // X fragment of block t of this wave's chunk in slice sl, rows mi*16 + j
+    // (clamped); a block past K reads zeros
+    auto x_frag = [&](int sl, int t, int mi) {
+        const uint16_t* p = xs + (sl & 1) * kBufH + xrow[mi] + (4 * wave + t) * 32;
+        SmX<WF> x;
+        if constexpr (WF == WF_Q4_0) {
+            x.lo = *reinterpret_cast<const u32x2_t*>(p + 4 * g);
+            x.hi = *reinterpret_cast<const u32x2_t*>(p + 16 + 4 * g);
+        } else {
+            x.v = *reinterpret_cast<const u32x4_t*>(p + 8 * g);
+        }
+        return sm_xfrag<WF>(x);
+    };
+
+    auto compute = [&](int sl, const Stage& st) {
+        uint32_t wt[NT][4], sct[NT][4];
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++) {
+            uint32_t q4[4] = {st.w[ni][0], st.w[ni][1], st.w[ni][2], st.w[ni][3]};
+            quad_transpose4(q4, (lane & 1) != 0, (lane & 2) != 0);
+            const uint32_t sc = WF == WF_Q4_0 ? (uint32_t)st.s0[ni] : ((uint32_t)st.s0[ni] | ((uint32_t)st.s1[ni] << 16));
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                wt[ni][t] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_w, (int)q4[t]);
+                sct[ni][t] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_s + 4 * t, (int)sc);
+            }
+        }
+        if constexpr (WF == WF_Q4_0) {
+            const bf16x8_t neg136 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                bf16x8_t xa[MT];
+                floatx4_t c0[MT];
+#pragma unroll
+                for (int mi = 0; mi < MT; mi++) {
+                    xa[mi] = x_frag(sl, t, mi);
+                    c0[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mi], neg136, zero4, 0, 0, 0);
+                }
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++) {
+                    const bf16x8_t wb = sm_weights(wt[ni][t], mask);
+                    const float d = f16_to_f32(sct[ni][t]);      // the low half
+#pragma unroll
+                    for (int mi = 0; mi < MT; mi++) {
+                        const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mi], wb, c0[mi], 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; v++) acc[mi][ni][v] = __builtin_fmaf(d, dv[v], acc[mi][ni][v]);
+                    }
+                }
+            }
+        } else {
+            const bf16x8_t neg128 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u});
+#pragma unroll
+            for (int h = 0; h < 2; h++) {          // the chunk's two groups of 64
+                bf16x8_t xa0[MT], xa1[MT];
+                floatx4_t cs[MT];                  // -128 * (sum of x over the group)
+#pragma unroll
+                for (int mi = 0; mi < MT; mi++) {
+                    xa0[mi] = x_frag(sl, 2 * h, mi);
+                    xa1[mi] = x_frag(sl, 2 * h + 1, mi);
+                    cs[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        xa1[mi], neg128, __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0[mi], neg128, zero4, 0, 0, 0), 0, 0, 0);
+                }
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++) {
+                    const bf16x8_t w0 = sm_weights(wt[ni][2 * h], mask);
+                    const bf16x8_t w1 = sm_weights(wt[ni][2 * h + 1], mask);
+                    const uint32_t sb = sct[ni][2 * h];
+                    const float sv = bf16_to_f32(sb & 0xFFFFu);
+                    const float bq = bf16_to_f32(sb >> 16) * -0.0078125f;   // b / -128 (exact)
+#pragma unroll
+                    for (int mi = 0; mi < MT; mi++) {
+                        const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            xa1[mi], w1, __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0[mi], w0, cs[mi], 0, 0, 0), 0, 0, 0);
+#pragma unroll
+                        for (int v = 0; v < 4; v++) {
+                            acc[mi][ni][v] = __builtin_fmaf(sv, dv[v], acc[mi][ni][v]);
+                            acc[mi][ni][v] = __builtin_fmaf(bq, cs[mi][v], acc[mi][ni][v]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // Slice sl: this wave's chunk is 8 sl + wave.  The weights run kRing
+    // slices ahead in a ring of register stages with fixed roles.  X runs
+    // two slices ahead: with two register sets (one 16-row tile), step sl
+    // loads slice sl+2 into the set that held slice sl, multiplies slice sl
+    // from LDS and then stores slice sl+1 (loaded a step earlier) into the
+    // other LDS buffer; with one set (two tiles, where registers are short)
+    // it stores slice sl+1 first and then loads slice sl+2 into the same
+    // set.  The slice count is padded to a multiple of kRing; chunks and
+    // slices past the end load clamped (valid) weights and multiply zero X.
+    // ONE: the slices fit one ring (K <= 4096 here), so there is no loop and
+    // the ring is deeper.
+    constexpr int kRing = ONE ? 4 : 2;
+    constexpr bool kTwoSets = MT == 1;
+    const int nsteps = (nslices + kRing - 1) / kRing * kRing;
+    auto chunk_of = [&](int sl) {
+        const int c = sl * kSmWaves + wave;
+        return c < nchunks ? c : nchunks - 1;
+    };
+    Stage ring[kRing];
+    // Each phase is fenced so that the scheduler moves no work on loaded
+    // values (and so no wait) across phases.  In the last ring of steps
+    // nothing is refilled, and slices that no step reads are neither loaded
+    // nor stored.
+    auto step = [&](int sl, auto last, auto r) {
+        constexpr bool kLast = decltype(last)::value;
+        constexpr int kR = decltype(r)::value;
+        constexpr bool kLoadX = !kLast || kR < kRing - 2;
+        constexpr bool kStoreX = !kLast || kR < kRing - 1;
+        Stage& cur = ring[kR];
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kTwoSets) {
+            if constexpr (kLoadX) x_load(sl + 2, xr[kR & 1]);
+        } else {
+            if constexpr (kStoreX) x_store(sl + 1, xr[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kLoadX) x_load(sl + 2, xr[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sl, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!kLast) w_load(chunk_of(sl + kRing), cur);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kTwoSets && kStoreX) x_store(sl + 1, xr[(kR + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+    auto group = [&](int sl0, auto last) {
+        step(sl0 + 0, last, std::integral_constant<int, 0>{});
+        step(sl0 + 1, last, std::integral_constant<int, 1>{});
+        if constexpr (kRing == 4) {
+            step(sl0 + 2, last, std::integral_constant<int, 2>{});
+            step(sl0 + 3, last, std::integral_constant<int, 3>{});
+        }
+    };
+    x_load(0, xr[0]);
+    if constexpr (kTwoSets) x_load(1, xr[1]);
+#pragma unroll
+    for (int r = 0; r < kRing; r++) w_load(chunk_of(r), ring[r]);
+    x_store(0, xr[0]);
+    if constexpr (!kTwoSets) x_load(1, xr[0]);
+    __syncthreads();
+    if constexpr (ONE) {
+        group(0, std::true_type{});
+    } else {
+        // the first ring is peeled: straight from the prologue its wait
+        // counts would otherwise be merged with the loop's
+        group(0, std::false_type{});
+        for (int sl = kRing; sl < nsteps - kRing; sl += kRing) group(sl, std::false_type{});
+        group(nsteps - kRing, std::true_type{});
+    }
+
+    // partial tiles to LDS (the X buffers are free after the last barrier);
+    // then every thread sums some outputs over the waves in order (lane holds
+    // column j, rows 4g + v of each 16x16 tile)
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++)
+#pragma unroll
+        for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+            for (int v = 0; v < 4; v++) red[wave * kTile + ((mi * NT + ni) * 4 + v) * 64 + lane] = acc[mi][ni][v];
+    __syncthreads();
+    for (int i = tid; i < kTile; i += kThreads) {
+        float t = red[i];
+#pragma unroll
+        for (int w = 1; w < kSmWaves; w++) t += red[w * kTile + i];
+        const int l = i & 63;
+        const int v = (i >> 6) & 3;
+        const int tile = i >> 8;                  // mi * NT + ni
+        const int mi = tile / NT, ni = tile % NT;
+        const int r = mi * 16 + 4 * (l >> 4) + v;
+        const int n = n0 + ni * 16 + (l & 15);
+        if (r < a.M && n < a.N) store_y(a.y, YDT, (int64_t)r * a.N + n, t);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 template <int WF, int MT, int NT, int XDT, int YDT>
@@ -1757,6 +2167,39 @@ static void launch_vec_w(const GemmArgs& ga, int xdt, int ydt, hipStream_t s) {
     }
 }
 
+template <int WF, int MT, int NT, int YDT, int XP>
+static void launch_small_t(GemmArgs ga, hipStream_t s) {
+    const dim3 grid((unsigned)((ga.N + NT * 16 - 1) / (NT * 16))), block(64 * kSmWaves);
+    const int nslices = (ga.K / 32 + 4 * kSmWaves - 1) / (4 * kSmWaves);
+    if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, true>), grid, block, 0, s, ga);
+    else hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, false>), grid, block, 0, s, ga);
+}
+
+// The widest column group (NT tiles of 16) that still gives every CU a
+// workgroup; NT = 1 when none does.
+template <int WF, int MT, int YDT, int XP>
+static void launch_small_n(GemmArgs ga, hipStream_t s) {
+    const int64_t cus = current_cu_count();
+    if ((ga.N + 47) / 48 >= cus) launch_small_t<WF, MT, 3, YDT, XP>(ga, s);
+    else if ((ga.N + 31) / 32 >= cus) launch_small_t<WF, MT, 2, YDT, XP>(ga, s);
+    else launch_small_t<WF, MT, 1, YDT, XP>(ga, s);
+}
+
+// Rows: one 16-row tile up to M = 16, two up to 32; X copy passes of 4 rows.
+template <int WF, int YDT>
+static void launch_small_m(GemmArgs ga, hipStream_t s) {
+    if (ga.M <= 4) launch_small_n<WF, 1, YDT, 1>(ga, s);
+    else if (ga.M <= 8) launch_small_n<WF, 1, YDT, 2>(ga, s);
+    else if (ga.M <= 16) launch_small_n<WF, 1, YDT, 4>(ga, s);
+    else launch_small_n<WF, 2, YDT, 8>(ga, s);
+}
+
+template <int WF>
+static void launch_small_w(GemmArgs ga, int ydt, hipStream_t s) {
+    if (ydt == DT_BF16) launch_small_m<WF, DT_BF16>(ga, s);
+    else launch_small_m<WF, DT_F32>(ga, s);
+}
+
 constexpr int kVecMaxM = 1;   // the skinny path's vector kernel serves M == 1 (MFMA beyond)
 
 hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
@@ -1765,8 +2208,11 @@ hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void
     GemmArgs ga{};
     ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
     ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
+    const bool small = xdt == DT_BF16 && M > kVecMaxM && M <= kSmMaxM;
     if (M <= kVecMaxM && wfmt == WF_Q4_0) launch_vec_w<WF_Q4_0>(ga, xdt, ydt, s);
     else if (M <= kVecMaxM && wfmt == WF_AFFINE4) launch_vec_w<WF_AFFINE4>(ga, xdt, ydt, s);
+    else if (small && wfmt == WF_Q4_0) launch_small_w<WF_Q4_0>(ga, ydt, s);
+    else if (small && wfmt == WF_AFFINE4) launch_small_w<WF_AFFINE4>(ga, ydt, s);
     else if (wfmt == WF_Q4_0) launch_skinny_w<WF_Q4_0>(ga, xdt, ydt, s);
     else if (wfmt == WF_AFFINE4) launch_skinny_w<WF_AFFINE4>(ga, xdt, ydt, s);
     else launch_skinny_w<WF_DENSE16>(ga, xdt, ydt, s);
