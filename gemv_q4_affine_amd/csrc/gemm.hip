@@ -1794,6 +1794,293 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
     }
 }
 
+// Small-M kernel, one 16-row tile (M <= 16): the arithmetic of
+// k_gemm_small, but the weights also pass through LDS.  A workgroup's NT*16
+// columns are consecutive rows of the weight planes, so each K slice of them
+// is read with whole contiguous 1 KiB wave loads (and its scales with
+// consecutive 2-byte loads) instead of one 64-byte piece per column per
+// load, and the MFMA layout comes from the LDS reads (lane 16g + j reads
+// dword g of its block of column j: the column stride of 132 dwords puts the
+// 64 lanes in distinct banks), with no transpose.  A slice's X, weights and
+// scales are loaded together, kRing slices ahead, into a ring of register
+// stages, and stored to LDS the step before they are used: loads complete
+// in issue order, so any other split would make the earliest one wait for
+// everything issued before it.
+template <int WF, int NT, int YDT, int XP, bool ONE>
+__global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small1(const GemmArgs a) {
+    static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
+    constexpr int kThreads = 64 * kSmWaves;
+    constexpr int kRows = 16;
+    constexpr int kSliceBlk = 4 * kSmWaves;               // blocks per K slice
+    constexpr int kRowH = kSliceBlk * 32 + 8;             // X row of a slice, bf16 (16 B pad)
+    constexpr int kXBufH = kRows * kRowH;
+    constexpr int kUnitsRow = kSliceBlk * 4;              // 16-byte X units per row of a slice
+    static_assert(XP * kThreads / kUnitsRow <= kRows, "X rows copied fit the slice buffer");
+    constexpr int kCols = NT * 16;
+    constexpr int kColB = kSliceBlk * 16 + 16;            // weight column of a slice, bytes (16 B pad)
+    constexpr int kWBufB = kCols * kColB;
+    constexpr int kWU = kCols * kSliceBlk / kThreads;     // 16-byte weight units per thread per slice
+    static_assert(kCols * kSliceBlk % kThreads == 0, "weight slice split");
+    constexpr int kNsc = WF == WF_Q4_0 ? kCols * kSliceBlk : kCols * kSliceBlk / 2;   // scales (per plane)
+    constexpr int kSU = (kNsc + kThreads - 1) / kThreads;
+    constexpr int kSBufB = (WF == WF_Q4_0 ? 1 : 2) * kNsc * 2;
+    constexpr int kTile = NT * 4 * 64;
+    constexpr int kXBytes = 2 * kXBufH * 2;
+    constexpr int kBytes = kXBytes + 2 * kWBufB + 2 * kSBufB;
+    constexpr int kRedBytes = kSmWaves * kTile * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kBytes > kRedBytes ? kBytes : kRedBytes];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                   // [2][16][kRowH]
+    uint8_t* wsm = smem + kXBytes;                                       // [2][kCols][kColB]
+    uint16_t* ssm = reinterpret_cast<uint16_t*>(smem + kXBytes + 2 * kWBufB);   // [2][planes][kNsc]
+    float* red = reinterpret_cast<float*>(smem);                         // after the last slice
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int n0 = blockIdx.x * kCols;
+    const int nb = a.K / 32;
+    const int ng = a.K / 64;
+    const int nslices = (nb + kSliceBlk - 1) / kSliceBlk;
+    const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
+    const int xrow = (j < a.M ? j : a.M - 1) * kRowH;
+
+    // ---- X slices (as in k_gemm_small) ----
+    auto x_load = [&](int sl, u32x4_t (&r)[XP]) {
+        const int slc = sl < nslices ? sl : nslices - 1;
+#pragma unroll
+        for (int i = 0; i < XP; i++) {
+            const int u = tid + i * kThreads;
+            const int row = u / kUnitsRow, cu = u % kUnitsRow;
+            const int k = slc * kSliceBlk * 32 + cu * 8;
+            r[i] = *reinterpret_cast<const u32x4_t*>(xg + (int64_t)(row < a.M ? row : a.M - 1) * a.K +
+                                                     (k < a.K ? k : k % a.K));
+        }
+    };
+    auto x_store = [&](int sl, const u32x4_t (&r)[XP]) {
+        uint16_t* buf = xs + (sl & 1) * kXBufH;
+#pragma unroll
+        for (int i = 0; i < XP; i++) {
+            const int u = tid + i * kThreads;
+            const int row = u / kUnitsRow, cu = u % kUnitsRow;
+            const int k = sl * kSliceBlk * 32 + cu * 8;
+            const u32x4_t v = k < a.K ? r[i] : u32x4_t{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4_t*>(buf + row * kRowH + cu * 8) = v;
+        }
+    };
+
+    // ---- weight slices: unit u = tid + 512 i is block u % kSliceBlk of
+    // column u / kSliceBlk; columns past N re-read column N-1 and blocks
+    // past K block nb-1 (their X is zero) ----
+    struct WStage {
+        u32x4_t x[XP];          // X units
+        u32x4_t w[kWU];
+        uint16_t s0[kSU];       // Q4_0 d; affine s
+        uint16_t s1[kSU];       // affine b
+    };
+    auto w_load = [&](int sl, WStage& st) {
+        const int slc = sl < nslices ? sl : nslices - 1;
+#pragma unroll
+        for (int i = 0; i < kWU; i++) {
+            const int u = tid + i * kThreads;
+            const int c = u / kSliceBlk, b = u % kSliceBlk;
+            const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
+            const int kb = slc * kSliceBlk + b;
+            const int kbc = kb < nb ? kb : nb - 1;
+            if constexpr (WF == WF_Q4_0)
+                st.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                    reinterpret_cast<const uint8_t*>(a.a) + (n * nb + kbc) * 16));
+            else
+                st.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                    reinterpret_cast<const uint8_t*>(a.a) + n * (a.K / 2) + (int64_t)kbc * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < kSU; i++) {
+            const int u = tid + i * kThreads;
+            if (kNsc % kThreads == 0 || i * kThreads < kNsc) {     // whole waves: a uniform condition
+                const int uu = u < kNsc ? u : kNsc - 1;
+                if constexpr (WF == WF_Q4_0) {
+                    const int c = uu / kSliceBlk, b = uu % kSliceBlk;
+                    const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
+                    const int kb = slc * kSliceBlk + b;
+                    st.s0[i] = reinterpret_cast<const uint16_t*>(a.b)[n * nb + (kb < nb ? kb : nb - 1)];
+                } else {
+                    constexpr int kGs = kSliceBlk / 2;
+                    const int c = uu / kGs, gr = uu % kGs;
+                    const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
+                    const int gi = slc * kGs + gr;
+                    const int64_t off = n * ng + (gi < ng ? gi : ng - 1);
+                    st.s0[i] = reinterpret_cast<const uint16_t*>(a.b)[off];
+                    st.s1[i] = reinterpret_cast<const uint16_t*>(a.c)[off];
+                }
+            }
+        }
+    };
+    auto w_store = [&](int sl, const WStage& st) {
+        uint8_t* wb = wsm + (sl & 1) * kWBufB;
+#pragma unroll
+        for (int i = 0; i < kWU; i++) {
+            const int u = tid + i * kThreads;
+            *reinterpret_cast<u32x4_t*>(wb + (u / kSliceBlk) * kColB + (u % kSliceBlk) * 16) = st.w[i];
+        }
+        uint16_t* sb = ssm + (sl & 1) * (kSBufB / 2);
+#pragma unroll
+        for (int i = 0; i < kSU; i++) {
+            const int u = tid + i * kThreads;
+            if (kNsc % kThreads == 0 || u < kNsc) {
+                sb[u] = st.s0[i];
+                if constexpr (WF == WF_AFFINE4) sb[kNsc + u] = st.s1[i];
+            }
+        }
+    };
+
+    floatx4_t acc[NT];
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++) acc[ni] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    uint32_t mask = 0x000F000Fu;
+    asm volatile("" : "+v"(mask));
+    const floatx4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto x_frag = [&](int sl, int t) {
+        const uint16_t* p = xs + (sl & 1) * kXBufH + xrow + (4 * wave + t) * 32;
+        SmX<WF> x;
+        if constexpr (WF == WF_Q4_0) {
+            x.lo = *reinterpret_cast<const u32x2_t*>(p + 4 * g);
+            x.hi = *reinterpret_cast<const u32x2_t*>(p + 16 + 4 * g);
+        } else {
+            x.v = *reinterpret_cast<const u32x4_t*>(p + 8 * g);
+        }
+        return sm_xfrag<WF>(x);
+    };
+    // dword g of block 4 wave + t of column ni*16 + j
+    auto w_word = [&](int sl, int ni, int t) {
+        return *reinterpret_cast<const uint32_t*>(wsm + (sl & 1) * kWBufB + (ni * 16 + j) * kColB +
+                                                  (4 * wave + t) * 16 + 4 * g);
+    };
+
+    auto compute = [&](int sl) {
+        const uint16_t* sb = ssm + (sl & 1) * (kSBufB / 2);
+        if constexpr (WF == WF_Q4_0) {
+            const bf16x8_t neg136 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
+            uint32_t dq[NT][2];
+#pragma unroll
+            for (int ni = 0; ni < NT; ni++) {
+                const u32x2_t dv = *reinterpret_cast<const u32x2_t*>(sb + (ni * 16 + j) * kSliceBlk + 4 * wave);
+                dq[ni][0] = dv[0];
+                dq[ni][1] = dv[1];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const bf16x8_t xa = x_frag(sl, t);
+                const floatx4_t c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, neg136, zero4, 0, 0, 0);
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++) {
+                    const bf16x8_t wb = sm_weights(w_word(sl, ni, t), mask);
+                    const float d = f16_to_f32(dq[ni][t >> 1] >> (16 * (t & 1)));
+                    const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wb, c0, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; v++) acc[ni][v] = __builtin_fmaf(d, dv[v], acc[ni][v]);
+                }
+            }
+        } else {
+            const bf16x8_t neg128 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u});
+            constexpr int kGs = kSliceBlk / 2;
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const bf16x8_t xa0 = x_frag(sl, 2 * h);
+                const bf16x8_t xa1 = x_frag(sl, 2 * h + 1);
+                const floatx4_t cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    xa1, neg128, __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, neg128, zero4, 0, 0, 0), 0, 0, 0);
+#pragma unroll
+                for (int ni = 0; ni < NT; ni++) {
+                    const int si = (ni * 16 + j) * kGs + 2 * wave + h;
+                    const float sv = bf16_to_f32(sb[si]);
+                    const float bq = bf16_to_f32(sb[kNsc + si]) * -0.0078125f;   // b / -128 (exact)
+                    const bf16x8_t w0 = sm_weights(w_word(sl, ni, 2 * h), mask);
+                    const bf16x8_t w1 = sm_weights(w_word(sl, ni, 2 * h + 1), mask);
+                    const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        xa1, w1, __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, w0, cs, 0, 0, 0), 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; v++) {
+                        acc[ni][v] = __builtin_fmaf(sv, dv[v], acc[ni][v]);
+                        acc[ni][v] = __builtin_fmaf(bq, cs[v], acc[ni][v]);
+                    }
+                }
+            }
+        }
+    };
+
+    constexpr int kRing = ONE ? 4 : 2;
+    const int nsteps = (nslices + kRing - 1) / kRing * kRing;
+    WStage ring[kRing];        // slot r holds slices r, r + kRing, ...
+    auto slice_load = [&](int sl, WStage& st) {
+        x_load(sl, st.x);
+        w_load(sl, st);
+    };
+    auto slice_store = [&](int sl, const WStage& st) {
+        x_store(sl, st.x);
+        w_store(sl, st);
+    };
+    // Step sl multiplies slice sl from LDS, stores slice sl+1 from its ring
+    // slot into the other LDS buffers and refills the slot with slice
+    // sl+1+kRing.  Phases are fenced so that no work on loaded values (and
+    // so no wait) moves between them.
+    auto step = [&](int sl, auto last, auto r) {
+        constexpr bool kLast = decltype(last)::value;
+        constexpr int kR = decltype(r)::value;
+        constexpr bool kStore = !kLast || kR < kRing - 1;
+        constexpr int kNext = (kR + 1) % kRing;
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sl);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kStore) slice_store(sl + 1, ring[kNext]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!kLast) slice_load(sl + 1 + kRing, ring[kNext]);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+    auto group = [&](int sl0, auto last) {
+        step(sl0 + 0, last, std::integral_constant<int, 0>{});
+        step(sl0 + 1, last, std::integral_constant<int, 1>{});
+        if constexpr (kRing == 4) {
+            step(sl0 + 2, last, std::integral_constant<int, 2>{});
+            step(sl0 + 3, last, std::integral_constant<int, 3>{});
+        }
+    };
+    // prologue: slices 0 .. kRing-1 requested; slice 0 stored and its slot
+    // refilled with slice kRing
+#pragma unroll
+    for (int r = 0; r < kRing; r++) slice_load(r, ring[r]);
+    slice_store(0, ring[0]);
+    if constexpr (!ONE) slice_load(kRing, ring[0]);
+    __syncthreads();
+    if constexpr (ONE) {
+        group(0, std::true_type{});
+    } else {
+        group(0, std::false_type{});
+        for (int sl = kRing; sl < nsteps - kRing; sl += kRing) group(sl, std::false_type{});
+        group(nsteps - kRing, std::true_type{});
+    }
+
+#pragma unroll
+    for (int ni = 0; ni < NT; ni++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) red[wave * kTile + (ni * 4 + v) * 64 + lane] = acc[ni][v];
+    __syncthreads();
+    for (int i = tid; i < kTile; i += kThreads) {
+        float t = red[i];
+#pragma unroll
+        for (int w = 1; w < kSmWaves; w++) t += red[w * kTile + i];
+        const int l = i & 63;
+        const int v = (i >> 6) & 3;
+        const int ni = i >> 8;
+        const int r = 4 * (l >> 4) + v;
+        const int n = n0 + ni * 16 + (l & 15);
+        if (r < a.M && n < a.N) store_y(a.y, YDT, (int64_t)r * a.N + n, t);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -2171,8 +2458,13 @@ template <int WF, int MT, int NT, int YDT, int XP>
 static void launch_small_t(GemmArgs ga, hipStream_t s) {
     const dim3 grid((unsigned)((ga.N + NT * 16 - 1) / (NT * 16))), block(64 * kSmWaves);
     const int nslices = (ga.K / 32 + 4 * kSmWaves - 1) / (4 * kSmWaves);
-    if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, true>), grid, block, 0, s, ga);
-    else hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, false>), grid, block, 0, s, ga);
+    if constexpr (MT == 1) {
+        if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small1<WF, NT, YDT, XP, true>), grid, block, 0, s, ga);
+        else hipLaunchKernelGGL((k_gemm_small1<WF, NT, YDT, XP, false>), grid, block, 0, s, ga);
+    } else {
+        if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, true>), grid, block, 0, s, ga);
+        else hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, false>), grid, block, 0, s, ga);
+    }
 }
 
 // The widest column group (NT tiles of 16) that still gives every CU a
