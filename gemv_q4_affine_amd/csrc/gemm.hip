@@ -1400,62 +1400,27 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemm_skinny(const GemmArgs a)
 // result differs from the exact one by fp32 accumulation and the output
 // rounding only.
 //
-// Lane l = 16 g + j.  The MFMA's B operand takes from lane (j, g) eight
-// weights of column j, all from one block.  Dword g of a block holds eight of
-// its weights (Q4_0: elements 4g..4g+3 and 16+4g..16+4g+3; affine: 8g..8g+7).
-// The loads are coalesced instead: lane 4j + i loads block 4c + i of column j
-// (one 128-bit load; four neighbouring lanes read a column's 64 contiguous
-// bytes).  A 4 x 4 DPP transpose inside each lane quad then gives lane 4j + i
-// dword i of each of the chunk's four blocks, and one ds_bpermute per dword
-// moves it to lane 16 i + j.  A dword's nibbles pair up as (byte 0, byte 2)
-// and (byte 1, byte 3); the X fragment is permuted into the same order.  The
-// block scales, loaded the same way, reach every lane of their column by
-// ds_bpermute.
-//
-// Workgroup: 8 waves on the same NT*16 columns.  K runs in slices of 32
-// blocks; in each slice wave w takes blocks 4w..4w+3 (one chunk).  X is the
-// costly operand here -- every workgroup needs all of it, and fragment loads
-// straight from memory would cost more vector-memory instructions than the
-// weights -- so the workgroup copies each X slice into LDS once, with 16-byte
-// loads, double-buffered: slice s+1 (and the weights of the wave's next
-// chunk) is in flight while slice s is multiplied, and one barrier per slice
-// hands the buffers over.  The partial tiles meet in LDS at the end and are
-// summed in wave order, so results are deterministic.
+// Workgroup: 8 waves on the same NT*16 columns (MT 16-row tiles).  K runs in
+// slices of 32/MT blocks; in each slice wave w multiplies blocks 4w/MT ..
+// (the waves split K).  A workgroup needs all of X and its columns are
+// consecutive rows of the weight planes, so each slice of X, of the weights
+// and of the scales is read with whole contiguous wave loads (1 KiB per
+// load) and stored to LDS, where every lane reads its MFMA operands: lane
+// 16g + j takes dword g of its block of column j (Q4_0: elements 4g..4g+3
+// and 16+4g..16+4g+3; affine: 8g..8g+7).  A dword's nibbles pair up as
+// (byte 0, byte 2) and (byte 1, byte 3); the X fragment is permuted into the
+// same order.  A weight column of a slice takes 4 (mod 64) dwords of LDS, so
+// the 64 lanes read distinct banks.  A slice's X, weights and scales are
+// loaded together, four slices ahead, into a ring of register stages and
+// stored to LDS (double-buffered) the step before they are used: loads
+// complete in issue order, so any other split would make the earliest wait
+// for everything issued before it.  One barrier per slice.  The partial
+// tiles meet in LDS at the end and are summed in wave order, so results are
+// deterministic.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr int kSmWaves = 8;
 constexpr int kSmMaxM = 32;
-
-// On entry lane row g (lanes 16g..16g+15) holds item g's dwords in r[0..3];
-// on exit it holds dword g of item t in r[t].
-__device__ __forceinline__ void row_transpose4(uint32_t (&r)[4]) {
-    const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
-    const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
-    const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
-    const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
-    r[0] = s01[0];
-    r[1] = s01[1];
-    r[2] = s23[0];
-    r[3] = s23[1];
-}
-
-// 4 x 4 transpose of dwords inside each quad of lanes: on entry lane 4q + i
-// holds item i's dwords in r[0..3]; on exit it holds dword i of item t in
-// r[t].  Two rounds of DPP exchanges, across lane ^ 1 and lane ^ 2.
-__device__ __forceinline__ void quad_transpose4(uint32_t (&r)[4], bool odd, bool hi2) {
-    auto x1 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false); };
-    auto x2 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false); };
-    const uint32_t t0 = x1(r[0]), t1 = x1(r[1]), t2 = x1(r[2]), t3 = x1(r[3]);
-    const uint32_t a0 = odd ? t1 : r[0];
-    const uint32_t a1 = odd ? r[1] : t0;
-    const uint32_t a2 = odd ? t3 : r[2];
-    const uint32_t a3 = odd ? r[3] : t2;
-    const uint32_t u0 = x2(a0), u1 = x2(a1), u2 = x2(a2), u3 = x2(a3);
-    r[0] = hi2 ? u2 : a0;
-    r[1] = hi2 ? u3 : a1;
-    r[2] = hi2 ? a2 : u0;
-    r[3] = hi2 ? a3 : u1;
-}
 
 // Eight weights of dword w as bf16 128 + q, in the pair order (byte 0,
 // byte 2), (byte 1, byte 3) of the low nibbles, then of the high nibbles.
@@ -1499,103 +1464,138 @@ __device__ __forceinline__ bf16x8_t sm_xfrag(const SmX<WF>& x) {
 template <int WF, int MT, int NT, int YDT, int XP, bool ONE>
 __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs a) {
     static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
+    static_assert(MT == 1 || MT == 2, "one or two row tiles");
     constexpr int kThreads = 64 * kSmWaves;
     constexpr int kRows = MT * 16;
-    constexpr int kSliceBlk = 4 * kSmWaves;               // blocks per K slice
-    constexpr int kRowH = kSliceBlk * 32 + 8;             // LDS row of a slice, bf16 (16 B pad)
-    constexpr int kBufH = kRows * kRowH;                  // one slice buffer, bf16
-    constexpr int kUnitsRow = kSliceBlk * 4;              // 16-byte units per row of a slice
+    constexpr int kSliceBlk = 32 / MT;                    // blocks per K slice
+    constexpr int kBpw = kSliceBlk / kSmWaves;            // blocks per wave per slice
+    constexpr int kRowH = kSliceBlk * 32 + 8;             // X row of a slice, bf16 (16 B pad)
+    constexpr int kXBufH = kRows * kRowH;
+    constexpr int kUnitsRow = kSliceBlk * 4;              // 16-byte X units per row of a slice
     static_assert(XP * kThreads / kUnitsRow <= kRows, "X rows copied fit the slice buffer");
+    constexpr int kCols = NT * 16;
+    constexpr int kColB = kSliceBlk * 16 + 16;            // weight column of a slice, bytes
+    static_assert(kColB / 4 % 64 == 4, "bank spread of the weight reads");
+    constexpr int kWBufB = kCols * kColB;
+    constexpr int kWTot = kCols * kSliceBlk;              // 16-byte weight units per slice
+    constexpr int kWU = (kWTot + kThreads - 1) / kThreads;
+    static_assert(kWTot % 64 == 0, "whole waves per weight pass");
+    constexpr int kGs = kSliceBlk / 2;                    // affine groups per slice
+    constexpr int kNsc = WF == WF_Q4_0 ? kCols * kSliceBlk : kCols * kGs;   // scales per plane
+    static_assert(kNsc % 64 == 0, "whole waves per scale pass");
+    constexpr int kSU = (kNsc + kThreads - 1) / kThreads;
+    constexpr int kSBufH = (WF == WF_Q4_0 ? 1 : 2) * kNsc;
     constexpr int kTile = MT * NT * 4 * 64;               // partial values per wave
-    constexpr int kXBytes = 2 * kBufH * 2;
+    constexpr int kXBytes = 2 * kXBufH * 2;
+    constexpr int kBytes = kXBytes + 2 * kWBufB + 2 * kSBufH * 2;
     constexpr int kRedBytes = kSmWaves * kTile * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kXBytes > kRedBytes ? kXBytes : kRedBytes];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);     // [2][kRows][kRowH]
-    float* red = reinterpret_cast<float*>(smem);          // [kSmWaves][kTile], after the last slice
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kBytes > kRedBytes ? kBytes : kRedBytes];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                   // [2][kRows][kRowH]
+    uint8_t* wsm = smem + kXBytes;                                       // [2][kCols][kColB]
+    uint16_t* ssm = reinterpret_cast<uint16_t*>(smem + kXBytes + 2 * kWBufB);   // [2][planes][kNsc]
+    float* red = reinterpret_cast<float*>(smem);                         // after the last slice
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int j = lane & 15;
     const int g = lane >> 4;
-    const int n0 = blockIdx.x * (NT * 16);
+    const int n0 = blockIdx.x * kCols;
     const int nb = a.K / 32;
-    const int nchunks = (nb + 3) / 4;
+    const int ng = a.K / 64;
     const int nslices = (nb + kSliceBlk - 1) / kSliceBlk;
     const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
-
-    // columns this lane loads (lane 4j' + i: column j' of each tile), clamped:
-    // a column past N is computed, never stored
-    int nld[NT];
-#pragma unroll
-    for (int ni = 0; ni < NT; ni++) {
-        const int n = n0 + ni * 16 + (lane >> 2);
-        nld[ni] = n < a.N ? n : a.N - 1;
-    }
     // LDS rows of the A fragments, clamped (rows past M are computed, never stored)
     int xrow[MT];
 #pragma unroll
-    for (int mi = 0; mi < MT; mi++) {
-        const int m = mi * 16 + j;
-        xrow[mi] = (m < a.M ? m : a.M - 1) * kRowH;
-    }
+    for (int mi = 0; mi < MT; mi++) xrow[mi] = (mi * 16 + j < a.M ? mi * 16 + j : a.M - 1) * kRowH;
 
-    // ---- X slices: global -> registers -> LDS ----
-    // XP passes of 16-byte units cover rows 0 .. 4 XP - 1 (>= M); rows past
-    // M re-read row M-1, and a unit past K reads another unit of its row
-    // (slices past the end re-read the last one), so every load is valid,
-    // unconditional and spread over lines; a unit past K is stored as zeros,
-    // so blocks past K (and whole slices past the end) contribute nothing
-    // whatever their scale.  The steps hold no branch and no select next to a load: either
-    // makes the compiler wait for every load in flight, which would drain
-    // the weight ring below.
-    u32x4_t xr[MT == 1 ? 2 : 1][XP];      // register sets (two: slice sl lives in set sl & 1)
-    auto x_load = [&](int sl, u32x4_t (&r)[XP]) {
-        const int slc = sl < nslices ? sl : nslices - 1;     // past the end: a real slice, stored as zeros
+    // ---- one slice: X, weights and scales (a record of the ring) ----
+    // X: unit u = tid + 512 i, XP passes over rows 0 .. XP*512/kUnitsRow - 1
+    // (>= M); rows past M re-read row M-1 and a unit past K reads another
+    // unit of its row (slices past the end re-read the last one), so every
+    // load is valid and unconditional; a unit past K is stored as zeros, so
+    // blocks past K (and whole slices past the end) contribute nothing
+    // whatever their scale.  Weights: unit u is block u % kSliceBlk of column
+    // u / kSliceBlk; columns past N re-read column N-1, blocks past K block
+    // nb-1.  No select or branch sits next to a load: either makes the
+    // compiler wait for every load in flight.
+    struct Rec {
+        u32x4_t x[XP];
+        u32x4_t w[kWU];
+        uint16_t s0[kSU];       // Q4_0 d; affine s
+        uint16_t s1[kSU];       // affine b
+    };
+    auto rec_load = [&](int sl, Rec& st) {
+        const int slc = sl < nslices ? sl : nslices - 1;
 #pragma unroll
         for (int i = 0; i < XP; i++) {
             const int u = tid + i * kThreads;
             const int row = u / kUnitsRow, cu = u % kUnitsRow;
             const int k = slc * kSliceBlk * 32 + cu * 8;
-            r[i] = *reinterpret_cast<const u32x4_t*>(xg + (int64_t)(row < a.M ? row : a.M - 1) * a.K +
-                                                     (k < a.K ? k : k % a.K));
+            st.x[i] = *reinterpret_cast<const u32x4_t*>(xg + (int64_t)(row < a.M ? row : a.M - 1) * a.K +
+                                                        (k < a.K ? k : k % a.K));
+        }
+#pragma unroll
+        for (int i = 0; i < kWU; i++) {
+            const int u = tid + i * kThreads;
+            if (kWTot % kThreads == 0 || u < kWTot) {       // whole waves: a uniform condition
+                const int c = u / kSliceBlk, b = u % kSliceBlk;
+                const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
+                const int kb = slc * kSliceBlk + b;
+                const int kbc = kb < nb ? kb : nb - 1;
+                if constexpr (WF == WF_Q4_0)
+                    st.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                        reinterpret_cast<const uint8_t*>(a.a) + (n * nb + kbc) * 16));
+                else
+                    st.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                        reinterpret_cast<const uint8_t*>(a.a) + n * (a.K / 2) + (int64_t)kbc * 16));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kSU; i++) {
+            const int u = tid + i * kThreads;
+            if (kNsc % kThreads == 0 || u < kNsc) {
+                if constexpr (WF == WF_Q4_0) {
+                    const int c = u / kSliceBlk, b = u % kSliceBlk;
+                    const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
+                    const int kb = slc * kSliceBlk + b;
+                    st.s0[i] = reinterpret_cast<const uint16_t*>(a.b)[n * nb + (kb < nb ? kb : nb - 1)];
+                } else {
+                    const int c = u / kGs, gr = u % kGs;
+                    const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
+                    const int gi = slc * kGs + gr;
+                    const int64_t off = n * ng + (gi < ng ? gi : ng - 1);
+                    st.s0[i] = reinterpret_cast<const uint16_t*>(a.b)[off];
+                    st.s1[i] = reinterpret_cast<const uint16_t*>(a.c)[off];
+                }
+            }
         }
     };
-    auto x_store = [&](int sl, const u32x4_t (&r)[XP]) {
-        uint16_t* buf = xs + (sl & 1) * kBufH;
+    auto rec_store = [&](int sl, const Rec& st) {
+        uint16_t* xb = xs + (sl & 1) * kXBufH;
 #pragma unroll
         for (int i = 0; i < XP; i++) {
             const int u = tid + i * kThreads;
             const int row = u / kUnitsRow, cu = u % kUnitsRow;
             const int k = sl * kSliceBlk * 32 + cu * 8;
-            const u32x4_t v = k < a.K ? r[i] : u32x4_t{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4_t*>(buf + row * kRowH + cu * 8) = v;
+            const u32x4_t v = k < a.K ? st.x[i] : u32x4_t{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4_t*>(xb + row * kRowH + cu * 8) = v;
         }
-    };
-
-    // ---- weights of one chunk: block 4c + g of each column, and its scale ----
-    struct Stage {
-        u32x4_t w[NT];
-        uint16_t s0[NT];      // Q4_0 d; affine s of its group
-        uint16_t s1[NT];      // affine b of its group
-    };
-    // Lane 4j' + i: block 4c + i of column j' of each tile.
-    auto w_load = [&](int c, Stage& st) {
-        const int kb = 4 * c + (lane & 3);
-        const int kbc = kb < nb ? kb : nb - 1;    // past K: any valid block (its X is zero)
+        uint8_t* wb = wsm + (sl & 1) * kWBufB;
 #pragma unroll
-        for (int ni = 0; ni < NT; ni++) {
-            const int64_t n = nld[ni];
-            if constexpr (WF == WF_Q4_0) {
-                st.w[ni] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                    reinterpret_cast<const uint8_t*>(a.a) + (n * nb + kbc) * 16));
-                st.s0[ni] = reinterpret_cast<const uint16_t*>(a.b)[n * nb + kbc];
-            } else {
-                st.w[ni] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                    reinterpret_cast<const uint8_t*>(a.a) + n * (a.K / 2) + (int64_t)kbc * 16));
-                const int64_t gi = n * (a.K / 64) + (kbc >> 1);
-                st.s0[ni] = reinterpret_cast<const uint16_t*>(a.b)[gi];
-                st.s1[ni] = reinterpret_cast<const uint16_t*>(a.c)[gi];
+        for (int i = 0; i < kWU; i++) {
+            const int u = tid + i * kThreads;
+            if (kWTot % kThreads == 0 || u < kWTot)
+                *reinterpret_cast<u32x4_t*>(wb + (u / kSliceBlk) * kColB + (u % kSliceBlk) * 16) = st.w[i];
+        }
+        uint16_t* sb = ssm + (sl & 1) * kSBufH;
+#pragma unroll
+        for (int i = 0; i < kSU; i++) {
+            const int u = tid + i * kThreads;
+            if (kNsc % kThreads == 0 || u < kNsc) {
+                sb[u] = st.s0[i];
+                if constexpr (WF == WF_AFFINE4) sb[kNsc + u] = st.s1[i];
             }
         }
     };
@@ -1605,19 +1605,13 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
     for (int mi = 0; mi < MT; mi++)
 #pragma unroll
         for (int ni = 0; ni < NT; ni++) acc[mi][ni] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
     uint32_t mask = 0x000F000Fu;
     asm volatile("" : "+v"(mask));           // a VGPR operand: one v_and_or_b32 per pair
     const floatx4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    // ds_bpermute byte addresses: lane 16g + j takes its weights from lane
-    // 4j + g and the scale of block t from lane 4j + t
-    const int bp_w = (4 * j + g) * 4;
-    const int bp_s = 4 * j * 4;
 
-    // X fragment of block t of this wave's chunk in slice sl, rows mi*16 + j
-    // (clamped); a block past K reads zeros
+    // operands of block kBpw*wave + t of slice sl
     auto x_frag = [&](int sl, int t, int mi) {
-        const uint16_t* p = xs + (sl & 1) * kBufH + xrow[mi] + (4 * wave + t) * 32;
+        const uint16_t* p = xs + (sl & 1) * kXBufH + xrow[mi] + (kBpw * wave + t) * 32;
         SmX<WF> x;
         if constexpr (WF == WF_Q4_0) {
             x.lo = *reinterpret_cast<const u32x2_t*>(p + 4 * g);
@@ -1627,24 +1621,17 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
         }
         return sm_xfrag<WF>(x);
     };
+    auto w_word = [&](int sl, int ni, int t) {
+        return *reinterpret_cast<const uint32_t*>(wsm + (sl & 1) * kWBufB + (ni * 16 + j) * kColB +
+                                                  (kBpw * wave + t) * 16 + 4 * g);
+    };
 
-    auto compute = [&](int sl, const Stage& st) {
-        uint32_t wt[NT][4], sct[NT][4];
-#pragma unroll
-        for (int ni = 0; ni < NT; ni++) {
-            uint32_t q4[4] = {st.w[ni][0], st.w[ni][1], st.w[ni][2], st.w[ni][3]};
-            quad_transpose4(q4, (lane & 1) != 0, (lane & 2) != 0);
-            const uint32_t sc = WF == WF_Q4_0 ? (uint32_t)st.s0[ni] : ((uint32_t)st.s0[ni] | ((uint32_t)st.s1[ni] << 16));
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                wt[ni][t] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_w, (int)q4[t]);
-                sct[ni][t] = (uint32_t)__builtin_amdgcn_ds_bpermute(bp_s + 4 * t, (int)sc);
-            }
-        }
+    auto compute = [&](int sl) {
+        const uint16_t* sb = ssm + (sl & 1) * kSBufH;
         if constexpr (WF == WF_Q4_0) {
             const bf16x8_t neg136 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
 #pragma unroll
-            for (int t = 0; t < 4; t++) {
+            for (int t = 0; t < kBpw; t++) {
                 bf16x8_t xa[MT];
                 floatx4_t c0[MT];
 #pragma unroll
@@ -1654,8 +1641,8 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
                 }
 #pragma unroll
                 for (int ni = 0; ni < NT; ni++) {
-                    const bf16x8_t wb = sm_weights(wt[ni][t], mask);
-                    const float d = f16_to_f32(sct[ni][t]);      // the low half
+                    const bf16x8_t wb = sm_weights(w_word(sl, ni, t), mask);
+                    const float d = f16_to_f32(sb[(ni * 16 + j) * kSliceBlk + kBpw * wave + t]);
 #pragma unroll
                     for (int mi = 0; mi < MT; mi++) {
                         const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mi], wb, c0[mi], 0, 0, 0);
@@ -1667,9 +1654,9 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
         } else {
             const bf16x8_t neg128 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u});
 #pragma unroll
-            for (int h = 0; h < 2; h++) {          // the chunk's two groups of 64
+            for (int h = 0; h < kBpw / 2; h++) {       // this wave's groups of 64
                 bf16x8_t xa0[MT], xa1[MT];
-                floatx4_t cs[MT];                  // -128 * (sum of x over the group)
+                floatx4_t cs[MT];                      // -128 * (sum of x over the group)
 #pragma unroll
                 for (int mi = 0; mi < MT; mi++) {
                     xa0[mi] = x_frag(sl, 2 * h, mi);
@@ -1679,11 +1666,11 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
                 }
 #pragma unroll
                 for (int ni = 0; ni < NT; ni++) {
-                    const bf16x8_t w0 = sm_weights(wt[ni][2 * h], mask);
-                    const bf16x8_t w1 = sm_weights(wt[ni][2 * h + 1], mask);
-                    const uint32_t sb = sct[ni][2 * h];
-                    const float sv = bf16_to_f32(sb & 0xFFFFu);
-                    const float bq = bf16_to_f32(sb >> 16) * -0.0078125f;   // b / -128 (exact)
+                    const int si = (ni * 16 + j) * kGs + (kBpw / 2) * wave + h;
+                    const float sv = bf16_to_f32(sb[si]);
+                    const float bq = bf16_to_f32(sb[kNsc + si]) * -0.0078125f;   // b / -128 (exact)
+                    const bf16x8_t w0 = sm_weights(w_word(sl, ni, 2 * h), mask);
+                    const bf16x8_t w1 = sm_weights(w_word(sl, ni, 2 * h + 1), mask);
 #pragma unroll
                     for (int mi = 0; mi < MT; mi++) {
                         const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1699,49 +1686,26 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
         }
     };
 
-    // Slice sl: this wave's chunk is 8 sl + wave.  The weights run kRing
-    // slices ahead in a ring of register stages with fixed roles.  X runs
-    // two slices ahead: with two register sets (one 16-row tile), step sl
-    // loads slice sl+2 into the set that held slice sl, multiplies slice sl
-    // from LDS and then stores slice sl+1 (loaded a step earlier) into the
-    // other LDS buffer; with one set (two tiles, where registers are short)
-    // it stores slice sl+1 first and then loads slice sl+2 into the same
-    // set.  The slice count is padded to a multiple of kRing; chunks and
-    // slices past the end load clamped (valid) weights and multiply zero X.
-    // ONE: the slices fit one ring (K <= 4096 here), so there is no loop and
-    // the ring is deeper.
+    // Step sl multiplies slice sl from LDS, stores slice sl+1 from its ring
+    // slot into the other LDS buffers and refills the slot with slice
+    // sl+1+kRing.  Phases are fenced so that no work on loaded values (and
+    // so no wait) moves between them.  The slice count is padded to a
+    // multiple of kRing; in the last ring nothing is refilled.  ONE: all
+    // slices fit one ring of four, so there is no loop; with a loop the ring
+    // holds two (four would spill).
     constexpr int kRing = ONE ? 4 : 2;
-    constexpr bool kTwoSets = MT == 1;
     const int nsteps = (nslices + kRing - 1) / kRing * kRing;
-    auto chunk_of = [&](int sl) {
-        const int c = sl * kSmWaves + wave;
-        return c < nchunks ? c : nchunks - 1;
-    };
-    Stage ring[kRing];
-    // Each phase is fenced so that the scheduler moves no work on loaded
-    // values (and so no wait) across phases.  In the last ring of steps
-    // nothing is refilled, and slices that no step reads are neither loaded
-    // nor stored.
+    Rec ring[kRing];           // slot r holds slices r, r + kRing, ...
     auto step = [&](int sl, auto last, auto r) {
         constexpr bool kLast = decltype(last)::value;
         constexpr int kR = decltype(r)::value;
-        constexpr bool kLoadX = !kLast || kR < kRing - 2;
-        constexpr bool kStoreX = !kLast || kR < kRing - 1;
-        Stage& cur = ring[kR];
+        constexpr int kNext = (kR + 1) % kRing;
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kTwoSets) {
-            if constexpr (kLoadX) x_load(sl + 2, xr[kR & 1]);
-        } else {
-            if constexpr (kStoreX) x_store(sl + 1, xr[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (kLoadX) x_load(sl + 2, xr[0]);
-        }
+        compute(sl);
         __builtin_amdgcn_sched_barrier(0);
-        compute(sl, cur);
+        if constexpr (!kLast || kR < kRing - 1) rec_store(sl + 1, ring[kNext]);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!kLast) w_load(chunk_of(sl + kRing), cur);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kTwoSets && kStoreX) x_store(sl + 1, xr[(kR + 1) & 1]);
+        if constexpr (!kLast) rec_load(sl + 1 + kRing, ring[kNext]);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     };
@@ -1753,12 +1717,10 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
             step(sl0 + 3, last, std::integral_constant<int, 3>{});
         }
     };
-    x_load(0, xr[0]);
-    if constexpr (kTwoSets) x_load(1, xr[1]);
 #pragma unroll
-    for (int r = 0; r < kRing; r++) w_load(chunk_of(r), ring[r]);
-    x_store(0, xr[0]);
-    if constexpr (!kTwoSets) x_load(1, xr[0]);
+    for (int r = 0; r < kRing; r++) rec_load(r, ring[r]);
+    rec_store(0, ring[0]);
+    if constexpr (!ONE) rec_load(kRing, ring[0]);
     __syncthreads();
     if constexpr (ONE) {
         group(0, std::true_type{});
@@ -1770,9 +1732,9 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
         group(nsteps - kRing, std::true_type{});
     }
 
-    // partial tiles to LDS (the X buffers are free after the last barrier);
-    // then every thread sums some outputs over the waves in order (lane holds
-    // column j, rows 4g + v of each 16x16 tile)
+    // partial tiles to LDS (free after the last barrier); every thread then
+    // sums some outputs over the waves in order (lane holds column j, rows
+    // 4g + v of each 16x16 tile)
 #pragma unroll
     for (int mi = 0; mi < MT; mi++)
 #pragma unroll
@@ -1789,293 +1751,6 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
         const int tile = i >> 8;                  // mi * NT + ni
         const int mi = tile / NT, ni = tile % NT;
         const int r = mi * 16 + 4 * (l >> 4) + v;
-        const int n = n0 + ni * 16 + (l & 15);
-        if (r < a.M && n < a.N) store_y(a.y, YDT, (int64_t)r * a.N + n, t);
-    }
-}
-
-// Small-M kernel, one 16-row tile (M <= 16): the arithmetic of
-// k_gemm_small, but the weights also pass through LDS.  A workgroup's NT*16
-// columns are consecutive rows of the weight planes, so each K slice of them
-// is read with whole contiguous 1 KiB wave loads (and its scales with
-// consecutive 2-byte loads) instead of one 64-byte piece per column per
-// load, and the MFMA layout comes from the LDS reads (lane 16g + j reads
-// dword g of its block of column j: the column stride of 132 dwords puts the
-// 64 lanes in distinct banks), with no transpose.  A slice's X, weights and
-// scales are loaded together, kRing slices ahead, into a ring of register
-// stages, and stored to LDS the step before they are used: loads complete
-// in issue order, so any other split would make the earliest one wait for
-// everything issued before it.
-template <int WF, int NT, int YDT, int XP, bool ONE>
-__global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small1(const GemmArgs a) {
-    static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
-    constexpr int kThreads = 64 * kSmWaves;
-    constexpr int kRows = 16;
-    constexpr int kSliceBlk = 4 * kSmWaves;               // blocks per K slice
-    constexpr int kRowH = kSliceBlk * 32 + 8;             // X row of a slice, bf16 (16 B pad)
-    constexpr int kXBufH = kRows * kRowH;
-    constexpr int kUnitsRow = kSliceBlk * 4;              // 16-byte X units per row of a slice
-    static_assert(XP * kThreads / kUnitsRow <= kRows, "X rows copied fit the slice buffer");
-    constexpr int kCols = NT * 16;
-    constexpr int kColB = kSliceBlk * 16 + 16;            // weight column of a slice, bytes (16 B pad)
-    constexpr int kWBufB = kCols * kColB;
-    constexpr int kWU = kCols * kSliceBlk / kThreads;     // 16-byte weight units per thread per slice
-    static_assert(kCols * kSliceBlk % kThreads == 0, "weight slice split");
-    constexpr int kNsc = WF == WF_Q4_0 ? kCols * kSliceBlk : kCols * kSliceBlk / 2;   // scales (per plane)
-    constexpr int kSU = (kNsc + kThreads - 1) / kThreads;
-    constexpr int kSBufB = (WF == WF_Q4_0 ? 1 : 2) * kNsc * 2;
-    constexpr int kTile = NT * 4 * 64;
-    constexpr int kXBytes = 2 * kXBufH * 2;
-    constexpr int kBytes = kXBytes + 2 * kWBufB + 2 * kSBufB;
-    constexpr int kRedBytes = kSmWaves * kTile * 4;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kBytes > kRedBytes ? kBytes : kRedBytes];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                   // [2][16][kRowH]
-    uint8_t* wsm = smem + kXBytes;                                       // [2][kCols][kColB]
-    uint16_t* ssm = reinterpret_cast<uint16_t*>(smem + kXBytes + 2 * kWBufB);   // [2][planes][kNsc]
-    float* red = reinterpret_cast<float*>(smem);                         // after the last slice
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int j = lane & 15;
-    const int g = lane >> 4;
-    const int n0 = blockIdx.x * kCols;
-    const int nb = a.K / 32;
-    const int ng = a.K / 64;
-    const int nslices = (nb + kSliceBlk - 1) / kSliceBlk;
-    const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
-    const int xrow = (j < a.M ? j : a.M - 1) * kRowH;
-
-    // ---- X slices (as in k_gemm_small) ----
-    auto x_load = [&](int sl, u32x4_t (&r)[XP]) {
-        const int slc = sl < nslices ? sl : nslices - 1;
-#pragma unroll
-        for (int i = 0; i < XP; i++) {
-            const int u = tid + i * kThreads;
-            const int row = u / kUnitsRow, cu = u % kUnitsRow;
-            const int k = slc * kSliceBlk * 32 + cu * 8;
-            r[i] = *reinterpret_cast<const u32x4_t*>(xg + (int64_t)(row < a.M ? row : a.M - 1) * a.K +
-                                                     (k < a.K ? k : k % a.K));
-        }
-    };
-    auto x_store = [&](int sl, const u32x4_t (&r)[XP]) {
-        uint16_t* buf = xs + (sl & 1) * kXBufH;
-#pragma unroll
-        for (int i = 0; i < XP; i++) {
-            const int u = tid + i * kThreads;
-            const int row = u / kUnitsRow, cu = u % kUnitsRow;
-            const int k = sl * kSliceBlk * 32 + cu * 8;
-            const u32x4_t v = k < a.K ? r[i] : u32x4_t{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4_t*>(buf + row * kRowH + cu * 8) = v;
-        }
-    };
-
-    // ---- weight slices: unit u = tid + 512 i is block u % kSliceBlk of
-    // column u / kSliceBlk; columns past N re-read column N-1 and blocks
-    // past K block nb-1 (their X is zero) ----
-    struct WStage {
-        u32x4_t x[XP];          // X units
-        u32x4_t w[kWU];
-        uint16_t s0[kSU];       // Q4_0 d; affine s
-        uint16_t s1[kSU];       // affine b
-    };
-    auto w_load = [&](int sl, WStage& st) {
-        const int slc = sl < nslices ? sl : nslices - 1;
-#pragma unroll
-        for (int i = 0; i < kWU; i++) {
-            const int u = tid + i * kThreads;
-            const int c = u / kSliceBlk, b = u % kSliceBlk;
-            const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
-            const int kb = slc * kSliceBlk + b;
-            const int kbc = kb < nb ? kb : nb - 1;
-            if constexpr (WF == WF_Q4_0)
-                st.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                    reinterpret_cast<const uint8_t*>(a.a) + (n * nb + kbc) * 16));
-            else
-                st.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-                    reinterpret_cast<const uint8_t*>(a.a) + n * (a.K / 2) + (int64_t)kbc * 16));
-        }
-#pragma unroll
-        for (int i = 0; i < kSU; i++) {
-            const int u = tid + i * kThreads;
-            if (kNsc % kThreads == 0 || i * kThreads < kNsc) {     // whole waves: a uniform condition
-                const int uu = u < kNsc ? u : kNsc - 1;
-                if constexpr (WF == WF_Q4_0) {
-                    const int c = uu / kSliceBlk, b = uu % kSliceBlk;
-                    const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
-                    const int kb = slc * kSliceBlk + b;
-                    st.s0[i] = reinterpret_cast<const uint16_t*>(a.b)[n * nb + (kb < nb ? kb : nb - 1)];
-                } else {
-                    constexpr int kGs = kSliceBlk / 2;
-                    const int c = uu / kGs, gr = uu % kGs;
-                    const int64_t n = n0 + c < a.N ? n0 + c : a.N - 1;
-                    const int gi = slc * kGs + gr;
-                    const int64_t off = n * ng + (gi < ng ? gi : ng - 1);
-                    st.s0[i] = reinterpret_cast<const uint16_t*>(a.b)[off];
-                    st.s1[i] = reinterpret_cast<const uint16_t*>(a.c)[off];
-                }
-            }
-        }
-    };
-    auto w_store = [&](int sl, const WStage& st) {
-        uint8_t* wb = wsm + (sl & 1) * kWBufB;
-#pragma unroll
-        for (int i = 0; i < kWU; i++) {
-            const int u = tid + i * kThreads;
-            *reinterpret_cast<u32x4_t*>(wb + (u / kSliceBlk) * kColB + (u % kSliceBlk) * 16) = st.w[i];
-        }
-        uint16_t* sb = ssm + (sl & 1) * (kSBufB / 2);
-#pragma unroll
-        for (int i = 0; i < kSU; i++) {
-            const int u = tid + i * kThreads;
-            if (kNsc % kThreads == 0 || u < kNsc) {
-                sb[u] = st.s0[i];
-                if constexpr (WF == WF_AFFINE4) sb[kNsc + u] = st.s1[i];
-            }
-        }
-    };
-
-    floatx4_t acc[NT];
-#pragma unroll
-    for (int ni = 0; ni < NT; ni++) acc[ni] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    uint32_t mask = 0x000F000Fu;
-    asm volatile("" : "+v"(mask));
-    const floatx4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-
-    auto x_frag = [&](int sl, int t) {
-        const uint16_t* p = xs + (sl & 1) * kXBufH + xrow + (4 * wave + t) * 32;
-        SmX<WF> x;
-        if constexpr (WF == WF_Q4_0) {
-            x.lo = *reinterpret_cast<const u32x2_t*>(p + 4 * g);
-            x.hi = *reinterpret_cast<const u32x2_t*>(p + 16 + 4 * g);
-        } else {
-            x.v = *reinterpret_cast<const u32x4_t*>(p + 8 * g);
-        }
-        return sm_xfrag<WF>(x);
-    };
-    // dword g of block 4 wave + t of column ni*16 + j
-    auto w_word = [&](int sl, int ni, int t) {
-        return *reinterpret_cast<const uint32_t*>(wsm + (sl & 1) * kWBufB + (ni * 16 + j) * kColB +
-                                                  (4 * wave + t) * 16 + 4 * g);
-    };
-
-    auto compute = [&](int sl) {
-        const uint16_t* sb = ssm + (sl & 1) * (kSBufB / 2);
-        if constexpr (WF == WF_Q4_0) {
-            const bf16x8_t neg136 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u});
-            uint32_t dq[NT][2];
-#pragma unroll
-            for (int ni = 0; ni < NT; ni++) {
-                const u32x2_t dv = *reinterpret_cast<const u32x2_t*>(sb + (ni * 16 + j) * kSliceBlk + 4 * wave);
-                dq[ni][0] = dv[0];
-                dq[ni][1] = dv[1];
-            }
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const bf16x8_t xa = x_frag(sl, t);
-                const floatx4_t c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, neg136, zero4, 0, 0, 0);
-#pragma unroll
-                for (int ni = 0; ni < NT; ni++) {
-                    const bf16x8_t wb = sm_weights(w_word(sl, ni, t), mask);
-                    const float d = f16_to_f32(dq[ni][t >> 1] >> (16 * (t & 1)));
-                    const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wb, c0, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; v++) acc[ni][v] = __builtin_fmaf(d, dv[v], acc[ni][v]);
-                }
-            }
-        } else {
-            const bf16x8_t neg128 = __builtin_bit_cast(bf16x8_t, u32x4_t{0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u});
-            constexpr int kGs = kSliceBlk / 2;
-#pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const bf16x8_t xa0 = x_frag(sl, 2 * h);
-                const bf16x8_t xa1 = x_frag(sl, 2 * h + 1);
-                const floatx4_t cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    xa1, neg128, __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, neg128, zero4, 0, 0, 0), 0, 0, 0);
-#pragma unroll
-                for (int ni = 0; ni < NT; ni++) {
-                    const int si = (ni * 16 + j) * kGs + 2 * wave + h;
-                    const float sv = bf16_to_f32(sb[si]);
-                    const float bq = bf16_to_f32(sb[kNsc + si]) * -0.0078125f;   // b / -128 (exact)
-                    const bf16x8_t w0 = sm_weights(w_word(sl, ni, 2 * h), mask);
-                    const bf16x8_t w1 = sm_weights(w_word(sl, ni, 2 * h + 1), mask);
-                    const floatx4_t dv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        xa1, w1, __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa0, w0, cs, 0, 0, 0), 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; v++) {
-                        acc[ni][v] = __builtin_fmaf(sv, dv[v], acc[ni][v]);
-                        acc[ni][v] = __builtin_fmaf(bq, cs[v], acc[ni][v]);
-                    }
-                }
-            }
-        }
-    };
-
-    constexpr int kRing = ONE ? 4 : 2;
-    const int nsteps = (nslices + kRing - 1) / kRing * kRing;
-    WStage ring[kRing];        // slot r holds slices r, r + kRing, ...
-    auto slice_load = [&](int sl, WStage& st) {
-        x_load(sl, st.x);
-        w_load(sl, st);
-    };
-    auto slice_store = [&](int sl, const WStage& st) {
-        x_store(sl, st.x);
-        w_store(sl, st);
-    };
-    // Step sl multiplies slice sl from LDS, stores slice sl+1 from its ring
-    // slot into the other LDS buffers and refills the slot with slice
-    // sl+1+kRing.  Phases are fenced so that no work on loaded values (and
-    // so no wait) moves between them.
-    auto step = [&](int sl, auto last, auto r) {
-        constexpr bool kLast = decltype(last)::value;
-        constexpr int kR = decltype(r)::value;
-        constexpr bool kStore = !kLast || kR < kRing - 1;
-        constexpr int kNext = (kR + 1) % kRing;
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sl);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kStore) slice_store(sl + 1, ring[kNext]);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (!kLast) slice_load(sl + 1 + kRing, ring[kNext]);
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-    };
-    auto group = [&](int sl0, auto last) {
-        step(sl0 + 0, last, std::integral_constant<int, 0>{});
-        step(sl0 + 1, last, std::integral_constant<int, 1>{});
-        if constexpr (kRing == 4) {
-            step(sl0 + 2, last, std::integral_constant<int, 2>{});
-            step(sl0 + 3, last, std::integral_constant<int, 3>{});
-        }
-    };
-    // prologue: slices 0 .. kRing-1 requested; slice 0 stored and its slot
-    // refilled with slice kRing
-#pragma unroll
-    for (int r = 0; r < kRing; r++) slice_load(r, ring[r]);
-    slice_store(0, ring[0]);
-    if constexpr (!ONE) slice_load(kRing, ring[0]);
-    __syncthreads();
-    if constexpr (ONE) {
-        group(0, std::true_type{});
-    } else {
-        group(0, std::false_type{});
-        for (int sl = kRing; sl < nsteps - kRing; sl += kRing) group(sl, std::false_type{});
-        group(nsteps - kRing, std::true_type{});
-    }
-
-#pragma unroll
-    for (int ni = 0; ni < NT; ni++)
-#pragma unroll
-        for (int v = 0; v < 4; v++) red[wave * kTile + (ni * 4 + v) * 64 + lane] = acc[ni][v];
-    __syncthreads();
-    for (int i = tid; i < kTile; i += kThreads) {
-        float t = red[i];
-#pragma unroll
-        for (int w = 1; w < kSmWaves; w++) t += red[w * kTile + i];
-        const int l = i & 63;
-        const int v = (i >> 6) & 3;
-        const int ni = i >> 8;
-        const int r = 4 * (l >> 4) + v;
         const int n = n0 + ni * 16 + (l & 15);
         if (r < a.M && n < a.N) store_y(a.y, YDT, (int64_t)r * a.N + n, t);
     }
@@ -2457,14 +2132,10 @@ static void launch_vec_w(const GemmArgs& ga, int xdt, int ydt, hipStream_t s) {
 template <int WF, int MT, int NT, int YDT, int XP>
 static void launch_small_t(GemmArgs ga, hipStream_t s) {
     const dim3 grid((unsigned)((ga.N + NT * 16 - 1) / (NT * 16))), block(64 * kSmWaves);
-    const int nslices = (ga.K / 32 + 4 * kSmWaves - 1) / (4 * kSmWaves);
-    if constexpr (MT == 1) {
-        if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small1<WF, NT, YDT, XP, true>), grid, block, 0, s, ga);
-        else hipLaunchKernelGGL((k_gemm_small1<WF, NT, YDT, XP, false>), grid, block, 0, s, ga);
-    } else {
-        if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, true>), grid, block, 0, s, ga);
-        else hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, false>), grid, block, 0, s, ga);
-    }
+    const int slice_blk = 32 / MT;
+    const int nslices = (ga.K / 32 + slice_blk - 1) / slice_blk;
+    if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, true>), grid, block, 0, s, ga);
+    else hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, false>), grid, block, 0, s, ga);
 }
 
 // The widest column group (NT tiles of 16) that still gives every CU a
@@ -2477,13 +2148,14 @@ static void launch_small_n(GemmArgs ga, hipStream_t s) {
     else launch_small_t<WF, MT, 1, YDT, XP>(ga, s);
 }
 
-// Rows: one 16-row tile up to M = 16, two up to 32; X copy passes of 4 rows.
+// Rows: one 16-row tile up to M = 16 (X copy passes of 4 rows), two up to
+// 32 (passes of 8 rows).
 template <int WF, int YDT>
 static void launch_small_m(GemmArgs ga, hipStream_t s) {
     if (ga.M <= 4) launch_small_n<WF, 1, YDT, 1>(ga, s);
     else if (ga.M <= 8) launch_small_n<WF, 1, YDT, 2>(ga, s);
     else if (ga.M <= 16) launch_small_n<WF, 1, YDT, 4>(ga, s);
-    else launch_small_n<WF, 2, YDT, 8>(ga, s);
+    else launch_small_n<WF, 2, YDT, 4>(ga, s);
 }
 
 template <int WF>
