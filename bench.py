@@ -1,6 +1,6 @@
 """Benchmark of the 4-bit GEMV / GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections decode,gemm,affine,llama,cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections decode,gemm,affine,small,llama,cpu]
 
 A step is one decode token through the decode-GEMV workload (Q4_0 W
 [12288, 4096], one bf16 activation [1, 4096] ~ N(0,1)): q4_gemv_act on W and
@@ -385,6 +385,59 @@ def affine_section(iters: int):
 
 
 # ---------------------------------------------------------------------------
+# small M: q4_gemm / affine4_gemm on the skinny paths
+# ---------------------------------------------------------------------------
+
+SMALL_MS = (1, 2, 4, 8, 16, 32)
+
+
+def small_section(iters: int):
+    """q4_gemm and affine4_gemm at small M on the prefill weight shape (the
+    skinny paths: the vector kernel at M = 1, the bf16-MFMA kernel above),
+    against dequantise-to-bf16 + hipBLASLt.  Bound: HBM (weights + X + Y)."""
+    wl = synth.PREFILL
+    N, K = wl.N, wl.K
+    rng = np.random.default_rng(wl.seed)
+    W = synth.weights(rng, N, K)
+    wd = bf16_dev(W)
+    qs, d = B.q4_quantize(wd)
+    aq, asc, abi = B.affine4_quantize(wd)
+    del W, wd
+    # ten copies of each (283 MB) rotate so that the weights stream from HBM,
+    # not from the 256 MB last-level cache
+    copies = 10
+    q4c = [(qs.clone(), d.clone()) for _ in range(copies)]
+    afc = [(aq.clone(), asc.clone(), abi.clone()) for _ in range(copies)]
+    wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    out = []
+    for M in SMALL_MS:
+        X = synth.activations(rng, M, K)
+        x = bf16_dev(X)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        rec = {"M": M}
+        for name, wbytes, run, deq in (
+            ("q4_0", N * K // 2 + N * (K // 32) * 2,
+             lambda i: B.q4_gemm(*q4c[i % copies], x, y=y, workspace=None),
+             lambda i: B.q4_dequantize(*q4c[i % copies], out_dtype=torch.bfloat16, out=wbf)),
+            ("affine4", N * K // 2 + 2 * N * (K // 64) * 2,
+             lambda i: B.affine4_gemm(*afc[i % copies], x, y=y, workspace=None),
+             lambda i: B.affine4_dequantize(*afc[i % copies], out_dtype=torch.bfloat16, out=wbf)),
+        ):
+            fused = min(region_us(run, iters) for _ in range(2))
+            jit = region_us(deq, iters) + region_us(lambda i: torch.matmul(x, wbf.t(), out=y), iters)
+            byts = wbytes + M * K * 2 + M * N * 2
+            rec[name] = {"us": fused, "gbs": byts / (fused * 1e-6) / 1e9,
+                         "roofline_frac": byts / (fused * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "dequant_bf16_hipblaslt_us": jit, "beats_dequant_then_gemm": fused < jit}
+        out.append(rec)
+        log(f"[small] M={M}: q4_0 {rec['q4_0']['us']:.2f} us ({rec['q4_0']['roofline_frac']:.2f}), "
+            f"affine4 {rec['affine4']['us']:.2f} us ({rec['affine4']['roofline_frac']:.2f}); "
+            f"dequant+hipBLASLt {rec['q4_0']['dequant_bf16_hipblaslt_us']:.1f} / "
+            f"{rec['affine4']['dequant_bf16_hipblaslt_us']:.1f} us")
+    return {"N": N, "K": K, "copies": copies, "sweep": out}
+
+
+# ---------------------------------------------------------------------------
 # Llama-3.2-1B-shaped 16-layer stack
 # ---------------------------------------------------------------------------
 
@@ -509,8 +562,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=20,
                     help="distinct weight copies rotated through (>= 19 keeps the 256 MB cache out)")
-    ap.add_argument("--sections", default="decode,gemm,affine,llama,cpu",
-                    help="comma list of decode (always run), gemm, affine, llama, cpu, calib")
+    ap.add_argument("--sections", default="decode,gemm,affine,small,llama,cpu",
+                    help="comma list of decode (always run), gemm, affine, small, llama, cpu, calib")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -527,6 +580,8 @@ def main():
         extra["gemm_m2048"] = gemm_section(20)
     if "affine" in sections:
         extra["affine4_sweep"] = affine_section(20)
+    if "small" in sections:
+        extra["small_m"] = small_section(100)
     if "llama" in sections:
         extra["llama1b_stack"] = llama_section(20)
     if "calib" in sections:
