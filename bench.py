@@ -483,14 +483,52 @@ def llama_section(iters: int):
     wsn = max(B.q4_gemm_workspace_size(Mp, n, k) for (n, k) in synth.LLAMA1B_SHAPES.values())
     ws = torch.empty(max(wsn, 16), dtype=torch.uint8, device="cuda")
 
-    def prefill(_i):
-        for lw in layers:
-            for name in ("q", "k", "v", "o", "gate", "up", "down"):
-                qs, d = lw[name]
-                n = d.shape[0]
-                k = d.shape[1] * 32
-                B.q4_gemm(qs, d, xp[k], y=yp[n], workspace=ws)
+    names = ("q", "k", "v", "o", "gate", "up", "down")
 
+    def prefill_per_call(_i):
+        # q4_gemm on the raw planes: each call also repacks the weights
+        for lw in layers:
+            for name in names:
+                qs, d = lw[name]
+                B.q4_gemm(qs, d, xp[d.shape[1] * 32], y=yp[d.shape[0]], workspace=ws)
+
+    # weights prepared once, as a model loader would (q4_pack_weight_image);
+    # the workspace has room for the split-K partial results of the small
+    # matrices
+    images = [{name: B.q4_pack_weight_image(*lw[name]) for name in names} for lw in layers]
+
+    def prefill_separate(_i):
+        for lw, im in zip(layers, images):
+            for name in names:
+                n, kb = lw[name][1].shape
+                B.q4_gemm_image(im[name], xp[kb * 32], n, y=yp[n], workspace=ws)
+
+    # the loader's usual fusion for prefill: q|k|v and gate|up concatenated
+    # along N into one weight each (the Q4_0 planes stacked by rows), so a
+    # layer is four GEMMs: qkv [3072 x 2048], o, gate|up [16384 x 2048], down
+    def stack(names_):
+        return (torch.cat([lw_[n_][0] for n_ in names_]), torch.cat([lw_[n_][1] for n_ in names_]))
+    fused = []
+    for lw_ in layers:
+        fused.append({"qkv": B.q4_pack_weight_image(*stack(("q", "k", "v"))),
+                      "o": images[len(fused)]["o"],
+                      "gateup": B.q4_pack_weight_image(*stack(("gate", "up"))),
+                      "down": images[len(fused)]["down"]})
+    yqkv_p = torch.empty((Mp, 3072), dtype=torch.bfloat16, device="cuda")
+    ygu_p = torch.empty((Mp, 16384), dtype=torch.bfloat16, device="cuda")
+    wsf = torch.empty(max(B.q4_gemm_workspace_size(Mp, n, k) for (n, k) in ((3072, H), (2048, H), (16384, H), (2048, F))),
+                      dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def prefill(_i):
+        for fm in fused:
+            B.q4_gemm_image(fm["qkv"], xp[H], 3072, y=yqkv_p, workspace=wsf)
+            B.q4_gemm_image(fm["o"], xp[H], 2048, y=yp[2048], workspace=wsf)
+            B.q4_gemm_image(fm["gateup"], xp[H], 16384, y=ygu_p, workspace=wsf)
+            B.q4_gemm_image(fm["down"], xp[F], 2048, y=yp[2048], workspace=wsf)
+
+    prefill_call_ms = region_us(prefill_per_call, max(3, iters // 4)) * 1e-3
+    prefill_sep_ms = region_us(prefill_separate, max(3, iters // 4)) * 1e-3
     prefill_ms = region_us(prefill, max(3, iters // 4)) * 1e-3
     res = {
         "decode_tokens_per_s": 1e3 / decode_ms,
@@ -498,12 +536,22 @@ def llama_section(iters: int):
         "decode_weight_gbs": total_bytes / (decode_ms * 1e-3) / 1e9,
         "prefill_tokens_per_s": Mp * 1e3 / prefill_ms,
         "prefill_tflops": flop512 / (prefill_ms * 1e-3) / 1e12,
+        "prefill_separate_matrices_tokens_per_s": Mp * 1e3 / prefill_sep_ms,
+        "prefill_separate_matrices_tflops": flop512 / (prefill_sep_ms * 1e-3) / 1e12,
+        "prefill_repacking_per_call_tokens_per_s": Mp * 1e3 / prefill_call_ms,
+        "prefill_repacking_per_call_tflops": flop512 / (prefill_call_ms * 1e-3) / 1e12,
         "weights_bytes": total_bytes,
         "launches": "decode: one HIP graph per token, 4 GEMV launches per layer (q4_gemv_multi_act on q/k/v, "
-                    "q4_gemv_act, q4_gemv_fused2_act); prefill: eager q4_gemm launches queued back to back",
+                    "q4_gemv_act, q4_gemv_fused2_act); prefill: eager q4_gemm_image launches on weight images "
+                    "prepared once (q|k|v and gate|up stacked into one weight each: 4 GEMMs per layer), queued "
+                    "back to back; also the 7 separate matrices on images, and q4_gemm repacking every call",
     }
     log(f"[llama] decode {res['decode_tokens_per_s']:.0f} tok/s ({res['decode_weight_gbs']:.0f} GB/s); "
-        f"prefill {res['prefill_tokens_per_s']:.0f} tok/s ({res['prefill_tflops']:.0f} TFLOP/s)")
+        f"prefill {res['prefill_tokens_per_s']:.0f} tok/s ({res['prefill_tflops']:.0f} TFLOP/s), "
+        f"separate matrices {res['prefill_separate_matrices_tokens_per_s']:.0f} tok/s "
+        f"({res['prefill_separate_matrices_tflops']:.0f} TFLOP/s), "
+        f"repacking per call {res['prefill_repacking_per_call_tokens_per_s']:.0f} tok/s "
+        f"({res['prefill_repacking_per_call_tflops']:.0f} TFLOP/s)")
     return res
 
 

@@ -406,10 +406,16 @@ int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* 
     if (rc) return rc;
     if (M == 0 || N == 0) return Q4_OK;
     if ((rc = check_ptrs_aligned({image, x, y}))) return rc;
-    if (workspace == nullptr || workspace_bytes < q4::x_image_bytes(M, K)) return Q4_ERR_WORKSPACE;
+    const int64_t ximg = q4::x_image_bytes(M, K);
+    if (workspace == nullptr || workspace_bytes < ximg) return Q4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q4_ERR_ALIGN;
     const int wf = fmt == Q4_FMT_Q4_0 ? q4::WF_Q4_0 : q4::WF_AFFINE4;
-    return hip_status(q4::launch_gemm_image(wf, image, x, x_dtype, y, y_dtype, M, N, K, workspace, as_stream(stream)));
+    // room for the split-K partial results after the X image: split small tile counts
+    const int64_t part = q4::splitk_bytes(M, N, K);
+    float* pp = (part > 0 && workspace_bytes >= ximg + part)
+                    ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ximg) : nullptr;
+    return hip_status(q4::launch_gemm_image(wf, image, x, x_dtype, y, y_dtype, M, N, K, workspace, pp,
+                                            as_stream(stream)));
 }
 
 int dense_gemm(const void* x, int x_dtype, const uint16_t* w_f16, void* y, int y_dtype, int64_t M, int64_t N,

@@ -150,6 +150,8 @@ struct GemmArgs {
     int M, N, K;
     int m_tiles;       // workgroup tiles along M
     int n_tiles;       // workgroup tiles along N
+    int ksplit;        // k_gemm_pk: K parts per tile (<= 1: none)
+    float* part;       // k_gemm_pk with ksplit > 1: fp32 partial results [ksplit][M][N]
 };
 
 __device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
@@ -863,18 +865,25 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // Persistent: workgroup b runs tiles b, b + G, b + 2G, ... (G = gridDim.x)
-    // as one stream of K steps: global step s is step s % nsteps of the
-    // workgroup's tile s / nsteps.  Tile t covers rows (t % m_tiles) * 128 and
-    // columns (t / m_tiles) * 256.
+    // Persistent: workgroup b runs the work units b, b + G, b + 2G, ...
+    // (G = gridDim.x) as one stream of K steps: global step s is step s % ust
+    // of the workgroup's unit s / ust.  Unit u is part u % ksplit (K steps
+    // p*ust .. p*ust + ust - 1) of tile u / ksplit; tile t covers rows
+    // (t % m_tiles) * 128 and columns (t / m_tiles) * 256.  With ksplit > 1
+    // each part writes its fp32 tile to the partial buffer, and a second
+    // kernel sums the parts in order.
     const int G = gridDim.x;
-    const int ntiles = a.m_tiles * a.n_tiles;
-    const int my_tiles = (ntiles - (int)blockIdx.x + G - 1) / G;
+    const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
+    const int nunits = a.m_tiles * a.n_tiles * ksplit;
+    const int my_units = (nunits - (int)blockIdx.x + G - 1) / G;
     const int nb = a.K / 32;
-    const int nsteps = (nb + 1) / 2;
-    const int S = my_tiles * nsteps;
-    auto tile_m0 = [&](int i) { return ((int)blockIdx.x + i * G) % a.m_tiles * kRows; };
-    auto tile_n0 = [&](int i) { return ((int)blockIdx.x + i * G) / a.m_tiles * kCols; };
+    const int nsteps = (nb + 1) / 2;                 // K steps of a tile
+    const int ust = nsteps / ksplit;                 // of a unit (ksplit divides nsteps)
+    const int S = my_units * ust;
+    auto unit_of = [&](int i) { return (int)blockIdx.x + i * G; };
+    auto tile_m0 = [&](int i) { return unit_of(i) / ksplit % a.m_tiles * kRows; };
+    auto tile_n0 = [&](int i) { return unit_of(i) / ksplit / a.m_tiles * kCols; };
+    auto part_of = [&](int i) { return unit_of(i) % ksplit; };
 
     if (wave < 4) {
         // ------------------------------ consumer ------------------------------
@@ -1034,7 +1043,15 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                         const int row = m0 + mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3) + (odd ? 1 : 0);
                         if (row >= a.M || col >= a.N) continue;
                         const int64_t off = (int64_t)row * a.N + col;
-                        if constexpr (YDT == DT_BF16) {
+                        if (ksplit > 1) {
+                            float* yp = a.part + (int64_t)part_of(i) * a.M * a.N + off;
+                            if (pair_ok && col + 1 < a.N) {
+                                *reinterpret_cast<f32x2_t*>(yp) = f32x2_t{lo, hi};
+                            } else {
+                                yp[0] = lo;
+                                if (col + 1 < a.N) yp[1] = hi;
+                            }
+                        } else if constexpr (YDT == DT_BF16) {
                             uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + off;
                             if (pair_ok && col + 1 < a.N) {
                                 const f32x2_t f = {lo, hi};
@@ -1071,10 +1088,10 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
             dequant(0, r, bfA);
             read_a(0, 0, a0);
         }
-        // kl: local index of the current step in its tile, ti: local tile
+        // kl: local index of the current step in its unit, ti: local unit
         int kl = 0, ti = 0;
         auto end_step = [&]() {
-            if (kl + 1 == nsteps) {
+            if (kl + 1 == ust) {
                 epilogue(ti);
                 ti++;
                 kl = 0;
@@ -1109,14 +1126,15 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
         // copies pw, pw + 4, ...: 7 for wave 0, 6 for the others
         constexpr int kCopies = 16 + kWChunk / 1024;
         const int my_copies = (kCopies - pw + kPkProducers - 1) / kPkProducers;
-        // the next step to request: global index rs = ri * nsteps + rk
+        // the next step to request: global index rs = ri * ust + rk
         int rs = 0, ri = 0, rk = 0;
         auto copy_next = [&]() {
             PkSlot& sl = lds.slot[rs % kPkSlots];
             const int mt_idx = tile_m0(ri) / kRows;
             const int nt_idx = tile_n0(ri) / kCols;
-            const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)mt_idx * nsteps + rk) * (kImgTile * 2);
-            const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)nt_idx * nsteps + rk) * kWChunk;
+            const int kg = part_of(ri) * ust + rk;      // K step within the tile
+            const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)mt_idx * nsteps + kg) * (kImgTile * 2);
+            const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)nt_idx * nsteps + kg) * kWChunk;
 #pragma unroll
             for (int i = 0; i < (kCopies + kPkProducers - 1) / kPkProducers; i++) {
                 const int c = pw + kPkProducers * i;
@@ -1124,7 +1142,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                 else if (c < kCopies) dma16(wsrc + (c - 16) * 1024 + lane * 16, sl.w + (c - 16) * 1024);
             }
             rs++;
-            if (++rk == nsteps) {
+            if (++rk == ust) {
                 rk = 0;
                 ri++;
             }
@@ -1803,7 +1821,10 @@ int64_t x_image_bytes(int64_t M, int64_t K) {
 
 int64_t weight_image_bytes(int64_t N, int64_t K) { return (N + 255) / 256 * ((K + 63) / 64) * (int64_t)kWChunk; }
 
-int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K) { return x_image_bytes(M, K) + weight_image_bytes(N, K); }
+int64_t splitk_bytes(int64_t M, int64_t N, int64_t K);
+int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K) {
+    return x_image_bytes(M, K) + weight_image_bytes(N, K) + splitk_bytes(M, N, K);
+}
 
 template <int WF, int XDT>
 static void launch_pack_t(const GemmArgs& ga, uint16_t* img, hipStream_t s) {
@@ -1822,19 +1843,75 @@ static void launch_pack_w_t(const void* a, const void* b, const void* c, int N, 
                        static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(c), wimg, N, K, n_tiles, ksteps);
 }
 
-// X image into ximg, then the GEMM on it and the weight image ga.a.
+// Y = the sum of the ksplit fp32 partial results, in part order; 4 outputs
+// per thread.
+template <int YDT>
+__global__ __launch_bounds__(256) void k_splitk_sum(const float* __restrict__ part, int ksplit, int64_t mn,
+                                                     void* __restrict__ y) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= mn) return;
+    if (e + 4 <= mn && (mn & 3) == 0) {        // every part's 4 values 16-byte aligned
+        floatx4_t t = *reinterpret_cast<const floatx4_t*>(part + e);
+        for (int p = 1; p < ksplit; p++) t += *reinterpret_cast<const floatx4_t*>(part + (int64_t)p * mn + e);
+        if constexpr (YDT == DT_BF16) {
+            const f32x2_t lo = {t[0], t[1]}, hi = {t[2], t[3]};
+            const u32x2_t v = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+                               __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t))};
+            *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint16_t*>(y) + e) = v;
+        } else {
+            *reinterpret_cast<floatx4_t*>(reinterpret_cast<float*>(y) + e) = t;
+        }
+    } else {
+        for (int64_t i = e; i < mn; i++) {
+            float t = part[i];
+            for (int p = 1; p < ksplit; p++) t += part[(int64_t)p * mn + i];
+            store_y(y, YDT, i, t);
+        }
+    }
+}
+
+// K parts per tile of k_gemm_pk: split only when fewer than half the CUs
+// would get a tile, into the most parts that divide the tile's K steps,
+// leave at least 4 of them per part and keep the parts within the CU count.
+static int splitk_parts(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + kImgRows - 1) / kImgRows) * ((N + 255) / 256);
+    const int64_t nsteps = (K + 63) / 64;
+    const int64_t cus = current_cu_count();
+    if (tiles * 2 > cus) return 1;
+    int best = 1;
+    for (int d = 2; d <= 16; d++)
+        if (nsteps % d == 0 && nsteps / d >= 4 && tiles * d <= cus) best = d;
+    return best;
+}
+
+int64_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
+    const int d = splitk_parts(M, N, K);
+    return d > 1 ? (int64_t)d * M * N * 4 : 0;
+}
+
+// X image into ximg, then the GEMM on it and the weight image ga.a; with a
+// partial buffer (splitk_bytes(M, N, K) bytes, or nullptr) small tile counts
+// are split along K.
 template <int WF>
-static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, hipStream_t s) {
+static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, float* part, hipStream_t s) {
     ga.m_tiles = (ga.M + kImgRows - 1) / kImgRows;
     ga.n_tiles = (ga.N + 255) / 256;
     if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
     else launch_pack_t<WF, DT_F32>(ga, ximg, s);
     ga.x = ximg;
+    ga.ksplit = part != nullptr ? splitk_parts(ga.M, ga.N, ga.K) : 1;
+    ga.part = part;
     const int cus = current_cu_count();
-    const int tiles = ga.m_tiles * ga.n_tiles;
-    const dim3 grid((unsigned)(tiles < cus ? tiles : cus)), block(256 + 64 * kPkProducers);
+    const int units = ga.m_tiles * ga.n_tiles * ga.ksplit;
+    const dim3 grid((unsigned)(units < cus ? units : cus)), block(256 + 64 * kPkProducers);
     if (ydt == DT_BF16) hipLaunchKernelGGL((k_gemm_pk<WF, DT_BF16>), grid, block, 0, s, ga);
     else hipLaunchKernelGGL((k_gemm_pk<WF, DT_F32>), grid, block, 0, s, ga);
+    if (ga.ksplit > 1) {
+        const int64_t mn = (int64_t)ga.M * ga.N;
+        const dim3 g2((unsigned)((mn / 4 + 1 + 255) / 256)), b2(256);
+        if (ydt == DT_BF16) hipLaunchKernelGGL((k_splitk_sum<DT_BF16>), g2, b2, 0, s, part, ga.ksplit, mn, ga.y);
+        else hipLaunchKernelGGL((k_splitk_sum<DT_F32>), g2, b2, 0, s, part, ga.ksplit, mn, ga.y);
+    }
 }
 
 hipError_t launch_pack_weight_image(int wfmt, const void* a, const void* b, const void* c, int64_t N, int64_t K,
@@ -1846,24 +1923,27 @@ hipError_t launch_pack_weight_image(int wfmt, const void* a, const void* b, cons
 }
 
 hipError_t launch_gemm_image(int wfmt, const void* wimg, const void* x, int xdt, void* y, int ydt, int64_t M,
-                             int64_t N, int64_t K, void* ximg, hipStream_t s) {
+                             int64_t N, int64_t K, void* ximg, float* part, hipStream_t s) {
     GemmArgs ga{};
     ga.a = wimg; ga.x = x; ga.y = y;
     ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
-    if (wfmt == WF_Q4_0) launch_on_images<WF_Q4_0>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), s);
-    else if (wfmt == WF_AFFINE4) launch_on_images<WF_AFFINE4>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), s);
+    if (wfmt == WF_Q4_0) launch_on_images<WF_Q4_0>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), part, s);
+    else if (wfmt == WF_AFFINE4) launch_on_images<WF_AFFINE4>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), part, s);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-// Both images in one workspace: the X image first, the weight image after it.
+// One workspace: the X image, the weight image, then the split-K partial
+// results when the tile count calls for them.
 hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
                               int ydt, int64_t M, int64_t N, int64_t K, void* img, hipStream_t s) {
     if (wfmt != WF_Q4_0 && wfmt != WF_AFFINE4) return hipErrorInvalidValue;
     uint8_t* wimg = static_cast<uint8_t*>(img) + x_image_bytes(M, K);
+    uint8_t* part = wimg + weight_image_bytes(N, K);
     hipError_t e = launch_pack_weight_image(wfmt, a, b, c, N, K, wimg, s);
     if (e != hipSuccess) return e;
-    return launch_gemm_image(wfmt, wimg, x, xdt, y, ydt, M, N, K, img, s);
+    return launch_gemm_image(wfmt, wimg, x, xdt, y, ydt, M, N, K, img,
+                             splitk_bytes(M, N, K) > 0 ? reinterpret_cast<float*>(part) : nullptr, s);
 }
 
 template <int WF, int MT, int NT, int XDT, int YDT>

@@ -263,8 +263,13 @@ int q4_gemv_multi_act(int nmat, const uint8_t* const* w_qs, const uint16_t* cons
  *               fastest path.  The MFMA path uses them for tile images of X
  *               (binary16) and of the weights (the same Q4_0 / affine blocks,
  *               regrouped per 256-column tile and 64-wide K step) that its
- *               matrix-core kernel copies straight into LDS; with less it
- *               converts X inside the GEMM (slower, same results).  The DEQUANT_GEMM path needs N*K*2 bytes for the
+ *               matrix-core kernel copies straight into LDS, and, when the
+ *               output has too few 128x256 tiles to occupy the GPU, for the
+ *               fp32 partial results of a K-split (each tile's K range spread
+ *               over up to 16 workgroups, the parts then summed in order:
+ *               deterministic, rounding order differs from an unsplit call);
+ *               with less it converts X inside the GEMM (slower, results
+ *               within the same bound).  The DEQUANT_GEMM path needs N*K*2 bytes for the
  *               dequantised weights: the automatic dispatch picks it only
  *               with that much, and forcing it without returns
  *               Q4_ERR_WORKSPACE.  Calls that share a workspace must not run
@@ -289,8 +294,11 @@ int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
 /*
  * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
  * 0 for SKINNY; for MFMA the X and weight tile images,
- * ceil(M/128)*128 * ceil(K/64)*64 * 2 + ceil(N/256) * ceil(K/64) * 9216 bytes;
- * for DEQUANT_GEMM N*K*2 (a dense binary16 W).
+ * ceil(M/128)*128 * ceil(K/64)*64 * 2 + ceil(N/256) * ceil(K/64) * 9216 bytes,
+ * plus parts*M*N*4 for the K-split partial results when the tile count is
+ * below half the device's CU count (parts: the most, up to 16, that divide
+ * ceil(K/64), leave at least 4 K steps each and keep tiles*parts within the
+ * CU count); for DEQUANT_GEMM N*K*2 (a dense binary16 W).
  * Returns 0 for invalid arguments.
  */
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt);
@@ -320,11 +328,14 @@ int q4_pack_weight_image(int fmt, const uint8_t* w_q, const uint16_t* w_s, const
 /*
  * q4_gemm_image -- Y = X . dequant(W)^T on the matrix-core path from a
  * weight image: the same results as q4_gemm / affine4_gemm on the MFMA path
- * with a workspace, for any M >= 1.
+ * with a workspace of the same size, for any M >= 1.
  *   workspace : device scratch for the X image, at least
  *               q4_gemm_image_workspace_size(M, K) =
  *               ceil(M/128)*128 * ceil(K/64)*64 * 2 bytes (else
- *               Q4_ERR_WORKSPACE).  Calls sharing it must not overlap.
+ *               Q4_ERR_WORKSPACE).  With room after it for the K-split
+ *               partial results (q4_gemm_workspace_size(M, N, K, fmt) bytes
+ *               are always enough), a launch with few tiles is split along
+ *               K as in q4_gemm.  Calls sharing it must not overlap.
  */
 int64_t q4_gemm_image_workspace_size(int64_t M, int64_t K);
 int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* y, int y_dtype,

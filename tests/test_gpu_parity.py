@@ -428,7 +428,8 @@ def test_q4_gemm_every_path_boundary_m(M):
                                        ("affine", 160, 640, 1024), ("affine", 129, 300, 128)])
 def test_gemm_image_equals_mfma_path(fmt, M, N, K):
     """A prepacked weight image gives the bits of q4_gemm / affine4_gemm on the
-    matrix-core path with a workspace, call after call with new activations."""
+    matrix-core path with a workspace, call after call with new activations
+    (these shapes have few tiles, so both split K)."""
     say(f"gemm_image {fmt} M={M} N={N} K={K}")
     rng = np.random.default_rng(M + N + K)
     W = synth.weights(rng, N, K)
@@ -441,14 +442,16 @@ def test_gemm_image_equals_mfma_path(fmt, M, N, K):
         run = lambda x, ws, ydt: B.affine4_gemm(*planes, x, y_dtype=ydt, workspace=ws)
         f = B.Q4_FMT_AFFINE4
     image = B.q4_pack_weight_image(*planes, fmt=f)
-    ws = torch.empty(B.lib().q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
     B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
     try:
+        ws = torch.empty(B.lib().q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
         for call in range(2):
             x = bf16_dev(synth.activations(rng, M, K))
             for ydt in (torch.bfloat16, torch.float32):
                 want = run(x, ws, ydt)
-                got = B.q4_gemm_image(image, x, N, fmt=f, y_dtype=ydt)
+                # the same workspace size: room for the split-K partial results
+                # of small tile counts, so both paths split alike
+                got = B.q4_gemm_image(image, x, N, fmt=f, y_dtype=ydt, workspace=ws)
                 assert torch.equal(got, want), (fmt, M, N, K, call, ydt)
     finally:
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
