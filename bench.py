@@ -345,6 +345,7 @@ def affine_section(iters: int):
     wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
     B.affine4_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf)
+    image = B.q4_pack_weight_image(q, s, b)        # weights prepared once
     out = []
     for M in synth.AFFINE_MS:
         W_, X = synth.workload_inputs(wl, M=M)
@@ -355,6 +356,12 @@ def affine_section(iters: int):
         ws = torch.empty(wsn, dtype=torch.uint8, device="cuda") if wsn else None
         it = max(5, min(iters, int(2000 / max(1, M // 32))))
         fused = region_us(lambda i: B.affine4_gemm(q, s, b, x, y=y, workspace=ws), it) * 1e-3
+        fused_img = None
+        if M > 32:      # the matrix-core path (smaller M takes the skinny kernels, which need no image)
+            wsi = torch.empty(max(B.q4_gemm_workspace_size(M, N, K, B.Q4_FMT_AFFINE4), 16), dtype=torch.uint8,
+                              device="cuda")
+            fused_img = region_us(lambda i: B.q4_gemm_image(image, x, N, fmt=B.Q4_FMT_AFFINE4, y=y, workspace=wsi),
+                                  it) * 1e-3
         deq16 = region_us(lambda i: B.affine4_dequantize(q, s, b, out=w16), it) * 1e-3
         deqbf = region_us(lambda i: B.affine4_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf), it) * 1e-3
         ref = region_us(lambda i: torch.matmul(x, wbf.t(), out=y), it) * 1e-3
@@ -364,7 +371,8 @@ def affine_section(iters: int):
         t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flop / (F16_MFMA_PEAK_TFLOPS * 1e12))
         rec = {
             "M": M,
-            "fused_us": fused * 1e3,
+            "fused_us": fused * 1e3,                   # affine4_gemm per call (repacks the weights at M > 32)
+            "fused_prepared_image_us": fused_img * 1e3 if fused_img is not None else fused * 1e3,
             "jit_us": (deqbf + ref) * 1e3,            # dequantise to bf16 + hipBLASLt bf16
             "ref_us": ref * 1e3,                       # hipBLASLt on pre-dequantised bf16 W
             "dequant_dense_f16_us": (deq16 + dense) * 1e3,
@@ -372,16 +380,16 @@ def affine_section(iters: int):
             "gbs": byts / (fused * 1e-3) / 1e9,
             "roofline_frac": t_roof / (fused * 1e-3),
             "fused_beats_jit": fused < deqbf + ref,
+            "fused_prepared_image_beats_jit": (fused_img if fused_img is not None else fused) < deqbf + ref,
         }
         out.append(rec)
-        log(f"[affine] M={M}: fused {rec['fused_us']:.1f} us, jit {rec['jit_us']:.1f} us, "
+        log(f"[affine] M={M}: fused {rec['fused_us']:.1f} us (prepared image {rec['fused_prepared_image_us']:.1f}), "
+            f"jit {rec['jit_us']:.1f} us, "
             f"ref {rec['ref_us']:.1f} us, roofline {rec['roofline_frac']:.2f}")
-    crossover = None
-    for rec in out:
-        if not rec["fused_beats_jit"]:
-            crossover = rec["M"]
-            break
-    return {"sweep": out, "first_M_where_dequant_then_gemm_wins": crossover}
+    crossover = next((rec["M"] for rec in out if not rec["fused_beats_jit"]), None)
+    crossover_img = next((rec["M"] for rec in out if not rec["fused_prepared_image_beats_jit"]), None)
+    return {"sweep": out, "first_M_where_dequant_then_gemm_wins": crossover,
+            "first_M_where_dequant_then_gemm_wins_over_prepared_images": crossover_img}
 
 
 # ---------------------------------------------------------------------------

@@ -851,7 +851,7 @@ struct PkLds {
     PkSlot slot[kPkSlots];
 };
 
-template <int WF, int YDT>
+template <int WF, int YDT, bool SPLIT>
 __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const GemmArgs a) {
     static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
     constexpr int MT = 4, NT = 2;
@@ -873,7 +873,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
     // each part writes its fp32 tile to the partial buffer, and a second
     // kernel sums the parts in order.
     const int G = gridDim.x;
-    const int ksplit = a.ksplit > 1 ? a.ksplit : 1;
+    const int ksplit = SPLIT ? a.ksplit : 1;        // a compile-time 1 without a split
     const int nunits = a.m_tiles * a.n_tiles * ksplit;
     const int my_units = (nunits - (int)blockIdx.x + G - 1) / G;
     const int nb = a.K / 32;
@@ -1043,7 +1043,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                         const int row = m0 + mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3) + (odd ? 1 : 0);
                         if (row >= a.M || col >= a.N) continue;
                         const int64_t off = (int64_t)row * a.N + col;
-                        if (ksplit > 1) {
+                        if constexpr (SPLIT) {
                             float* yp = a.part + (int64_t)part_of(i) * a.M * a.N + off;
                             if (pair_ok && col + 1 < a.N) {
                                 *reinterpret_cast<f32x2_t*>(yp) = f32x2_t{lo, hi};
@@ -1904,8 +1904,13 @@ static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, floa
     const int cus = current_cu_count();
     const int units = ga.m_tiles * ga.n_tiles * ga.ksplit;
     const dim3 grid((unsigned)(units < cus ? units : cus)), block(256 + 64 * kPkProducers);
-    if (ydt == DT_BF16) hipLaunchKernelGGL((k_gemm_pk<WF, DT_BF16>), grid, block, 0, s, ga);
-    else hipLaunchKernelGGL((k_gemm_pk<WF, DT_F32>), grid, block, 0, s, ga);
+    if (ga.ksplit > 1) {
+        if (ydt == DT_BF16) hipLaunchKernelGGL((k_gemm_pk<WF, DT_BF16, true>), grid, block, 0, s, ga);
+        else hipLaunchKernelGGL((k_gemm_pk<WF, DT_F32, true>), grid, block, 0, s, ga);
+    } else {
+        if (ydt == DT_BF16) hipLaunchKernelGGL((k_gemm_pk<WF, DT_BF16, false>), grid, block, 0, s, ga);
+        else hipLaunchKernelGGL((k_gemm_pk<WF, DT_F32, false>), grid, block, 0, s, ga);
+    }
     if (ga.ksplit > 1) {
         const int64_t mn = (int64_t)ga.M * ga.N;
         const dim3 g2((unsigned)((mn / 4 + 1 + 255) / 256)), b2(256);
