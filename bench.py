@@ -107,6 +107,32 @@ def region_us(fn, n: int, warmup: int = 3, hold_us: float | None = None) -> floa
     return s.elapsed_time(e) * 1e3 / n
 
 
+def steady_us(fn, n: int, busy_ms: float = 150.0) -> float:
+    """Mean microseconds per call of fn(i), i < n, in steady state: the same
+    calls run back to back for about busy_ms first and the timed calls follow
+    with no idle gap.  For long compute-bound kernels: after an idle or
+    spinning GPU the clock takes milliseconds to settle under the power limit,
+    which a short region behind a hold would include.  The host must queue a
+    call faster than the GPU runs it (true above some tens of microseconds)."""
+    fn(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(3):
+        fn(i % n)
+    torch.cuda.synchronize()
+    one = max((time.perf_counter() - t0) / 3, 1e-6)
+    for i in range(max(1, int(busy_ms * 1e-3 / one))):
+        fn(i % n)
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(n):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / n
+
+
 def graph_of(fns, stream):
     """A HIP graph of the launches made by fns() on `stream`."""
     g = torch.cuda.CUDAGraph()
@@ -292,22 +318,22 @@ def gemm_section(iters: int):
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
     flop = 2.0 * M * N * K
-    fused_ms = region_us(lambda i: B.q4_gemm(qs, d, x, y=y, workspace=ws), iters) * 1e-3
+    fused_ms = steady_us(lambda i: B.q4_gemm(qs, d, x, y=y, workspace=ws), iters) * 1e-3
     # the same matrix-core GEMM on a weight image prepared once
     image = B.q4_pack_weight_image(qs, d)
     xws = torch.empty(B.lib().q4_gemm_image_workspace_size(M, K), dtype=torch.uint8, device="cuda")
-    image_ms = region_us(lambda i: B.q4_gemm_image(image, x, N, y=y, workspace=xws), iters) * 1e-3
+    image_ms = steady_us(lambda i: B.q4_gemm_image(image, x, N, y=y, workspace=xws), iters) * 1e-3
     # dequantise-then-GEMM: our dequantiser, then (a) the library's dense MFMA
     # GEMM on fp16 W, (b) hipBLASLt through torch on bf16 W (the pages' "jit")
     w16 = torch.empty((N, K), dtype=torch.float16, device="cuda")
     wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
-    deq16_ms = region_us(lambda i: B.q4_dequantize(qs, d, out=w16), iters) * 1e-3
-    deqbf_ms = region_us(lambda i: B.q4_dequantize(qs, d, out_dtype=torch.bfloat16, out=wbf), iters) * 1e-3
-    dense_ms = region_us(lambda i: B.dense_gemm(x, w16, y=y), iters) * 1e-3
-    blas_bf16_ms = region_us(lambda i: torch.matmul(x, wbf.t(), out=y), iters) * 1e-3
+    deq16_ms = steady_us(lambda i: B.q4_dequantize(qs, d, out=w16), iters) * 1e-3
+    deqbf_ms = steady_us(lambda i: B.q4_dequantize(qs, d, out_dtype=torch.bfloat16, out=wbf), iters) * 1e-3
+    dense_ms = steady_us(lambda i: B.dense_gemm(x, w16, y=y), iters) * 1e-3
+    blas_bf16_ms = steady_us(lambda i: torch.matmul(x, wbf.t(), out=y), iters) * 1e-3
     x16 = x.to(torch.float16)
     y16 = torch.empty((M, N), dtype=torch.float16, device="cuda")
-    blas_f16_ms = region_us(lambda i: torch.matmul(x16, w16.t(), out=y16), iters) * 1e-3
+    blas_f16_ms = steady_us(lambda i: torch.matmul(x16, w16.t(), out=y16), iters) * 1e-3
     best_deq = deq16_ms + min(dense_ms, blas_f16_ms)
     res = {
         "fused_us": fused_ms * 1e3,
@@ -355,17 +381,19 @@ def affine_section(iters: int):
         wsn = B.q4_gemm_workspace_size(M, N, K, B.Q4_FMT_AFFINE4)
         ws = torch.empty(wsn, dtype=torch.uint8, device="cuda") if wsn else None
         it = max(5, min(iters, int(2000 / max(1, M // 32))))
-        fused = region_us(lambda i: B.affine4_gemm(q, s, b, x, y=y, workspace=ws), it) * 1e-3
+        # compute-bound sizes are timed in steady state, the short calls behind a hold
+        timer = steady_us if M >= 512 else region_us
+        fused = timer(lambda i: B.affine4_gemm(q, s, b, x, y=y, workspace=ws), it) * 1e-3
         fused_img = None
         if M > 32:      # the matrix-core path (smaller M takes the skinny kernels, which need no image)
             wsi = torch.empty(max(B.q4_gemm_workspace_size(M, N, K, B.Q4_FMT_AFFINE4), 16), dtype=torch.uint8,
                               device="cuda")
-            fused_img = region_us(lambda i: B.q4_gemm_image(image, x, N, fmt=B.Q4_FMT_AFFINE4, y=y, workspace=wsi),
+            fused_img = timer(lambda i: B.q4_gemm_image(image, x, N, fmt=B.Q4_FMT_AFFINE4, y=y, workspace=wsi),
                                   it) * 1e-3
-        deq16 = region_us(lambda i: B.affine4_dequantize(q, s, b, out=w16), it) * 1e-3
-        deqbf = region_us(lambda i: B.affine4_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf), it) * 1e-3
-        ref = region_us(lambda i: torch.matmul(x, wbf.t(), out=y), it) * 1e-3
-        dense = region_us(lambda i: B.dense_gemm(x, w16, y=y), it) * 1e-3
+        deq16 = timer(lambda i: B.affine4_dequantize(q, s, b, out=w16), it) * 1e-3
+        deqbf = timer(lambda i: B.affine4_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf), it) * 1e-3
+        ref = timer(lambda i: torch.matmul(x, wbf.t(), out=y), it) * 1e-3
+        dense = timer(lambda i: B.dense_gemm(x, w16, y=y), it) * 1e-3
         flop = 2.0 * M * N * K
         byts = N * K // 2 + 2 * N * (K // 64) * 2 + M * K * 2 + M * N * 2
         t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flop / (F16_MFMA_PEAK_TFLOPS * 1e12))
@@ -535,9 +563,9 @@ def llama_section(iters: int):
             B.q4_gemm_image(fm["gateup"], xp[H], 16384, y=ygu_p, workspace=wsf)
             B.q4_gemm_image(fm["down"], xp[F], 2048, y=yp[2048], workspace=wsf)
 
-    prefill_call_ms = region_us(prefill_per_call, max(3, iters // 4)) * 1e-3
-    prefill_sep_ms = region_us(prefill_separate, max(3, iters // 4)) * 1e-3
-    prefill_ms = region_us(prefill, max(3, iters // 4)) * 1e-3
+    prefill_call_ms = steady_us(prefill_per_call, max(3, iters // 4)) * 1e-3
+    prefill_sep_ms = steady_us(prefill_separate, max(3, iters // 4)) * 1e-3
+    prefill_ms = steady_us(prefill, max(3, iters // 4)) * 1e-3
     res = {
         "decode_tokens_per_s": 1e3 / decode_ms,
         "decode_us_per_token": decode_ms * 1e3,
