@@ -321,9 +321,13 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
             if (M > kSkinnyLimit) return Q4_ERR_ARG;
             return hip_status(q4::launch_gemm_skinny(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
         case Q4_PATH_MFMA:
-            if (workspace != nullptr && workspace_bytes >= q4::packed_x_bytes(M, N, K)) {
+            // the images alone run the packed GEMM; room for the partial
+            // results as well lets small tile counts split K
+            if (workspace != nullptr && workspace_bytes >= q4::x_image_bytes(M, K) + q4::weight_image_bytes(N, K)) {
                 if (!aligned16(workspace)) return Q4_ERR_ALIGN;
-                return hip_status(q4::launch_gemm_packed(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, workspace, s));
+                const bool split = workspace_bytes >= q4::packed_x_bytes(M, N, K);
+                return hip_status(
+                    q4::launch_gemm_packed(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, workspace, split, s));
             }
             return hip_status(q4::launch_gemm_mfma(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
         case Q4_PATH_DEQUANT_GEMM: {

@@ -1938,17 +1938,17 @@ hipError_t launch_gemm_image(int wfmt, const void* wimg, const void* x, int xdt,
     return hipGetLastError();
 }
 
-// One workspace: the X image, the weight image, then the split-K partial
-// results when the tile count calls for them.
+// One workspace: the X image, the weight image, then (with `split`) the
+// split-K partial results when the tile count calls for them.
 hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
-                              int ydt, int64_t M, int64_t N, int64_t K, void* img, hipStream_t s) {
+                              int ydt, int64_t M, int64_t N, int64_t K, void* img, bool split, hipStream_t s) {
     if (wfmt != WF_Q4_0 && wfmt != WF_AFFINE4) return hipErrorInvalidValue;
     uint8_t* wimg = static_cast<uint8_t*>(img) + x_image_bytes(M, K);
     uint8_t* part = wimg + weight_image_bytes(N, K);
     hipError_t e = launch_pack_weight_image(wfmt, a, b, c, N, K, wimg, s);
     if (e != hipSuccess) return e;
     return launch_gemm_image(wfmt, wimg, x, xdt, y, ydt, M, N, K, img,
-                             splitk_bytes(M, N, K) > 0 ? reinterpret_cast<float*>(part) : nullptr, s);
+                             split && splitk_bytes(M, N, K) > 0 ? reinterpret_cast<float*>(part) : nullptr, s);
 }
 
 template <int WF, int MT, int NT, int XDT, int YDT>

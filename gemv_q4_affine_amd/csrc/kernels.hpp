@@ -42,15 +42,16 @@ hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* 
                             const void* x, int xdt, void* y, int ydt,
                             int64_t M, int64_t N, int64_t K, hipStream_t s);
 // Large-M quantised GEMM on packed images: converts X into a binary16 tile
-// image and the weights into a tile image, both in `img` (packed_x_bytes(M,
-// N, K) bytes, 16-byte aligned, which include the split-K partial results
-// when the tile count is small), then multiplies.
+// image and the weights into a tile image, both in `img` (16-byte aligned),
+// then multiplies.  `img` holds x_image_bytes(M, K) + weight_image_bytes(N, K)
+// bytes; with `split` it holds packed_x_bytes(M, N, K), which adds the
+// split-K partial results a small tile count asks for.
 int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K);
 // fp32 partial results of a K-split launch (0: no split for this shape).
 int64_t splitk_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void* c,
                               const void* x, int xdt, void* y, int ydt,
-                              int64_t M, int64_t N, int64_t K, void* img, hipStream_t s);
+                              int64_t M, int64_t N, int64_t K, void* img, bool split, hipStream_t s);
 // The two halves of it: the weight image alone (weight_image_bytes(N, K),
 // kept by the caller across calls), and the GEMM on a weight image with the
 // X image in ximg (x_image_bytes(M, K)) and, if part is not null, the

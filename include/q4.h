@@ -267,9 +267,10 @@ int q4_gemv_multi_act(int nmat, const uint8_t* const* w_qs, const uint16_t* cons
  *               output has too few 128x256 tiles to occupy the GPU, for the
  *               fp32 partial results of a K-split (each tile's K range spread
  *               over up to 16 workgroups, the parts then summed in order:
- *               deterministic, rounding order differs from an unsplit call);
- *               with less it converts X inside the GEMM (slower, results
- *               within the same bound).  The DEQUANT_GEMM path needs N*K*2 bytes for the
+ *               deterministic, rounding order differs from an unsplit call).
+ *               Room for the two images but not the partial results runs the
+ *               same kernel unsplit; less than the images converts X inside
+ *               the GEMM (slower, results within the same bound).  The DEQUANT_GEMM path needs N*K*2 bytes for the
  *               dequantised weights: the automatic dispatch picks it only
  *               with that much, and forcing it without returns
  *               Q4_ERR_WORKSPACE.  Calls that share a workspace must not run

@@ -453,6 +453,14 @@ def test_gemm_image_equals_mfma_path(fmt, M, N, K):
                 # of small tile counts, so both paths split alike
                 got = B.q4_gemm_image(image, x, N, fmt=f, y_dtype=ydt, workspace=ws)
                 assert torch.equal(got, want), (fmt, M, N, K, call, ydt)
+        # room for the two images only: both run the packed kernel unsplit
+        nimg = B.lib().q4_gemm_image_workspace_size(M, K) + B.lib().q4_weight_image_size(N, K, f)
+        ws2 = torch.empty(nimg, dtype=torch.uint8, device="cuda")
+        xws = torch.empty(max(B.lib().q4_gemm_image_workspace_size(M, K), 16), dtype=torch.uint8, device="cuda")
+        x = bf16_dev(synth.activations(rng, M, K))
+        want = run(x, ws2, torch.float32)
+        got = B.q4_gemm_image(image, x, N, fmt=f, y_dtype=torch.float32, workspace=xws)
+        assert torch.equal(got, want), (fmt, M, N, K, "unsplit")
     finally:
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
 
