@@ -60,6 +60,9 @@ def _load():
             "or_affine4_quantize": [_P, _I, _I, _I, _P, _P, _P],
             "or_affine4_dequantize": [_P, _P, _P, _I, _I, _I, _P],
             "or_affine4_dequantize_half": [_P, _P, _P, _I, _I, _I, ctypes.c_int, _P],
+            "or_affine8_quantize": [_P, _I, _I, _I, _P, _P, _P],
+            "or_affine8_dequantize": [_P, _P, _P, _I, _I, _I, _P],
+            "or_affine8_dequantize_half": [_P, _P, _P, _I, _I, _I, ctypes.c_int, _P],
             "or_f32_to_f16_array": [_P, _I, _P],
             "or_f16_to_f32_array": [_P, _I, _P],
             "or_f32_to_bf16_array": [_P, _I, _P],
@@ -260,6 +263,43 @@ def affine4_dequantize_half(q, s, b, kind: str, group: int = 64):
     K = q.shape[1] * 2
     out = np.empty((N, K), np.uint16)
     _load().or_affine4_dequantize_half(_ptr(q), _ptr(s), _ptr(b), N, K, group,
+                                       {"f16": 0, "bf16": 1}[kind], _ptr(out))
+    return out
+
+
+# ---- affine 8-bit -------------------------------------------------------------
+
+def affine8_quantize(w_bf16_bits, group: int = 64):
+    """W bf16 bits [N, K] -> (q uint8 [N, K], s uint16 [N, K/G], b uint16 [N, K/G])."""
+    w = _c(w_bf16_bits, np.uint16)
+    N, K = w.shape
+    assert K % group == 0
+    q = np.empty((N, K), np.uint8)
+    s = np.empty((N, K // group), np.uint16)
+    b = np.empty((N, K // group), np.uint16)
+    _load().or_affine8_quantize(_ptr(w), N, K, group, _ptr(q), _ptr(s), _ptr(b))
+    return q, s, b
+
+
+def affine8_dequantize(q, s, b, group: int = 64):
+    """Exact q*s + b as float64 [N, K]."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint16)
+    b = _c(b, np.uint16)
+    N, K = q.shape
+    out = np.empty((N, K), np.float64)
+    _load().or_affine8_dequantize(_ptr(q), _ptr(s), _ptr(b), N, K, group, _ptr(out))
+    return out
+
+
+def affine8_dequantize_half(q, s, b, kind: str, group: int = 64):
+    """q*s + b rounded to 'f16' or 'bf16' (RNE of the nearest binary32), as uint16 bits."""
+    q = _c(q, np.uint8)
+    s = _c(s, np.uint16)
+    b = _c(b, np.uint16)
+    N, K = q.shape
+    out = np.empty((N, K), np.uint16)
+    _load().or_affine8_dequantize_half(_ptr(q), _ptr(s), _ptr(b), N, K, group,
                                        {"f16": 0, "bf16": 1}[kind], _ptr(out))
     return out
 

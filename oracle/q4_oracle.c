@@ -411,6 +411,73 @@ void or_affine4_dequantize_half(const uint8_t* wq, const uint16_t* scales, const
         }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Affine 8-bit, group G: the same min/max rule with 255 steps, one code per */
+/* byte (byte k of a row is element k).  The MLX page measures quantize /   */
+/* dequantize / quantized_matmul at bits = 4 and bits = 8 (Repro); the rule  */
+/* is read exactly as for 4 bits above.                                      */
+/* ------------------------------------------------------------------------ */
+void or_affine8_quantize(const uint16_t* wbf, int64_t N, int64_t K, int64_t G,
+                         uint8_t* wq, uint16_t* scales, uint16_t* biases) {
+    const int64_t ng = K / G;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t g = 0; g < ng; g++) {
+            const uint16_t* grp = wbf + n * K + g * G;
+            float lo = or_bf16_to_f32(grp[0]), hi = lo;
+            for (int64_t j = 1; j < G; j++) {
+                float v = or_bf16_to_f32(grp[j]);
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            lo = lo + 0.0f;   /* -0 -> +0 */
+            hi = hi + 0.0f;
+            float step32 = (hi - lo) / 255.0f;
+            uint16_t sb = or_f32_to_bf16(step32);
+            uint16_t bb = or_f32_to_bf16(lo);
+            float sf = or_bf16_to_f32(sb), bf = or_bf16_to_f32(bb);
+            scales[n * ng + g] = sb;
+            biases[n * ng + g] = bb;
+            for (int64_t j = 0; j < G; j++) {
+                int code = 0;
+                if (sf != 0.0f) {
+                    float t = (or_bf16_to_f32(grp[j]) - bf) / sf;
+                    float f8 = floorf(t + 0.5f);
+                    code = f8 < 0.0f ? 0 : (f8 > 255.0f ? 255 : (int)f8);
+                }
+                wq[n * K + g * G + j] = (uint8_t)code;
+            }
+        }
+}
+
+/* Exact dequantised 8-bit weights: w^ = q*s + b in binary64. */
+void or_affine8_dequantize(const uint8_t* wq, const uint16_t* scales, const uint16_t* biases,
+                           int64_t N, int64_t K, int64_t G, double* out) {
+    const int64_t ng = K / G;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            double sv = (double)or_bf16_to_f32(scales[n * ng + k / G]);
+            double bv = (double)or_bf16_to_f32(biases[n * ng + k / G]);
+            out[n * K + k] = (double)wq[n * K + k] * sv + bv;
+        }
+}
+
+/* 8-bit codes to binary16 (half_kind 0) or bfloat16 (1): the binary32 value
+ * nearest to q*s + b, then rounded to nearest even into the 16-bit type. */
+void or_affine8_dequantize_half(const uint8_t* wq, const uint16_t* scales, const uint16_t* biases,
+                                int64_t N, int64_t K, int64_t G, int half_kind, uint16_t* out) {
+    const int64_t ng = K / G;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++) {
+            double sv = (double)or_bf16_to_f32(scales[n * ng + k / G]);
+            double bv = (double)or_bf16_to_f32(biases[n * ng + k / G]);
+            float v = (float)((double)wq[n * K + k] * sv + bv);
+            out[n * K + k] = half_kind ? or_f32_to_bf16(v) : or_f32_to_f16(v);
+        }
+}
+
 /* Helpers for the Python side. */
 void or_f32_to_f16_array(const float* in, int64_t n, uint16_t* out) {
     #pragma omp parallel for schedule(static)

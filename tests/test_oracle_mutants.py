@@ -49,6 +49,11 @@ MUTANTS = [
      "wq[n * (K / 2) + (g * G + j) / 2] = (uint8_t)(c[1] | (c[0] << 4));"),
     ("affine_dequant_bias_dropped", "out[n * K + k] = (double)affine_code(wq, K, n, k) * s + b;",
      "out[n * K + k] = (double)affine_code(wq, K, n, k) * s;"),
+    ("affine8_scale_256_levels", "float step32 = (hi - lo) / 255.0f;", "float step32 = (hi - lo) / 256.0f;"),
+    ("affine8_round_down", "float f8 = floorf(t + 0.5f);", "float f8 = floorf(t);"),
+    ("affine8_clamp_254", "(f8 > 255.0f ? 255 : (int)f8)", "(f8 > 254.0f ? 254 : (int)f8)"),
+    ("affine8_dequant_bias_dropped", "out[n * K + k] = (double)wq[n * K + k] * sv + bv;",
+     "out[n * K + k] = (double)wq[n * K + k] * sv;"),
 ]
 
 

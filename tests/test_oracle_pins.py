@@ -432,6 +432,54 @@ def test_affine4_roundtrip_bound_and_dequant_exact():
 
 
 # --------------------------------------------------------------------------
+# affine 8-bit
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", list(_golden_lines("affine8_groups.txt")), ids=lambda c: c[0])
+def test_affine8_golden_groups(case):
+    name, vals, shex, bhex, codes = case
+    w = np.array(_rle(vals, float), np.float32)
+    assert w.size == 64
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(w).reshape(1, 64), 64)
+    assert int(s[0, 0]) == int(shex, 16) and int(b[0, 0]) == int(bhex, 16), name
+    assert q[0].tolist() == _rle(codes, int), name
+
+
+def test_affine8_ramp_codes():
+    """w_j = j/64: min 0, max 63/64, s = bfloat16(63/16320) = 253/65536, q_j = round(1024 j / 253)."""
+    j = np.arange(64)
+    w = (j / 64.0).astype(np.float32)
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(w).reshape(1, 64), 64)
+    assert _bf16_frac(s[0, 0]) == Fraction(253, 65536) and int(b[0, 0]) == 0
+    want = [int(Fraction(1024 * i, 253) + Fraction(1, 2)) for i in range(64)]
+    assert q[0].tolist() == want
+
+
+def test_affine8_roundtrip_bound_and_dequant_exact():
+    rng = np.random.default_rng(19)
+    W = synth.bf16_bits(synth.weights(rng, 48, 512))
+    q, s, b = oracle.affine8_quantize(W, 64)
+    What = oracle.affine8_dequantize(q, s, b, 64)
+    Wf = synth.bf16_bits_to_f32(W).astype(np.float64).reshape(48, -1, 64)
+    s64 = np.vectorize(lambda v: float(_bf16_frac(v)))(s)
+    b64 = np.vectorize(lambda v: float(_bf16_frac(v)))(b)
+    mn, mx = Wf.min(axis=2), Wf.max(axis=2)
+    assert np.array_equal(b64, mn)                      # bias is the exact group minimum
+    s32 = (mx - mn) / 255.0
+    err = np.abs(Wf - What.reshape(Wf.shape))
+    assert np.all(err <= (s64 / 2 + 255 * np.abs(s32 - s64) + 1e-9)[..., None])
+    assert err.max() < np.abs(Wf).max() / 200           # 8 bits: far finer than 4
+    for n in (0, 17, 47):
+        for k in (0, 1, 63, 64, 200, 511):
+            assert Fraction(What[n, k]) == int(q[n, k]) * _bf16_frac(s[n, k // 64]) + _bf16_frac(b[n, k // 64])
+    ex = What.astype(np.float32)                        # q*s + b is exact in binary32 here
+    assert np.array_equal(ex.astype(np.float64), What)
+    assert np.array_equal(oracle.affine8_dequantize_half(q, s, b, "f16"), ex.astype(np.float16).view(np.uint16))
+    want_bf = torch.from_numpy(ex).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.affine8_dequantize_half(q, s, b, "bf16"), want_bf)
+
+
+# --------------------------------------------------------------------------
 # dequantise to 16-bit dense types: RNE of the binary32 value
 # --------------------------------------------------------------------------
 
