@@ -1,6 +1,6 @@
 """Benchmark of the 4-bit GEMV / GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections decode,gemm,affine,small,llama,cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections decode,gemm,affine,affine8,small,llama,cpu]
 
 A step is one decode token through the decode-GEMV workload (Q4_0 W
 [12288, 4096], one bf16 activation [1, 4096] ~ N(0,1)): q4_gemv_act on W and
@@ -17,7 +17,8 @@ the launching stream.
 
 The other sections add, under "extra": the prefill GEMM (Q4_0, M=2048,
 TFLOP/s) against dequantise-then-GEMM, the affine-4 group-64 sweep over
-M in {1, 32, 512, 2048, 8192} with its crossover, and the Llama-3.2-1B-shaped
+M in {1, 32, 512, 2048, 8192} with its crossover, the same sweep for affine
+8-bit weights, the small-M paths, and the Llama-3.2-1B-shaped
 16-layer stack (aggregate tokens/s).  The CPU oracle is timed on the host
 cores on a bounded sample of the decode workload (N=1 only).
 
@@ -421,6 +422,57 @@ def affine_section(iters: int):
 
 
 # ---------------------------------------------------------------------------
+# affine 8-bit sweep: the same shapes at bits=8
+# ---------------------------------------------------------------------------
+
+def affine8_section(iters: int):
+    """affine8_gemm (fused at M <= 16, dequantise-then-GEMM above) against the
+    page's jit (dequantise to bf16 + hipBLASLt) and ref (hipBLASLt on bf16 W
+    dequantised once), at the sweep's M values.  At M = 1 the weights rotate
+    over ten copies (535 MB) so that they stream from HBM."""
+    wl = synth.AFFINE
+    N, K = wl.N, wl.K
+    rng = np.random.default_rng(wl.seed)
+    W = synth.weights(rng, N, K)
+    q, s, b = B.affine8_quantize(bf16_dev(W))
+    del W
+    copies = 10
+    qc = [(q.clone(), s.clone(), b.clone()) for _ in range(copies)]
+    wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    B.affine8_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf)
+    out = []
+    for M in sorted(set(synth.AFFINE_MS) | {16}):      # 16: the largest fused M
+        X = synth.activations(rng, M, K)
+        x = bf16_dev(X)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        wsn = B.lib().affine8_gemm_workspace_size(M, N, K)
+        ws = torch.empty(wsn, dtype=torch.uint8, device="cuda") if wsn else None
+        it = max(5, min(iters, int(2000 / max(1, M // 32))))
+        timer = steady_us if M >= 512 else region_us
+        fused = timer(lambda i: B.affine8_gemm(*qc[i % copies], x, y=y, workspace=ws), it) * 1e-3
+        deqbf = timer(lambda i: B.affine8_dequantize(*qc[i % copies], out_dtype=torch.bfloat16, out=wbf), it) * 1e-3
+        ref = timer(lambda i: torch.matmul(x, wbf.t(), out=y), it) * 1e-3
+        flop = 2.0 * M * N * K
+        byts = N * K + 2 * N * (K // 64) * 2 + M * K * 2 + M * N * 2
+        t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flop / (F16_MFMA_PEAK_TFLOPS * 1e12))
+        rec = {
+            "M": M,
+            "path": "fused" if M <= 16 else "dequantise to binary16 + dense GEMM",
+            "affine8_gemm_us": fused * 1e3,
+            "jit_us": (deqbf + ref) * 1e3,
+            "ref_us": ref * 1e3,
+            "gbs": byts / (fused * 1e-3) / 1e9,
+            "tflops": flop / (fused * 1e-3) / 1e12,
+            "roofline_frac": t_roof / (fused * 1e-3),
+            "affine8_gemm_beats_jit": fused < deqbf + ref,
+        }
+        out.append(rec)
+        log(f"[affine8] M={M}: affine8_gemm {rec['affine8_gemm_us']:.1f} us ({rec['path']}), "
+            f"jit {rec['jit_us']:.1f} us, ref {rec['ref_us']:.1f} us, roofline {rec['roofline_frac']:.2f}")
+    return {"sweep": out}
+
+
+# ---------------------------------------------------------------------------
 # small M: q4_gemm / affine4_gemm on the skinny paths
 # ---------------------------------------------------------------------------
 
@@ -646,7 +698,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=20,
                     help="distinct weight copies rotated through (>= 19 keeps the 256 MB cache out)")
-    ap.add_argument("--sections", default="decode,gemm,affine,small,llama,cpu",
+    ap.add_argument("--sections", default="decode,gemm,affine,affine8,small,llama,cpu",
                     help="comma list of decode (always run), gemm, affine, small, llama, cpu, calib")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -664,6 +716,8 @@ def main():
         extra["gemm_m2048"] = gemm_section(20)
     if "affine" in sections:
         extra["affine4_sweep"] = affine_section(20)
+    if "affine8" in sections:
+        extra["affine8_sweep"] = affine8_section(20)
     if "small" in sections:
         extra["small_m"] = small_section(100)
     if "llama" in sections:

@@ -51,6 +51,10 @@ SIGNATURES = {
     "q4_dispatch_path": (_INT, [_I64, _I64, _I64, _INT, _INT]),
     "q4_set_dispatch": (_INT, [_INT, _I64]),
     "q4_get_dispatch": (_INT, [_INT, ctypes.POINTER(ctypes.c_int64)]),
+    "affine8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "affine8_dequantize": (_INT, [_P, _P, _P, _I64, _I64, _I64, _P, _INT, _P]),
+    "affine8_gemm_workspace_size": (_I64, [_I64, _I64, _I64]),
+    "affine8_gemm": (_INT, [_P, _P, _P, _I64, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "q4_status_string": (ctypes.c_char_p, [_INT]),
     "q4_version": (ctypes.c_char_p, []),
 }
@@ -278,6 +282,42 @@ def affine4_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, 
     workspace = _workspace(workspace, M, N, K, Q4_FMT_AFFINE4, x)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("affine4_gemm", lib().affine4_gemm(_p(w_q), _p(scales), _p(biases), group_size, _p(x), _dt(x), _p(y),
+                                              _dt(y), M, N, K, _p(workspace), ws_bytes, _stream(stream)))
+    return y
+
+
+# ---- affine 8-bit ---------------------------------------------------------------
+
+def affine8_quantize(w, group_size=64, w_q=None, scales=None, biases=None, stream=None):
+    """W [N, K] (bf16 or f32) -> (q uint8 [N, K], scales, biases int16 bits [N, K/G])."""
+    N, K = w.shape
+    w_q = _empty((N, K), torch.uint8, w) if w_q is None else w_q
+    scales = _empty((N, K // group_size), torch.int16, w) if scales is None else scales
+    biases = _empty((N, K // group_size), torch.int16, w) if biases is None else biases
+    _check("affine8_quantize", lib().affine8_quantize(_p(w), _dt(w), N, K, group_size, _p(w_q), _p(scales),
+                                                      _p(biases), _stream(stream)))
+    return w_q, scales, biases
+
+
+def affine8_dequantize(w_q, scales, biases, group_size=64, out_dtype=torch.float16, out=None, stream=None):
+    N, K = w_q.shape
+    out = _empty((N, K), out_dtype, w_q) if out is None else out
+    _check("affine8_dequantize", lib().affine8_dequantize(_p(w_q), _p(scales), _p(biases), group_size, N, K,
+                                                          _p(out), _dt(out), _stream(stream)))
+    return out
+
+
+def affine8_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, y=None, workspace="auto",
+                 stream=None):
+    """Y [M, N] = X . dequant(W)^T for affine 8-bit weights (workspace "auto": allocated when M needs one)."""
+    N, K = w_q.shape
+    M = x.shape[0]
+    y = _empty((M, N), y_dtype, x) if y is None else y
+    if isinstance(workspace, str):
+        n = int(lib().affine8_gemm_workspace_size(M, N, K))
+        workspace = _empty((n,), torch.uint8, x) if n > 0 else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("affine8_gemm", lib().affine8_gemm(_p(w_q), _p(scales), _p(biases), group_size, _p(x), _dt(x), _p(y),
                                               _dt(y), M, N, K, _p(workspace), ws_bytes, _stream(stream)))
     return y
 

@@ -422,6 +422,59 @@ int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* 
                                             as_stream(stream)));
 }
 
+// ---- affine 8-bit ------------------------------------------------------------------
+
+int affine8_quantize(const void* w, int w_dtype, int64_t N, int64_t K, int64_t group_size, uint8_t* w_q,
+                     uint16_t* scales, uint16_t* biases, void* stream) {
+    if (w_dtype != Q4_F32 && w_dtype != Q4_BF16) return Q4_ERR_DTYPE;
+    if (group_size != 64) return Q4_ERR_SHAPE;
+    int rc = check_dims(0, N, K, 64);
+    if (rc) return rc;
+    if (N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w, w_q, scales, biases}))) return rc;
+    return hip_status(q4::launch_affine8_quantize(w, w_dtype, N, K, w_q, scales, biases, as_stream(stream)));
+}
+
+int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases, int64_t group_size,
+                       int64_t N, int64_t K, void* out, int out_dtype, void* stream) {
+    if (out_dtype != Q4_F32 && out_dtype != Q4_BF16 && out_dtype != Q4_F16) return Q4_ERR_DTYPE;
+    if (group_size != 64) return Q4_ERR_SHAPE;
+    int rc = check_dims(0, N, K, 64);
+    if (rc) return rc;
+    if (N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_q, scales, biases, out}))) return rc;
+    return hip_status(q4::launch_affine8_dequantize(w_q, scales, biases, N, K, out, out_dtype, as_stream(stream)));
+}
+
+int64_t affine8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (check_dims(M, N, K, 64) != Q4_OK) return 0;
+    return M <= q4::kAffine8GemvMaxM ? 0 : N * K * 2;
+}
+
+int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases, int64_t group_size,
+                 const void* x, int x_dtype, void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
+    if ((x_dtype != Q4_BF16 && x_dtype != Q4_F32) || (y_dtype != Q4_BF16 && y_dtype != Q4_F32)) return Q4_ERR_DTYPE;
+    if (group_size != 64) return Q4_ERR_SHAPE;
+    int rc = check_dims(M, N, K, 64);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_q, scales, biases, x, y}))) return rc;
+    read_env();
+    hipStream_t s = as_stream(stream);
+    if (M <= q4::kAffine8GemvMaxM)
+        return hip_status(q4::launch_affine8_gemv(w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, s));
+    // larger M: dequantise to binary16 in the workspace, then the dense GEMM
+    if (workspace == nullptr || workspace_bytes < N * K * 2) return Q4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return Q4_ERR_ALIGN;
+    if (q4::launch_affine8_dequantize(w_q, scales, biases, N, K, workspace, q4::DT_F16, s) != hipSuccess)
+        return Q4_ERR_HIP;
+    if (M <= g_skinny_max_m)
+        return hip_status(
+            q4::launch_gemm_skinny(q4::WF_DENSE16, workspace, nullptr, nullptr, x, x_dtype, y, y_dtype, M, N, K, s));
+    return hip_status(q4::launch_gemm_mfma(q4::WF_DENSE16, workspace, nullptr, nullptr, x, x_dtype, y, y_dtype, M, N, K, s));
+}
+
 int dense_gemm(const void* x, int x_dtype, const uint16_t* w_f16, void* y, int y_dtype, int64_t M, int64_t N,
                int64_t K, void* stream) {
     if ((x_dtype != Q4_BF16 && x_dtype != Q4_F32) || (y_dtype != Q4_BF16 && y_dtype != Q4_F32)) return Q4_ERR_DTYPE;

@@ -25,6 +25,16 @@ hipError_t launch_q4_dequantize(const uint8_t* qs, const uint16_t* d, int64_t N,
 hipError_t launch_affine4_dequantize(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, int64_t G,
                                      int64_t N, int64_t K, void* out, int odt, hipStream_t s);
 
+// Affine 8-bit, group 64 (affine8.hip): quantiser, dequantiser, and the fused
+// GEMV for 1 <= M <= kAffine8GemvMaxM.
+constexpr int kAffine8GemvMaxM = 16;
+hipError_t launch_affine8_quantize(const void* w, int wdt, int64_t N, int64_t K, uint8_t* wq, uint16_t* sc,
+                                   uint16_t* bi, hipStream_t s);
+hipError_t launch_affine8_dequantize(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, int64_t N, int64_t K,
+                                     void* out, int odt, hipStream_t s);
+hipError_t launch_affine8_gemv(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, const void* x, int xdt,
+                               void* y, int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
 // Decode GEMV over 1..kGemvMats weight matrices sharing one activation: the
 // Q8_1 planes (x == nullptr), or a raw bf16 / f32 activation x quantised to
 // Q8_1 inside the kernel (the same bits; M <= 4).  Host arrays of nmat

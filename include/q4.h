@@ -292,6 +292,54 @@ int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
                  int64_t M, int64_t N, int64_t K,
                  void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ======================================================================== */
+/* Affine 8-bit, group 64 (MLX quantize / dequantize / quantized_matmul with  */
+/* bits=8: the MLX page's Repro runs bits 4 and 8, and its Summary finds the  */
+/* fused kernel ahead at decode sizes and dequantise-then-matmul ahead from   */
+/* 512 tokens at both widths)                                                 */
+/* ======================================================================== */
+
+/*
+ * affine8_quantize -- affine 8-bit quantisation, the affine4_quantize rule
+ * with 255 steps: s = bfloat16((mx - mn)/255), b = bfloat16(mn),
+ * q = clamp(floor((w - b)/s + 0.5), 0, 255) in binary32 (q = 0 when s == 0).
+ * Bit-exact.
+ *   w          : device, [N][K] of w_dtype (Q4_BF16 or Q4_F32)
+ *   group_size : 64 (other values: Q4_ERR_SHAPE); K % 64 == 0
+ *   w_q        : device out, uint8 [N][K], byte k of a row = element k
+ *   scales, biases : device out, uint16 [N][K/64] (bfloat16 bits)
+ */
+int affine8_quantize(const void* w, int w_dtype, int64_t N, int64_t K, int64_t group_size,
+                     uint8_t* w_q, uint16_t* scales, uint16_t* biases, void* stream);
+
+/*
+ * affine8_dequantize -- dense W^ = q*s + b: the binary32 value nearest the
+ * exact one (one fma), then RNE into out_dtype (Q4_F16, Q4_BF16 or Q4_F32).
+ */
+int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases,
+                       int64_t group_size, int64_t N, int64_t K,
+                       void* out, int out_dtype, void* stream);
+
+/*
+ * affine8_gemm -- Y = X . dequant(Wq)^T for affine 8-bit group-64 weights
+ * (quantized_matmul with transpose=True, bits=8, group_size=64).
+ *   1 <= M <= 16: one fused launch, no workspace: each weight is dequantised
+ *     once in binary32 (q*s + b, one fma) and multiplied with the M rows in
+ *     binary32; the summation order depends on K only.
+ *   M > 16: dequantise-then-GEMM: the weights are dequantised to binary16 in
+ *     the workspace (at least affine8_gemm_workspace_size(M, N, K) = N*K*2
+ *     bytes, 16-byte aligned; less: Q4_ERR_WORKSPACE), then the dense
+ *     binary16 GEMM of dense_gemm runs on them.
+ *   x : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32); y : device out, [M][N]
+ *   of y_dtype (Q4_BF16 RNE, or Q4_F32).  group_size 64 only, K % 64 == 0.
+ *   Calls that share a workspace must not run concurrently.
+ */
+int64_t affine8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases,
+                 int64_t group_size, const void* x, int x_dtype, void* y, int y_dtype,
+                 int64_t M, int64_t N, int64_t K,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
 /*
  * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
  * 0 for SKINNY; for MFMA the X and weight tile images,

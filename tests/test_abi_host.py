@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 28, names
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in q4.h but not exported"
@@ -144,6 +144,30 @@ def test_gemm_validation():
     d = lib().dense_gemm
     assert d(P, B.Q4_BF16, P, P, B.Q4_BF16, 4, 8, 48, None) == B.Q4_ERR_SHAPE
     assert d(P, B.Q4_BF16, None, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_NULL
+
+
+def test_affine8_validation():
+    """Affine 8-bit entry points reject bad arguments on the host, before any HIP call."""
+    q = lib().affine8_quantize
+    assert q(P, B.Q4_F16, 8, 64, 64, P, P, P, None) == B.Q4_ERR_DTYPE
+    assert q(P, B.Q4_BF16, 8, 64, 32, P, P, P, None) == B.Q4_ERR_SHAPE
+    assert q(P, B.Q4_BF16, 8, 96, 64, P, P, P, None) == B.Q4_ERR_SHAPE
+    assert q(P, B.Q4_BF16, 8, 64, 64, P, None, P, None) == B.Q4_ERR_NULL
+    assert q(P, B.Q4_BF16, 0, 64, 64, P, P, P, None) == B.Q4_OK
+    dq = lib().affine8_dequantize
+    assert dq(P, P, P, 64, 8, 64, P, 7, None) == B.Q4_ERR_DTYPE
+    assert dq(P, P, MIS, 64, 8, 64, P, B.Q4_F16, None) == B.Q4_ERR_ALIGN
+    g = lib().affine8_gemm
+    assert g(P, P, P, 64, P, B.Q4_F16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_DTYPE
+    assert g(P, P, P, 128, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_SHAPE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, None, 0, None) == B.Q4_ERR_SHAPE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None, 0, None) == B.Q4_OK
+    # M > 16 dequantises into the workspace: N*K*2 bytes or Q4_ERR_WORKSPACE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 17, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 17, 8, 64, P, 8 * 64 * 2 - 1, None) == B.Q4_ERR_WORKSPACE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 17, 8, 64, MIS, 8 * 64 * 2, None) == B.Q4_ERR_ALIGN
+    ws = lib().affine8_gemm_workspace_size
+    assert ws(16, 12288, 4096) == 0 and ws(17, 12288, 4096) == 12288 * 4096 * 2 and ws(17, 8, 96) == 0
 
 
 def test_gemv_multi_validation():

@@ -630,3 +630,87 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, r), f"replay {rep} differs"
         work()                                   # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# affine 8-bit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(64, 128), (33, 192), (12288, 4096)])
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_affine8_quantize_bitexact(N, K, wdt):
+    say(f"affine8_quantize N={N} K={K} {wdt}")
+    rng = np.random.default_rng(N * 7 + K)
+    W = synth.weights(rng, N, K)
+    W[0, :64] = 0.25                    # constant group: s = 0
+    W[-1, -64:] = np.linspace(-1.0, 2.0, 64, dtype=np.float32)
+    Wb = synth.bf16_bits(W)
+    wt = dev(Wb).view(torch.bfloat16) if wdt == "bf16" else dev(W)
+    q, s, b = B.affine8_quantize(wt)
+    torch.cuda.synchronize()
+    rq, rs, rb = oracle.affine8_quantize(oracle.f32_to_bf16_bits(W), 64)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s, np.uint16), rs)
+    assert np.array_equal(host(b, np.uint16), rb)
+
+
+@pytest.mark.parametrize("N,K", [(37, 64), (12288, 4096)])
+def test_affine8_dequantize_bitexact(N, K):
+    say(f"affine8_dequantize N={N} K={K}")
+    rng = np.random.default_rng(9)
+    W = synth.weights(rng, N, K) * np.float32(40.0)
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(W), 64)
+    aq, as_, ab = dev(q), dev(s), dev(b)
+    for kind, dt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        got = host(B.affine8_dequantize(aq, as_, ab, out_dtype=dt), np.uint16)
+        assert np.array_equal(got, oracle.affine8_dequantize_half(q, s, b, kind)), kind
+    got32 = host(B.affine8_dequantize(aq, as_, ab, out_dtype=torch.float32))
+    assert np.array_equal(got32, oracle.affine8_dequantize(q, s, b).astype(np.float32))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16, 17, 130])
+@pytest.mark.parametrize("N,K", [(257, 1024), (40, 64), (96, 4160)])
+def test_affine8_gemm_parity(M, N, K):
+    say(f"affine8_gemm M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 31 + N + K)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(W), 64)
+    t = [dev(a) for a in (q, s, b)]
+    xb = synth.bf16_bits(X)
+    ref = oracle.matmul_f64(synth.bf16_bits_to_f32(xb).astype(np.float64), oracle.affine8_dequantize(q, s, b))
+    for ydt in (torch.bfloat16, torch.float32):
+        y = B.affine8_gemm(*t, bf16_dev(X), y_dtype=ydt)
+        torch.cuda.synchronize()
+        e = oracle.rel_frobenius(out_f64(y), ref)
+        assert e <= BAR, (M, N, K, ydt, e)
+        if ydt == torch.float32:
+            # fused (M <= 16): binary32 weights and products; above: binary16 weights
+            assert e <= (GEMV_TIGHT if M <= 16 else 1e-3), (M, N, K, e)
+    if M <= 16:
+        # a binary32 activation (the same values): binary32 weights times x
+        Xf = synth.bf16_bits_to_f32(xb)
+        y32 = B.affine8_gemm(*t, dev(Xf), y_dtype=torch.float32)
+        torch.cuda.synchronize()
+        e = oracle.rel_frobenius(out_f64(y32), ref)
+        assert e <= GEMV_TIGHT, (M, N, K, "f32 x", e)
+
+
+def test_affine8_gemm_full_size_sampled():
+    """N=12288, K=4096 at M = 1 and 16 (fused) and M = 64 (dequantise-then-GEMM): sampled outputs against binary64."""
+    N, K = 12288, 4096
+    rng = np.random.default_rng(2024)
+    W = synth.weights(rng, N, K)
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(W), 64)
+    t = [dev(a) for a in (q, s, b)]
+    What = oracle.affine8_dequantize(q, s, b)
+    for M in (1, 16, 64):
+        say(f"affine8_gemm full size M={M}")
+        X = synth.activations(rng, M, K)
+        xb = synth.bf16_bits(X)
+        y = out_f64(B.affine8_gemm(*t, bf16_dev(X), y_dtype=torch.float32))
+        ms = rng.integers(0, M, 64)
+        ns = rng.integers(0, N, 64)
+        want = oracle.matmul_f64_sampled(synth.bf16_bits_to_f32(xb).astype(np.float64), What, ms, ns)
+        got = y[ms, ns]
+        assert np.linalg.norm(got - want) <= (GEMV_TIGHT if M <= 16 else 1e-3) * np.linalg.norm(want), M
