@@ -426,7 +426,7 @@ def affine_section(iters: int):
 # ---------------------------------------------------------------------------
 
 def affine8_section(iters: int):
-    """affine8_gemm (fused at M <= 16, dequantise-then-GEMM above) against the
+    """affine8_gemm (fused up to M = 32 on bf16 X, dequantise-then-GEMM above) against the
     page's jit (dequantise to bf16 + hipBLASLt) and ref (hipBLASLt on bf16 W
     dequantised once), at the sweep's M values.  At M = 1 the weights rotate
     over ten copies (535 MB) so that they stream from HBM."""
@@ -441,7 +441,7 @@ def affine8_section(iters: int):
     wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     B.affine8_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf)
     out = []
-    for M in sorted(set(synth.AFFINE_MS) | {16}):      # 16: the largest fused M
+    for M in sorted(set(synth.AFFINE_MS) | {16}):
         X = synth.activations(rng, M, K)
         x = bf16_dev(X)
         y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -457,7 +457,7 @@ def affine8_section(iters: int):
         t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flop / (F16_MFMA_PEAK_TFLOPS * 1e12))
         rec = {
             "M": M,
-            "path": "fused" if M <= 16 else "dequantise to binary16 + dense GEMM",
+            "path": "fused vector" if M <= 4 else ("fused bf16 MFMA" if M <= 32 else "dequantise to binary16 + dense GEMM"),
             "affine8_gemm_us": fused * 1e3,
             "jit_us": (deqbf + ref) * 1e3,
             "ref_us": ref * 1e3,

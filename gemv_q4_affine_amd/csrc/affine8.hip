@@ -235,6 +235,121 @@ __global__ __launch_bounds__(256) void k_affine8_gemv(const uint8_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core kernel for 4 < M <= 32 on a bfloat16 activation.  Codes 0..255
+// are exact in bfloat16, so v_mfma_f32_16x16x32_bf16 takes X and the raw codes
+// and sums q*x exactly per product; per group g of column n the result is
+// scaled in binary32: y += s[n,g] * sum_k q x + b[n,g] * sum_k x (the second
+// sum an MFMA of X against ones, so it arrives in the output layout).
+// A workgroup of 4 waves owns 16 weight rows (output columns); the waves split
+// the groups and add their tiles through LDS in wave order.  MFMA operand
+// layout: lane l = 16 h + j supplies row j of X (column j of W) and the 8
+// K slots 8h..8h+7; it holds the outputs of rows 4h..4h+3 of column j.  Lane
+// (h, j) loads bytes 16h..16h+15 of the group for weight row j (16 rows x 64
+// contiguous bytes per instruction); MFMA 0 takes its bytes 0..7, MFMA 1 its
+// bytes 8..15, and the X fragments are loaded in the same K order.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// 8 codes (two words) as 8 exact bfloat16 values
+__device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w0, uint32_t w1) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const uint32_t w = i == 0 ? w0 : w1;
+        const f32x2_t lo = {(float)(w & 0xFFu), (float)((w >> 8) & 0xFFu)};
+        const f32x2_t hi = {(float)((w >> 16) & 0xFFu), (float)(w >> 24)};
+        r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+        r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+    }
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+
+constexpr int kA8MmaGroupsInFlight = 2;
+
+template <int MT, int YDT>
+__global__ __launch_bounds__(256) void k_affine8_mma(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ sc,
+                                                     const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
+                                                     void* __restrict__ y, int M, int N, int K) {
+    constexpr int U = kA8MmaGroupsInFlight;
+    __shared__ floatx4_t red[4][MT][64];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const int j = lane & 15;
+    const int h = lane >> 4;
+    const int n0 = (int)blockIdx.x * 16;
+    const int nr = min(n0 + j, N - 1);                  // columns past N read the last row, never stored
+    const uint8_t* wrow = wq + (int64_t)nr * K;
+    const int ng = K / 64;
+    const uint16_t* srow = sc + (int64_t)nr * ng;
+    const uint16_t* brow = bi + (int64_t)nr * ng;
+    const uint16_t* xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) xrow[mt] = x + (int64_t)min(mt * 16 + j, M - 1) * K;   // rows past M repeat
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    const floatx4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[mt] = zero4;
+    for (int g0 = w; g0 < ng; g0 += 4 * U) {
+        u32x4_t qv[U], xv[U][MT][2];
+        uint32_t sv[U], bv[U];
+        bool okv[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int gi = g0 + 4 * u;
+            okv[u] = gi < ng;
+            const int gg = okv[u] ? gi : 0;
+            const int k0 = gg * 64 + 16 * h;
+            qv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(wrow + k0));
+            sv[u] = srow[gg];
+            bv[u] = brow[gg];
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xrow[mt] + k0);
+                xv[u][mt][0] = xp[0];
+                xv[u][mt][1] = xp[1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const bf16x8_t b0 = codes_bf16(qv[u][0], qv[u][1]);
+            const bf16x8_t b1 = codes_bf16(qv[u][2], qv[u][3]);
+            const float s = okv[u] ? bf16_to_f32(sv[u]) : 0.0f;
+            const float b = okv[u] ? bf16_to_f32(bv[u]) : 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+                const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, xv[u][mt][0]);
+                const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, xv[u][mt][1]);
+                floatx4_t qx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, zero4, 0, 0, 0);
+                qx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, qx, 0, 0, 0);
+                floatx4_t sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, ones, zero4, 0, 0, 0);
+                sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, ones, sx, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[mt][v] = fmaf(s, qx[v], fmaf(b, sx[v], acc[mt][v]));
+            }
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) red[w][mt][lane] = acc[mt];
+    __syncthreads();
+    if (w == 0) {
+        const int n = n0 + j;
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+            const floatx4_t t = ((red[0][mt][lane] + red[1][mt][lane]) + red[2][mt][lane]) + red[3][mt][lane];
+#pragma unroll
+            for (int v = 0; v < 4; v++) {
+                const int m = mt * 16 + 4 * h + v;
+                if (n < N && m < M) {
+                    if constexpr (YDT == DT_BF16) reinterpret_cast<uint16_t*>(y)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16(t[v]);
+                    else reinterpret_cast<float*>(y)[(int64_t)m * N + n] = t[v];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static inline unsigned grid_for8(int64_t items, int per_block) {
@@ -289,6 +404,21 @@ hipError_t launch_affine8_gemv(const uint8_t* wq, const uint16_t* sc, const uint
     else if (m == 4) launch_gemv8_m<4>(wq, sc, bi, x, xdt, y, ydt, (int)N, (int)K, m, s);
     else if (m <= 8) launch_gemv8_m<8>(wq, sc, bi, x, xdt, y, ydt, (int)N, (int)K, m, s);
     else launch_gemv8_m<16>(wq, sc, bi, x, xdt, y, ydt, (int)N, (int)K, m, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_affine8_mma(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, const void* x, void* y,
+                              int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+    if (M < 1 || M > kAffine8MmaMaxM) return hipErrorInvalidValue;
+    const dim3 g((unsigned)((N + 15) / 16)), b(256);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    if (M <= 16) {
+        if (ydt == DT_BF16) hipLaunchKernelGGL((k_affine8_mma<1, DT_BF16>), g, b, 0, s, wq, sc, bi, xb, y, (int)M, (int)N, (int)K);
+        else hipLaunchKernelGGL((k_affine8_mma<1, DT_F32>), g, b, 0, s, wq, sc, bi, xb, y, (int)M, (int)N, (int)K);
+    } else {
+        if (ydt == DT_BF16) hipLaunchKernelGGL((k_affine8_mma<2, DT_BF16>), g, b, 0, s, wq, sc, bi, xb, y, (int)M, (int)N, (int)K);
+        else hipLaunchKernelGGL((k_affine8_mma<2, DT_F32>), g, b, 0, s, wq, sc, bi, xb, y, (int)M, (int)N, (int)K);
+    }
     return hipGetLastError();
 }
 

@@ -448,7 +448,7 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
 
 int64_t affine8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (check_dims(M, N, K, 64) != Q4_OK) return 0;
-    return M <= q4::kAffine8GemvMaxM ? 0 : N * K * 2;
+    return M <= q4::kAffine8GemvMaxM ? 0 : N * K * 2;   // bf16 X up to kAffine8MmaMaxM rows uses none
 }
 
 int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases, int64_t group_size,
@@ -462,8 +462,12 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
     if ((rc = check_ptrs_aligned({w_q, scales, biases, x, y}))) return rc;
     read_env();
     hipStream_t s = as_stream(stream);
-    if (M <= q4::kAffine8GemvMaxM)
+    // M <= 4: the fused vector kernel; bf16 X up to 32 rows: the bf16-MFMA
+    // kernel on the raw codes; f32 X up to 16 rows: the vector kernel
+    if (M <= 4 || (x_dtype == Q4_F32 && M <= q4::kAffine8GemvMaxM))
         return hip_status(q4::launch_affine8_gemv(w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, s));
+    if (x_dtype == Q4_BF16 && M <= q4::kAffine8MmaMaxM)
+        return hip_status(q4::launch_affine8_mma(w_q, scales, biases, x, y, y_dtype, M, N, K, s));
     // larger M: dequantise to binary16 in the workspace, then the dense GEMM
     if (workspace == nullptr || workspace_bytes < N * K * 2) return Q4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q4_ERR_ALIGN;

@@ -34,6 +34,10 @@ hipError_t launch_affine8_dequantize(const uint8_t* wq, const uint16_t* sc, cons
                                      void* out, int odt, hipStream_t s);
 hipError_t launch_affine8_gemv(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, const void* x, int xdt,
                                void* y, int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s);
+// bf16-MFMA kernel for 1 <= M <= kAffine8MmaMaxM on a bf16 activation.
+constexpr int kAffine8MmaMaxM = 32;
+hipError_t launch_affine8_mma(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, const void* x, void* y,
+                              int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s);
 
 // Decode GEMV over 1..kGemvMats weight matrices sharing one activation: the
 // Q8_1 planes (x == nullptr), or a raw bf16 / f32 activation x quantised to

@@ -323,13 +323,18 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
 /*
  * affine8_gemm -- Y = X . dequant(Wq)^T for affine 8-bit group-64 weights
  * (quantized_matmul with transpose=True, bits=8, group_size=64).
- *   1 <= M <= 16: one fused launch, no workspace: each weight is dequantised
- *     once in binary32 (q*s + b, one fma) and multiplied with the M rows in
- *     binary32; the summation order depends on K only.
- *   M > 16: dequantise-then-GEMM: the weights are dequantised to binary16 in
- *     the workspace (at least affine8_gemm_workspace_size(M, N, K) = N*K*2
- *     bytes, 16-byte aligned; less: Q4_ERR_WORKSPACE), then the dense
- *     binary16 GEMM of dense_gemm runs on them.
+ *   M <= 4 (and M <= 16 on a Q4_F32 activation): one fused launch, no
+ *     workspace: each weight is dequantised once in binary32 (q*s + b, one
+ *     fma) and multiplied with the M rows in binary32.
+ *   5 <= M <= 32 on a Q4_BF16 activation: one fused launch, no workspace:
+ *     the bf16 matrix cores multiply X with the raw codes (exact in
+ *     bfloat16) per 64-weight group, and s and b scale the group's sums in
+ *     binary32.  Both fused kernels sum in an order that depends on K only.
+ *   Otherwise: dequantise-then-GEMM: the weights are dequantised to binary16
+ *     in the workspace (at least N*K*2 bytes, 16-byte aligned; less:
+ *     Q4_ERR_WORKSPACE), then the dense binary16 GEMM of dense_gemm runs on
+ *     them.  affine8_gemm_workspace_size(M, N, K) is 0 for M <= 16 and N*K*2
+ *     above (enough for either activation type).
  *   x : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32); y : device out, [M][N]
  *   of y_dtype (Q4_BF16 RNE, or Q4_F32).  group_size 64 only, K % 64 == 0.
  *   Calls that share a workspace must not run concurrently.

@@ -162,10 +162,12 @@ def test_affine8_validation():
     assert g(P, P, P, 128, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_SHAPE
     assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, None, 0, None) == B.Q4_ERR_SHAPE
     assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None, 0, None) == B.Q4_OK
-    # M > 16 dequantises into the workspace: N*K*2 bytes or Q4_ERR_WORKSPACE
-    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 17, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
-    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 17, 8, 64, P, 8 * 64 * 2 - 1, None) == B.Q4_ERR_WORKSPACE
-    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 17, 8, 64, MIS, 8 * 64 * 2, None) == B.Q4_ERR_ALIGN
+    # above the fused kernels (f32 X: M > 16, bf16 X: M > 32) the call dequantises
+    # into the workspace: N*K*2 bytes or Q4_ERR_WORKSPACE, checked before any launch
+    assert g(P, P, P, 64, P, B.Q4_F32, P, B.Q4_BF16, 17, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, P, 8 * 64 * 2 - 1, None) == B.Q4_ERR_WORKSPACE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, MIS, 8 * 64 * 2, None) == B.Q4_ERR_ALIGN
     ws = lib().affine8_gemm_workspace_size
     assert ws(16, 12288, 4096) == 0 and ws(17, 12288, 4096) == 12288 * 4096 * 2 and ws(17, 8, 96) == 0
 
