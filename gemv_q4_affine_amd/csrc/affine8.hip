@@ -290,13 +290,15 @@ __global__ __launch_bounds__(256) void k_affine8_mma(const uint8_t* __restrict__
     floatx4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) acc[mt] = zero4;
-    for (int g0 = w; g0 < ng; g0 += 4 * U) {
+    // wave w takes the U adjacent groups w*U .. w*U + U - 1, then those 4U on:
+    // a row's U*64 bytes of a step are contiguous
+    for (int g0 = w * U; g0 < ng; g0 += 4 * U) {
         u32x4_t qv[U], xv[U][MT][2];
         uint32_t sv[U], bv[U];
         bool okv[U];
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int gi = g0 + 4 * u;
+            const int gi = g0 + u;
             okv[u] = gi < ng;
             const int gg = okv[u] ? gi : 0;
             const int k0 = gg * 64 + 16 * h;
