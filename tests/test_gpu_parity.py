@@ -715,3 +715,25 @@ def test_affine8_gemm_full_size_sampled():
         want = oracle.matmul_f64_sampled(synth.bf16_bits_to_f32(xb).astype(np.float64), What, ms, ns)
         got = y[ms, ns]
         assert np.linalg.norm(got - want) <= (GEMV_TIGHT if M <= 32 else 1e-3) * np.linalg.norm(want), M
+
+
+@pytest.mark.parametrize("M", [1, 5, 32, 33])
+@pytest.mark.parametrize("N,K", [(1, 64), (17, 128), (3, 4096)])
+def test_affine8_gemm_edges_and_determinism(M, N, K):
+    """One output row, one group (three of the MFMA kernel's four waves get none), and repeated calls
+    giving the same bits (the summation order depends on K only)."""
+    say(f"affine8_gemm edges M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 101 + N * 7 + K)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(W), 64)
+    t = [dev(a) for a in (q, s, b)]
+    xb = synth.bf16_bits(X)
+    ref = oracle.matmul_f64(synth.bf16_bits_to_f32(xb).astype(np.float64), oracle.affine8_dequantize(q, s, b))
+    x = bf16_dev(X)
+    y1 = B.affine8_gemm(*t, x, y_dtype=torch.float32)
+    y2 = B.affine8_gemm(*t, x, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2), (M, N, K)
+    e = oracle.rel_frobenius(out_f64(y1), ref)
+    assert e <= (GEMV_TIGHT if M <= 32 else 1e-3), (M, N, K, e)
