@@ -737,3 +737,39 @@ def test_affine8_gemm_edges_and_determinism(M, N, K):
     assert torch.equal(y1, y2), (M, N, K)
     e = oracle.rel_frobenius(out_f64(y1), ref)
     assert e <= (GEMV_TIGHT if M <= 32 else 1e-3), (M, N, K, e)
+
+
+def test_affine8_graph_replays_match_eager():
+    """affine8_gemm on each of its three paths (vector kernel, bf16-MFMA kernel, dequantise-then-GEMM
+    with a caller workspace) captured in one graph: every replay, with eager work and synchronisations
+    between replays, reproduces the eager results exactly."""
+    rng = np.random.default_rng(77)
+    N, K = 300, 1024
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(synth.weights(rng, N, K)), 64)
+    t = [dev(a) for a in (q, s, b)]
+    xs = {M: bf16_dev(synth.activations(rng, M, K)) for M in (1, 20, 40)}
+    ys = {M: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for M in xs}
+    ws = torch.empty(B.lib().affine8_gemm_workspace_size(40, N, K), dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+
+    def work():
+        for M, x in xs.items():
+            B.affine8_gemm(*t, x, y=ys[M], workspace=ws if M == 40 else None)
+
+    work()
+    torch.cuda.synchronize()
+    ref = {M: y.clone() for M, y in ys.items()}
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        work()
+    for rep in range(4):
+        for y in ys.values():
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for M in ys:
+            assert torch.equal(ys[M], ref[M]), (rep, M)
+        work()                                          # eager work between replays
+        torch.cuda.synchronize()
