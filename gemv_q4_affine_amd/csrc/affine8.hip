@@ -240,8 +240,8 @@ __global__ __launch_bounds__(256) void k_affine8_gemv(const uint8_t* __restrict_
 // and sums q*x exactly per product; per group g of column n the result is
 // scaled in binary32: y += s[n,g] * sum_k q x + b[n,g] * sum_k x (the second
 // sum an MFMA of X against ones, so it arrives in the output layout).
-// A workgroup of 4 waves owns 16 weight rows (output columns); the waves split
-// the groups and add their tiles through LDS in wave order.  MFMA operand
+// A workgroup of kA8MmaWaves waves owns 16 weight rows (output columns); the
+// waves split the groups and add their tiles through LDS in wave order.  MFMA operand
 // layout: lane l = 16 h + j supplies row j of X (column j of W) and the 8
 // K slots 8h..8h+7; it holds the outputs of rows 4h..4h+3 of column j.  Lane
 // (h, j) loads bytes 16h..16h+15 of the group for weight row j (16 rows x 64
@@ -265,13 +265,14 @@ __device__ __forceinline__ bf16x8_t codes_bf16(uint32_t w0, uint32_t w1) {
 }
 
 constexpr int kA8MmaGroupsInFlight = 2;
+constexpr int kA8MmaWaves = 4;          // waves per workgroup, splitting the groups
 
 template <int MT, int YDT>
-__global__ __launch_bounds__(256) void k_affine8_mma(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ sc,
+__global__ __launch_bounds__(64 * kA8MmaWaves) void k_affine8_mma(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ sc,
                                                      const uint16_t* __restrict__ bi, const uint16_t* __restrict__ x,
                                                      void* __restrict__ y, int M, int N, int K) {
     constexpr int U = kA8MmaGroupsInFlight;
-    __shared__ floatx4_t red[4][MT][64];
+    __shared__ floatx4_t red[kA8MmaWaves][MT][64];
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int j = lane & 15;
@@ -290,9 +291,9 @@ __global__ __launch_bounds__(256) void k_affine8_mma(const uint8_t* __restrict__
     floatx4_t acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) acc[mt] = zero4;
-    // wave w takes the U adjacent groups w*U .. w*U + U - 1, then those 4U on:
-    // a row's U*64 bytes of a step are contiguous
-    for (int g0 = w * U; g0 < ng; g0 += 4 * U) {
+    // wave w takes the U adjacent groups w*U .. w*U + U - 1, then those
+    // kA8MmaWaves*U on: a row's U*64 bytes of a step are contiguous
+    for (int g0 = w * U; g0 < ng; g0 += kA8MmaWaves * U) {
         u32x4_t qv[U], xv[U][MT][2];
         uint32_t sv[U], bv[U];
         bool okv[U];
@@ -338,7 +339,9 @@ __global__ __launch_bounds__(256) void k_affine8_mma(const uint8_t* __restrict__
         const int n = n0 + j;
 #pragma unroll
         for (int mt = 0; mt < MT; mt++) {
-            const floatx4_t t = ((red[0][mt][lane] + red[1][mt][lane]) + red[2][mt][lane]) + red[3][mt][lane];
+            floatx4_t t = red[0][mt][lane];
+#pragma unroll
+            for (int ww = 1; ww < kA8MmaWaves; ww++) t += red[ww][mt][lane];
 #pragma unroll
             for (int v = 0; v < 4; v++) {
                 const int m = mt * 16 + 4 * h + v;
@@ -412,7 +415,7 @@ hipError_t launch_affine8_gemv(const uint8_t* wq, const uint16_t* sc, const uint
 hipError_t launch_affine8_mma(const uint8_t* wq, const uint16_t* sc, const uint16_t* bi, const void* x, void* y,
                               int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
     if (M < 1 || M > kAffine8MmaMaxM) return hipErrorInvalidValue;
-    const dim3 g((unsigned)((N + 15) / 16)), b(256);
+    const dim3 g((unsigned)((N + 15) / 16)), b(64 * kA8MmaWaves);
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     if (M <= 16) {
         if (ydt == DT_BF16) hipLaunchKernelGGL((k_affine8_mma<1, DT_BF16>), g, b, 0, s, wq, sc, bi, xb, y, (int)M, (int)N, (int)K);
