@@ -773,3 +773,40 @@ def test_affine8_graph_replays_match_eager():
             assert torch.equal(ys[M], ref[M]), (rep, M)
         work()                                          # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes_every_entry_point(case):
+    """Seeded random shapes through the automatic dispatch of q4_gemm, affine4_gemm and affine8_gemm
+    (with and without a workspace), bf16 output, against the binary64 oracle."""
+    rng = np.random.default_rng(9000 + case)
+    M = int(rng.choice([1, 2, 3, 5, 8, 13, 17, 31, 32, 33, 64, 65, 128, 129, 200, 300]))
+    N = int(rng.integers(1, 700))
+    K = 64 * int(rng.integers(1, 40))
+    say(f"random shapes case {case}: M={M} N={N} K={K}")
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    xb = synth.bf16_bits(X)
+    x = bf16_dev(X)
+    xf64 = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    qs, d = oracle.q4_0_quantize(W)
+    aq, as_, ab = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+    eq, es, eb = oracle.affine8_quantize(synth.bf16_bits(W), 64)
+    refs = {
+        "q4_0": oracle.matmul_f64(xf64, oracle.q4_0_dequantize(qs, d)),
+        "affine4": oracle.matmul_f64(xf64, oracle.affine4_dequantize(aq, as_, ab)),
+        "affine8": oracle.matmul_f64(xf64, oracle.affine8_dequantize(eq, es, eb)),
+    }
+    calls = {
+        "q4_0": lambda ws: B.q4_gemm(dev(qs), dev(d), x, workspace=ws),
+        "affine4": lambda ws: B.affine4_gemm(dev(aq), dev(as_), dev(ab), x, workspace=ws),
+        "affine8": lambda ws: B.affine8_gemm(dev(eq), dev(es), dev(eb), x, workspace=ws),
+    }
+    for fmt, call in calls.items():
+        for ws in ("auto", None):
+            if fmt == "affine8" and ws is None and M > 32:
+                continue                                 # that path needs its workspace
+            y = call(ws)
+            torch.cuda.synchronize()
+            e = oracle.rel_frobenius(out_f64(y), refs[fmt])
+            assert e <= BAR, (fmt, ws, M, N, K, e)
