@@ -810,3 +810,31 @@ def test_random_shapes_every_entry_point(case):
             torch.cuda.synchronize()
             e = oracle.rel_frobenius(out_f64(y), refs[fmt])
             assert e <= BAR, (fmt, ws, M, N, K, e)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_shapes_gemv(case):
+    """Seeded random shapes through q4_gemv (M up to 16) against the Q8_1 oracle, and through
+    q4_gemv_act / q4_gemv_fused2_act (M up to 4), bit-identical to quantise-then-GEMV."""
+    rng = np.random.default_rng(7000 + case)
+    M = int(rng.integers(1, 17))
+    N = int(rng.integers(1, 3000))
+    N1 = int(rng.integers(1, 3000))
+    K = 32 * int(rng.integers(1, 200))
+    say(f"random gemv case {case}: M={M} N={N} N1={N1} K={K}")
+    wqs, wd = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    w1qs, w1d = oracle.q4_0_quantize(synth.weights(rng, N1, K))
+    X = synth.activations(rng, M, K)
+    x = bf16_dev(X)
+    xq, xd = B.q8_1_quantize_act(x)
+    t0, t1 = (dev(wqs), dev(wd)), (dev(w1qs), dev(w1d))
+    y = B.q4_gemv(*t0, xq, xd)
+    xqs, xds = oracle.q8_1_quantize(synth.bf16_bits_to_f32(synth.bf16_bits(X)))
+    assert np.array_equal(host(xq), xqs) and np.array_equal(host(xd, np.uint16), xds)
+    assert rel(host(y).astype(np.float64), oracle.q4q8_gemv(wqs, wd, xqs, xds)) <= GEMV_TIGHT, (M, N, K)
+    y0, y1 = B.q4_gemv_fused2(*t0, *t1, xq, xd)
+    assert torch.equal(y0, y) and torch.equal(y1, B.q4_gemv(*t1, xq, xd))
+    if M <= 4:
+        assert torch.equal(B.q4_gemv_act(*t0, x), y)
+        a0, a1 = B.q4_gemv_fused2_act(*t0, *t1, x)
+        assert torch.equal(a0, y0) and torch.equal(a1, y1)
