@@ -313,6 +313,7 @@ __global__ __launch_bounds__(64 * kA8MmaWaves) void k_affine8_mma(const uint8_t*
                 xv[u][mt][1] = xp[1];
             }
         }
+        __builtin_amdgcn_sched_barrier(0);              // every load of the step issued before any arithmetic
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const bf16x8_t b0 = codes_bf16(qv[u][0], qv[u][1]);
