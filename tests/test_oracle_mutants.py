@@ -24,12 +24,16 @@ MUTANTS = [
     ("q4_last_max_wins", "if (a > amax) { amax = a; maxv = blk[j]; }", "if (a >= amax) { amax = a; maxv = blk[j]; }"),
     ("q4_round_half_even", "int c = (int)u;              /* u >= 0.5: truncation == floor */",
      "int c = (int)rintf(t + 8.0f);"),
+    ("q4_id_from_d16", "float dd = maxv / -8.0f;\n            float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;",
+     "float dd = maxv / -8.0f;\n            float id = (dd != 0.0f) ? 1.0f / or_f16_to_f32(or_f32_to_f16(dd)) : 0.0f;"),
     ("q4_no_clamp", "code[j] = c < 15 ? c : 15;", "code[j] = c & 15;"),
     ("q4_dequant_offset", "out[n * K + b * 32 + j] = (double)(q4_code(blk, j) - 8) * dd;",
      "out[n * K + b * 32 + j] = (double)(q4_code(blk, j) - 7) * dd;"),
     ("q4_code_high_low_swapped", "return j < 16 ? (blk16[j] & 0x0F) : (blk16[j - 16] >> 4);",
      "return j < 16 ? (blk16[j] >> 4) : (blk16[j - 16] & 0x0F);"),
     ("q8_round_half_even", "int q = (int)roundf(t);", "int q = (int)rintf(t);"),
+    ("q8_id_from_d16", "float dd = amax / 127.0f;\n            float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;",
+     "float dd = amax / 127.0f;\n            float id = (dd != 0.0f) ? 1.0f / or_f16_to_f32(or_f32_to_f16(dd)) : 0.0f;"),
     ("q8_sum_unscaled", "float s = dd * (float)sum;", "float s = (float)sum;"),
     ("q8_scale_128", "float dd = amax / 127.0f;", "float dd = amax / 128.0f;"),
     ("dots_offset_dropped", "for (int j = 0; j < 32; j++) s += (q4_code(blk, j) - 8) * (int32_t)a[j];\n                isum",
@@ -45,12 +49,14 @@ MUTANTS = [
      "bits = 0;"),
     ("affine_scale_16_levels", "float s32 = (mx - mn) / 15.0f;", "float s32 = (mx - mn) / 16.0f;"),
     ("affine_round_down", "float f = floorf(r + 0.5f);", "float f = floorf(r);"),
+    ("affine_round_half_even", "float f = floorf(r + 0.5f);", "float f = rintf(r);"),
     ("affine_nibble_swap", "wq[n * (K / 2) + (g * G + j) / 2] = (uint8_t)(c[0] | (c[1] << 4));",
      "wq[n * (K / 2) + (g * G + j) / 2] = (uint8_t)(c[1] | (c[0] << 4));"),
     ("affine_dequant_bias_dropped", "out[n * K + k] = (double)affine_code(wq, K, n, k) * s + b;",
      "out[n * K + k] = (double)affine_code(wq, K, n, k) * s;"),
     ("affine8_scale_256_levels", "float step32 = (hi - lo) / 255.0f;", "float step32 = (hi - lo) / 256.0f;"),
     ("affine8_round_down", "float f8 = floorf(t + 0.5f);", "float f8 = floorf(t);"),
+    ("affine8_round_half_even", "float f8 = floorf(t + 0.5f);", "float f8 = rintf(t);"),
     ("affine8_clamp_254", "(f8 > 255.0f ? 255 : (int)f8)", "(f8 > 254.0f ? 254 : (int)f8)"),
     ("affine8_dequant_bias_dropped", "out[n * K + k] = (double)wq[n * K + k] * sv + bv;",
      "out[n * K + k] = (double)wq[n * K + k] * sv;"),
