@@ -691,6 +691,76 @@ def cpu_baseline(budget_s: float):
     }
 
 
+def cpu_baseline_gemm(budget_s: float):
+    """The oracle on the prefill GEMM (Q4_0 W [12288, 4096], bf16 X [2048, 4096]):
+    dequantise W once, then the fp64 matmul on a sample of X rows, grown until
+    it runs for about budget_s; the full call's time is the dequantisation plus
+    the sample's matmul time scaled linearly to 2048 rows (every row costs the
+    same N*K multiply-adds)."""
+    import oracle
+    wl = synth.PREFILL
+    M, N, K = wl.M, wl.N, wl.K
+    W, X = synth.workload_inputs(wl)
+    Xf = synth.bf16_bits_to_f32(synth.bf16_bits(X)).astype(np.float64)
+    qs, d = oracle.q4_0_quantize(W)
+    del W
+    t0 = time.perf_counter()
+    What = oracle.q4_0_dequantize(qs, d)
+    t_deq = time.perf_counter() - t0
+    rows, t_mm = 2, 0.0
+    while True:
+        t0 = time.perf_counter()
+        oracle.matmul_f64(Xf[:rows], What)
+        t_mm = time.perf_counter() - t0
+        if t_mm >= budget_s / 4 or rows >= M:
+            break
+        rows = min(M, rows * max(2, int(budget_s / 4 / max(t_mm, 1e-3))))
+    t_full = t_deq + t_mm * M / rows
+    flop = 2.0 * M * N * K
+    return {
+        "value": flop / t_full / 1e9,
+        "unit": "GFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"prefill GEMM M={M} N={N} K={K}: dequantise ({t_deq:.2f} s) + fp64 matmul on {rows} of "
+                  f"{M} X rows ({t_mm:.2f} s), matmul scaled linearly to {M} rows: {t_full:.1f} s per call",
+    }
+
+
+def environment():
+    """ROCm, HIP runtime/driver and torch versions, and a hash of the library
+    sources (the GPU machine's copy of the tree carries no git metadata; the git
+    commit is added when there is one)."""
+    import ctypes
+    import glob
+    import subprocess
+    env = {"torch": torch.__version__, "torch_hip": getattr(torch.version, "hip", None)}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipRuntimeGetVersion(ctypes.byref(v)) == 0:
+            env["hip_runtime_version"] = v.value
+        if hip.hipDriverGetVersion(ctypes.byref(v)) == 0:
+            env["hip_driver_version"] = v.value
+    except OSError:
+        pass
+    srcs = sorted(glob.glob(os.path.join(ROOT, "gemv_q4_affine_amd", "csrc", "*"))) + [os.path.join(ROOT, "include", "q4.h")]
+    env["library_sources_sha256_16"] = sources_hash([os.path.relpath(p, ROOT) for p in srcs])
+    try:
+        env["git_commit"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                                           timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        env["git_commit"] = None
+    env["device"] = torch.cuda.get_device_name(0)
+    env["host_cpus_in_affinity"] = len(os.sched_getaffinity(0))
+    return env
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -725,6 +795,11 @@ def main():
     if "calib" in sections:
         extra["counter_calibration"] = calib_section()
     cpu = cpu_baseline(args.cpu_seconds) if "cpu" in sections else None
+    if "cpu" in sections and "gemm_m2048" in extra:
+        extra["gemm_cpu_baseline"] = cpu_baseline_gemm(args.cpu_seconds)
+        log(f"[cpu] oracle GEMM {extra['gemm_cpu_baseline']['value']:.2f} GFLOP/s on "
+            f"{extra['gemm_cpu_baseline']['cores']} threads")
+    extra["environment"] = environment()
 
     g = dec["fused2_act"]
     line = {
@@ -768,6 +843,7 @@ def main():
             "what": "q4_gemm per call: X image + weight image + matrix-core GEMM",
             "achieved_prepacked_weights": round(gm["image_tflops"], 1),
             "frac_prepacked_weights": round(gm["image_tflops"] / F16_MFMA_PEAK_TFLOPS, 4),
+            "cpu_baseline": extra.get("gemm_cpu_baseline"),
         }
     print(json.dumps(line), flush=True)
 

@@ -126,8 +126,24 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _empty(shape, dtype, like):
-    return torch.empty(shape, dtype=dtype, device=like.device)
+def _alloc_stream(stream):
+    """The torch stream that owns memory this call allocates: the stream the
+    kernels are enqueued on, so that the caching allocator hands a freed block
+    (an "auto" workspace, dropped on return) to no other stream's work while
+    the kernels may still use it."""
+    if stream is None:
+        return None
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _empty(shape, dtype, like, stream=None):
+    s = _alloc_stream(stream)
+    if s is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    with torch.cuda.stream(s):
+        return torch.empty(shape, dtype=dtype, device=like.device)
 
 
 # ---- quantisers ---------------------------------------------------------------
@@ -135,8 +151,8 @@ def _empty(shape, dtype, like):
 def q4_quantize(w, w_qs=None, w_d=None, stream=None):
     """W [N, K] (f32 or bf16) -> (qs uint8 [N, K/32, 16], d int16 bits [N, K/32])."""
     N, K = w.shape
-    w_qs = _empty((N, K // 32, 16), torch.uint8, w) if w_qs is None else w_qs
-    w_d = _empty((N, K // 32), torch.int16, w) if w_d is None else w_d
+    w_qs = _empty((N, K // 32, 16), torch.uint8, w, stream) if w_qs is None else w_qs
+    w_d = _empty((N, K // 32), torch.int16, w, stream) if w_d is None else w_d
     _check("q4_quantize", lib().q4_quantize(_p(w), _dt(w), N, K, _p(w_qs), _p(w_d), _stream(stream)))
     return w_qs, w_d
 
@@ -144,8 +160,8 @@ def q4_quantize(w, w_qs=None, w_d=None, stream=None):
 def q8_1_quantize_act(x, x_qs=None, x_ds=None, stream=None):
     """X [M, K] (f32 or bf16) -> (qs int8 [M, K], ds int16 bits [M, K/32, 2])."""
     M, K = x.shape
-    x_qs = _empty((M, K), torch.int8, x) if x_qs is None else x_qs
-    x_ds = _empty((M, K // 32, 2), torch.int16, x) if x_ds is None else x_ds
+    x_qs = _empty((M, K), torch.int8, x, stream) if x_qs is None else x_qs
+    x_ds = _empty((M, K // 32, 2), torch.int16, x, stream) if x_ds is None else x_ds
     _check("q8_1_quantize_act",
            lib().q8_1_quantize_act(_p(x), _dt(x), M, K, _p(x_qs), _p(x_ds), _stream(stream)))
     return x_qs, x_ds
@@ -154,9 +170,9 @@ def q8_1_quantize_act(x, x_qs=None, x_ds=None, stream=None):
 def affine4_quantize(w, group_size=64, w_q=None, scales=None, biases=None, stream=None):
     """W [N, K] (bf16 or f32) -> (q uint8 [N, K/2], scales, biases int16 bits [N, K/G])."""
     N, K = w.shape
-    w_q = _empty((N, K // 2), torch.uint8, w) if w_q is None else w_q
-    scales = _empty((N, K // group_size), torch.int16, w) if scales is None else scales
-    biases = _empty((N, K // group_size), torch.int16, w) if biases is None else biases
+    w_q = _empty((N, K // 2), torch.uint8, w, stream) if w_q is None else w_q
+    scales = _empty((N, K // group_size), torch.int16, w, stream) if scales is None else scales
+    biases = _empty((N, K // group_size), torch.int16, w, stream) if biases is None else biases
     _check("affine4_quantize", lib().affine4_quantize(_p(w), _dt(w), N, K, group_size, _p(w_q), _p(scales),
                                                       _p(biases), _stream(stream)))
     return w_q, scales, biases
@@ -165,14 +181,14 @@ def affine4_quantize(w, group_size=64, w_q=None, scales=None, biases=None, strea
 def q4_dequantize(w_qs, w_d, out_dtype=torch.float16, out=None, stream=None):
     N, nb = w_d.shape[0], w_d.shape[1]
     K = nb * 32
-    out = _empty((N, K), out_dtype, w_qs) if out is None else out
+    out = _empty((N, K), out_dtype, w_qs, stream) if out is None else out
     _check("q4_dequantize", lib().q4_dequantize(_p(w_qs), _p(w_d), N, K, _p(out), _dt(out), _stream(stream)))
     return out
 
 
 def affine4_dequantize(w_q, scales, biases, group_size=64, out_dtype=torch.float16, out=None, stream=None):
     N, K = w_q.shape[0], w_q.shape[1] * 2
-    out = _empty((N, K), out_dtype, w_q) if out is None else out
+    out = _empty((N, K), out_dtype, w_q, stream) if out is None else out
     _check("affine4_dequantize", lib().affine4_dequantize(_p(w_q), _p(scales), _p(biases), group_size, N, K,
                                                           _p(out), _dt(out), _stream(stream)))
     return out
@@ -184,7 +200,7 @@ def q4_gemv(w_qs, w_d, x_qs, x_ds, y=None, stream=None):
     """y float32 [M, N] from Q4_0 planes and Q8_1 activation planes."""
     N = w_d.shape[0]
     M, K = x_qs.shape
-    y = _empty((M, N), torch.float32, x_qs) if y is None else y
+    y = _empty((M, N), torch.float32, x_qs, stream) if y is None else y
     _check("q4_gemv", lib().q4_gemv(_p(w_qs), _p(w_d), _p(x_qs), _p(x_ds), _p(y), M, N, K, _stream(stream)))
     return y
 
@@ -192,8 +208,8 @@ def q4_gemv(w_qs, w_d, x_qs, x_ds, y=None, stream=None):
 def q4_gemv_fused2(w0_qs, w0_d, w1_qs, w1_d, x_qs, x_ds, y0=None, y1=None, stream=None):
     N0, N1 = w0_d.shape[0], w1_d.shape[0]
     M, K = x_qs.shape
-    y0 = _empty((M, N0), torch.float32, x_qs) if y0 is None else y0
-    y1 = _empty((M, N1), torch.float32, x_qs) if y1 is None else y1
+    y0 = _empty((M, N0), torch.float32, x_qs, stream) if y0 is None else y0
+    y1 = _empty((M, N1), torch.float32, x_qs, stream) if y1 is None else y1
     _check("q4_gemv_fused2", lib().q4_gemv_fused2(_p(w0_qs), _p(w0_d), N0, _p(w1_qs), _p(w1_d), N1, _p(x_qs),
                                                   _p(x_ds), _p(y0), _p(y1), M, K, _stream(stream)))
     return y0, y1
@@ -204,7 +220,7 @@ def q4_gemv_act(w_qs, w_d, x, y=None, stream=None):
     the kernel; bit-identical to q8_1_quantize_act followed by q4_gemv."""
     N = w_d.shape[0]
     M, K = x.shape
-    y = _empty((M, N), torch.float32, x) if y is None else y
+    y = _empty((M, N), torch.float32, x, stream) if y is None else y
     _check("q4_gemv_act", lib().q4_gemv_act(_p(w_qs), _p(w_d), _p(x), _dt(x), _p(y), M, N, K, _stream(stream)))
     return y
 
@@ -212,8 +228,8 @@ def q4_gemv_act(w_qs, w_d, x, y=None, stream=None):
 def q4_gemv_fused2_act(w0_qs, w0_d, w1_qs, w1_d, x, y0=None, y1=None, stream=None):
     N0, N1 = w0_d.shape[0], w1_d.shape[0]
     M, K = x.shape
-    y0 = _empty((M, N0), torch.float32, x) if y0 is None else y0
-    y1 = _empty((M, N1), torch.float32, x) if y1 is None else y1
+    y0 = _empty((M, N0), torch.float32, x, stream) if y0 is None else y0
+    y1 = _empty((M, N1), torch.float32, x, stream) if y1 is None else y1
     _check("q4_gemv_fused2_act", lib().q4_gemv_fused2_act(_p(w0_qs), _p(w0_d), N0, _p(w1_qs), _p(w1_d), N1,
                                                           _p(x), _dt(x), _p(y0), _p(y1), M, K,
                                                           _stream(stream)))
@@ -233,7 +249,7 @@ def q4_gemv_multi(mats, x_qs, x_ds, ys=None, stream=None):
     """One launch over several Q4_0 matrices [(qs, d), ...] sharing the Q8_1
     activation; returns a list of float32 [M, N_i]."""
     M, K = x_qs.shape
-    ys = [_empty((M, d.shape[0]), torch.float32, x_qs) for _, d in mats] if ys is None else ys
+    ys = [_empty((M, d.shape[0]), torch.float32, x_qs, stream) for _, d in mats] if ys is None else ys
     qs, ds, rows, yp = _mat_arrays(mats, ys)
     _check("q4_gemv_multi", lib().q4_gemv_multi(len(mats), qs, ds, rows, _p(x_qs), _p(x_ds), yp, M, K,
                                                 _stream(stream)))
@@ -243,7 +259,7 @@ def q4_gemv_multi(mats, x_qs, x_ds, ys=None, stream=None):
 def q4_gemv_multi_act(mats, x, ys=None, stream=None):
     """q4_gemv_multi on a raw bf16 / f32 activation, quantised to Q8_1 in the kernel."""
     M, K = x.shape
-    ys = [_empty((M, d.shape[0]), torch.float32, x) for _, d in mats] if ys is None else ys
+    ys = [_empty((M, d.shape[0]), torch.float32, x, stream) for _, d in mats] if ys is None else ys
     qs, ds, rows, yp = _mat_arrays(mats, ys)
     _check("q4_gemv_multi_act", lib().q4_gemv_multi_act(len(mats), qs, ds, rows, _p(x), _dt(x), yp, M, K,
                                                         _stream(stream)))
@@ -252,22 +268,23 @@ def q4_gemv_multi_act(mats, x, ys=None, stream=None):
 
 # ---- GEMM -----------------------------------------------------------------------------
 
-def _workspace(workspace, M, N, K, fmt, like):
+def _workspace(workspace, M, N, K, fmt, like, stream=None):
     """"auto": a fresh scratch tensor of q4_gemm_workspace_size bytes (None if
-    that is 0); None: no workspace; else the caller's tensor."""
+    that is 0), owned by the call's stream; None: no workspace; else the
+    caller's tensor."""
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
         n = q4_gemm_workspace_size(M, N, K, fmt)
-        return torch.empty(n, dtype=torch.uint8, device=like.device) if n > 0 else None
+        return _empty((n,), torch.uint8, like, stream) if n > 0 else None
     return workspace
 
 
 def q4_gemm(w_qs, w_d, x, y_dtype=torch.bfloat16, y=None, workspace="auto", stream=None):
     N = w_d.shape[0]
     M, K = x.shape
-    y = _empty((M, N), y_dtype, x) if y is None else y
-    workspace = _workspace(workspace, M, N, K, Q4_FMT_Q4_0, x)
+    y = _empty((M, N), y_dtype, x, stream) if y is None else y
+    workspace = _workspace(workspace, M, N, K, Q4_FMT_Q4_0, x, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("q4_gemm", lib().q4_gemm(_p(w_qs), _p(w_d), _p(x), _dt(x), _p(y), _dt(y), M, N, K, _p(workspace),
                                     ws_bytes, _stream(stream)))
@@ -278,8 +295,8 @@ def affine4_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, 
                  stream=None):
     N = w_q.shape[0]
     M, K = x.shape
-    y = _empty((M, N), y_dtype, x) if y is None else y
-    workspace = _workspace(workspace, M, N, K, Q4_FMT_AFFINE4, x)
+    y = _empty((M, N), y_dtype, x, stream) if y is None else y
+    workspace = _workspace(workspace, M, N, K, Q4_FMT_AFFINE4, x, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("affine4_gemm", lib().affine4_gemm(_p(w_q), _p(scales), _p(biases), group_size, _p(x), _dt(x), _p(y),
                                               _dt(y), M, N, K, _p(workspace), ws_bytes, _stream(stream)))
@@ -291,9 +308,9 @@ def affine4_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, 
 def affine8_quantize(w, group_size=64, w_q=None, scales=None, biases=None, stream=None):
     """W [N, K] (bf16 or f32) -> (q uint8 [N, K], scales, biases int16 bits [N, K/G])."""
     N, K = w.shape
-    w_q = _empty((N, K), torch.uint8, w) if w_q is None else w_q
-    scales = _empty((N, K // group_size), torch.int16, w) if scales is None else scales
-    biases = _empty((N, K // group_size), torch.int16, w) if biases is None else biases
+    w_q = _empty((N, K), torch.uint8, w, stream) if w_q is None else w_q
+    scales = _empty((N, K // group_size), torch.int16, w, stream) if scales is None else scales
+    biases = _empty((N, K // group_size), torch.int16, w, stream) if biases is None else biases
     _check("affine8_quantize", lib().affine8_quantize(_p(w), _dt(w), N, K, group_size, _p(w_q), _p(scales),
                                                       _p(biases), _stream(stream)))
     return w_q, scales, biases
@@ -301,7 +318,7 @@ def affine8_quantize(w, group_size=64, w_q=None, scales=None, biases=None, strea
 
 def affine8_dequantize(w_q, scales, biases, group_size=64, out_dtype=torch.float16, out=None, stream=None):
     N, K = w_q.shape
-    out = _empty((N, K), out_dtype, w_q) if out is None else out
+    out = _empty((N, K), out_dtype, w_q, stream) if out is None else out
     _check("affine8_dequantize", lib().affine8_dequantize(_p(w_q), _p(scales), _p(biases), group_size, N, K,
                                                           _p(out), _dt(out), _stream(stream)))
     return out
@@ -312,10 +329,10 @@ def affine8_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, 
     """Y [M, N] = X . dequant(W)^T for affine 8-bit weights (workspace "auto": allocated when M needs one)."""
     N, K = w_q.shape
     M = x.shape[0]
-    y = _empty((M, N), y_dtype, x) if y is None else y
+    y = _empty((M, N), y_dtype, x, stream) if y is None else y
     if isinstance(workspace, str):
         n = int(lib().affine8_gemm_workspace_size(M, N, K))
-        workspace = _empty((n,), torch.uint8, x) if n > 0 else None
+        workspace = _empty((n,), torch.uint8, x, stream) if n > 0 else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("affine8_gemm", lib().affine8_gemm(_p(w_q), _p(scales), _p(biases), group_size, _p(x), _dt(x), _p(y),
                                               _dt(y), M, N, K, _p(workspace), ws_bytes, _stream(stream)))
@@ -324,6 +341,18 @@ def affine8_gemm(w_q, scales, biases, x, group_size=64, y_dtype=torch.bfloat16, 
 
 def q4_gemm_workspace_size(M, N, K, fmt=Q4_FMT_Q4_0) -> int:
     return int(lib().q4_gemm_workspace_size(M, N, K, fmt))
+
+
+def affine8_gemm_workspace_size(M, N, K) -> int:
+    return int(lib().affine8_gemm_workspace_size(M, N, K))
+
+
+def q4_weight_image_size(N, K, fmt=Q4_FMT_Q4_0) -> int:
+    return int(lib().q4_weight_image_size(N, K, fmt))
+
+
+def q4_gemm_image_workspace_size(M, K) -> int:
+    return int(lib().q4_gemm_image_workspace_size(M, K))
 
 
 def q4_pack_weight_image(w_q, w_s, w_b=None, fmt=None, image=None, stream=None):
@@ -335,7 +364,7 @@ def q4_pack_weight_image(w_q, w_s, w_b=None, fmt=None, image=None, stream=None):
     K = w_s.shape[1] * (32 if fmt == Q4_FMT_Q4_0 else 64)
     if image is None:
         n = lib().q4_weight_image_size(N, K, fmt)
-        image = _empty((max(n, 16),), torch.uint8, w_q)
+        image = _empty((max(n, 16),), torch.uint8, w_q, stream)
     _check("q4_pack_weight_image", lib().q4_pack_weight_image(fmt, _p(w_q), _p(w_s), _p(w_b),
                                                               N, K, _p(image), _stream(stream)))
     return image
@@ -344,9 +373,9 @@ def q4_pack_weight_image(w_q, w_s, w_b=None, fmt=None, image=None, stream=None):
 def q4_gemm_image(image, x, N, fmt=Q4_FMT_Q4_0, y_dtype=torch.bfloat16, y=None, workspace=None, stream=None):
     """Y [M, N] = X . dequant(W)^T from a weight image (q4_pack_weight_image)."""
     M, K = x.shape
-    y = _empty((M, N), y_dtype, x) if y is None else y
+    y = _empty((M, N), y_dtype, x, stream) if y is None else y
     if workspace is None:
-        workspace = _empty((max(lib().q4_gemm_image_workspace_size(M, K), 16),), torch.uint8, x)
+        workspace = _empty((max(lib().q4_gemm_image_workspace_size(M, K), 16),), torch.uint8, x, stream)
     _check("q4_gemm_image", lib().q4_gemm_image(fmt, _p(image), _p(x), _dt(x), _p(y), _dt(y), M, N, K,
                                                 _p(workspace), workspace.numel() * workspace.element_size(),
                                                 _stream(stream)))
@@ -356,7 +385,7 @@ def q4_gemm_image(image, x, N, fmt=Q4_FMT_Q4_0, y_dtype=torch.bfloat16, y=None, 
 def dense_gemm(x, w_f16, y_dtype=torch.bfloat16, y=None, stream=None):
     N, K = w_f16.shape
     M = x.shape[0]
-    y = _empty((M, N), y_dtype, x) if y is None else y
+    y = _empty((M, N), y_dtype, x, stream) if y is None else y
     _check("dense_gemm", lib().dense_gemm(_p(x), _dt(x), _p(w_f16), _p(y), _dt(y), M, N, K, _stream(stream)))
     return y
 

@@ -38,6 +38,12 @@ bool env_int(const char* name, int64_t* out) {
     return true;
 }
 
+// Values Q4_KEY_FORCE_PATH accepts: automatic (-1), or a path q4_gemm /
+// affine4_gemm can run.
+bool force_path_ok(int64_t v) {
+    return v == -1 || v == Q4_PATH_SKINNY || v == Q4_PATH_MFMA || v == Q4_PATH_DEQUANT_GEMM;
+}
+
 // Environment overrides, read once per process and clamped (the clamped
 // token-count gate pattern of vllm.cpp issue #838, Scope).
 void read_env() {
@@ -45,7 +51,8 @@ void read_env() {
         int64_t v;
         if (env_int("Q4_SKINNY_MAX_M", &v)) g_skinny_max_m = clamp64(v, 0, kSkinnyLimit);
         if (env_int("Q4_DEQUANT_MIN_M", &v)) g_dequant_min_m = clamp64(v, 1, kMaxDim + 1);
-        if (env_int("Q4_FORCE_PATH", &v)) g_force_path = clamp64(v, -1, Q4_PATH_DEQUANT_GEMM);
+        // the setter's rule: a value it would reject leaves the default
+        if (env_int("Q4_FORCE_PATH", &v) && force_path_ok(v)) g_force_path = v;
     });
 }
 
@@ -117,7 +124,7 @@ int q4_set_dispatch(int key, int64_t value) {
         case Q4_KEY_SKINNY_MAX_M: g_skinny_max_m = clamp64(value, 0, kSkinnyLimit); return Q4_OK;
         case Q4_KEY_DEQUANT_MIN_M: g_dequant_min_m = clamp64(value, 1, kMaxDim + 1); return Q4_OK;
         case Q4_KEY_FORCE_PATH:
-            if (value < -1 || value > Q4_PATH_DEQUANT_GEMM || value == Q4_PATH_GEMV) return Q4_ERR_ARG;
+            if (!force_path_ok(value)) return Q4_ERR_ARG;
             g_force_path = value;
             return Q4_OK;
         default: return Q4_ERR_ARG;

@@ -154,8 +154,10 @@ struct GemmArgs {
     float* part;       // k_gemm_pk with ksplit > 1: fp32 partial results [ksplit][M][N]
 };
 
+// Two binary32 values -> packed binary16, each rounded to nearest even (the
+// rounding of the X image, so that every path converts X alike).
 __device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
-    return h2_bits(__builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(lo, hi)));
+    return f32_to_f16(lo) | (f32_to_f16(hi) << 16);
 }
 
 // 8 consecutive X values (bf16 or f32) -> 8 binary16 values (skinny kernel).
@@ -1862,7 +1864,8 @@ __global__ __launch_bounds__(256) void k_splitk_sum(const float* __restrict__ pa
             *reinterpret_cast<floatx4_t*>(reinterpret_cast<float*>(y) + e) = t;
         }
     } else {
-        for (int64_t i = e; i < mn; i++) {
+        const int64_t end = e + 4 < mn ? e + 4 : mn;   // this thread's 4 outputs only
+        for (int64_t i = e; i < end; i++) {
             float t = part[i];
             for (int p = 1; p < ksplit; p++) t += part[(int64_t)p * mn + i];
             store_y(y, YDT, i, t);

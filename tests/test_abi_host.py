@@ -272,7 +272,8 @@ sys.path.insert(0, {root!r})
 from gemv_q4_affine_amd import binding as B
 print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUANT_MIN_M),
       B.q4_get_dispatch(B.Q4_KEY_FORCE_PATH),
-      B.q4_dispatch_path(19, 4096, 4096), B.q4_dispatch_path(64, 4096, 4096, have_workspace=True))
+      B.q4_dispatch_path(19, 4096, 4096), B.q4_dispatch_path(64, 4096, 4096, have_workspace=True),
+      int(B.q4_gemm_workspace_size(64, 4096, 4096) > 0))
 """
 
 
@@ -282,7 +283,11 @@ print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUA
     ({"Q4_SKINNY_MAX_M": "-3"}, (0, None, -1, B.Q4_PATH_MFMA, B.Q4_PATH_MFMA)),
     ({"Q4_SKINNY_MAX_M": "8", "Q4_DEQUANT_MIN_M": "64"}, (8, 64, -1, B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM)),
     ({"Q4_FORCE_PATH": "3"}, (None, None, 3, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM)),
-    ({"Q4_FORCE_PATH": "17"}, (None, None, 3, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM)),
+    # values the setter rejects leave the automatic dispatch (17: no such path;
+    # 0: the integer-dot GEMV, which q4_gemm / affine4_gemm do not run)
+    ({"Q4_FORCE_PATH": "17"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
+    ({"Q4_FORCE_PATH": "0"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA, 1)),
+    ({"Q4_FORCE_PATH": "-5"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
     ({"Q4_FORCE_PATH": "junk"}, (None, None, -1, None, None)),
 ])
 def test_dispatch_environment_overrides(env, expect):

@@ -838,3 +838,158 @@ def test_random_shapes_gemv(case):
         assert torch.equal(B.q4_gemv_act(*t0, x), y)
         a0, a1 = B.q4_gemv_fused2_act(*t0, *t1, x)
         assert torch.equal(a0, y0) and torch.equal(a1, y1)
+
+
+# ---------------------------------------------------------------------------
+# the large-M configuration of the in-kernel-converting GEMM (no workspace)
+# and of the dense binary16 GEMM, at the prefill sizes: MLX issue #4621,
+# Repro (2048 and 8192 tokens against W 12288 x 4096)
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def prefill_q4():
+    wl = synth.PREFILL
+    W, X = synth.workload_inputs(wl)
+    qs, d = oracle.q4_0_quantize(W)
+    xb = synth.bf16_bits(X)
+    return dict(qs=qs, d=d, xb=xb, Xf64=synth.bf16_bits_to_f32(xb).astype(np.float64),
+                What=oracle.q4_0_dequantize(qs, d))
+
+
+def test_q4_gemm_no_workspace_prefill_sampled(prefill_q4):
+    p = prefill_q4
+    say("q4_gemm M=2048 without a workspace (in-kernel X conversion)")
+    y = B.q4_gemm(dev(p["qs"]), dev(p["d"]), dev(p["xb"]).view(torch.bfloat16), workspace=None)
+    torch.cuda.synchronize()
+    e = _sampled_check(y, p["Xf64"], p["What"], 5)
+    say(f"  sampled rel err {e:.3e}")
+    assert e <= BAR
+
+
+def test_dense_and_dequant_path_prefill_sampled(prefill_q4):
+    p = prefill_q4
+    M, N, K = p["xb"].shape[0], p["d"].shape[0], p["xb"].shape[1]
+    tq, td, tx = dev(p["qs"]), dev(p["d"]), dev(p["xb"]).view(torch.bfloat16)
+    say("dense_gemm M=2048 on dequantised binary16 weights")
+    w16 = B.q4_dequantize(tq, td, out_dtype=torch.float16)
+    z = B.dense_gemm(tx, w16)
+    torch.cuda.synchronize()
+    e = _sampled_check(z, p["Xf64"], p["What"], 6)
+    say(f"  dense sampled rel err {e:.3e}")
+    assert e <= BAR
+    say("q4_gemm M=2048 forced dequantise-then-GEMM")
+    ws = torch.empty(N * K * 2, dtype=torch.uint8, device="cuda")
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+    try:
+        y = B.q4_gemm(tq, td, tx, workspace=ws)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+    torch.cuda.synchronize()
+    assert torch.equal(y, z)
+
+
+@pytest.mark.parametrize("M", [2048, 8192])
+def test_affine_large_m_no_workspace_and_affine8_sampled(M):
+    wl = synth.AFFINE
+    say(f"affine4 / affine8 M={M} N={wl.N} K={wl.K}")
+    W, X = synth.workload_inputs(wl, M=M)
+    wb = synth.bf16_bits(W)
+    xb = synth.bf16_bits(X)
+    Xf64 = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    tx = dev(xb).view(torch.bfloat16)
+    q, s, b = oracle.affine4_quantize(wb, 64)
+    y = B.affine4_gemm(dev(q), dev(s), dev(b), tx, workspace=None)
+    torch.cuda.synchronize()
+    e = _sampled_check(y, Xf64, oracle.affine4_dequantize(q, s, b), M + 1)
+    say(f"  affine4 without workspace: sampled rel err {e:.3e}")
+    assert e <= BAR
+    del y
+    q8, s8, b8 = oracle.affine8_quantize(wb, 64)
+    y = B.affine8_gemm(dev(q8), dev(s8), dev(b8), tx)
+    torch.cuda.synchronize()
+    e = _sampled_check(y, Xf64, oracle.affine8_dequantize(q8, s8, b8), M + 2)
+    say(f"  affine8: sampled rel err {e:.3e}")
+    assert e <= BAR
+
+
+def test_splitk_odd_output_count():
+    """K split over workgroups with M*N odd (the partial sums' scalar tail):
+    the same as the unsplit kernel within the bar, against the oracle, and a
+    call that takes milliseconds, not seconds."""
+    M, N, K = 33, 4095, 4096
+    rng = np.random.default_rng(3301)
+    qs, d = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    xb = synth.bf16_bits(synth.activations(rng, M, K))
+    tq, td, tx = dev(qs), dev(d), dev(xb).view(torch.bfloat16)
+    full = B.q4_gemm_workspace_size(M, N, K)
+    imgs = B.q4_gemm_image_workspace_size(M, K) + B.q4_weight_image_size(N, K)
+    assert full > imgs, "this shape should split K"
+    ys = {}
+    for name, nbytes in (("split", full), ("unsplit", imgs)):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)       # warm
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        ys[name] = B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1)
+        say(f"  {name}: {ms:.3f} ms")
+        assert ms < 20.0, (name, ms)
+    ref = _q4_gemm_ref(qs, d, synth.bf16_bits_to_f32(xb).astype(np.float64))
+    for name, y in ys.items():
+        assert rel(out_f64(y), ref) <= 1e-3, name
+    assert rel(out_f64(ys["split"]), out_f64(ys["unsplit"])) <= 1e-5
+
+
+def test_side_stream_auto_workspace_is_not_reused_early():
+    """q4_gemm on a side stream with workspace "auto": the scratch tensor
+    belongs to that stream, so work on the default stream right after the call
+    cannot be handed the same memory while the side stream still uses it."""
+    M, N, K = 1024, 4096, 4096
+    rng = np.random.default_rng(404)
+    qs, d = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    tq, td = dev(qs), dev(d)
+    x = bf16_dev(synth.activations(rng, M, K))
+    want = B.q4_gemm(tq, td, x)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        y = B.q4_gemm(tq, td, x, stream=side)
+        # default-stream allocations and writes of the workspace's size
+        junk = torch.full((B.q4_gemm_workspace_size(M, N, K),), 255, dtype=torch.uint8, device="cuda")
+        junk.fill_(7)
+        torch.cuda.synchronize()
+        assert torch.equal(y, want)
+        del junk
+
+
+def test_f32_activation_rounds_to_nearest_even():
+    """f32 X on the MFMA paths is rounded to binary16 to nearest even on every
+    path (with and without a workspace), so the result is the fp32 product of
+    the RNE-rounded X with the binary16 weights (q-8)*d: values 1 + 3*2^-12
+    round up to 1 + 2^-10 (toward zero they would give 1, a bias of about
+    1e-3 on two thirds of the x)."""
+    M, N, K = 96, 256, 1024
+    rng = np.random.default_rng(55)
+    qs, d = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    sign = np.where(rng.random((M, K)) < 0.5, -1.0, 1.0).astype(np.float32)
+    X = (sign * np.float32(1 + 3 * 2 ** -12) * rng.integers(1, 4, (M, K)).astype(np.float32)).astype(np.float32)
+    Xr = oracle.f16_bits_to_f32(oracle.f32_to_f16_bits(X)).astype(np.float64)
+    assert not np.array_equal(Xr, X.astype(np.float64))
+    W16 = oracle.f16_bits_to_f32(oracle.q4_0_dequantize_half(qs, d, "f16")).astype(np.float64)
+    ref = oracle.matmul_f64(Xr, W16)
+    tq, td, tx = dev(qs), dev(d), dev(X)
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
+    try:
+        for ws in ("auto", None):
+            y = B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)
+            torch.cuda.synchronize()
+            e = rel(out_f64(y), ref)
+            say(f"  f32 X workspace={ws}: rel {e:.3e} against RNE-rounded X")
+            assert e <= 2e-5, (ws, e)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
