@@ -21,7 +21,7 @@ Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_DTYPE, Q4_ERR_HIP, Q4_ERR
 Q4_F32, Q4_BF16, Q4_F16 = 0, 1, 2
 Q4_FMT_Q4_0, Q4_FMT_AFFINE4 = 0, 1
 Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM = 0, 1, 2, 3
-Q4_KEY_SKINNY_MAX_M, Q4_KEY_DEQUANT_MIN_M, Q4_KEY_FORCE_PATH = 0, 1, 2
+Q4_KEY_SKINNY_MAX_M, Q4_KEY_DEQUANT_MIN_M, Q4_KEY_FORCE_PATH, Q4_KEY_TILE_ROWS = 0, 1, 2, 3
 Q4_GEMV_MAX_M = 16
 Q4_GEMV_ACT_MAX_M = 4
 Q4_GEMV_MAX_MATS = 4

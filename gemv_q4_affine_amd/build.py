@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq4.so")
 
-SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "affine8.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip", "affine8.hip", "capi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -34,6 +34,8 @@ FLAGS = [
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # gemm_big.hip names m0 among its copy instruction's clobbers on purpose
+    "-Wno-inline-asm",
     "-I", INCLUDE,
     "-I", CSRC,
 ]
@@ -50,7 +52,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]

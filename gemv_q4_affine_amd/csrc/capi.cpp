@@ -24,6 +24,7 @@ constexpr int64_t kSkinnyLimit = 64;          // the skinny kernel's largest M
 std::atomic<int64_t> g_skinny_max_m{32};
 std::atomic<int64_t> g_dequant_min_m{kMaxDim + 1};   // dequantise-then-GEMM never wins by default
 std::atomic<int64_t> g_force_path{-1};
+std::atomic<int64_t> g_tile_rows{128};
 std::once_flag g_env_once;
 
 int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -53,6 +54,7 @@ void read_env() {
         if (env_int("Q4_DEQUANT_MIN_M", &v)) g_dequant_min_m = clamp64(v, 1, kMaxDim + 1);
         // the setter's rule: a value it would reject leaves the default
         if (env_int("Q4_FORCE_PATH", &v) && force_path_ok(v)) g_force_path = v;
+        if (env_int("Q4_TILE_ROWS", &v) && (v == 128 || v == 256)) g_tile_rows = v;
     });
 }
 
@@ -80,6 +82,11 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 }  // namespace
 
 namespace q4 {
+
+bool use_big_tiles(int64_t M, int64_t N, int64_t K) {
+    read_env();
+    return g_tile_rows == 256 && gemm_big_applies(M, N, K);
+}
 
 int current_cu_count() {
     constexpr int kMaxDevices = 64;
@@ -127,6 +134,10 @@ int q4_set_dispatch(int key, int64_t value) {
             if (!force_path_ok(value)) return Q4_ERR_ARG;
             g_force_path = value;
             return Q4_OK;
+        case Q4_KEY_TILE_ROWS:
+            if (value != 128 && value != 256) return Q4_ERR_ARG;
+            g_tile_rows = value;
+            return Q4_OK;
         default: return Q4_ERR_ARG;
     }
 }
@@ -138,6 +149,7 @@ int q4_get_dispatch(int key, int64_t* value) {
         case Q4_KEY_SKINNY_MAX_M: *value = g_skinny_max_m; return Q4_OK;
         case Q4_KEY_DEQUANT_MIN_M: *value = g_dequant_min_m; return Q4_OK;
         case Q4_KEY_FORCE_PATH: *value = g_force_path; return Q4_OK;
+        case Q4_KEY_TILE_ROWS: *value = g_tile_rows; return Q4_OK;
         default: return Q4_ERR_ARG;
     }
 }

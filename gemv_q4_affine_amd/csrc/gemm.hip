@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "gemm_common.hpp"
 #include "kernels.hpp"
 
 namespace q4 {
@@ -53,10 +54,6 @@ namespace q4 {
 // from LDS uses the same kofs.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ uint32_t perm(uint32_t a, uint32_t sel) { return __builtin_amdgcn_perm(a, a, sel); }
-
-__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
-__device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
 // Two nibble codes (in bits 0-3 and 16-19 after masking) -> binary16 (q-8)*d.
 __device__ __forceinline__ uint32_t q4_pair(uint32_t t, half2_t dd) {
@@ -97,8 +94,6 @@ struct RawAff {     // raw affine data: 8 nibble bytes, scale and bias (bf16 bit
     uint32_t s, b;
 };
 
-// binary32 -> binary16 bits (RNE), for the affine scale and bias.
-__device__ __forceinline__ uint32_t f16b(float f) { return f32_to_f16(f); }
 
 // Affine: byte i holds elements 2i (low) and 2i+1 (high).  Lane group g takes
 // bytes 8g..8g+7 = elements 16g..16g+15: s = 0 gets 16g+v, s = 1 gets
@@ -140,19 +135,6 @@ __device__ __forceinline__ Frag16 affine_frag(const RawAff& r) {
 // ---------------------------------------------------------------------------
 constexpr int kStep = 64;            // K per iteration
 constexpr int kLdsStride = 72;       // halves per staged X row (64 + 8 padding)
-
-struct GemmArgs {
-    const void* a;     // Q4_0 qs / affine q / dense binary16 W
-    const void* b;     // Q4_0 d / affine scales
-    const void* c;     // affine biases
-    const void* x;
-    void* y;
-    int M, N, K;
-    int m_tiles;       // workgroup tiles along M
-    int n_tiles;       // workgroup tiles along N
-    int ksplit;        // k_gemm_pk: K parts per tile (<= 1: none)
-    float* part;       // k_gemm_pk with ksplit > 1: fp32 partial results [ksplit][M][N]
-};
 
 // Two binary32 values -> packed binary16, each rounded to nearest even (the
 // rounding of the X image, so that every path converts X alike).
@@ -217,15 +199,6 @@ __device__ __forceinline__ void store_y(void* y, int ydt, int64_t off, float v) 
     else reinterpret_cast<uint16_t*>(y)[off] = (uint16_t)f32_to_bf16(v);
 }
 
-// Raw weight data of one whole 32-weight block of one column.
-struct BlkQ4 { u32x4_t q; uint32_t d; };
-struct BlkAff { u32x4_t q; uint32_t s, b; };
-struct BlkF16 { u32x4_t h[4]; };
-
-template <int WF> struct BlkOf;
-template <> struct BlkOf<WF_Q4_0> { using T = BlkQ4; };
-template <> struct BlkOf<WF_AFFINE4> { using T = BlkAff; };
-template <> struct BlkOf<WF_DENSE16> { using T = BlkF16; };
 
 // Block kblk of column n.  Callers pass a clamped, valid (n, kblk): the load
 // is unconditional so that it never waits inside a branch.
@@ -252,21 +225,6 @@ __device__ __forceinline__ typename BlkOf<WF>::T load_blk(const GemmArgs& a, int
     return r;
 }
 
-// A block past the end of K (K = 32 mod 64) contributes zeros.
-template <int WF>
-__device__ __forceinline__ void zero_blk(typename BlkOf<WF>::T& r, bool keep) {
-    if constexpr (WF == WF_Q4_0) {
-        r.d = keep ? r.d : 0u;
-    } else if constexpr (WF == WF_AFFINE4) {
-        r.s = keep ? r.s : 0u;
-        r.b = keep ? r.b : 0u;
-    } else {
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) r.h[t][e] = keep ? r.h[t][e] : 0u;
-    }
-}
 
 // Elements 8t..8t+7 of a block as 8 binary16 values, t = 0..3.
 template <int WF>
@@ -336,32 +294,6 @@ struct WStage<WF_DENSE16, NT> {
     uint32_t unused;
 };
 
-__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-__device__ __forceinline__ void dma2(const void* src, void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 2, 0, 0);
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and
-// 15:14, expcnt 6:4, lgkmcnt 11:8).
-#define Q4_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 0xF) | ((((n) >> 4) & 3) << 14))
-
-// Workgroup barrier for the main loop: this wave's LDS writes are complete
-// (lgkmcnt 0) and all but the newest `vm` vector-memory loads have landed,
-// which covers the direct-to-LDS copies the next step reads.  Unlike
-// __syncthreads() it does not wait for every outstanding load (the release
-// fence there would, because a direct-to-LDS copy counts as a pending LDS
-// store).  The signal fences stop the compiler from moving memory accesses
-// across the barrier; they emit no instructions.
-template <int VM>
-__device__ __forceinline__ void step_barrier() {
-    static_assert(VM >= 0 && VM < 64, "vmcnt range (63 = no constraint)");
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0070 | (VM & 0xF) | (((VM >> 4) & 3) << 14));   // lgkmcnt(0), vmcnt(VM)
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 template <int WF, int MT, int NT, int XDT, int YDT>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
@@ -612,91 +544,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 constexpr int kPkSlots = 6;              // ring depth: steps k..k+5 resident
 constexpr int kPkAhead = kPkSlots - 1;   // producers request step k+5 during step k
 constexpr int kPkProducers = 4;          // producer waves, one per SIMD
-constexpr int kImgRows = 128;            // rows of an image tile
-constexpr int kImgTile = kImgRows * 64;  // halves of an image tile (16 KiB)
-
-// Row r of an image tile: chunk c sits at c ^ img_swz(r).  A permutation of
-// rows 0..7 and, separately, of the even and of the odd rows among 0..15.
-__device__ __forceinline__ int img_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// Shift-free dequantiser of the packed-X kernel.
-//
-// A nibble in bits 0-3 of a binary16 with exponent field 0x64 (value 1024,
-// unit 1) reads as 1024+q; a nibble in bits 4-7 of a binary16 with exponent
-// field 0x54 (value 64, unit 1/16) reads as 64+q.  So the four nibble pairs
-// of a 32-bit word come out of word & 0x000F000F, word & 0x00F000F0 and the
-// same two masks on word >> 8, each with one AND-OR, one packed subtract
-// (exact) and one packed multiply (Q4_0, one rounding) or fma (affine, one
-// rounding): 13 instructions per 8 weights.  The price is the order of the
-// halves inside each 8-weight fragment, which the X tile in LDS copies:
-//   Q4_0   (bytes carry elements b and b+16): positions hold k = 0,2,1,3,4,6,5,7
-//   affine (bytes carry elements 2b, 2b+1):  positions hold k = 0,4,1,5,2,6,3,7
-// The two masks live in VGPRs (NibMasks, made opaque once per kernel) so that
-// each AND-OR is one v_and_or_b32 (a gfx9 VOP3 takes no literal and one SGPR).
-struct NibMasks {
-    uint32_t lo, hi;
-    __device__ __forceinline__ static NibMasks make() {
-        NibMasks m{0x000F000Fu, 0x00F000F0u};
-        asm volatile("" : "+v"(m.lo), "+v"(m.hi));
-        return m;
-    }
-};
-__device__ __forceinline__ uint32_t nib_lo(uint32_t w, const NibMasks& m) { return (w & m.lo) | 0x64006400u; }   // 1024+q
-__device__ __forceinline__ uint32_t nib_hi(uint32_t w, const NibMasks& m) { return (w & m.hi) | 0x54005400u; }   // 64+q
-
-// Per-block constants of the dequantiser: Q4_0 d in both halves; affine
-// scale and bias in both halves (binary16).
-struct BlkConst {
-    half2_t c0, c1;
-};
-template <int WF>
-__device__ __forceinline__ BlkConst blk_const(const typename BlkOf<WF>::T& r) {
-    if constexpr (WF == WF_Q4_0) {
-        const half2_t dd = as_h2(__builtin_amdgcn_perm(r.d, r.d, 0x01000100u));
-        return {dd, dd};
-    } else {
-        static_assert(WF == WF_AFFINE4, "quantised formats only");
-        const uint32_t s16 = f16b(bf16_to_f32(r.s));
-        const uint32_t b16 = f16b(bf16_to_f32(r.b));
-        return {as_h2(s16 | (s16 << 16)), as_h2(b16 | (b16 << 16))};
-    }
-}
-
-// The 8 weights of 32-bit word w of a block, into their fragment slots.
-//  Q4_0: word w holds the low nibbles of elements 4w..4w+3 (fragment w/2,
-//        pairs 2(w%2), 2(w%2)+1) and the high nibbles 16+4w.. (fragment
-//        2 + w/2, same pairs).
-//  affine: word w holds elements 8w..8w+7 (fragment w, all four pairs).
-template <int WF>
-__device__ __forceinline__ void blk_word(const typename BlkOf<WF>::T& r, const BlkConst& c, int w, const NibMasks& m,
-                                         u32x4_t (&out)[4]) {
-    const uint32_t word = r.q[w];
-    const uint32_t sh = word >> 8;
-    if constexpr (WF == WF_Q4_0) {
-        const half2_t clo = as_h2(0xE408E408u);   // -1032
-        const half2_t chi = as_h2(0xD480D480u);   // -72
-        const int h = w >> 1, p = 2 * (w & 1);
-        out[h][p + 0] = h2_bits((as_h2(nib_lo(word, m)) + clo) * c.c0);
-        out[h][p + 1] = h2_bits((as_h2(nib_lo(sh, m)) + clo) * c.c0);
-        out[2 + h][p + 0] = h2_bits((as_h2(nib_hi(word, m)) + chi) * c.c0);
-        out[2 + h][p + 1] = h2_bits((as_h2(nib_hi(sh, m)) + chi) * c.c0);
-    } else {
-        const half2_t clo = as_h2(0xE400E400u);   // -1024
-        const half2_t chi = as_h2(0xD400D400u);   // -64
-        out[w][0] = h2_bits(__builtin_elementwise_fma(as_h2(nib_lo(word, m)) + clo, c.c0, c.c1));
-        out[w][1] = h2_bits(__builtin_elementwise_fma(as_h2(nib_hi(word, m)) + chi, c.c0, c.c1));
-        out[w][2] = h2_bits(__builtin_elementwise_fma(as_h2(nib_lo(sh, m)) + clo, c.c0, c.c1));
-        out[w][3] = h2_bits(__builtin_elementwise_fma(as_h2(nib_hi(sh, m)) + chi, c.c0, c.c1));
-    }
-}
-
-template <int WF>
-__device__ __forceinline__ void blk_frags_perm(const typename BlkOf<WF>::T& r, const NibMasks& m, u32x4_t (&out)[4]) {
-    const BlkConst c = blk_const<WF>(r);
-#pragma unroll
-    for (int w = 0; w < 4; w++) blk_word<WF>(r, c, w, m, out);
-}
-
 // X -> image (see above).  One thread per 16-byte image chunk.  binary16
 // values are rounded to nearest even (exact for bfloat16 input in binary16's
 // normal range).
@@ -742,16 +589,6 @@ __global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint
     *reinterpret_cast<u32x4_t*>(img + t * 8) = o;
 }
 
-// Weight image for k_gemm_pk: for every 256-column tile and 64-wide K step a
-// contiguous 9 KiB chunk, ((nt * ksteps) + k) * kWChunk bytes in,
-//   bytes    0..8191  nibble blocks, block-plane major: [blk 0..1][col 0..255][16 B]
-//   bytes 8192..9215  Q4_0:   d  as binary16 [blk 0..1][col 0..255]
-//                     affine: s  as bfloat16 [col 0..255], then b [col 0..255]
-// Columns past N and blocks past K are zero (scale 0: the weights are 0).
-// The block-plane order puts the 16-byte block reads of consecutive columns in
-// consecutive LDS units (no bank conflicts), and a chunk travels as nine
-// contiguous 1 KiB direct-to-LDS copies.
-constexpr int kWChunk = 9216;
 
 // planar weights -> image, one workgroup per (256-column tile, 4 K steps).
 // Loads go row by row (8 lanes read a row's 128 contiguous bytes of nibble
@@ -1823,7 +1660,6 @@ int64_t x_image_bytes(int64_t M, int64_t K) {
 
 int64_t weight_image_bytes(int64_t N, int64_t K) { return (N + 255) / 256 * ((K + 63) / 64) * (int64_t)kWChunk; }
 
-int64_t splitk_bytes(int64_t M, int64_t N, int64_t K);
 int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K) {
     return x_image_bytes(M, K) + weight_image_bytes(N, K) + splitk_bytes(M, N, K);
 }
@@ -1887,7 +1723,10 @@ static int splitk_parts(int64_t M, int64_t N, int64_t K) {
     return best;
 }
 
+// The split-K partial results after the two images (none where the 256 x
+// 256-tile kernel runs: it never splits K).
 int64_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
+    if (use_big_tiles(M, N, K)) return 0;
     const int d = splitk_parts(M, N, K);
     return d > 1 ? (int64_t)d * M * N * 4 : 0;
 }
@@ -1899,6 +1738,13 @@ template <int WF>
 static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, float* part, hipStream_t s) {
     ga.m_tiles = (ga.M + kImgRows - 1) / kImgRows;
     ga.n_tiles = (ga.N + 255) / 256;
+    if (use_big_tiles(ga.M, ga.N, ga.K)) {
+        // 256 x 256 tiles (at least one per CU): no K split, no partials
+        if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
+        else launch_pack_t<WF, DT_F32>(ga, ximg, s);
+        launch_gemm_big(WF, ga.a, ximg, ga.y, ydt, ga.M, ga.N, ga.K, s);
+        return;
+    }
     if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
     else launch_pack_t<WF, DT_F32>(ga, ximg, s);
     ga.x = ximg;

@@ -76,6 +76,14 @@ hipError_t launch_pack_weight_image(int wfmt, const void* a, const void* b, cons
                                     void* wimg, hipStream_t s);
 hipError_t launch_gemm_image(int wfmt, const void* wimg, const void* x, int xdt, void* y, int ydt, int64_t M,
                              int64_t N, int64_t K, void* ximg, float* part, hipStream_t s);
+// The 256 x 256-tile matrix-core GEMM (gemm_big.hip) on the X and weight
+// images, for launches with at least one such tile per CU
+// (gemm_big_applies); use_big_tiles adds the dispatch setting
+// (Q4_KEY_TILE_ROWS) that can turn it off.  It needs no scratch.
+bool gemm_big_applies(int64_t M, int64_t N, int64_t K);
+bool use_big_tiles(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_big(int wfmt, const void* wimg, const void* ximg, void* y, int ydt, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s);
 hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void* c,
                               const void* x, int xdt, void* y, int ydt,
                               int64_t M, int64_t N, int64_t K, hipStream_t s);

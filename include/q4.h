@@ -88,6 +88,8 @@ extern "C" {
 #define Q4_KEY_SKINNY_MAX_M    0  /* q4_gemm/affine4_gemm: M <= this -> SKINNY          */
 #define Q4_KEY_DEQUANT_MIN_M   1  /* M >= this (and workspace given) -> DEQUANT_GEMM    */
 #define Q4_KEY_FORCE_PATH      2  /* -1 = automatic, else a Q4_PATH_* for q4_gemm etc.  */
+#define Q4_KEY_TILE_ROWS       3  /* MFMA path: 128 = 128x256 output tiles (default),
+                                     256 = 256x256 tiles where every CU gets at least one */
 
 /* Largest M that q4_gemv / q4_gemv_fused2 accept. */
 #define Q4_GEMV_MAX_M 16

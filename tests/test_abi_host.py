@@ -132,6 +132,7 @@ def test_gemm_validation():
     # the matrix-core path's workspace holds the X image (M and K rounded up
     # to the 128-row tile and the 64-wide K step, binary16) and the weight
     # image (9216 bytes per 256-column tile and K step)
+    # image (9216 bytes per 256-column tile and K step)
     assert lib().q4_gemm_workspace_size(2048, 12288, 4096, 0) == 2048 * 4096 * 2 + 48 * 64 * 9216
     assert lib().q4_gemm_workspace_size(129, 300, 96, 0) == 256 * 128 * 2 + 2 * 2 * 9216
     assert lib().q4_gemm_workspace_size(4, 300, 4096, 0) == 0            # skinny: none
@@ -259,6 +260,14 @@ def test_dispatch_predicate_boundaries():
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_GEMV)
     with pytest.raises(B.Q4Error):
         B.q4_set_dispatch(77, 1)
+    # tile rows: 128 (default) or 256, nothing else
+    assert B.q4_get_dispatch(B.Q4_KEY_TILE_ROWS) == 128
+    for bad in (0, 64, 192, 512):
+        with pytest.raises(B.Q4Error):
+            B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, bad)
+    B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 256)
+    assert B.q4_get_dispatch(B.Q4_KEY_TILE_ROWS) == 256
+    B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 128)
     B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
     try:
         assert B.q4_dispatch_path(1, 64, 64) == B.Q4_PATH_MFMA

@@ -993,3 +993,80 @@ def test_f32_activation_rounds_to_nearest_even():
             assert e <= 2e-5, (ws, e)
     finally:
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+
+
+# ---------------------------------------------------------------------------
+# the 256 x 256-tile matrix-core kernel (Q4_KEY_TILE_ROWS = 256, at least one
+# such tile per CU): ragged edges, determinism, weight images
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def big_tiles():
+    B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 256)
+    try:
+        yield
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 128)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 4100, 4000, 1056), ("affine", 2050, 8200, 1088),
+                                       ("q4_0", 4096, 4096, 4096), ("affine", 256, 65536, 512)])
+def test_big_tile_kernel_ragged_against_oracle(big_tiles, fmt, M, N, K):
+    """Shapes with at least one 256 x 256 tile per CU, ragged in M and N, and
+    K = 32 mod 64 for Q4_0 (a last K step with one block): sampled outputs
+    against binary64, the workspace and weight-image entry points giving the
+    same bits, and the same bits call after call."""
+    say(f"big-tile kernel {fmt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    xb = synth.bf16_bits(X)
+    tx = dev(xb).view(torch.bfloat16)
+    if fmt == "q4_0":
+        planes = oracle.q4_0_quantize(W)
+        What = oracle.q4_0_dequantize(*planes)
+        f = B.Q4_FMT_Q4_0
+        run = lambda ws: B.q4_gemm(*tp, tx, y_dtype=torch.float32, workspace=ws)
+    else:
+        planes = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+        What = oracle.affine4_dequantize(*planes)
+        f = B.Q4_FMT_AFFINE4
+        run = lambda ws: B.affine4_gemm(*tp, tx, y_dtype=torch.float32, workspace=ws)
+    tp = [dev(a) for a in planes]
+    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
+    y = run(ws)
+    torch.cuda.synchronize()
+    e = _sampled_check(y, synth.bf16_bits_to_f32(xb).astype(np.float64), What, M, count=4000)
+    say(f"  sampled rel err {e:.3e}")
+    assert e <= 1e-3
+    for _ in range(2):
+        assert torch.equal(run(ws), y)
+    image = B.q4_pack_weight_image(*tp, fmt=f)
+    yi = B.q4_gemm_image(image, tx, N, fmt=f, y_dtype=torch.float32, workspace=ws)
+    assert torch.equal(yi, y)
+    # the same bf16 output is the RNE of the fp32 one
+    yb = B.q4_gemm(*tp, tx, workspace=ws) if fmt == "q4_0" else B.affine4_gemm(*tp, tx, workspace=ws)
+    assert torch.equal(yb, y.to(torch.bfloat16))
+
+
+def test_big_tile_kernel_matches_128_row_kernel(big_tiles):
+    """M = 2048, N = 12288, K = 4096 (384 tiles of 256 x 256: one round of
+    whole tiles, then the last 128 tiles as 256 x 128 column halves): within
+    fp32 rounding of the 128-row kernel (Q4_KEY_TILE_ROWS = 128), on the
+    same workspace."""
+    M, N, K = 2048, 12288, 4096
+    rng = np.random.default_rng(12)
+    qs, d = oracle.q4_0_quantize(synth.weights(rng, N, K))
+    tq, td = dev(qs), dev(d)
+    tx = bf16_dev(synth.activations(rng, M, K))
+    ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+    y_big = B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)
+    B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 128)
+    try:
+        y_pk = B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 256)
+    torch.cuda.synchronize()
+    d_ = (y_big.double() - y_pk.double()).norm() / y_pk.double().norm()
+    say(f"  256-row vs 128-row kernel: rel {float(d_):.3e}")
+    assert float(d_) <= 1e-5
