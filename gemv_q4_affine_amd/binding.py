@@ -16,8 +16,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libq4.so")
 
 # status, dtype, format and path codes (include/q4.h)
-Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_DTYPE, Q4_ERR_HIP, Q4_ERR_ARG, Q4_ERR_WORKSPACE = (
-    0, -1, -2, -3, -4, -5, -6, -7)
+(Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_DTYPE, Q4_ERR_HIP, Q4_ERR_ARG, Q4_ERR_WORKSPACE,
+ Q4_ERR_SCRATCH) = (0, -1, -2, -3, -4, -5, -6, -7, -8)
+Q4_NOALLOC_SCRATCH_BYTES = 32 << 20
 Q4_F32, Q4_BF16, Q4_F16 = 0, 1, 2
 Q4_FMT_Q4_0, Q4_FMT_AFFINE4 = 0, 1
 Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM = 0, 1, 2, 3
@@ -48,6 +49,7 @@ SIGNATURES = {
     "q4_pack_weight_image": (_INT, [_INT, _P, _P, _P, _I64, _I64, _P, _P]),
     "q4_gemm_image_workspace_size": (_I64, [_I64, _I64]),
     "q4_gemm_image": (_INT, [_INT, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
+    "q4_gemm_image_noalloc": (_INT, [_INT, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _P]),
     "q4_dispatch_path": (_INT, [_I64, _I64, _I64, _INT, _INT]),
     "q4_set_dispatch": (_INT, [_INT, _I64]),
     "q4_get_dispatch": (_INT, [_INT, ctypes.POINTER(ctypes.c_int64)]),
@@ -379,6 +381,16 @@ def q4_gemm_image(image, x, N, fmt=Q4_FMT_Q4_0, y_dtype=torch.bfloat16, y=None, 
     _check("q4_gemm_image", lib().q4_gemm_image(fmt, _p(image), _p(x), _dt(x), _p(y), _dt(y), M, N, K,
                                                 _p(workspace), workspace.numel() * workspace.element_size(),
                                                 _stream(stream)))
+    return y
+
+
+def q4_gemm_image_noalloc(image, x, N, fmt=Q4_FMT_Q4_0, y_dtype=torch.bfloat16, y=None, stream=None):
+    """q4_gemm_image with the library's fixed per-GPU scratch as workspace:
+    no device allocation when `y` is given.  Calls on one GPU must not overlap."""
+    M, _ = x.shape
+    y = _empty((M, N), y_dtype, x, stream) if y is None else y
+    _check("q4_gemm_image_noalloc", lib().q4_gemm_image_noalloc(fmt, _p(image), _p(x), _dt(x), _p(y), _dt(y), M, N,
+                                                                x.shape[1], _stream(stream)))
     return y
 
 

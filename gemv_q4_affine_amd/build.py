@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq4.so")
 
-SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip", "affine8.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip", "affine8.hip", "noalloc.hip", "capi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -117,6 +117,7 @@ const char* q4_status_string(int status) {
         case Q4_ERR_HIP: return "HIP launch or runtime error";
         case Q4_ERR_ARG: return "invalid argument";
         case Q4_ERR_WORKSPACE: return "the workspace is missing or smaller than the path needs";
+        case Q4_ERR_SCRATCH: return "the call needs more than the library's fixed scratch (Q4_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -439,6 +440,21 @@ int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* 
                     ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ximg) : nullptr;
     return hip_status(q4::launch_gemm_image(wf, image, x, x_dtype, y, y_dtype, M, N, K, workspace, pp,
                                             as_stream(stream)));
+}
+
+// For callers that cannot allocate: the workspace is the library's fixed
+// per-GPU scratch array.
+int q4_gemm_image_noalloc(int fmt, const void* image, const void* x, int x_dtype, void* y, int y_dtype, int64_t M,
+                          int64_t N, int64_t K, void* stream) {
+    if ((x_dtype != Q4_BF16 && x_dtype != Q4_F32) || (y_dtype != Q4_BF16 && y_dtype != Q4_F32)) return Q4_ERR_DTYPE;
+    int rc = image_dims(fmt, M, N, K);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({image, x, y}))) return rc;
+    if (q4::x_image_bytes(M, K) > Q4_NOALLOC_SCRATCH_BYTES) return Q4_ERR_SCRATCH;
+    void* scratch = nullptr;
+    if (q4::noalloc_scratch(&scratch) != hipSuccess) return Q4_ERR_HIP;
+    return q4_gemm_image(fmt, image, x, x_dtype, y, y_dtype, M, N, K, scratch, Q4_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ---- affine 8-bit ------------------------------------------------------------------

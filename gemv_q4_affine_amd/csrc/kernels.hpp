@@ -14,6 +14,10 @@ enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 // query fails).
 int current_cu_count();
 
+// Device address of the current GPU's copy of the library's fixed scratch
+// array (Q4_NOALLOC_SCRATCH_BYTES), looked up once per device (noalloc.hip).
+hipError_t noalloc_scratch(void** out);
+
 hipError_t launch_q4_quantize(const void* w, int wdt, int64_t N, int64_t K, uint8_t* qs, uint16_t* d,
                               hipStream_t s);
 hipError_t launch_q8_1_quantize(const void* x, int xdt, int64_t M, int64_t K, int8_t* qs, uint16_t* ds,

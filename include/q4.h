@@ -69,6 +69,7 @@ extern "C" {
 #define Q4_ERR_HIP      -5   /* a HIP launch or runtime call failed             */
 #define Q4_ERR_ARG      -6   /* other invalid argument (dispatch key, path...)  */
 #define Q4_ERR_WORKSPACE -7  /* a path that needs workspace got too little */
+#define Q4_ERR_SCRATCH  -8   /* the call needs more than Q4_NOALLOC_SCRATCH_BYTES */
 
 /* ---- dtype codes ---------------------------------------------------------- */
 #define Q4_F32   0
@@ -397,6 +398,30 @@ int64_t q4_gemm_image_workspace_size(int64_t M, int64_t K);
 int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* y, int y_dtype,
                   int64_t M, int64_t N, int64_t K,
                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Size of the library's fixed device scratch (32 MiB per GPU). */
+#define Q4_NOALLOC_SCRATCH_BYTES (32ll << 20)
+
+/*
+ * q4_gemm_image_noalloc -- q4_gemm_image for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
+ * q4_gemm_image with a Q4_NOALLOC_SCRATCH_BYTES workspace, except that the
+ * workspace is a fixed array inside the library: one per GPU, created when
+ * the library's code is loaded on that GPU and held until the process ends.
+ * The call allocates nothing and calls no allocating routine.
+ *   Limit: q4_gemm_image_workspace_size(M, K) <= Q4_NOALLOC_SCRATCH_BYTES
+ *          (e.g. M <= 4096 at K = 4096), else Q4_ERR_SCRATCH and nothing is
+ *          enqueued.  Split-K partial results are used when they fit after
+ *          the X image, as in q4_gemm_image.
+ *   The scratch keeps the last call's contents; every byte a call reads is
+ *   written earlier in the same call, so nothing needs clearing.  All calls on
+ *   one GPU share that GPU's scratch: calls that can overlap (different
+ *   streams, or host threads enqueueing concurrently) race and give wrong
+ *   results; serialise them on one stream.
+ */
+int q4_gemm_image_noalloc(int fmt, const void* image, const void* x, int x_dtype, void* y, int y_dtype,
+                          int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * dense_gemm -- Y = X . W^T with a dense binary16 W [N][K] (the GEMM half of

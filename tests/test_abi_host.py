@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in q4.h but not exported"
@@ -46,7 +46,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     assert "gfx950" in B.version()
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert B.status_string(code) and B.status_string(code) != "unknown status"
     assert B.status_string(-99) == "unknown status"
 
@@ -218,6 +218,26 @@ def test_weight_image_validation_and_sizes():
     assert g(B.Q4_FMT_Q4_0, None, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, P2, 1 << 20, None) == B.Q4_ERR_NULL
     assert g(B.Q4_FMT_AFFINE4, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, P2, 1 << 20, None) == B.Q4_ERR_SHAPE
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None, 0, None) == B.Q4_OK
+
+
+def test_noalloc_gemm_rejects_before_any_device_call():
+    """q4_gemm_image_noalloc: the same argument checks as q4_gemm_image, and
+    an X image beyond the fixed scratch is refused with its own status before
+    anything is enqueued (no GPU here, so reaching a HIP call would fail
+    differently)."""
+    assert B.Q4_NOALLOC_SCRATCH_BYTES == 32 << 20
+    g = lib().q4_gemm_image_noalloc
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_F16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_DTYPE
+    assert g(5, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_ARG
+    assert g(B.Q4_FMT_AFFINE4, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, None) == B.Q4_ERR_SHAPE
+    assert g(B.Q4_FMT_Q4_0, None, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_NULL
+    assert g(B.Q4_FMT_Q4_0, P, MIS, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_ALIGN
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None) == B.Q4_OK
+    # X image: ceil(M/128)*128 * ceil(K/64)*64 * 2 bytes against 32 MiB
+    assert lib().q4_gemm_image_workspace_size(4097, 4096) > B.Q4_NOALLOC_SCRATCH_BYTES
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4097, 256, 4096, None) == B.Q4_ERR_SCRATCH
+    assert g(B.Q4_FMT_AFFINE4, P, P, B.Q4_F32, P, B.Q4_F32, 8192, 256, 4096, None) == B.Q4_ERR_SCRATCH
+    assert "scratch" in B.status_string(B.Q4_ERR_SCRATCH)
 
 
 def test_forced_dequant_path_without_workspace_is_an_error():
