@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libq4.so")
 # status, dtype, format and path codes (include/q4.h)
 (Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_DTYPE, Q4_ERR_HIP, Q4_ERR_ARG, Q4_ERR_WORKSPACE,
  Q4_ERR_SCRATCH) = (0, -1, -2, -3, -4, -5, -6, -7, -8)
-Q4_NOALLOC_SCRATCH_BYTES = 32 << 20
+Q4_NOALLOC_SCRATCH_BYTES = 33 << 20
 Q4_F32, Q4_BF16, Q4_F16 = 0, 1, 2
 Q4_FMT_Q4_0, Q4_FMT_AFFINE4 = 0, 1
 Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM = 0, 1, 2, 3

@@ -544,49 +544,104 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 constexpr int kPkSlots = 6;              // ring depth: steps k..k+5 resident
 constexpr int kPkAhead = kPkSlots - 1;   // producers request step k+5 during step k
 constexpr int kPkProducers = 4;          // producer waves, one per SIMD
-// X -> image (see above).  One thread per 16-byte image chunk.  binary16
-// values are rounded to nearest even (exact for bfloat16 input in binary16's
-// normal range).
+// X -> image (see above), one workgroup of 256 threads per image row.  The
+// workgroup first finds the row's largest |x|.  A row whose largest lies in
+// [2^-2, 2^15) is converted as it is (e = 0: the same bits as a direct
+// conversion); any other row is scaled by 2^e, e = 14 - floor(log2 max), so
+// its largest lands in [2^14, 2^15) (a zero or non-finite maximum keeps
+// e = 0).  Then the row's chunks are written as binary16 of x * 2^e, rounded
+// to nearest even, and e to the exponent table.  For bfloat16 X of a scaled
+// row every value within 2^-31 of the row's largest converts exactly.  Rows
+// past M and steps past K are zero.
 template <int WF, int XDT>
-__global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint16_t* __restrict__ img, int M, int K,
-                                                int ksteps, int64_t nchunks) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (t >= nchunks) return;
-    const int pc = (int)(t & 7);
-    const int r = (int)((t >> 3) & (kImgRows - 1));
-    const int64_t tile = t >> 10;
-    const int ks = (int)(tile % ksteps);
-    const int mt = (int)(tile / ksteps);
-    const int c = pc ^ img_swz(r);
-    const int m = mt * kImgRows + r;
-    const int k0 = ks * 64 + c * 8;
-    u32x4_t o = {0u, 0u, 0u, 0u};
-    if (m < M && k0 < K) {                       // K % 32 == 0: a chunk is wholly inside or outside
-        float f[8];
+__global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint16_t* __restrict__ img,
+                                                int8_t* __restrict__ xexp, int M, int K, int ksteps) {
+    constexpr int kBatch = 2;                   // chunks per thread held in registers (K <= 4096 in one batch)
+    using Raw = RawX8<XDT>;
+    __shared__ float wave_max[4];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nch = ksteps * 8;                 // 16-byte chunks of an image row
+    const int kch = m < M ? K / 8 : 0;          // chunks holding X (K % 32 == 0)
+    const int64_t xoff = (int64_t)m * K;
+    auto absmax = [](const Raw& v, float mx) {
         if constexpr (XDT == DT_BF16) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(x) + (int64_t)m * K + k0);
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                f[2 * i] = __uint_as_float(v[i] << 16);
-                f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
-            }
+            for (int i = 0; i < 4; i++)
+                mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(v.lo[i] << 16)), fabsf(__uint_as_float(v.lo[i] & 0xFFFF0000u))));
         } else {
-            const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + (int64_t)m * K + k0);
-            const float4 v0 = p[0], v1 = p[1];
-            f[0] = v0.x; f[1] = v0.y; f[2] = v0.z; f[3] = v0.w;
-            f[4] = v1.x; f[5] = v1.y; f[6] = v1.z; f[7] = v1.w;
-        }
-        // position p of the chunk holds k = perm[p]
-        constexpr int kPermQ[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-        constexpr int kPermA[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int p0 = (WF == WF_Q4_0) ? kPermQ[2 * i] : kPermA[2 * i];
-            const int p1 = (WF == WF_Q4_0) ? kPermQ[2 * i + 1] : kPermA[2 * i + 1];
-            o[i] = f32_to_f16(f[p0]) | (f32_to_f16(f[p1]) << 16);
+            for (int i = 0; i < 4; i++)
+                mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(v.lo[i])), fabsf(__uint_as_float(v.hi[i]))));
+        }
+        return mx;
+    };
+    // pass 1: the row's largest |x|
+    Raw keep[kBatch];
+    float mx = 0.0f;
+    for (int c0 = 0; c0 < kch; c0 += 256 * kBatch) {
+#pragma unroll
+        for (int b = 0; b < kBatch; b++) {
+            const int c = c0 + b * 256 + tid;
+            if (c < kch) keep[b] = load_x8_raw<XDT>(x, xoff + (int64_t)c * 8);
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; b++)
+            if (c0 + b * 256 + tid < kch) mx = absmax(keep[b], mx);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((tid & 63) == 0) wave_max[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    int e = 0;
+    if (mx > 0.0f && mx <= 3.4028234663852886e38f) {
+        e = 14 - (__builtin_amdgcn_frexp_expf(mx) - 1);        // 14 - floor(log2(mx))
+        if (e >= 0 && e <= 16) e = 0;                           // largest in [2^-2, 2^15): as it is
+        e = e < kXexpMin ? kXexpMin : (e > kXexpMax ? kXexpMax : e);
+    }
+    // pass 2: binary16 of x * 2^e into the image (a row of one batch is still
+    // in registers; longer rows are read again)
+    const int r = m & (kImgRows - 1);
+    const int64_t tile0 = (int64_t)(m / kImgRows) * ksteps;
+    const bool one_batch = kch <= 256 * kBatch;
+    for (int c0 = 0; c0 < nch; c0 += 256 * kBatch) {
+#pragma unroll
+        for (int b = 0; b < kBatch; b++) {
+            const int c = c0 + b * 256 + tid;
+            if (c >= nch) break;
+            u32x4_t o = {0u, 0u, 0u, 0u};
+            if (c < kch) {
+                const Raw v = one_batch ? keep[b] : load_x8_raw<XDT>(x, xoff + (int64_t)c * 8);
+                float f[8];
+                if constexpr (XDT == DT_BF16) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        f[2 * i] = __uint_as_float(v.lo[i] << 16);
+                        f[2 * i + 1] = __uint_as_float(v.lo[i] & 0xFFFF0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        f[i] = __uint_as_float(v.lo[i]);
+                        f[4 + i] = __uint_as_float(v.hi[i]);
+                    }
+                }
+                // position p of the chunk holds k = perm[p]
+                constexpr int kPermQ[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+                constexpr int kPermA[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int p0 = (WF == WF_Q4_0) ? kPermQ[2 * i] : kPermA[2 * i];
+                    const int p1 = (WF == WF_Q4_0) ? kPermQ[2 * i + 1] : kPermA[2 * i + 1];
+                    o[i] = f32_to_f16(ldexpf(f[p0], e)) | (f32_to_f16(ldexpf(f[p1], e)) << 16);
+                }
+            }
+            const int64_t t = (tile0 + (c >> 3)) * (kImgTile / 8) + r * 8 + ((c & 7) ^ img_swz(r));
+            *reinterpret_cast<u32x4_t*>(img + t * 8) = o;
         }
     }
-    *reinterpret_cast<u32x4_t*>(img + t * 8) = o;
+    if (tid == 0) xexp[xexp_pos(m)] = (int8_t)e;
 }
 
 
@@ -869,7 +924,18 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
             const int m0 = tile_m0(i);
             const int nw0 = tile_n0(i) + wave * NT * 32;
 #pragma unroll
-            for (int mi = 0; mi < MT; mi++)
+            for (int mi = 0; mi < MT; mi++) {
+                // the row exponents of sub-tile mi: its 32 bytes through the
+                // scalar cache (a uniform address), then this lane's 8
+                using const_u32 = __attribute__((address_space(4))) const uint32_t;
+                const const_u32* sp = (const const_u32*)(a.xexp + m0 + mi * 32);
+                uint32_t w[8];
+#pragma unroll
+                for (int t = 0; t < 8; t++) w[t] = sp[t];
+                const int c = 2 * g + (odd ? 1 : 0);
+                u32x2_t ex;
+                ex[0] = c == 0 ? w[0] : c == 1 ? w[2] : c == 2 ? w[4] : w[6];
+                ex[1] = c == 0 ? w[1] : c == 1 ? w[3] : c == 2 ? w[5] : w[7];
 #pragma unroll
                 for (int ni = 0; ni < NT; ni++) {
                     const int col = nw0 + ni * 32 + (j & ~1);    // even column of the pair
@@ -877,8 +943,10 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                     for (int v = 0; v < 16; v += 2) {
                         const float a0v = acc[mi][ni][v], a1v = acc[mi][ni][v + 1];
                         const float d0 = swap_pair(a0v), d1 = swap_pair(a1v);
-                        const float lo = odd ? d1 : a0v;         // column col
-                        const float hi = odd ? a1v : d0;         // column col + 1
+                        // row r of the X image was scaled by 2^e(r)
+                        const int ue = -xexp_of(ex, v >> 2, (v >> 1) & 1);
+                        const float lo = ldexpf(odd ? d1 : a0v, ue);   // column col
+                        const float hi = ldexpf(odd ? a1v : d0, ue);   // column col + 1
                         const int row = m0 + mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3) + (odd ? 1 : 0);
                         if (row >= a.M || col >= a.N) continue;
                         const int64_t off = (int64_t)row * a.N + col;
@@ -911,6 +979,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                         }
                     }
                 }
+            }
 #pragma unroll
             for (int mi = 0; mi < MT; mi++)
 #pragma unroll
@@ -1654,8 +1723,17 @@ hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* 
     return hipGetLastError();
 }
 
-int64_t x_image_bytes(int64_t M, int64_t K) {
+// The binary16 tiles, then one exponent byte per image row.
+static int64_t x_tiles_bytes(int64_t M, int64_t K) {
     return (M + kImgRows - 1) / kImgRows * ((K + 63) / 64) * (int64_t)kImgTile * 2;
+}
+
+int64_t x_image_bytes(int64_t M, int64_t K) {
+    return x_tiles_bytes(M, K) + (M + kImgRows - 1) / kImgRows * kImgRows;
+}
+
+const int8_t* x_image_exponents(const void* ximg, int64_t M, int64_t K) {
+    return static_cast<const int8_t*>(ximg) + x_tiles_bytes(M, K);
 }
 
 int64_t weight_image_bytes(int64_t N, int64_t K) { return (N + 255) / 256 * ((K + 63) / 64) * (int64_t)kWChunk; }
@@ -1667,9 +1745,9 @@ int64_t packed_x_bytes(int64_t M, int64_t N, int64_t K) {
 template <int WF, int XDT>
 static void launch_pack_t(const GemmArgs& ga, uint16_t* img, hipStream_t s) {
     const int ksteps = (ga.K + 63) / 64;
-    const int64_t nchunks = (int64_t)ga.m_tiles * ksteps * (kImgTile / 8);
-    const dim3 grid((unsigned)((nchunks + 255) / 256)), block(256);
-    hipLaunchKernelGGL((k_pack_x<WF, XDT>), grid, block, 0, s, ga.x, img, ga.M, ga.K, ksteps, nchunks);
+    const dim3 grid((unsigned)(ga.m_tiles * kImgRows)), block(256);
+    int8_t* xexp = const_cast<int8_t*>(x_image_exponents(img, ga.M, ga.K));
+    hipLaunchKernelGGL((k_pack_x<WF, XDT>), grid, block, 0, s, ga.x, img, xexp, ga.M, ga.K, ksteps);
 }
 
 template <int WF>
@@ -1748,6 +1826,7 @@ static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, floa
     if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
     else launch_pack_t<WF, DT_F32>(ga, ximg, s);
     ga.x = ximg;
+    ga.xexp = x_image_exponents(ximg, ga.M, ga.K);
     ga.ksplit = part != nullptr ? splitk_parts(ga.M, ga.N, ga.K) : 1;
     ga.part = part;
     const int cus = current_cu_count();

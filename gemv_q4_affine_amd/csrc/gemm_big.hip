@@ -50,6 +50,7 @@ constexpr int kBigXBytes = kBigRows * 64 * 2;      // X of one K step: two 128-r
 struct BigArgs {
     const uint8_t* wimg;     // weight image (256-column tiles, 64-wide K steps)
     const uint8_t* ximg;     // binary16 X image (128-row tiles, 64-wide K steps)
+    const int8_t* xexp;      // its row exponents
     void* y;
     int M, N, K;
     int m_tiles, n_tiles;    // 256-row and 256-column tiles
@@ -245,7 +246,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
         const int j = ln & 31, g = ln >> 5;
         const bool odd = (ln & 1) != 0;
 #pragma unroll
-        for (int mi = 0; mi < MT; mi++)
+        for (int mi = 0; mi < MT; mi++) {
+            // the X image's exponents of sub-tile mi through the scalar cache
+            // (the table covers 128-row tiles: a sub-tile wholly past M reads
+            // none and stores nothing), then this lane's 8
+            if (m0 + mi * 32 >= a.M) continue;
+            using const_u32 = __attribute__((address_space(4))) const uint32_t;
+            const const_u32* sp = (const const_u32*)(a.xexp + m0 + mi * 32);
+            uint32_t w[8];
+#pragma unroll
+            for (int t = 0; t < 8; t++) w[t] = sp[t];
+            const int c = 2 * g + (odd ? 1 : 0);
+            u32x2_t ex;
+            ex[0] = c == 0 ? w[0] : c == 1 ? w[2] : c == 2 ? w[4] : w[6];
+            ex[1] = c == 0 ? w[1] : c == 1 ? w[3] : c == 2 ? w[5] : w[7];
 #pragma unroll
             for (int ni = 0; ni < NT; ni++) {
                 const int col = nw0 + ni * 32 + (j & ~1);
@@ -253,8 +267,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
                 for (int e = 0; e < 16; e += 2) {
                     const float a0v = acc[mi][ni][e], a1v = acc[mi][ni][e + 1];
                     const float d0 = swap_pair(a0v), d1 = swap_pair(a1v);
-                    const float lo_v = odd ? d1 : a0v;
-                    const float hi_v = odd ? a1v : d0;
+                    // row r of the X image was scaled by 2^e(r)
+                    const int ue = -xexp_of(ex, e >> 2, (e >> 1) & 1);
+                    const float lo_v = ldexpf(odd ? d1 : a0v, ue);
+                    const float hi_v = ldexpf(odd ? a1v : d0, ue);
                     const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3) + (odd ? 1 : 0);
                     if (row >= a.M || col >= a.N) continue;
                     const int64_t off = (int64_t)row * a.N + col;
@@ -280,6 +296,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+        }
     };
 
     // ---- one unit: S steps of one tile, NT = 2 (whole) or 1 (column half) ------
@@ -476,6 +493,7 @@ hipError_t launch_gemm_big(int wfmt, const void* wimg, const void* ximg, void* y
     BigArgs ba{};
     ba.wimg = static_cast<const uint8_t*>(wimg);
     ba.ximg = static_cast<const uint8_t*>(ximg);
+    ba.xexp = x_image_exponents(ximg, M, K);
     ba.y = y;
     ba.M = (int)M;
     ba.N = (int)N;

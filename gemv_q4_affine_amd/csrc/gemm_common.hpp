@@ -28,6 +28,7 @@ struct GemmArgs {
     int n_tiles;       // workgroup tiles along N
     int ksplit;        // k_gemm_pk: K parts per tile (<= 1: none)
     float* part;       // k_gemm_pk with ksplit > 1: fp32 partial results [ksplit][M][N]
+    const int8_t* xexp;  // k_gemm_pk: the X image's row exponents
 };
 
 
@@ -90,6 +91,29 @@ constexpr int kImgTile = kImgRows * 64;  // halves of an image tile (16 KiB)
 // Row r of an image tile: chunk c sits at c ^ img_swz(r).  A permutation of
 // rows 0..7 and, separately, of the even and of the odd rows among 0..15.
 __device__ __forceinline__ int img_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Row exponents of the X image.  The image holds x * 2^e(m) for an integer
+// e(m) per row: 0 where the row's largest |x| already lies in [2^-2, 2^15),
+// else the e that brings it into [2^14, 2^15), so binary16 keeps the whole
+// bfloat16 range.  The GEMM epilogues multiply the fp32 results of row m by
+// 2^-e(m).  Both scalings are exact.
+//
+// The int8 table follows the image (one byte per image row).  An epilogue
+// lane (MFMA half h, lane parity p) stores rows 8q + 4h + 2t + p of every
+// 32-row sub-tile (q = 0..3, t = 0..1); those 8 exponents sit together at
+// byte 8 * (2h + p) of the sub-tile's 32, exponent (q, t) at byte 2q + t, so
+// the lane reads them with one 8-byte load and extracts them with constant
+// shifts.
+__device__ __forceinline__ int xexp_pos(int m) {
+    const int r = m & 31;
+    const int q = r >> 3, h = (r >> 2) & 1, t = (r >> 1) & 1, p = r & 1;
+    return (m & ~31) + 8 * (2 * h + p) + 2 * q + t;
+}
+// Exponent (q, t) of a lane's 8-byte load.
+__device__ __forceinline__ int xexp_of(u32x2_t ex, int q, int t) {
+    return (int)(int8_t)(uint8_t)(ex[q >> 1] >> (8 * (2 * (q & 1) + t)));
+}
+constexpr int kXexpMin = -113, kXexpMax = 127;   // every finite row maximum fits
 
 // Shift-free dequantiser of the packed-X kernel.
 //

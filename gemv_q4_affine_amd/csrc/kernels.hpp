@@ -75,6 +75,8 @@ hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void
 // X image in ximg (x_image_bytes(M, K)) and, if part is not null, the
 // split-K partial results in part (splitk_bytes(M, N, K)).
 int64_t x_image_bytes(int64_t M, int64_t K);
+// The row exponent table inside an X image of x_image_bytes(M, K) bytes.
+const int8_t* x_image_exponents(const void* ximg, int64_t M, int64_t K);
 int64_t weight_image_bytes(int64_t N, int64_t K);
 hipError_t launch_pack_weight_image(int wfmt, const void* a, const void* b, const void* c, int64_t N, int64_t K,
                                     void* wimg, hipStream_t s);

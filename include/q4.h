@@ -255,10 +255,20 @@ int q4_gemv_multi_act(int nmat, const uint8_t* const* w_qs, const uint16_t* cons
  * q4_gemm -- Y = X . dequant(Wq)^T for Q4_0 weights, fp32 accumulation
  * (the prefill matrix-engine GEMM of the ET-SoC-1 PR, Overview).  The M
  * dispatch (q4_dispatch_path) picks SKINNY, MFMA or DEQUANT_GEMM.  The fused
- * paths multiply on the matrix cores in binary16: X is converted to binary16
- * (exact for bfloat16 values with 2^-24 <= |x| <= 65504 at 8-bit precision)
- * and the weights are dequantised to binary16 (relative rounding <= 2^-11);
- * inputs outside binary16 range are outside the fused paths' domain.
+ * paths multiply on the matrix cores in binary16, with the weights
+ * dequantised to binary16 (relative rounding <= 2^-11) and X converted to
+ * binary16 by round to nearest even:
+ *   - the MFMA path with its X image (a workspace of at least the two tile
+ *     images, and q4_gemm_image) first scales each X row by a power of two
+ *     2^e that brings the row's largest |x| into [2^14, 2^15), and scales the
+ *     row's fp32 results back by 2^-e: the whole bfloat16 / binary32 range is
+ *     in its domain, and bfloat16 values within a factor 2^31 of their row's
+ *     largest convert exactly;
+ *   - the paths without an X image (SKINNY with binary32 X, MFMA with too
+ *     little workspace, DEQUANT_GEMM) convert X directly: exact for bfloat16
+ *     values with 2^-17 <= |x| <= 65504; |x| > 65504 becomes +-inf.  The SKINNY
+ *     path with bfloat16 X (2 <= M <= 32) multiplies in bfloat16 and has the
+ *     whole range.
  *   x         : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32)
  *   y         : device out, [M][N] of y_dtype (Q4_BF16 RNE, or Q4_F32)
  *   workspace : device scratch owned by the caller (16-byte aligned), or
@@ -351,7 +361,8 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
 /*
  * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
  * 0 for SKINNY; for MFMA the X and weight tile images,
- * ceil(M/128)*128 * ceil(K/64)*64 * 2 + ceil(N/256) * ceil(K/64) * 9216 bytes,
+ * ceil(M/128)*128 * (ceil(K/64)*64 * 2 + 1) + ceil(N/256) * ceil(K/64) * 9216
+ * bytes (the X image holds one exponent byte per row after its tiles),
  * plus parts*M*N*4 for the K-split partial results when the tile count is
  * below half the device's CU count (parts: the most, up to 16, that divide
  * ceil(K/64), leave at least 4 K steps each and keep tiles*parts within the
@@ -388,7 +399,7 @@ int q4_pack_weight_image(int fmt, const uint8_t* w_q, const uint16_t* w_s, const
  * with a workspace of the same size, for any M >= 1.
  *   workspace : device scratch for the X image, at least
  *               q4_gemm_image_workspace_size(M, K) =
- *               ceil(M/128)*128 * ceil(K/64)*64 * 2 bytes (else
+ *               ceil(M/128)*128 * (ceil(K/64)*64 * 2 + 1) bytes (else
  *               Q4_ERR_WORKSPACE).  With room after it for the K-split
  *               partial results (q4_gemm_workspace_size(M, N, K, fmt) bytes
  *               are always enough), a launch with few tiles is split along
@@ -399,8 +410,8 @@ int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* 
                   int64_t M, int64_t N, int64_t K,
                   void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Size of the library's fixed device scratch (32 MiB per GPU). */
-#define Q4_NOALLOC_SCRATCH_BYTES (32ll << 20)
+/* Size of the library's fixed device scratch (33 MiB per GPU). */
+#define Q4_NOALLOC_SCRATCH_BYTES (33ll << 20)
 
 /*
  * q4_gemm_image_noalloc -- q4_gemm_image for callers that cannot allocate

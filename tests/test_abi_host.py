@@ -133,8 +133,8 @@ def test_gemm_validation():
     # to the 128-row tile and the 64-wide K step, binary16) and the weight
     # image (9216 bytes per 256-column tile and K step)
     # image (9216 bytes per 256-column tile and K step)
-    assert lib().q4_gemm_workspace_size(2048, 12288, 4096, 0) == 2048 * 4096 * 2 + 48 * 64 * 9216
-    assert lib().q4_gemm_workspace_size(129, 300, 96, 0) == 256 * 128 * 2 + 2 * 2 * 9216
+    assert lib().q4_gemm_workspace_size(2048, 12288, 4096, 0) == 2048 * (4096 * 2 + 1) + 48 * 64 * 9216
+    assert lib().q4_gemm_workspace_size(129, 300, 96, 0) == 256 * (128 * 2 + 1) + 2 * 2 * 9216
     assert lib().q4_gemm_workspace_size(4, 300, 4096, 0) == 0            # skinny: none
     assert lib().q4_gemm_workspace_size(4, 300, 4000, 0) == 0            # invalid K
     B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
@@ -201,8 +201,8 @@ def test_weight_image_validation_and_sizes():
     assert lib().q4_weight_image_size(300, 96, B.Q4_FMT_Q4_0) == 2 * 2 * 9216
     assert lib().q4_weight_image_size(300, 96, B.Q4_FMT_AFFINE4) == 0        # K % 64 != 0
     assert lib().q4_weight_image_size(300, 128, 5) == 0
-    assert lib().q4_gemm_image_workspace_size(2048, 4096) == 2048 * 4096 * 2
-    assert lib().q4_gemm_image_workspace_size(129, 96) == 256 * 128 * 2
+    assert lib().q4_gemm_image_workspace_size(2048, 4096) == 2048 * (4096 * 2 + 1)
+    assert lib().q4_gemm_image_workspace_size(129, 96) == 256 * (128 * 2 + 1)
     p = lib().q4_pack_weight_image
     assert p(5, P, P, None, 8, 64, P, None) == B.Q4_ERR_ARG
     assert p(B.Q4_FMT_Q4_0, P, P, None, 8, 48, P, None) == B.Q4_ERR_SHAPE
@@ -213,7 +213,7 @@ def test_weight_image_validation_and_sizes():
     g = lib().q4_gemm_image
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_F16, P, B.Q4_BF16, 4, 8, 64, P2, 1 << 20, None) == B.Q4_ERR_DTYPE
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
-    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, P2, 128 * 64 * 2 - 1, None) == B.Q4_ERR_WORKSPACE
+    assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, P2, 128 * (64 * 2 + 1) - 1, None) == B.Q4_ERR_WORKSPACE
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, MIS, 1 << 20, None) == B.Q4_ERR_ALIGN
     assert g(B.Q4_FMT_Q4_0, None, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, P2, 1 << 20, None) == B.Q4_ERR_NULL
     assert g(B.Q4_FMT_AFFINE4, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, P2, 1 << 20, None) == B.Q4_ERR_SHAPE
@@ -225,7 +225,7 @@ def test_noalloc_gemm_rejects_before_any_device_call():
     an X image beyond the fixed scratch is refused with its own status before
     anything is enqueued (no GPU here, so reaching a HIP call would fail
     differently)."""
-    assert B.Q4_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert B.Q4_NOALLOC_SCRATCH_BYTES == 33 << 20
     g = lib().q4_gemm_image_noalloc
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_F16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_DTYPE
     assert g(5, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_ARG
@@ -233,7 +233,8 @@ def test_noalloc_gemm_rejects_before_any_device_call():
     assert g(B.Q4_FMT_Q4_0, None, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_NULL
     assert g(B.Q4_FMT_Q4_0, P, MIS, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None) == B.Q4_ERR_ALIGN
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None) == B.Q4_OK
-    # X image: ceil(M/128)*128 * ceil(K/64)*64 * 2 bytes against 32 MiB
+    # X image: ceil(M/128)*128 * (ceil(K/64)*64 * 2 + 1) bytes against 33 MiB
+    assert lib().q4_gemm_image_workspace_size(4096, 4096) <= B.Q4_NOALLOC_SCRATCH_BYTES
     assert lib().q4_gemm_image_workspace_size(4097, 4096) > B.Q4_NOALLOC_SCRATCH_BYTES
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 4097, 256, 4096, None) == B.Q4_ERR_SCRATCH
     assert g(B.Q4_FMT_AFFINE4, P, P, B.Q4_F32, P, B.Q4_F32, 8192, 256, 4096, None) == B.Q4_ERR_SCRATCH

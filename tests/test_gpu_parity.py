@@ -1070,3 +1070,91 @@ def test_big_tile_kernel_matches_128_row_kernel(big_tiles):
     d_ = (y_big.double() - y_pk.double()).norm() / y_pk.double().norm()
     say(f"  256-row vs 128-row kernel: rel {float(d_):.3e}")
     assert float(d_) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# X outside binary16's range on the MFMA path with an X image: the per-row
+# power-of-two prescale of k_pack_x and the epilogues' inverse
+# ---------------------------------------------------------------------------
+
+def _wide_range_x(rng, M, K):
+    """Rows cycling through: N(0,1); x 1e5 (beyond 65504); x 1e-6 (below
+    binary16's normal range 2^-14); half the entries x 1e5 and half x 1e-6;
+    a row of zeros."""
+    X = synth.activations(rng, M, K).astype(np.float32)
+    kind = np.arange(M) % 5
+    X[kind == 1] *= np.float32(1e5)
+    X[kind == 2] *= np.float32(1e-6)
+    mix = kind == 3
+    scale = np.where(np.arange(K) % 2 == 0, np.float32(1e5), np.float32(1e-6)).astype(np.float32)
+    X[mix] *= scale[None, :]
+    X[kind == 4] = 0.0
+    return X
+
+
+def _per_row_rel(y, ref):
+    """Largest per-row relative Frobenius error (rows with a zero reference
+    must be exactly zero)."""
+    worst = 0.0
+    for m in range(ref.shape[0]):
+        den = np.linalg.norm(ref[m])
+        num = np.linalg.norm(y[m] - ref[m])
+        if den == 0:
+            assert num == 0, m
+        else:
+            worst = max(worst, num / den)
+    return worst
+
+
+@pytest.mark.parametrize("fmt,M,N,K,xdt,tile_rows", [
+    ("q4_0", 64, 512, 2048, "bf16", 128),       # 2 x 128-row tiles: a K split
+    ("q4_0", 2048, 512, 2048, "bf16", 128),
+    ("affine", 2048, 512, 2048, "f32", 128),
+    ("q4_0", 2048, 8192, 512, "bf16", 256),     # the 256 x 256-tile kernel
+    ("affine", 2048, 8192, 512, "f32", 256),
+])
+def test_wide_range_x_on_the_image_path(fmt, M, N, K, xdt, tile_rows):
+    """Rows holding +-1e5 and +-1e-6 values: every row within 2e-3 of the
+    binary64 oracle on its own (bf16 X is converted exactly after the row's
+    prescale, f32 X is rounded to 11 bits), zero rows exactly zero, and the
+    image entry point giving the same bits."""
+    say(f"wide-range X {fmt} M={M} N={N} K={K} x={xdt} tile_rows={tile_rows}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    W = synth.weights(rng, N, K)
+    X = _wide_range_x(rng, M, K)
+    if xdt == "bf16":
+        xb = synth.bf16_bits(X)
+        tx = dev(xb).view(torch.bfloat16)
+        Xf64 = synth.bf16_bits_to_f32(xb).astype(np.float64)
+    else:
+        tx = torch.from_numpy(X).cuda()
+        Xf64 = X.astype(np.float64)
+    if fmt == "q4_0":
+        planes = oracle.q4_0_quantize(W)
+        What = oracle.q4_0_dequantize(*planes)
+        f = B.Q4_FMT_Q4_0
+    else:
+        planes = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+        What = oracle.affine4_dequantize(*planes)
+        f = B.Q4_FMT_AFFINE4
+    tp = [dev(a) for a in planes]
+    ref = Xf64 @ What.T
+    B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, tile_rows)
+    try:
+        assert B.q4_dispatch_path(M, N, K, f, True) == B.Q4_PATH_MFMA
+        ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
+        if fmt == "q4_0":
+            y = B.q4_gemm(*tp, tx, y_dtype=torch.float32, workspace=ws)
+        else:
+            y = B.affine4_gemm(*tp, tx, y_dtype=torch.float32, workspace=ws)
+        image = B.q4_pack_weight_image(*tp, fmt=f)
+        yi = B.q4_gemm_image(image, tx, N, fmt=f, y_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 128)
+    got = out_f64(y)
+    assert np.isfinite(got).all()
+    e = _per_row_rel(got, ref)
+    say(f"  worst per-row rel err {e:.3e}; whole {rel(got, ref):.3e}")
+    assert e <= BAR
+    assert torch.equal(yi, y)
