@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libq4.so")
+# Q4_LIB_PATH: another build of the same library (the host-side sanitizer
+# build that tests load); by default the in-tree libq4.so.
+LIB_PATH = os.environ.get("Q4_LIB_PATH") or os.path.join(_PKG, "libq4.so")
 
 # status, dtype, format and path codes (include/q4.h)
 (Q4_OK, Q4_ERR_NULL, Q4_ERR_SHAPE, Q4_ERR_ALIGN, Q4_ERR_DTYPE, Q4_ERR_HIP, Q4_ERR_ARG, Q4_ERR_WORKSPACE,

@@ -65,6 +65,59 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# ---- host-side AddressSanitizer / UndefinedBehaviorSanitizer build -------------
+# The host half of each source (argument checks, dispatch, size arithmetic,
+# launch set-up) is instrumented; the device code is built plainly (at -O1:
+# this build serves tests that make no GPU call, tests/test_abi_host.py).
+# Load it into a process that preloads SAN_RUNTIME, with Q4_LIB_PATH
+# pointing at it.
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libq4_host_san.so")
+SAN_RUNTIME = "/opt/rocm/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
+SAN_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O1", "-g", "-fPIC", "-std=c++17", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument", "-Wno-inline-asm", "-Wno-unused-result",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def _compile_san(src: str) -> str:
+    obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (host, sanitized) failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Build SAN_LIB if any source is newer than it; return its path."""
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, "q4.h")]
+    if os.path.exists(SAN_LIB) and os.path.getmtime(SAN_LIB) >= max(os.path.getmtime(f) for f in srcs):
+        return SAN_LIB
+    os.makedirs(SAN_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile_san, SOURCES))
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized) failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--host-sanitized" in sys.argv[1:]:
+        build_host_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

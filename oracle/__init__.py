@@ -38,6 +38,20 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int64
 
 
+def build_sanitized(out: str) -> str:
+    """The oracle built with clang's AddressSanitizer and
+    UndefinedBehaviorSanitizer (serial: no OpenMP), for the sanitizer test."""
+    if not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        tmp = out + ".tmp"
+        subprocess.check_call(["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+                               "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC", "-std=c11",
+                               "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-shared-libsan",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
 def _load():
     global _lib
     if _lib is None:
