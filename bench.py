@@ -336,6 +336,11 @@ def gemm_section(iters: int):
     y16 = torch.empty((M, N), dtype=torch.float16, device="cuda")
     blas_f16_ms = steady_us(lambda i: torch.matmul(x16, w16.t(), out=y16), iters) * 1e-3
     best_deq = deq16_ms + min(dense_ms, blas_f16_ms)
+    # the integer-dot form on the int8 matrix cores: X quantised to Q8_1, then
+    # q4_gemm_q8 (also what q4_gemm runs with the INT8 path forced)
+    xq, xds = B.q8_1_quantize_act(x)
+    q8_ms = steady_us(lambda i: B.q4_gemm_q8(qs, d, xq, xds, y=y), iters) * 1e-3
+    q8_quant_ms = steady_us(lambda i: B.q8_1_quantize_act(x, xq, xds), iters) * 1e-3
     res = {
         "fused_us": fused_ms * 1e3,
         "fused_tflops": flop / (fused_ms * 1e-3) / 1e12,
@@ -349,12 +354,16 @@ def gemm_section(iters: int):
         "jit_bf16_us": (deqbf_ms + blas_bf16_ms) * 1e3,
         "dequant_then_gemm_best_us": best_deq * 1e3,
         "fused_vs_dequant_then_gemm": best_deq / fused_ms,
+        "int8_gemm_q8_us": q8_ms * 1e3,
+        "int8_gemm_q8_tops": flop / (q8_ms * 1e-3) / 1e12,
+        "int8_q8_1_quantize_us": q8_quant_ms * 1e3,
         "flop": flop,
     }
     log(f"[gemm] fused {res['fused_us']:.1f} us = {res['fused_tflops']:.0f} TFLOP/s; "
         f"prepacked weights {res['image_us']:.1f} us = {res['image_tflops']:.0f} TFLOP/s; "
         f"dequant f16 {res['dequant_f16_us']:.1f} us; dense {res['dense_gemm_f16_us']:.1f} us; "
-        f"hipBLASLt bf16 {res['hipblaslt_bf16_us']:.1f} us, f16 {res['hipblaslt_f16_us']:.1f} us")
+        f"hipBLASLt bf16 {res['hipblaslt_bf16_us']:.1f} us, f16 {res['hipblaslt_f16_us']:.1f} us; "
+        f"int8 MFMA (Q8_1 X) {res['int8_gemm_q8_us']:.1f} us + quantise {res['int8_q8_1_quantize_us']:.1f} us")
     return res
 
 

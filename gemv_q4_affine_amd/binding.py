@@ -23,7 +23,7 @@ LIB_PATH = os.environ.get("Q4_LIB_PATH") or os.path.join(_PKG, "libq4.so")
 Q4_NOALLOC_SCRATCH_BYTES = 33 << 20
 Q4_F32, Q4_BF16, Q4_F16 = 0, 1, 2
 Q4_FMT_Q4_0, Q4_FMT_AFFINE4 = 0, 1
-Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM = 0, 1, 2, 3
+Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM, Q4_PATH_INT8 = 0, 1, 2, 3, 4
 Q4_KEY_SKINNY_MAX_M, Q4_KEY_DEQUANT_MIN_M, Q4_KEY_FORCE_PATH, Q4_KEY_TILE_ROWS = 0, 1, 2, 3
 Q4_GEMV_MAX_M = 16
 Q4_GEMV_ACT_MAX_M = 4
@@ -52,6 +52,7 @@ SIGNATURES = {
     "q4_gemm_image_workspace_size": (_I64, [_I64, _I64]),
     "q4_gemm_image": (_INT, [_INT, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _P, _I64, _P]),
     "q4_gemm_image_noalloc": (_INT, [_INT, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _P]),
+    "q4_gemm_q8": (_INT, [_P, _P, _P, _P, _P, _INT, _I64, _I64, _I64, _P]),
     "q4_dispatch_path": (_INT, [_I64, _I64, _I64, _INT, _INT]),
     "q4_set_dispatch": (_INT, [_INT, _I64]),
     "q4_get_dispatch": (_INT, [_INT, ctypes.POINTER(ctypes.c_int64)]),
@@ -393,6 +394,16 @@ def q4_gemm_image_noalloc(image, x, N, fmt=Q4_FMT_Q4_0, y_dtype=torch.bfloat16, 
     y = _empty((M, N), y_dtype, x, stream) if y is None else y
     _check("q4_gemm_image_noalloc", lib().q4_gemm_image_noalloc(fmt, _p(image), _p(x), _dt(x), _p(y), _dt(y), M, N,
                                                                 x.shape[1], _stream(stream)))
+    return y
+
+
+def q4_gemm_q8(w_qs, w_d, x_qs, x_ds, y_dtype=torch.float32, y=None, stream=None):
+    """Q4_0 planes x Q8_1 planes (q8_1_quantize_act) on the int8 matrix cores, any M."""
+    N = w_d.shape[0]
+    M, K = x_qs.shape
+    y = _empty((M, N), y_dtype, x_qs, stream) if y is None else y
+    _check("q4_gemm_q8", lib().q4_gemm_q8(_p(w_qs), _p(w_d), _p(x_qs), _p(x_ds), _p(y), _dt(y), M, N, K,
+                                          _stream(stream)))
     return y
 
 

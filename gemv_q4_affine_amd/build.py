@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libq4.so")
 
-SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip", "affine8.hip", "noalloc.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip", "gemm_q8.hip", "affine8.hip", "noalloc.hip",
+           "capi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -52,7 +53,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]

@@ -42,8 +42,12 @@ bool env_int(const char* name, int64_t* out) {
 // Values Q4_KEY_FORCE_PATH accepts: automatic (-1), or a path q4_gemm /
 // affine4_gemm can run.
 bool force_path_ok(int64_t v) {
-    return v == -1 || v == Q4_PATH_SKINNY || v == Q4_PATH_MFMA || v == Q4_PATH_DEQUANT_GEMM;
+    return v == -1 || v == Q4_PATH_GEMV || v == Q4_PATH_SKINNY || v == Q4_PATH_MFMA || v == Q4_PATH_DEQUANT_GEMM ||
+           v == Q4_PATH_INT8;
 }
+
+// Workspace of the INT8 path: the Q8_1 planes of X (codes, then {d, s} pairs).
+int64_t q8_planes_bytes(int64_t M, int64_t K) { return M * K + M * (K / 32) * 4; }
 
 // Environment overrides, read once per process and clamped (the clamped
 // token-count gate pattern of vllm.cpp issue #838, Scope).
@@ -171,6 +175,7 @@ int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt) {
     const int path = q4_dispatch_path(M, N, K, fmt, 1);
     if (path == Q4_PATH_MFMA) return q4::packed_x_bytes(M, N, K);
     if (path == Q4_PATH_DEQUANT_GEMM) return N * K * 2;
+    if (path == Q4_PATH_INT8 && fmt == Q4_FMT_Q4_0) return q8_planes_bytes(M, K);
     return 0;
 }
 
@@ -337,6 +342,26 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
     if (M == 0 || N == 0) return Q4_OK;
     hipStream_t s = as_stream(stream);
     switch (path) {
+        case Q4_PATH_GEMV: {
+            // the integer-dot GEMV on X quantised to Q8_1 inside the kernel
+            if (wf != q4::WF_Q4_0 || M > Q4_GEMV_ACT_MAX_M || y_dtype != Q4_F32) return Q4_ERR_ARG;
+            const uint8_t* qs[1] = {static_cast<const uint8_t*>(a)};
+            const uint16_t* d[1] = {static_cast<const uint16_t*>(b)};
+            const int64_t n[1] = {N};
+            float* ys[1] = {static_cast<float*>(y)};
+            return gemv_common(1, qs, d, n, ys, nullptr, nullptr, x, x_dtype, M, K, stream);
+        }
+        case Q4_PATH_INT8: {
+            // X quantised to Q8_1 in the workspace, then the int8 matrix-core GEMM
+            if (wf != q4::WF_Q4_0) return Q4_ERR_ARG;
+            if (workspace == nullptr || workspace_bytes < q8_planes_bytes(M, K)) return Q4_ERR_WORKSPACE;
+            if (!aligned16(workspace)) return Q4_ERR_ALIGN;
+            int8_t* xq = static_cast<int8_t*>(workspace);
+            uint16_t* xds = reinterpret_cast<uint16_t*>(xq + M * K);
+            if (q4::launch_q8_1_quantize(x, x_dtype, M, K, xq, xds, s) != hipSuccess) return Q4_ERR_HIP;
+            return hip_status(q4::launch_gemm_q8(static_cast<const uint8_t*>(a), static_cast<const uint16_t*>(b), xq,
+                                                 xds, y, y_dtype, M, N, K, s));
+        }
         case Q4_PATH_SKINNY:
             if (M > kSkinnyLimit) return Q4_ERR_ARG;
             return hip_status(q4::launch_gemm_skinny(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, s));
@@ -394,6 +419,16 @@ int affine4_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
     if ((rc = check_ptrs_aligned({w_q, scales, biases, x, y}))) return rc;
     return gemm_common(q4::WF_AFFINE4, w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, workspace,
                        workspace_bytes, stream);
+}
+
+int q4_gemm_q8(const uint8_t* w_qs, const uint16_t* w_d, const int8_t* x_qs, const uint16_t* x_ds, void* y,
+               int y_dtype, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (y_dtype != Q4_BF16 && y_dtype != Q4_F32) return Q4_ERR_DTYPE;
+    int rc = check_dims(M, N, K, 32);
+    if (rc) return rc;
+    if (M == 0 || N == 0) return Q4_OK;
+    if ((rc = check_ptrs_aligned({w_qs, w_d, x_qs, x_ds, y}))) return rc;
+    return hip_status(q4::launch_gemm_q8(w_qs, w_d, x_qs, x_ds, y, y_dtype, M, N, K, as_stream(stream)));
 }
 
 static int image_dims(int fmt, int64_t M, int64_t N, int64_t K) {

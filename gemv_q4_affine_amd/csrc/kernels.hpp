@@ -14,6 +14,10 @@ enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 // query fails).
 int current_cu_count();
 
+// Q4_0 x Q8_1 on the int8 matrix cores (gemm_q8.hip): y [M][N] of ydt.
+hipError_t launch_gemm_q8(const uint8_t* wqs, const uint16_t* wd, const int8_t* xqs, const uint16_t* xds, void* y,
+                          int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
 // Device address of the current GPU's copy of the library's fixed scratch
 // array (Q4_NOALLOC_SCRATCH_BYTES), looked up once per device (noalloc.hip).
 hipError_t noalloc_scratch(void** out);

@@ -84,11 +84,16 @@ extern "C" {
 #define Q4_PATH_SKINNY        1  /* fused, weights streamed once, small M              */
 #define Q4_PATH_MFMA          2  /* fused dequant-in-LDS MFMA GEMM, large M             */
 #define Q4_PATH_DEQUANT_GEMM  3  /* dequantise to a dense fp16 W, then dense MFMA GEMM  */
+#define Q4_PATH_INT8          4  /* X quantised to Q8_1, int8 MFMA GEMM (q4_gemm_q8)     */
 
 /* dispatch keys for q4_set_dispatch / q4_get_dispatch */
 #define Q4_KEY_SKINNY_MAX_M    0  /* q4_gemm/affine4_gemm: M <= this -> SKINNY          */
 #define Q4_KEY_DEQUANT_MIN_M   1  /* M >= this (and workspace given) -> DEQUANT_GEMM    */
-#define Q4_KEY_FORCE_PATH      2  /* -1 = automatic, else a Q4_PATH_* for q4_gemm etc.  */
+#define Q4_KEY_FORCE_PATH      2  /* -1 = automatic, else a Q4_PATH_* for q4_gemm etc.;
+                                     GEMV and INT8 compute on X quantised to Q8_1 and
+                                     serve Q4_0 only (q4_gemm: GEMV needs M <= 4 and an
+                                     f32 y, INT8 a workspace of M*K + M*(K/32)*4 bytes;
+                                     other cases return Q4_ERR_ARG)                      */
 #define Q4_KEY_TILE_ROWS       3  /* MFMA path: 128 = 128x256 output tiles (default),
                                      256 = 256x256 tiles where every CU gets at least one */
 
@@ -360,7 +365,8 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
 
 /*
  * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
- * 0 for SKINNY; for MFMA the X and weight tile images,
+ * 0 for SKINNY and GEMV; M*K + M*(K/32)*4 (the Q8_1 planes of X) for INT8;
+ * for MFMA the X and weight tile images,
  * ceil(M/128)*128 * (ceil(K/64)*64 * 2 + 1) + ceil(N/256) * ceil(K/64) * 9216
  * bytes (the X image holds one exponent byte per row after its tiles),
  * plus parts*M*N*4 for the K-split partial results when the tile count is
@@ -433,6 +439,25 @@ int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* 
  */
 int q4_gemm_image_noalloc(int fmt, const void* image, const void* x, int x_dtype, void* y, int y_dtype,
                           int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * q4_gemm_q8 -- y[m][n] = sum_b d4[n][b] * d8[m][b] * isum[m][n][b] for any M,
+ * the integer-dot product of q4_gemv on the int8 matrix cores (the DP4A /
+ * matrix-engine variant of the Q4_0 x Q8_1 kernel: trueno page,
+ * KERNEL_WEIGHTS; the MMVQ pair of the llama.cpp SYCL repro page, Important
+ * source touch points).  Each 32-weight block's int32 dots are exact
+ * (v_mfma_i32_32x32x32_i8); each is scaled by the fp32 product d4*d8 (exact
+ * for binary16 scales) with one fma into fp32 accumulators, in K order.
+ *   w_qs, w_d   : Q4_0 planes as in q4_gemv
+ *   x_qs, x_ds  : Q8_1 planes as q8_1_quantize_act writes them, [M][K] and
+ *                 [M][K/32][2]
+ *   y           : device out, [M][N] of y_dtype (Q4_BF16 RNE, or Q4_F32)
+ * The per-block rescale is vector-ALU work (a convert, a multiply and an fma
+ * per output and block) that the binary16 MFMA path does not have; q4_gemm
+ * takes this path only when Q4_KEY_FORCE_PATH is Q4_PATH_INT8.
+ */
+int q4_gemm_q8(const uint8_t* w_qs, const uint16_t* w_d, const int8_t* x_qs, const uint16_t* x_ds,
+               void* y, int y_dtype, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * dense_gemm -- Y = X . W^T with a dense binary16 W [N][K] (the GEMM half of

@@ -33,7 +33,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function():
     names = _declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in q4.h but not exported"
@@ -220,6 +220,17 @@ def test_weight_image_validation_and_sizes():
     assert g(B.Q4_FMT_Q4_0, P, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None, 0, None) == B.Q4_OK
 
 
+def test_gemm_q8_validation():
+    g = lib().q4_gemm_q8
+    assert g(P, P, P, P, P, B.Q4_F16, 4, 8, 64, None) == B.Q4_ERR_DTYPE
+    assert g(P, P, P, P, P, B.Q4_F32, 4, 8, 48, None) == B.Q4_ERR_SHAPE
+    assert g(P, P, P, P, P, B.Q4_F32, -1, 8, 64, None) == B.Q4_ERR_SHAPE
+    assert g(P, P, None, P, P, B.Q4_F32, 4, 8, 64, None) == B.Q4_ERR_NULL
+    assert g(P, P, P, MIS, P, B.Q4_F32, 4, 8, 64, None) == B.Q4_ERR_ALIGN
+    assert g(P, P, P, P, P, B.Q4_BF16, 0, 8, 64, None) == B.Q4_OK
+    assert g(None, None, None, None, None, B.Q4_BF16, 4, 0, 64, None) == B.Q4_OK
+
+
 def test_noalloc_gemm_rejects_before_any_device_call():
     """q4_gemm_image_noalloc: the same argument checks as q4_gemm_image, and
     an X image beyond the fixed scratch is refused with its own status before
@@ -278,9 +289,35 @@ def test_dispatch_predicate_boundaries():
     with pytest.raises(B.Q4Error):
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, 9)
     with pytest.raises(B.Q4Error):
-        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_GEMV)
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, 5)
     with pytest.raises(B.Q4Error):
         B.q4_set_dispatch(77, 1)
+    # the Q8_1 paths: forced only, Q4_0 only; INT8 wants the Q8_1 planes as workspace
+    g = lib().q4_gemm
+    a = lib().affine4_gemm
+    for path in (B.Q4_PATH_GEMV, B.Q4_PATH_INT8):
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, path)
+        try:
+            assert B.q4_dispatch_path(8, 64, 64) == path
+            assert a(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_F32, 4, 8, 128, P2, 1 << 20, None) == B.Q4_ERR_ARG
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_GEMV)
+    try:
+        assert B.q4_gemm_workspace_size(4, 64, 64) == 0
+        assert g(P, P, P, B.Q4_BF16, P, B.Q4_F32, 5, 8, 64, None, 0, None) == B.Q4_ERR_ARG      # M > 4
+        assert g(P, P, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_ARG     # bf16 y
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_INT8)
+    try:
+        assert B.q4_gemm_workspace_size(100, 64, 4096) == 100 * 4096 + 100 * 128 * 4
+        need = 4 * 64 + 4 * 2 * 4
+        assert g(P, P, P, B.Q4_BF16, P, B.Q4_F32, 4, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
+        assert g(P, P, P, B.Q4_BF16, P, B.Q4_F32, 4, 8, 64, P2, need - 1, None) == B.Q4_ERR_WORKSPACE
+        assert g(P, P, P, B.Q4_BF16, P, B.Q4_F32, 4, 8, 64, MIS, need, None) == B.Q4_ERR_ALIGN
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
     # tile rows: 128 (default) or 256, nothing else
     assert B.q4_get_dispatch(B.Q4_KEY_TILE_ROWS) == 128
     for bad in (0, 64, 192, 512):
@@ -313,10 +350,10 @@ print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUA
     ({"Q4_SKINNY_MAX_M": "-3"}, (0, None, -1, B.Q4_PATH_MFMA, B.Q4_PATH_MFMA)),
     ({"Q4_SKINNY_MAX_M": "8", "Q4_DEQUANT_MIN_M": "64"}, (8, 64, -1, B.Q4_PATH_MFMA, B.Q4_PATH_DEQUANT_GEMM)),
     ({"Q4_FORCE_PATH": "3"}, (None, None, 3, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM)),
-    # values the setter rejects leave the automatic dispatch (17: no such path;
-    # 0: the integer-dot GEMV, which q4_gemm / affine4_gemm do not run)
+    ({"Q4_FORCE_PATH": "0"}, (None, None, 0, B.Q4_PATH_GEMV, B.Q4_PATH_GEMV, 0)),
+    ({"Q4_FORCE_PATH": "4"}, (None, None, 4, B.Q4_PATH_INT8, B.Q4_PATH_INT8, 1)),
+    # values the setter rejects leave the automatic dispatch (17: no such path)
     ({"Q4_FORCE_PATH": "17"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
-    ({"Q4_FORCE_PATH": "0"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA, 1)),
     ({"Q4_FORCE_PATH": "-5"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
     ({"Q4_FORCE_PATH": "junk"}, (None, None, -1, None, None)),
 ])

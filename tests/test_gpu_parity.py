@@ -1158,3 +1158,110 @@ def test_wide_range_x_on_the_image_path(fmt, M, N, K, xdt, tile_rows):
     say(f"  worst per-row rel err {e:.3e}; whole {rel(got, ref):.3e}")
     assert e <= BAR
     assert torch.equal(yi, y)
+
+
+# ---------------------------------------------------------------------------
+# Q4_0 x Q8_1 on the int8 matrix cores (q4_gemm_q8, path Q4_PATH_INT8)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(130, 300, 4128), (1, 33, 32), (64, 256, 512), (257, 129, 1056)])
+def test_gemm_q8_unit_scales_are_exact_integer_sums(M, N, K):
+    """d4 = d8 = 1: every output is the integer sum of its block dots, bit for
+    bit (ragged M and N, K = 32 mod 64 and a last chunk of scales short)."""
+    say(f"gemm_q8 unit scales M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 3 + N + K)
+    wqs = rng.integers(0, 256, (N, K // 32, 16), dtype=np.uint8)
+    wd = np.full((N, K // 32), 0x3C00, np.uint16)
+    xqs = rng.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    xds = np.zeros((M, K // 32, 2), np.uint16)
+    xds[..., 0] = 0x3C00
+    y = B.q4_gemm_q8(dev(wqs), dev(wd), dev(xqs), dev(xds), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    isum = oracle.q4q8_block_dots(wqs, xqs).astype(np.int64).sum(axis=2)   # [M, N]
+    assert np.array_equal(host(y).astype(np.int64), isum)
+    assert np.array_equal(host(y), isum.astype(np.float32))
+
+
+def test_gemm_q8_block_dot_extremes():
+    """The largest block dots: nibbles 0 or 15 against codes +-127."""
+    N, K = 2, 32
+    wqs = np.zeros((N, 1, 16), np.uint8)
+    wqs[1] = 0xFF
+    wd = np.full((N, 1), 0x3C00, np.uint16)
+    for v, want in ((-127, [32512, -28448]), (127, [-32512, 28448])):
+        xqs = np.full((3, K), v, np.int8)
+        xds = np.zeros((3, 1, 2), np.uint16)
+        xds[..., 0] = 0x3C00
+        y = host(B.q4_gemm_q8(dev(wqs), dev(wd), dev(xqs), dev(xds), y_dtype=torch.float32))
+        assert y.tolist() == [want] * 3
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 700, 2048), (33, 4096, 4096), (1, 257, 96)])
+def test_gemm_q8_against_oracle(M, N, K):
+    """Real scales against the binary64 q4 x q8 oracle: fp32 output within the
+    GEMV's 1e-5 (exact block terms, fp32 accumulation), bf16 output its RNE."""
+    say(f"gemm_q8 oracle M={M} N={N} K={K}")
+    wqs, wd, xqs, xds = _gemv_case(M, N, K, M + N + K)
+    ref = oracle.q4q8_gemv(wqs, wd, xqs, xds)
+    args = (dev(wqs), dev(wd), dev(xqs), dev(xds))
+    y = B.q4_gemm_q8(*args, y_dtype=torch.float32)
+    yb = B.q4_gemm_q8(*args, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    e = rel(out_f64(y), ref)
+    say(f"  rel err {e:.3e}")
+    assert e <= GEMV_TIGHT
+    assert torch.equal(yb, y.to(torch.bfloat16))
+
+
+def test_gemm_q8_prefill_config_sampled():
+    """M = 2048, N = 12288, K = 4096 with X quantised to Q8_1 on the GPU (bit-
+    exact with the oracle's codes, checked): 24 whole rows against the oracle."""
+    wl = synth.PREFILL
+    M, N, K = wl.M, wl.N, wl.K
+    say(f"gemm_q8 prefill M={M} N={N} K={K}")
+    rng = np.random.default_rng(5)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    wqs, wd = oracle.q4_0_quantize(W)
+    xb = synth.bf16_bits(X)
+    tx = dev(xb).view(torch.bfloat16)
+    xq, xds = B.q8_1_quantize_act(tx)
+    rows = np.random.default_rng(6).choice(M, 24, replace=False)
+    rows.sort()
+    rxq, rxd = oracle.q8_1_quantize(synth.bf16_bits_to_f32(xb)[rows])
+    assert np.array_equal(host(xq)[rows], rxq) and np.array_equal(host(xds, np.uint16)[rows], rxd)
+    y = B.q4_gemm_q8(dev(wqs), dev(wd), xq, xds, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.q4q8_gemv(wqs, wd, rxq, rxd)
+    e = rel(out_f64(y)[rows], ref)
+    say(f"  sampled rows rel err {e:.3e}")
+    assert e <= GEMV_TIGHT
+
+
+@pytest.mark.parametrize("M", [1, 4, 77, 2048])
+def test_forced_q8_paths_equal_their_two_steps(M):
+    """q4_gemm with Q4_KEY_FORCE_PATH = INT8: the bits of q8_1_quantize_act +
+    q4_gemm_q8; with GEMV (M <= 4, f32 out): the bits of q4_gemv_act."""
+    N, K = 1024, 4096
+    say(f"forced Q8_1 paths M={M}")
+    rng = np.random.default_rng(M)
+    qs, d = (dev(a) for a in oracle.q4_0_quantize(synth.weights(rng, N, K)))
+    tx = bf16_dev(synth.activations(rng, M, K))
+    xq, xds = B.q8_1_quantize_act(tx)
+    want = B.q4_gemm_q8(qs, d, xq, xds, y_dtype=torch.float32)
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_INT8)
+    try:
+        got = B.q4_gemm(qs, d, tx, y_dtype=torch.float32)
+        gotb = B.q4_gemm(qs, d, tx, y_dtype=torch.bfloat16)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    assert torch.equal(gotb, want.to(torch.bfloat16))
+    if M <= B.Q4_GEMV_ACT_MAX_M:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_GEMV)
+        try:
+            g = B.q4_gemm(qs, d, tx, y_dtype=torch.float32)
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+        assert torch.equal(g, B.q4_gemv_act(qs, d, tx))
