@@ -423,7 +423,8 @@ def affine_section(iters: int):
         out.append(rec)
         log(f"[affine] M={M}: fused {rec['fused_us']:.1f} us (prepared image {rec['fused_prepared_image_us']:.1f}), "
             f"jit {rec['jit_us']:.1f} us, "
-            f"ref {rec['ref_us']:.1f} us, roofline {rec['roofline_frac']:.2f}")
+            f"ref {rec['ref_us']:.1f} us, dequant + dense_gemm {rec['dequant_dense_f16_us']:.1f} us, "
+            f"roofline {rec['roofline_frac']:.2f}")
     crossover = next((rec["M"] for rec in out if not rec["fused_beats_jit"]), None)
     crossover_img = next((rec["M"] for rec in out if not rec["fused_prepared_image_beats_jit"]), None)
     return {"sweep": out, "first_M_where_dequant_then_gemm_wins": crossover,
