@@ -22,9 +22,9 @@ LIB_PATH = os.environ.get("Q4_LIB_PATH") or os.path.join(_PKG, "libq4.so")
  Q4_ERR_SCRATCH) = (0, -1, -2, -3, -4, -5, -6, -7, -8)
 Q4_NOALLOC_SCRATCH_BYTES = 33 << 20
 Q4_F32, Q4_BF16, Q4_F16 = 0, 1, 2
-Q4_FMT_Q4_0, Q4_FMT_AFFINE4 = 0, 1
+Q4_FMT_Q4_0, Q4_FMT_AFFINE4, Q4_FMT_AFFINE8 = 0, 1, 2
 Q4_PATH_GEMV, Q4_PATH_SKINNY, Q4_PATH_MFMA, Q4_PATH_DEQUANT_GEMM, Q4_PATH_INT8 = 0, 1, 2, 3, 4
-Q4_KEY_SKINNY_MAX_M, Q4_KEY_DEQUANT_MIN_M, Q4_KEY_FORCE_PATH, Q4_KEY_TILE_ROWS = 0, 1, 2, 3
+Q4_KEY_SKINNY_MAX_M, Q4_KEY_DEQUANT_MIN_M, Q4_KEY_FORCE_PATH, Q4_KEY_TILE_ROWS, Q4_KEY_AFFINE8_FUSED_MAX_M = 0, 1, 2, 3, 4
 Q4_GEMV_MAX_M = 16
 Q4_GEMV_ACT_MAX_M = 4
 Q4_GEMV_MAX_MATS = 4

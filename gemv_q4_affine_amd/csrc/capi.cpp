@@ -25,6 +25,8 @@ std::atomic<int64_t> g_skinny_max_m{32};
 std::atomic<int64_t> g_dequant_min_m{kMaxDim + 1};   // dequantise-then-GEMM never wins by default
 std::atomic<int64_t> g_force_path{-1};
 std::atomic<int64_t> g_tile_rows{128};
+constexpr int64_t kAffine8FusedLimit = 32;     // the fused affine 8-bit kernels' largest M
+std::atomic<int64_t> g_affine8_fused_max_m{kAffine8FusedLimit};
 std::once_flag g_env_once;
 
 int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -59,6 +61,7 @@ void read_env() {
         // the setter's rule: a value it would reject leaves the default
         if (env_int("Q4_FORCE_PATH", &v) && force_path_ok(v)) g_force_path = v;
         if (env_int("Q4_TILE_ROWS", &v) && (v == 128 || v == 256)) g_tile_rows = v;
+        if (env_int("Q4_AFFINE8_FUSED_MAX_M", &v)) g_affine8_fused_max_m = clamp64(v, 0, kAffine8FusedLimit);
     });
 }
 
@@ -143,6 +146,7 @@ int q4_set_dispatch(int key, int64_t value) {
             if (value != 128 && value != 256) return Q4_ERR_ARG;
             g_tile_rows = value;
             return Q4_OK;
+        case Q4_KEY_AFFINE8_FUSED_MAX_M: g_affine8_fused_max_m = clamp64(value, 0, kAffine8FusedLimit); return Q4_OK;
         default: return Q4_ERR_ARG;
     }
 }
@@ -155,16 +159,23 @@ int q4_get_dispatch(int key, int64_t* value) {
         case Q4_KEY_DEQUANT_MIN_M: *value = g_dequant_min_m; return Q4_OK;
         case Q4_KEY_FORCE_PATH: *value = g_force_path; return Q4_OK;
         case Q4_KEY_TILE_ROWS: *value = g_tile_rows; return Q4_OK;
+        case Q4_KEY_AFFINE8_FUSED_MAX_M: *value = g_affine8_fused_max_m; return Q4_OK;
         default: return Q4_ERR_ARG;
     }
 }
 
 int q4_dispatch_path(int64_t M, int64_t N, int64_t K, int fmt, int have_workspace) {
     read_env();
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE4) return Q4_ERR_ARG;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE4 && fmt != Q4_FMT_AFFINE8) return Q4_ERR_ARG;
     const int rc = check_dims(M, N, K, fmt == Q4_FMT_Q4_0 ? 32 : 64);
     if (rc) return rc;
     const int64_t forced = g_force_path;
+    if (fmt == Q4_FMT_AFFINE8) {
+        // the fused kernels (small M) or dequantise-then-GEMM; a forced path
+        // that affine8_gemm has no kernel for leaves the automatic choice
+        if (forced == Q4_PATH_SKINNY || forced == Q4_PATH_DEQUANT_GEMM) return (int)forced;
+        return M <= g_affine8_fused_max_m ? Q4_PATH_SKINNY : Q4_PATH_DEQUANT_GEMM;
+    }
     if (forced >= 0) return (int)forced;
     if (M <= g_skinny_max_m) return Q4_PATH_SKINNY;
     if (have_workspace && M >= g_dequant_min_m) return Q4_PATH_DEQUANT_GEMM;
@@ -518,7 +529,10 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
 
 int64_t affine8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (check_dims(M, N, K, 64) != Q4_OK) return 0;
-    return M <= q4::kAffine8GemvMaxM ? 0 : N * K * 2;   // bf16 X up to kAffine8MmaMaxM rows uses none
+    // the fused kernels use none; enough for either activation type (f32 X
+    // above 16 rows and bf16 X above 32 dequantise)
+    const int path = q4_dispatch_path(M, N, K, Q4_FMT_AFFINE8, 1);
+    return (path == Q4_PATH_SKINNY && M <= q4::kAffine8GemvMaxM) ? 0 : N * K * 2;
 }
 
 int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases, int64_t group_size,
@@ -530,16 +544,21 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
     if (rc) return rc;
     if (M == 0 || N == 0) return Q4_OK;
     if ((rc = check_ptrs_aligned({w_q, scales, biases, x, y}))) return rc;
-    read_env();
     hipStream_t s = as_stream(stream);
-    // M <= 4: the fused vector kernel; bf16 X up to 32 rows: the bf16-MFMA
-    // kernel on the raw codes; f32 X up to 16 rows: the vector kernel
-    if (M <= 4 || (x_dtype == Q4_F32 && M <= q4::kAffine8GemvMaxM))
-        return hip_status(q4::launch_affine8_gemv(w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, s));
-    if (x_dtype == Q4_BF16 && M <= q4::kAffine8MmaMaxM)
-        return hip_status(q4::launch_affine8_mma(w_q, scales, biases, x, y, y_dtype, M, N, K, s));
-    // larger M: dequantise to binary16 in the workspace, then the dense GEMM
-    if (workspace == nullptr || workspace_bytes < N * K * 2) return Q4_ERR_WORKSPACE;
+    const bool have_ws = workspace != nullptr && workspace_bytes >= N * K * 2;
+    const int path = q4_dispatch_path(M, N, K, Q4_FMT_AFFINE8, have_ws ? 1 : 0);
+    if (path < 0) return path;
+    if (path == Q4_PATH_SKINNY) {
+        // M <= 4: the fused vector kernel; bf16 X up to 32 rows: the bf16-MFMA
+        // kernel on the raw codes; f32 X up to 16 rows: the vector kernel;
+        // f32 X above that goes on to dequantise-then-GEMM
+        if (M <= 4 || (x_dtype == Q4_F32 && M <= q4::kAffine8GemvMaxM))
+            return hip_status(q4::launch_affine8_gemv(w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, s));
+        if (x_dtype == Q4_BF16 && M <= q4::kAffine8MmaMaxM)
+            return hip_status(q4::launch_affine8_mma(w_q, scales, biases, x, y, y_dtype, M, N, K, s));
+    }
+    // dequantise to binary16 in the workspace, then the dense GEMM
+    if (!have_ws) return Q4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q4_ERR_ALIGN;
     if (q4::launch_affine8_dequantize(w_q, scales, biases, N, K, workspace, q4::DT_F16, s) != hipSuccess)
         return Q4_ERR_HIP;

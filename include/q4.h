@@ -79,6 +79,7 @@ extern "C" {
 /* ---- formats and dispatch paths ------------------------------------------- */
 #define Q4_FMT_Q4_0     0
 #define Q4_FMT_AFFINE4  1
+#define Q4_FMT_AFFINE8  2  /* q4_dispatch_path only: the paths of affine8_gemm */
 
 #define Q4_PATH_GEMV          0  /* integer-dot GEMV on Q8_1 activations (q4_gemv)     */
 #define Q4_PATH_SKINNY        1  /* fused, weights streamed once, small M              */
@@ -96,6 +97,9 @@ extern "C" {
                                      other cases return Q4_ERR_ARG)                      */
 #define Q4_KEY_TILE_ROWS       3  /* MFMA path: 128 = 128x256 output tiles (default),
                                      256 = 256x256 tiles where every CU gets at least one */
+#define Q4_KEY_AFFINE8_FUSED_MAX_M 4 /* affine8_gemm: M <= this (0..32) -> the fused
+                                     kernels (SKINNY), above -> DEQUANT_GEMM; f32 X
+                                     above 16 rows always takes DEQUANT_GEMM          */
 
 /* Largest M that q4_gemv / q4_gemv_fused2 accept. */
 #define Q4_GEMV_MAX_M 16
@@ -341,6 +345,10 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
 /*
  * affine8_gemm -- Y = X . dequant(Wq)^T for affine 8-bit group-64 weights
  * (quantized_matmul with transpose=True, bits=8, group_size=64).
+ * Paths (q4_dispatch_path with Q4_FMT_AFFINE8): SKINNY up to
+ * Q4_KEY_AFFINE8_FUSED_MAX_M rows (default 32: the fused kernels below),
+ * DEQUANT_GEMM above it; Q4_KEY_FORCE_PATH = SKINNY or DEQUANT_GEMM forces
+ * one of them, other forced values leave the automatic choice.  On SKINNY:
  *   M <= 4 (and M <= 16 on a Q4_F32 activation): one fused launch, no
  *     workspace: each weight is dequantised once in binary32 (q*s + b, one
  *     fma) and multiplied with the M rows in binary32.
@@ -348,7 +356,7 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
  *     the bf16 matrix cores multiply X with the raw codes (exact in
  *     bfloat16) per 64-weight group, and s and b scale the group's sums in
  *     binary32.  Both fused kernels sum in an order that depends on K only.
- *   Otherwise: dequantise-then-GEMM: the weights are dequantised to binary16
+ *   Otherwise (and on DEQUANT_GEMM): dequantise-then-GEMM: the weights are dequantised to binary16
  *     in the workspace (at least N*K*2 bytes, 16-byte aligned; less:
  *     Q4_ERR_WORKSPACE), then the dense binary16 GEMM of dense_gemm runs on
  *     them.  affine8_gemm_workspace_size(M, N, K) is 0 for M <= 16 and N*K*2
@@ -473,8 +481,8 @@ int dense_gemm(const void* x, int x_dtype, const uint16_t* w_f16, void* y, int y
 /* ======================================================================== */
 
 /*
- * q4_dispatch_path -- the path q4_gemm (fmt Q4_FMT_Q4_0) or affine4_gemm
- * (Q4_FMT_AFFINE4) takes for this shape, given whether a large enough
+ * q4_dispatch_path -- the path q4_gemm (fmt Q4_FMT_Q4_0), affine4_gemm
+ * (Q4_FMT_AFFINE4) or affine8_gemm (Q4_FMT_AFFINE8) takes for this shape, given whether a large enough
  * workspace is supplied: Q4_PATH_SKINNY / Q4_PATH_MFMA / Q4_PATH_DEQUANT_GEMM,
  * or a negative status for invalid arguments.  Token-count thresholds follow
  * the pages' pattern (ET-SoC-1 PR Overview: one token goes to the vector-dot

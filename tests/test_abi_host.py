@@ -292,6 +292,34 @@ def test_dispatch_predicate_boundaries():
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, 5)
     with pytest.raises(B.Q4Error):
         B.q4_set_dispatch(77, 1)
+    # affine 8-bit: fused kernels up to Q4_KEY_AFFINE8_FUSED_MAX_M (default 32),
+    # dequantise-then-GEMM above; only SKINNY and DEQUANT_GEMM can be forced
+    A8 = B.Q4_FMT_AFFINE8
+    assert B.q4_get_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M) == 32
+    assert B.q4_dispatch_path(32, 4096, 4096, A8) == B.Q4_PATH_SKINNY
+    assert B.q4_dispatch_path(33, 4096, 4096, A8) == B.Q4_PATH_DEQUANT_GEMM
+    assert B.q4_dispatch_path(1, 4096, 4064, A8) == B.Q4_ERR_SHAPE     # K % 64
+    ws8 = lib().affine8_gemm_workspace_size
+    B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 4)
+    try:
+        assert B.q4_dispatch_path(5, 4096, 4096, A8) == B.Q4_PATH_DEQUANT_GEMM
+        assert ws8(5, 4096, 4096) == 4096 * 4096 * 2 and ws8(4, 4096, 4096) == 0
+        assert lib().affine8_gemm(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 5, 8, 64, None, 0, None) == \
+            B.Q4_ERR_WORKSPACE
+        B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 1000)
+        assert B.q4_get_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M) == 32
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 32)
+    for forced, want_small, want_big in ((B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM),
+                                         (B.Q4_PATH_SKINNY, B.Q4_PATH_SKINNY, B.Q4_PATH_SKINNY),
+                                         (B.Q4_PATH_MFMA, B.Q4_PATH_SKINNY, B.Q4_PATH_DEQUANT_GEMM),
+                                         (B.Q4_PATH_INT8, B.Q4_PATH_SKINNY, B.Q4_PATH_DEQUANT_GEMM)):
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, forced)
+        try:
+            assert B.q4_dispatch_path(1, 64, 64, A8) == want_small
+            assert B.q4_dispatch_path(2048, 64, 64, A8) == want_big
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
     # the Q8_1 paths: forced only, Q4_0 only; INT8 wants the Q8_1 planes as workspace
     g = lib().q4_gemm
     a = lib().affine4_gemm
@@ -340,7 +368,8 @@ from gemv_q4_affine_amd import binding as B
 print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUANT_MIN_M),
       B.q4_get_dispatch(B.Q4_KEY_FORCE_PATH),
       B.q4_dispatch_path(19, 4096, 4096), B.q4_dispatch_path(64, 4096, 4096, have_workspace=True),
-      int(B.q4_gemm_workspace_size(64, 4096, 4096) > 0))
+      int(B.q4_gemm_workspace_size(64, 4096, 4096) > 0),
+      B.q4_get_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M), B.q4_dispatch_path(20, 4096, 4096, B.Q4_FMT_AFFINE8))
 """
 
 
@@ -356,10 +385,12 @@ print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUA
     ({"Q4_FORCE_PATH": "17"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
     ({"Q4_FORCE_PATH": "-5"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
     ({"Q4_FORCE_PATH": "junk"}, (None, None, -1, None, None)),
+    ({"Q4_AFFINE8_FUSED_MAX_M": "16"}, (None, None, -1, None, None, None, 16, B.Q4_PATH_DEQUANT_GEMM)),
+    ({"Q4_AFFINE8_FUSED_MAX_M": "99"}, (None, None, -1, None, None, None, 32, B.Q4_PATH_SKINNY)),
 ])
 def test_dispatch_environment_overrides(env, expect):
     full = dict(os.environ)
-    for k in ("Q4_SKINNY_MAX_M", "Q4_DEQUANT_MIN_M", "Q4_FORCE_PATH"):
+    for k in ("Q4_SKINNY_MAX_M", "Q4_DEQUANT_MIN_M", "Q4_FORCE_PATH", "Q4_AFFINE8_FUSED_MAX_M"):
         full.pop(k, None)
     full.update(env)
     out = subprocess.run([sys.executable, "-c", _ENV_PROBE.format(root=ROOT)], env=full, capture_output=True,

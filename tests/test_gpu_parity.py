@@ -697,6 +697,40 @@ def test_affine8_gemm_parity(M, N, K):
         assert e <= GEMV_TIGHT, (M, N, K, "f32 x", e)
 
 
+def test_affine8_dispatch_routes():
+    """affine8_gemm follows q4_dispatch_path (Q4_FMT_AFFINE8): a forced
+    DEQUANT_GEMM, or Q4_KEY_AFFINE8_FUSED_MAX_M below M, gives the bits of
+    affine8_dequantize + dense_gemm; the default stays on the fused kernel;
+    all within the bar of the binary64 oracle."""
+    M, N, K = 8, 300, 256
+    rng = np.random.default_rng(88)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(W), 64)
+    t = [dev(a) for a in (q, s, b)]
+    x = bf16_dev(X)
+    ref = oracle.matmul_f64(synth.bf16_bits_to_f32(synth.bf16_bits(X)).astype(np.float64),
+                            oracle.affine8_dequantize(q, s, b))
+    want_deq = B.dense_gemm(x, B.affine8_dequantize(*t, out_dtype=torch.float16), y_dtype=torch.float32)
+    fused = B.affine8_gemm(*t, x, y_dtype=torch.float32)
+    assert not torch.equal(fused, want_deq)          # a different path
+    for how in ("force", "key"):
+        if how == "force":
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+        else:
+            B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 4)
+        try:
+            assert B.affine8_gemm_workspace_size(M, N, K) == N * K * 2
+            y = B.affine8_gemm(*t, x, y_dtype=torch.float32)
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+            B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 32)
+        torch.cuda.synchronize()
+        assert torch.equal(y, want_deq), how
+    for y in (fused, want_deq):
+        assert rel(out_f64(y), ref) <= BAR
+
+
 def test_affine8_gemm_full_size_sampled():
     """N=12288, K=4096 at M = 1, 16 and 32 (fused) and M = 64 (dequantise-then-GEMM): sampled outputs against binary64."""
     N, K = 12288, 4096
