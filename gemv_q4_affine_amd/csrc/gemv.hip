@@ -333,15 +333,20 @@ static GemvShape pick_shape(int64_t rows, int64_t nb, int64_t M) {
 
 // The quantising variant keeps to 3 rows per lane, 2 for two matrices (its
 // registers), and, with rows enough for two per lane on every CU, takes at
-// least two: its per-column quantisation is then shared by more rows.  Two
-// matrices that would want more take two virtual waves per physical wave.
+// least two (up to that cap): its per-column quantisation is then shared by
+// more rows.  Two matrices whose shape already wants more take two virtual
+// waves per physical wave.
 static GemvShape raw_shape(GemvShape g, int64_t rows, int64_t nb, int64_t M, bool two_mats) {
+    const int cap = two_mats ? 2 : 3;
     if (g.f == 1 && M == 1) {
+        // never past the cap: raising rows per lane only to halve the waves
+        // again (two virtual waves per wave) loses more than the shared
+        // quantisation saves
         const int64_t two = rows / (16 * (int64_t)current_cu_count());
-        const int want = (int)(two < 1 ? 1 : (two > 3 ? 3 : two));
+        int want = (int)(two < 1 ? 1 : (two > 3 ? 3 : two));
+        want = want > cap ? cap : want;
         if (g.ri < want) g.ri = want;
     }
-    const int cap = two_mats ? 2 : 3;
     if (g.ri > cap) {
         if (g.f == 1 && M == 1 && g.v % 2 == 0) g.f = 2;
         g.ri = cap;
