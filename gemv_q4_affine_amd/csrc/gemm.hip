@@ -1337,7 +1337,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void k_gemm_skinny(const GemmArgs a)
 // (byte 0, byte 2) and (byte 1, byte 3); the X fragment is permuted into the
 // same order.  A weight column of a slice takes 4 (mod 64) dwords of LDS, so
 // the 64 lanes read distinct banks.  A slice's X, weights and scales are
-// loaded together, four slices ahead, into a ring of register stages and
+// loaded together, two slices ahead, into a ring of register stages and
 // stored to LDS (double-buffered) the step before they are used: loads
 // complete in issue order, so any other split would make the earliest wait
 // for everything issued before it.  One barrier per slice.  The partial
@@ -1616,9 +1616,9 @@ __global__ __launch_bounds__(64 * kSmWaves, 1) void k_gemm_small(const GemmArgs 
     // slot into the other LDS buffers and refills the slot with slice
     // sl+1+kRing.  Phases are fenced so that no work on loaded values (and
     // so no wait) moves between them.  The slice count is padded to a
-    // multiple of kRing; in the last ring nothing is refilled.  ONE: all
-    // slices fit one ring of four, so there is no loop; with a loop the ring
-    // holds two (four would spill).
+    // multiple of kRing; in the last ring nothing is refilled.  ONE (one or
+    // two slices): all of them load at once, so there is no loop; with a
+    // loop the ring holds two (four would spill).
     constexpr int kRing = ONE ? 4 : 2;
     const int nsteps = (nslices + kRing - 1) / kRing * kRing;
     Rec ring[kRing];           // slot r holds slices r, r + kRing, ...
@@ -2147,7 +2147,11 @@ static void launch_small_t(GemmArgs ga, hipStream_t s) {
     const dim3 grid((unsigned)((ga.N + NT * 16 - 1) / (NT * 16))), block(64 * kSmWaves);
     const int slice_blk = 32 / MT;
     const int nslices = (ga.K / 32 + slice_blk - 1) / slice_blk;
-    if (nslices <= 4) hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, true>), grid, block, 0, s, ga);
+    // everything at once only for one or two slices: with more requested
+    // together, HBM returns all of a workgroup's slices late and together,
+    // and no arithmetic overlaps the loads (two slices in flight keep HBM
+    // busy: 4-6% faster at K = 4096, M = 2..16)
+    if (nslices <= 2) hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, true>), grid, block, 0, s, ga);
     else hipLaunchKernelGGL((k_gemm_small<WF, MT, NT, YDT, XP, false>), grid, block, 0, s, ga);
 }
 
