@@ -436,8 +436,8 @@ def affine_section(iters: int):
 # ---------------------------------------------------------------------------
 
 def affine8_section(iters: int):
-    """affine8_gemm (fused up to M = 32 on bf16 X, dequantise-then-GEMM above) against the
-    page's jit (dequantise to bf16 + hipBLASLt) and ref (hipBLASLt on bf16 W
+    """affine8_gemm (fused up to M = 32 on bf16 X, the matrix-core GEMM on images above; also
+    forced dequantise-then-GEMM there) against the page's jit (dequantise to bf16 + hipBLASLt) and ref (hipBLASLt on bf16 W
     dequantised once), at the sweep's M values.  At M = 1 the weights rotate
     over ten copies (535 MB) so that they stream from HBM."""
     wl = synth.AFFINE
@@ -450,6 +450,7 @@ def affine8_section(iters: int):
     qc = [(q.clone(), s.clone(), b.clone()) for _ in range(copies)]
     wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     B.affine8_dequantize(q, s, b, out_dtype=torch.bfloat16, out=wbf)
+    image = B.q4_pack_weight_image(q, s, b, fmt=B.Q4_FMT_AFFINE8)     # weights prepared once
     out = []
     for M in sorted(set(synth.AFFINE_MS) | {16}):
         X = synth.activations(rng, M, K)
@@ -460,6 +461,21 @@ def affine8_section(iters: int):
         it = max(5, min(iters, int(2000 / max(1, M // 32))))
         timer = steady_us if M >= 512 else region_us
         fused = timer(lambda i: B.affine8_gemm(*qc[i % copies], x, y=y, workspace=ws), it) * 1e-3
+        deq_path = None
+        fused_img = None
+        if M > 32:
+            wsi = torch.empty(max(B.q4_gemm_workspace_size(M, N, K, B.Q4_FMT_AFFINE8), 16), dtype=torch.uint8,
+                              device="cuda")
+            fused_img = timer(lambda i: B.q4_gemm_image(image, x, N, fmt=B.Q4_FMT_AFFINE8, y=y, workspace=wsi),
+                              it) * 1e-3
+            del wsi
+            wsd = torch.empty(N * K * 2, dtype=torch.uint8, device="cuda")
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+            try:
+                deq_path = timer(lambda i: B.affine8_gemm(*qc[i % copies], x, y=y, workspace=wsd), it) * 1e-3
+            finally:
+                B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+            del wsd
         deqbf = timer(lambda i: B.affine8_dequantize(*qc[i % copies], out_dtype=torch.bfloat16, out=wbf), it) * 1e-3
         ref = timer(lambda i: torch.matmul(x, wbf.t(), out=y), it) * 1e-3
         flop = 2.0 * M * N * K
@@ -467,8 +483,12 @@ def affine8_section(iters: int):
         t_roof = max(byts / (HBM_PEAK_GBS * 1e9), flop / (F16_MFMA_PEAK_TFLOPS * 1e12))
         rec = {
             "M": M,
-            "path": "fused vector" if M <= 4 else ("fused bf16 MFMA" if M <= 32 else "dequantise to binary16 + dense GEMM"),
+            "path": "fused vector" if M <= 4 else ("fused bf16 MFMA" if M <= 32 else
+                                                   "matrix-core GEMM on X and weight images (both built per call)"),
             "affine8_gemm_us": fused * 1e3,
+            "forced_dequant_gemm_us": deq_path * 1e3 if deq_path is not None else None,
+            "prepared_image_us": fused_img * 1e3 if fused_img is not None else None,
+            "prepared_image_beats_jit": (fused_img if fused_img is not None else fused) < deqbf + ref,
             "jit_us": (deqbf + ref) * 1e3,
             "ref_us": ref * 1e3,
             "gbs": byts / (fused * 1e-3) / 1e9,
@@ -477,7 +497,9 @@ def affine8_section(iters: int):
             "affine8_gemm_beats_jit": fused < deqbf + ref,
         }
         out.append(rec)
-        log(f"[affine8] M={M}: affine8_gemm {rec['affine8_gemm_us']:.1f} us ({rec['path']}), "
+        dq = (f", prepared image {fused_img * 1e3:.1f} us, forced dequant + dense GEMM {deq_path * 1e3:.1f} us"
+              if deq_path is not None else "")
+        log(f"[affine8] M={M}: affine8_gemm {rec['affine8_gemm_us']:.1f} us ({rec['path']}){dq}, "
             f"jit {rec['jit_us']:.1f} us, ref {rec['ref_us']:.1f} us, roofline {rec['roofline_frac']:.2f}")
     return {"sweep": out}
 

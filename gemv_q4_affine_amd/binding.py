@@ -362,10 +362,14 @@ def q4_gemm_image_workspace_size(M, K) -> int:
 
 def q4_pack_weight_image(w_q, w_s, w_b=None, fmt=None, image=None, stream=None):
     """The matrix-core GEMM's weight image of Q4_0 planes (w_q = qs [N, K/32, 16],
-    w_s = d) or affine planes (w_q [N, K/2], w_s = scales, w_b = biases)."""
-    if fmt is None:
-        fmt = Q4_FMT_AFFINE4 if w_b is not None else Q4_FMT_Q4_0
+    w_s = d) or affine planes (w_s = scales, w_b = biases; w_q [N, K/2] for
+    4-bit codes, [N, K] for 8-bit codes)."""
     N = w_s.shape[0]
+    if fmt is None:
+        if w_b is None:
+            fmt = Q4_FMT_Q4_0
+        else:
+            fmt = Q4_FMT_AFFINE8 if w_q.shape[-1] == w_s.shape[1] * 64 else Q4_FMT_AFFINE4
     K = w_s.shape[1] * (32 if fmt == Q4_FMT_Q4_0 else 64)
     if image is None:
         n = lib().q4_weight_image_size(N, K, fmt)

@@ -171,10 +171,11 @@ int q4_dispatch_path(int64_t M, int64_t N, int64_t K, int fmt, int have_workspac
     if (rc) return rc;
     const int64_t forced = g_force_path;
     if (fmt == Q4_FMT_AFFINE8) {
-        // the fused kernels (small M) or dequantise-then-GEMM; a forced path
-        // that affine8_gemm has no kernel for leaves the automatic choice
-        if (forced == Q4_PATH_SKINNY || forced == Q4_PATH_DEQUANT_GEMM) return (int)forced;
-        return M <= g_affine8_fused_max_m ? Q4_PATH_SKINNY : Q4_PATH_DEQUANT_GEMM;
+        // the fused kernels (small M) or the matrix-core GEMM on images;
+        // dequantise-then-GEMM only when forced; a forced path that
+        // affine8_gemm has no kernel for leaves the automatic choice
+        if (forced == Q4_PATH_SKINNY || forced == Q4_PATH_MFMA || forced == Q4_PATH_DEQUANT_GEMM) return (int)forced;
+        return M <= g_affine8_fused_max_m ? Q4_PATH_SKINNY : Q4_PATH_MFMA;
     }
     if (forced >= 0) return (int)forced;
     if (M <= g_skinny_max_m) return Q4_PATH_SKINNY;
@@ -183,6 +184,7 @@ int q4_dispatch_path(int64_t M, int64_t N, int64_t K, int fmt, int have_workspac
 }
 
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt) {
+    if (fmt == Q4_FMT_AFFINE8) return affine8_gemm_workspace_size(M, N, K);
     const int path = q4_dispatch_path(M, N, K, fmt, 1);
     if (path == Q4_PATH_MFMA) return q4::packed_x_bytes(M, N, K);
     if (path == Q4_PATH_DEQUANT_GEMM) return N * K * 2;
@@ -443,13 +445,17 @@ int q4_gemm_q8(const uint8_t* w_qs, const uint16_t* w_d, const int8_t* x_qs, con
 }
 
 static int image_dims(int fmt, int64_t M, int64_t N, int64_t K) {
-    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE4) return Q4_ERR_ARG;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE4 && fmt != Q4_FMT_AFFINE8) return Q4_ERR_ARG;
     return check_dims(M, N, K, fmt == Q4_FMT_Q4_0 ? 32 : 64);
+}
+
+static int image_wf(int fmt) {
+    return fmt == Q4_FMT_Q4_0 ? q4::WF_Q4_0 : fmt == Q4_FMT_AFFINE4 ? q4::WF_AFFINE4 : q4::WF_AFFINE8;
 }
 
 int64_t q4_weight_image_size(int64_t N, int64_t K, int fmt) {
     if (image_dims(fmt, 0, N, K) != Q4_OK) return 0;
-    return q4::weight_image_bytes(N, K);
+    return fmt == Q4_FMT_AFFINE8 ? q4::weight_image8_bytes(N, K) : q4::weight_image_bytes(N, K);
 }
 
 int q4_pack_weight_image(int fmt, const uint8_t* w_q, const uint16_t* w_s, const uint16_t* w_b, int64_t N,
@@ -458,10 +464,9 @@ int q4_pack_weight_image(int fmt, const uint8_t* w_q, const uint16_t* w_s, const
     if (rc) return rc;
     if (N == 0) return Q4_OK;
     if ((rc = check_ptrs_aligned({w_q, w_s, image}))) return rc;
-    if (fmt == Q4_FMT_AFFINE4 && (rc = check_ptrs_aligned({w_b}))) return rc;
-    const int wf = fmt == Q4_FMT_Q4_0 ? q4::WF_Q4_0 : q4::WF_AFFINE4;
-    return hip_status(q4::launch_pack_weight_image(wf, w_q, w_s, fmt == Q4_FMT_Q4_0 ? nullptr : w_b, N, K, image,
-                                                   as_stream(stream)));
+    if (fmt != Q4_FMT_Q4_0 && (rc = check_ptrs_aligned({w_b}))) return rc;
+    return hip_status(q4::launch_pack_weight_image(image_wf(fmt), w_q, w_s, fmt == Q4_FMT_Q4_0 ? nullptr : w_b, N, K,
+                                                   image, as_stream(stream)));
 }
 
 int64_t q4_gemm_image_workspace_size(int64_t M, int64_t K) {
@@ -479,12 +484,11 @@ int q4_gemm_image(int fmt, const void* image, const void* x, int x_dtype, void* 
     const int64_t ximg = q4::x_image_bytes(M, K);
     if (workspace == nullptr || workspace_bytes < ximg) return Q4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q4_ERR_ALIGN;
-    const int wf = fmt == Q4_FMT_Q4_0 ? q4::WF_Q4_0 : q4::WF_AFFINE4;
     // room for the split-K partial results after the X image: split small tile counts
     const int64_t part = q4::splitk_bytes(M, N, K);
     float* pp = (part > 0 && workspace_bytes >= ximg + part)
                     ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ximg) : nullptr;
-    return hip_status(q4::launch_gemm_image(wf, image, x, x_dtype, y, y_dtype, M, N, K, workspace, pp,
+    return hip_status(q4::launch_gemm_image(image_wf(fmt), image, x, x_dtype, y, y_dtype, M, N, K, workspace, pp,
                                             as_stream(stream)));
 }
 
@@ -529,10 +533,13 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
 
 int64_t affine8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (check_dims(M, N, K, 64) != Q4_OK) return 0;
-    // the fused kernels use none; enough for either activation type (f32 X
-    // above 16 rows and bf16 X above 32 dequantise)
+    // the fused kernels use none; dequantise-then-GEMM the binary16 weights;
+    // the matrix-core GEMM its two images and split-K partials.  Enough for
+    // either activation type (f32 X above 16 rows leaves the fused kernels).
     const int path = q4_dispatch_path(M, N, K, Q4_FMT_AFFINE8, 1);
-    return (path == Q4_PATH_SKINNY && M <= q4::kAffine8GemvMaxM) ? 0 : N * K * 2;
+    if (path == Q4_PATH_SKINNY && M <= q4::kAffine8GemvMaxM) return 0;
+    if (path == Q4_PATH_DEQUANT_GEMM) return N * K * 2;
+    return q4::affine8_packed_bytes(M, N, K);
 }
 
 int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* biases, int64_t group_size,
@@ -545,20 +552,29 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
     if (M == 0 || N == 0) return Q4_OK;
     if ((rc = check_ptrs_aligned({w_q, scales, biases, x, y}))) return rc;
     hipStream_t s = as_stream(stream);
-    const bool have_ws = workspace != nullptr && workspace_bytes >= N * K * 2;
-    const int path = q4_dispatch_path(M, N, K, Q4_FMT_AFFINE8, have_ws ? 1 : 0);
+    const int path = q4_dispatch_path(M, N, K, Q4_FMT_AFFINE8, workspace != nullptr ? 1 : 0);
     if (path < 0) return path;
     if (path == Q4_PATH_SKINNY) {
         // M <= 4: the fused vector kernel; bf16 X up to 32 rows: the bf16-MFMA
         // kernel on the raw codes; f32 X up to 16 rows: the vector kernel;
-        // f32 X above that goes on to dequantise-then-GEMM
+        // f32 X above that goes on to the matrix-core GEMM
         if (M <= 4 || (x_dtype == Q4_F32 && M <= q4::kAffine8GemvMaxM))
             return hip_status(q4::launch_affine8_gemv(w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K, s));
         if (x_dtype == Q4_BF16 && M <= q4::kAffine8MmaMaxM)
             return hip_status(q4::launch_affine8_mma(w_q, scales, biases, x, y, y_dtype, M, N, K, s));
     }
+    if (path != Q4_PATH_DEQUANT_GEMM) {
+        // the weight and X images in the workspace (with room for them, the
+        // split-K partials too), then the matrix-core GEMM
+        if (workspace == nullptr || workspace_bytes < q4::x_image_bytes(M, K) + q4::weight_image8_bytes(N, K))
+            return Q4_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return Q4_ERR_ALIGN;
+        const bool split = workspace_bytes >= q4::affine8_packed_bytes(M, N, K);
+        return hip_status(q4::launch_affine8_gemm_packed(w_q, scales, biases, x, x_dtype, y, y_dtype, M, N, K,
+                                                         workspace, split, s));
+    }
     // dequantise to binary16 in the workspace, then the dense GEMM
-    if (!have_ws) return Q4_ERR_WORKSPACE;
+    if (workspace == nullptr || workspace_bytes < N * K * 2) return Q4_ERR_WORKSPACE;
     if (!aligned16(workspace)) return Q4_ERR_ALIGN;
     if (q4::launch_affine8_dequantize(w_q, scales, biases, N, K, workspace, q4::DT_F16, s) != hipSuccess)
         return Q4_ERR_HIP;

@@ -541,8 +541,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 // output straight from the accumulators (pairs of columns per store) and
 // go on with the next tile, whose first steps are already in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kPkSlots = 6;              // ring depth: steps k..k+5 resident
-constexpr int kPkAhead = kPkSlots - 1;   // producers request step k+5 during step k
+// Ring depth: steps k..k+5 resident (k..k+3 for the 17 KiB affine 8-bit
+// chunks, which keeps the ring within LDS); producers request step
+// k + depth - 1 during step k.
+template <int WF> constexpr int pk_slots() { return WF == WF_AFFINE8 ? 4 : 6; }
 constexpr int kPkProducers = 4;          // producer waves, one per SIMD
 // X -> image (see above), one workgroup of 256 threads per image row.  The
 // workgroup first finds the row's largest |x|.  A row whose largest lies in
@@ -628,12 +630,13 @@ __global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint
                     }
                 }
                 // position p of the chunk holds k = perm[p]
-                constexpr int kPermQ[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-                constexpr int kPermA[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+                // (Q4_0, affine 4-bit, affine 8-bit: element order)
+                constexpr int kPerm[3][8] = {{0, 2, 1, 3, 4, 6, 5, 7}, {0, 4, 1, 5, 2, 6, 3, 7}, {0, 1, 2, 3, 4, 5, 6, 7}};
+                constexpr int kP = WF == WF_Q4_0 ? 0 : WF == WF_AFFINE4 ? 1 : 2;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int p0 = (WF == WF_Q4_0) ? kPermQ[2 * i] : kPermA[2 * i];
-                    const int p1 = (WF == WF_Q4_0) ? kPermQ[2 * i + 1] : kPermA[2 * i + 1];
+                    const int p0 = kPerm[kP][2 * i];
+                    const int p1 = kPerm[kP][2 * i + 1];
                     o[i] = f32_to_f16(ldexpf(f[p0], e)) | (f32_to_f16(ldexpf(f[p1], e)) << 16);
                 }
             }
@@ -736,23 +739,76 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ wq, 
     }
 }
 
-// One ring slot: the X tile (16 KiB) and the weight chunk (9 KiB) of a step.
+// Affine 8-bit codes [N][K] with group-64 scales and biases [N][K/64] ->
+// image, one workgroup per (256-column tile, 2 K steps).  Loads go row by
+// row (8 lanes read a row's 128 contiguous code bytes, two groups) into an
+// LDS tile swizzled by row; stores go plane by plane (each thread writes one
+// column's 16 bytes), so both sides are coalesced.  Columns past N get zero
+// codes, scales and biases.
+__global__ __launch_bounds__(256) void k_pack_w8(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsc,
+                                                 const uint16_t* __restrict__ wbias, uint8_t* __restrict__ img, int N,
+                                                 int K, int ksteps) {
+    __shared__ u32x4_t lq[256 * 8];            // [column][8 chunks], chunk slot c ^ (column & 7)
+    const int tid = threadIdx.x;
+    const int kq = (ksteps + 1) / 2;
+    const int grp = blockIdx.x % kq;
+    const int nt = blockIdx.x / kq;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int u = tid + 256 * i;
+        const int row = u >> 3, c = u & 7;     // 16-byte chunk c of the row's 128 bytes
+        const int n = nt * 256 + row;
+        const int64_t kb = (int64_t)grp * 128 + c * 16;
+        u32x4_t q = {0u, 0u, 0u, 0u};
+        if (n < N && kb < K) q = *reinterpret_cast<const u32x4_t*>(wq + (int64_t)n * K + kb);
+        lq[row * 8 + (c ^ (row & 7))] = q;
+    }
+    const int n = nt * 256 + tid;
+    const int ngr = K / 64;
+    uint16_t sc[2] = {0, 0}, bi[2] = {0, 0};
+#pragma unroll
+    for (int st = 0; st < 2; st++)
+        if (n < N && grp * 2 + st < ngr) {
+            sc[st] = wsc[(int64_t)n * ngr + grp * 2 + st];
+            bi[st] = wbias[(int64_t)n * ngr + grp * 2 + st];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 2; st++) {
+        const int k = grp * 2 + st;
+        if (k >= ksteps) break;
+        uint8_t* chunk = img + ((int64_t)nt * ksteps + k) * kWChunk8;
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const int c = 4 * st + p;          // elements 16p .. 16p+15 of group k
+            *reinterpret_cast<u32x4_t*>(chunk + (p * 256 + tid) * 16) = lq[tid * 8 + (c ^ (tid & 7))];
+        }
+        reinterpret_cast<uint16_t*>(chunk + 16384)[tid] = sc[st];
+        reinterpret_cast<uint16_t*>(chunk + 16896)[tid] = bi[st];
+    }
+}
+
+// One ring slot: the X tile (16 KiB) and the weight chunk (9 KiB; affine
+// 8-bit 17 KiB) of a step.
+template <int WF>
 struct PkSlot {
     uint16_t x[kImgTile];
-    uint8_t w[kWChunk];
+    uint8_t w[w_chunk_bytes<WF>()];
 };
+template <int WF>
 struct PkLds {
-    PkSlot slot[kPkSlots];
+    PkSlot<WF> slot[pk_slots<WF>()];
 };
 
 template <int WF, int YDT, bool SPLIT>
 __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const GemmArgs a) {
-    static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4, "quantised weights only");
+    static_assert(WF == WF_Q4_0 || WF == WF_AFFINE4 || WF == WF_AFFINE8, "quantised weights only");
     constexpr int MT = 4, NT = 2;
     constexpr int kCols = 4 * NT * 32;
     constexpr int kRows = MT * 32;
     static_assert(kRows == kImgRows && kCols == 256, "tile shape");
-    __shared__ __attribute__((aligned(16))) PkLds lds;
+    constexpr int kSlots = pk_slots<WF>();
+    __shared__ __attribute__((aligned(16))) PkLds<WF> lds;
     using Blk = typename BlkOf<WF>::T;
 
     const int tid = threadIdx.x;
@@ -791,18 +847,25 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
 #pragma unroll
                 for (int v = 0; v < 16; v++) acc[mi][ni][v] = 0.0f;
         u32x4_t bfA[NT][4], bfB[NT][4];
-        const NibMasks masks = NibMasks::make();
+        using Consts = typename DequantConsts<WF>::T;
+        const Consts masks = Consts::make();
 
         // raw weight blocks of step k from its ring slot
         auto read_w = [&](int k, Blk (&r)[NT]) {
-            const uint8_t* wb = lds.slot[k % kPkSlots].w;
+            const uint8_t* wb = lds.slot[k % kSlots].w;
 #pragma unroll
             for (int ni = 0; ni < NT; ni++) {
                 const int cw = wave * NT * 32 + ni * 32 + j;
-                r[ni].q = *reinterpret_cast<const u32x4_t*>(wb + (g * 256 + cw) * 16);
-                if constexpr (WF == WF_Q4_0) {
+                if constexpr (WF == WF_AFFINE8) {
+                    r[ni].q[0] = *reinterpret_cast<const u32x4_t*>(wb + ((2 * g) * 256 + cw) * 16);
+                    r[ni].q[1] = *reinterpret_cast<const u32x4_t*>(wb + ((2 * g + 1) * 256 + cw) * 16);
+                    r[ni].s = reinterpret_cast<const uint16_t*>(wb + 16384)[cw];
+                    r[ni].b = reinterpret_cast<const uint16_t*>(wb + 16896)[cw];
+                } else if constexpr (WF == WF_Q4_0) {
+                    r[ni].q = *reinterpret_cast<const u32x4_t*>(wb + (g * 256 + cw) * 16);
                     r[ni].d = reinterpret_cast<const uint16_t*>(wb + 8192)[g * 256 + cw];
                 } else {
+                    r[ni].q = *reinterpret_cast<const u32x4_t*>(wb + (g * 256 + cw) * 16);
                     r[ni].s = reinterpret_cast<const uint16_t*>(wb + 8192)[cw];
                     r[ni].b = reinterpret_cast<const uint16_t*>(wb + 8704)[cw];
                 }
@@ -824,7 +887,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
 #pragma unroll
         for (int s = 0; s < 4; s++) aofs[s] = j * 64 + (((4 * g + s) ^ img_swz(j)) * 8);   // rows mi*32 + j
         auto read_a = [&](int k, int s, u32x4_t (&av)[MT]) {
-            const uint16_t* la = lds.slot[k % kPkSlots].x;
+            const uint16_t* la = lds.slot[k % kSlots].x;
 #pragma unroll
             for (int mi = 0; mi < MT; mi++)
                 av[mi] = *reinterpret_cast<const u32x4_t*>(&la[mi * 32 * 64 + aofs[s]]);
@@ -856,7 +919,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
             }
             __builtin_amdgcn_sched_barrier(0);
         };
-        constexpr int kWReads = NT * (WF == WF_Q4_0 ? 2 : 3);
+        constexpr int kWReads = NT * (WF == WF_Q4_0 ? 2 : WF == WF_AFFINE4 ? 3 : 4);
         // One K step in four segments (K slices s = 0..3) fenced by
         // sched_barrier, so that every LDS read is issued one segment ahead of
         // its use: the slice s+1 X fragments during slice s, the next step's
@@ -879,25 +942,25 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
             read_a(k, 2, a2);
             mfma_slice(1, a1, cur, false);
             const BlkConst c0 = blk_const<WF>(r[0]);
-            blk_word<WF>(r[0], c0, 0, masks, nxt[0]);
-            blk_word<WF>(r[0], c0, 1, masks, nxt[0]);
-            blk_word<WF>(r[0], c0, 2, masks, nxt[0]);
+            blk_fragment<WF>(r[0], c0, 0, masks, nxt[0]);
+            blk_fragment<WF>(r[0], c0, 1, masks, nxt[0]);
+            blk_fragment<WF>(r[0], c0, 2, masks, nxt[0]);
             segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 7>{});
 
             mfma_slice(2, a2, cur, true);
             read_a(k, 3, a3);
             mfma_slice(2, a2, cur, false);
             const BlkConst c1 = blk_const<WF>(r[1]);
-            blk_word<WF>(r[0], c0, 3, masks, nxt[0]);
-            blk_word<WF>(r[1], c1, 0, masks, nxt[1]);
-            blk_word<WF>(r[1], c1, 1, masks, nxt[1]);
+            blk_fragment<WF>(r[0], c0, 3, masks, nxt[0]);
+            blk_fragment<WF>(r[1], c1, 0, masks, nxt[1]);
+            blk_fragment<WF>(r[1], c1, 1, masks, nxt[1]);
             segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 7>{});
 
             mfma_slice(3, a3, cur, true);
             read_a(k + 1, 0, a0);
             mfma_slice(3, a3, cur, false);
-            blk_word<WF>(r[1], c1, 2, masks, nxt[1]);
-            blk_word<WF>(r[1], c1, 3, masks, nxt[1]);
+            blk_fragment<WF>(r[1], c1, 2, masks, nxt[1]);
+            blk_fragment<WF>(r[1], c1, 3, masks, nxt[1]);
             segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 5>{});
             // the fragments must be complete here: without this the compiler
             // may sink their dequantisation past the barrier into the next step
@@ -1030,19 +1093,21 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
         // (1 KiB copies), of the weight blocks (32 columns x 2 blocks per copy)
         // and of the scales.
         const int pw = wave - 4;
-        // per step 25 copies of 1 KiB (16 of X, 9 of weights); wave pw takes
-        // copies pw, pw + 4, ...: 7 for wave 0, 6 for the others
-        constexpr int kCopies = 16 + kWChunk / 1024;
+        // per step 25 copies of 1 KiB (16 of X, 9 of weights; affine 8-bit 33:
+        // 17 of weights); wave pw takes copies pw, pw + 4, ...
+        constexpr int kWBytes = w_chunk_bytes<WF>();
+        constexpr int kCopies = 16 + kWBytes / 1024;
+        static_assert(kWBytes % 1024 == 0, "whole 1 KiB copies");
         const int my_copies = (kCopies - pw + kPkProducers - 1) / kPkProducers;
         // the next step to request: global index rs = ri * ust + rk
         int rs = 0, ri = 0, rk = 0;
         auto copy_next = [&]() {
-            PkSlot& sl = lds.slot[rs % kPkSlots];
+            PkSlot<WF>& sl = lds.slot[rs % kSlots];
             const int mt_idx = tile_m0(ri) / kRows;
             const int nt_idx = tile_n0(ri) / kCols;
             const int kg = part_of(ri) * ust + rk;      // K step within the tile
             const uint8_t* xs = reinterpret_cast<const uint8_t*>(a.x) + ((int64_t)mt_idx * nsteps + kg) * (kImgTile * 2);
-            const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)nt_idx * nsteps + kg) * kWChunk;
+            const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(a.a) + ((int64_t)nt_idx * nsteps + kg) * kWBytes;
 #pragma unroll
             for (int i = 0; i < (kCopies + kPkProducers - 1) / kPkProducers; i++) {
                 const int c = pw + kPkProducers * i;
@@ -1055,20 +1120,23 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                 ri++;
             }
         };
-        // prologue: steps 0..4 requested, steps 0 and 1 landed.  Steps k+3..k+5
-        // may stay in flight: 3 steps of this wave's copies.
-        static_assert(kCopies == 25 && kPkProducers == 4 && kPkAhead == 5, "wait counts below");
+        // prologue: steps 0 .. kAhead-1 requested, steps 0 and 1 landed.
+        // Steps k+3 .. k+kAhead may stay in flight: kAhead - 2 steps of this
+        // wave's copies (3 steps of 7 or 6; affine 8-bit 1 step of 9 or 8).
+        constexpr int kAhead = kSlots - 1;
+        constexpr int kMaxC = (kCopies + kPkProducers - 1) / kPkProducers, kMinC = kCopies / kPkProducers;
+        static_assert(kAhead >= 3 && (kAhead - 2) * kMaxC < 64, "wait counts below");
         auto wait_step = [&]() {
-            if (my_copies == 7) step_barrier<3 * 7>();
-            else step_barrier<3 * 6>();
+            if (my_copies == kMaxC) step_barrier<(kAhead - 2) * kMaxC>();
+            else step_barrier<(kAhead - 2) * kMinC>();
         };
-        for (int i = 0; i < kPkAhead; i++)
+        for (int i = 0; i < kAhead; i++)
             if (i < S) copy_next();
-        if (S >= kPkAhead) wait_step();
+        if (S >= kAhead) wait_step();
         else step_barrier<0>();
-        // during step k: request step k+5, then make sure step k+2 has landed
+        // during step k: request step k+kAhead, then make sure step k+2 has landed
         for (int k = 0; k < S; k++) {
-            if (k + kPkAhead < S) {
+            if (k + kAhead < S) {
                 copy_next();
                 wait_step();
             } else {
@@ -1816,12 +1884,14 @@ template <int WF>
 static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, float* part, hipStream_t s) {
     ga.m_tiles = (ga.M + kImgRows - 1) / kImgRows;
     ga.n_tiles = (ga.N + 255) / 256;
-    if (use_big_tiles(ga.M, ga.N, ga.K)) {
-        // 256 x 256 tiles (at least one per CU): no K split, no partials
-        if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
-        else launch_pack_t<WF, DT_F32>(ga, ximg, s);
-        launch_gemm_big(WF, ga.a, ximg, ga.y, ydt, ga.M, ga.N, ga.K, s);
-        return;
+    if constexpr (WF != WF_AFFINE8) {
+        if (use_big_tiles(ga.M, ga.N, ga.K)) {
+            // 256 x 256 tiles (at least one per CU): no K split, no partials
+            if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
+            else launch_pack_t<WF, DT_F32>(ga, ximg, s);
+            launch_gemm_big(WF, ga.a, ximg, ga.y, ydt, ga.M, ga.N, ga.K, s);
+            return;
+        }
     }
     if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
     else launch_pack_t<WF, DT_F32>(ga, ximg, s);
@@ -1849,9 +1919,20 @@ static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, floa
 
 hipError_t launch_pack_weight_image(int wfmt, const void* a, const void* b, const void* c, int64_t N, int64_t K,
                                     void* wimg, hipStream_t s) {
-    if (wfmt == WF_Q4_0) launch_pack_w_t<WF_Q4_0>(a, b, c, (int)N, (int)K, static_cast<uint8_t*>(wimg), s);
-    else if (wfmt == WF_AFFINE4) launch_pack_w_t<WF_AFFINE4>(a, b, c, (int)N, (int)K, static_cast<uint8_t*>(wimg), s);
-    else return hipErrorInvalidValue;
+    if (wfmt == WF_Q4_0) {
+        launch_pack_w_t<WF_Q4_0>(a, b, c, (int)N, (int)K, static_cast<uint8_t*>(wimg), s);
+    } else if (wfmt == WF_AFFINE4) {
+        launch_pack_w_t<WF_AFFINE4>(a, b, c, (int)N, (int)K, static_cast<uint8_t*>(wimg), s);
+    } else if (wfmt == WF_AFFINE8) {
+        if (K % 64 != 0) return hipErrorInvalidValue;
+        const int ksteps = (int)(K / 64);
+        const int n_tiles = (int)((N + 255) / 256);
+        hipLaunchKernelGGL(k_pack_w8, dim3((unsigned)(n_tiles * ((ksteps + 1) / 2))), dim3(256), 0, s,
+                           static_cast<const uint8_t*>(a), static_cast<const uint16_t*>(b),
+                           static_cast<const uint16_t*>(c), static_cast<uint8_t*>(wimg), (int)N, (int)K, ksteps);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -1862,8 +1943,29 @@ hipError_t launch_gemm_image(int wfmt, const void* wimg, const void* x, int xdt,
     ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
     if (wfmt == WF_Q4_0) launch_on_images<WF_Q4_0>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), part, s);
     else if (wfmt == WF_AFFINE4) launch_on_images<WF_AFFINE4>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), part, s);
+    else if (wfmt == WF_AFFINE8) launch_on_images<WF_AFFINE8>(ga, xdt, ydt, static_cast<uint16_t*>(ximg), part, s);
     else return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+// Affine 8-bit on the same kernel: the weight image (17 KiB chunks), then
+// the X image (element order) and the GEMM; one workspace as below.
+int64_t weight_image8_bytes(int64_t N, int64_t K) { return (N + 255) / 256 * ((K + 63) / 64) * (int64_t)kWChunk8; }
+
+int64_t affine8_packed_bytes(int64_t M, int64_t N, int64_t K) {
+    const int d = splitk_parts(M, N, K);
+    return x_image_bytes(M, K) + weight_image8_bytes(N, K) + (d > 1 ? (int64_t)d * M * N * 4 : 0);
+}
+
+hipError_t launch_affine8_gemm_packed(const uint8_t* wq, const uint16_t* scales, const uint16_t* biases, const void* x,
+                                      int xdt, void* y, int ydt, int64_t M, int64_t N, int64_t K, void* img, bool split,
+                                      hipStream_t s) {
+    uint8_t* wimg = static_cast<uint8_t*>(img) + x_image_bytes(M, K);
+    float* part = reinterpret_cast<float*>(wimg + weight_image8_bytes(N, K));
+    hipError_t e = launch_pack_weight_image(WF_AFFINE8, wq, scales, biases, N, K, wimg, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_image(WF_AFFINE8, wimg, x, xdt, y, ydt, M, N, K, img,
+                             split && splitk_parts(M, N, K) > 1 ? part : nullptr, s);
 }
 
 // One workspace: the X image, the weight image, then (with `split`) the

@@ -36,18 +36,21 @@ struct GemmArgs {
 struct BlkQ4 { u32x4_t q; uint32_t d; };
 struct BlkAff { u32x4_t q; uint32_t s, b; };
 struct BlkF16 { u32x4_t h[4]; };
+// affine 8-bit: one lane's 32 codes (half a group), bytes 0..15 and 16..31
+struct BlkAff8 { u32x4_t q[2]; uint32_t s, b; };
 
 template <int WF> struct BlkOf;
 template <> struct BlkOf<WF_Q4_0> { using T = BlkQ4; };
 template <> struct BlkOf<WF_AFFINE4> { using T = BlkAff; };
 template <> struct BlkOf<WF_DENSE16> { using T = BlkF16; };
+template <> struct BlkOf<WF_AFFINE8> { using T = BlkAff8; };
 
 // A block past the end of K (K = 32 mod 64) contributes zeros.
 template <int WF>
 __device__ __forceinline__ void zero_blk(typename BlkOf<WF>::T& r, bool keep) {
     if constexpr (WF == WF_Q4_0) {
         r.d = keep ? r.d : 0u;
-    } else if constexpr (WF == WF_AFFINE4) {
+    } else if constexpr (WF == WF_AFFINE4 || WF == WF_AFFINE8) {
         r.s = keep ? r.s : 0u;
         r.b = keep ? r.b : 0u;
     } else {
@@ -151,7 +154,7 @@ __device__ __forceinline__ BlkConst blk_const(const typename BlkOf<WF>::T& r) {
         const half2_t dd = as_h2(__builtin_amdgcn_perm(r.d, r.d, 0x01000100u));
         return {dd, dd};
     } else {
-        static_assert(WF == WF_AFFINE4, "quantised formats only");
+        static_assert(WF == WF_AFFINE4 || WF == WF_AFFINE8, "quantised formats only");
         const uint32_t s16 = f16b(bf16_to_f32(r.s));
         const uint32_t b16 = f16b(bf16_to_f32(r.b));
         return {as_h2(s16 | (s16 << 16)), as_h2(b16 | (b16 << 16))};
@@ -186,11 +189,52 @@ __device__ __forceinline__ void blk_word(const typename BlkOf<WF>::T& r, const B
     }
 }
 
-template <int WF>
-__device__ __forceinline__ void blk_frags_perm(const typename BlkOf<WF>::T& r, const NibMasks& m, u32x4_t (&out)[4]) {
+// The affine 8-bit dequantiser.  A code byte q placed under the high byte
+// 0x64 reads as the binary16 1024+q (unit 1), so one v_perm_b32 makes two
+// weights' 1024+q from a 32-bit word of codes and the constant 0x64646464;
+// a packed subtract (exact) and a packed fma with the group's scale and bias
+// (one rounding) finish them: 12 instructions per 8 weights, in element
+// order (the X tile keeps its natural order).  The constant and the two
+// byte selectors live in VGPRs (made opaque once per kernel).
+struct Perm8 {
+    uint32_t hi, sel01, sel23;
+    __device__ __forceinline__ static Perm8 make() {
+        Perm8 p{0x64646464u, 0x04010400u, 0x04030402u};
+        asm volatile("" : "+v"(p.hi), "+v"(p.sel01), "+v"(p.sel23));
+        return p;
+    }
+};
+// Fragment f (elements 8f..8f+7 of the lane's 32 codes) into out[f].
+__device__ __forceinline__ void blk_word(const BlkAff8& r, const BlkConst& c, int f, const Perm8& p,
+                                         u32x4_t (&out)[4]) {
+    const half2_t base = as_h2(0xE400E400u);   // -1024
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const uint32_t word = r.q[f >> 1][2 * (f & 1) + h];
+        const half2_t v01 = as_h2(__builtin_amdgcn_perm(p.hi, word, p.sel01)) + base;
+        const half2_t v23 = as_h2(__builtin_amdgcn_perm(p.hi, word, p.sel23)) + base;
+        out[f][2 * h] = h2_bits(__builtin_elementwise_fma(v01, c.c0, c.c1));
+        out[f][2 * h + 1] = h2_bits(__builtin_elementwise_fma(v23, c.c0, c.c1));
+    }
+}
+
+// Fragment w of a block: the nibble dequantiser (NibMasks) or the 8-bit one
+// (Perm8).
+template <int WF, class MK>
+__device__ __forceinline__ void blk_fragment(const typename BlkOf<WF>::T& r, const BlkConst& c, int w, const MK& m,
+                                             u32x4_t (&out)[4]) {
+    if constexpr (WF == WF_AFFINE8) blk_word(r, c, w, m, out);
+    else blk_word<WF>(r, c, w, m, out);
+}
+// The constants each dequantiser keeps in VGPRs.
+template <int WF> struct DequantConsts { using T = NibMasks; };
+template <> struct DequantConsts<WF_AFFINE8> { using T = Perm8; };
+
+template <int WF, class MK>
+__device__ __forceinline__ void blk_frags_perm(const typename BlkOf<WF>::T& r, const MK& m, u32x4_t (&out)[4]) {
     const BlkConst c = blk_const<WF>(r);
 #pragma unroll
-    for (int w = 0; w < 4; w++) blk_word<WF>(r, c, w, m, out);
+    for (int w = 0; w < 4; w++) blk_fragment<WF>(r, c, w, m, out);
 }
 
 
@@ -204,5 +248,15 @@ __device__ __forceinline__ void blk_frags_perm(const typename BlkOf<WF>::T& r, c
 // consecutive LDS units (no bank conflicts), and a chunk travels as nine
 // contiguous 1 KiB direct-to-LDS copies.
 constexpr int kWChunk = 9216;
+
+// Affine 8-bit weight image, the same tiling with a 17 KiB chunk:
+//   bytes     0..16383  codes, plane major: [plane 0..3][col 0..255][16 B],
+//                       plane 2g + h holding elements 32g + 16h .. +15 of the
+//                       column's 64-code group
+//   bytes 16384..17407  s as bfloat16 [col 0..255], then b [col 0..255]
+// A lane that dequantises elements 32g .. 32g+31 of a column reads planes 2g
+// and 2g+1: two conflict-free 16-byte reads.
+constexpr int kWChunk8 = 17408;
+template <int WF> constexpr int w_chunk_bytes() { return WF == WF_AFFINE8 ? kWChunk8 : kWChunk; }
 
 }  // namespace q4

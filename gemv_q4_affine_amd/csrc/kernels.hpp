@@ -58,7 +58,7 @@ hipError_t launch_q4_gemv_multi(int nmat, const uint8_t* const* qs, const uint16
 
 // GEMM paths.  fmt: 0 = Q4_0 planes (a = qs, b = d), 1 = affine (a = q,
 // b = scales, c = biases), 2 = dense binary16 W (a = w).
-enum : int { WF_Q4_0 = 0, WF_AFFINE4 = 1, WF_DENSE16 = 2 };
+enum : int { WF_Q4_0 = 0, WF_AFFINE4 = 1, WF_DENSE16 = 2, WF_AFFINE8 = 3 };
 
 hipError_t launch_gemm_mfma(int wfmt, const void* a, const void* b, const void* c,
                             const void* x, int xdt, void* y, int ydt,
@@ -86,6 +86,16 @@ hipError_t launch_pack_weight_image(int wfmt, const void* a, const void* b, cons
                                     void* wimg, hipStream_t s);
 hipError_t launch_gemm_image(int wfmt, const void* wimg, const void* x, int xdt, void* y, int ydt, int64_t M,
                              int64_t N, int64_t K, void* ximg, float* part, hipStream_t s);
+// Affine 8-bit weights (codes [N][K], group-64 bf16 scales and biases) on
+// the same matrix-core GEMM: the weight image (weight_image8_bytes(N, K)) and
+// the X image in `img`, which holds affine8_packed_bytes(M, N, K) bytes with
+// the split-K partial results (`split`), or x_image_bytes(M, K) +
+// weight_image8_bytes(N, K) without them.  K % 64 == 0.
+int64_t weight_image8_bytes(int64_t N, int64_t K);
+int64_t affine8_packed_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_affine8_gemm_packed(const uint8_t* wq, const uint16_t* scales, const uint16_t* biases, const void* x,
+                                      int xdt, void* y, int ydt, int64_t M, int64_t N, int64_t K, void* img, bool split,
+                                      hipStream_t s);
 // The 256 x 256-tile matrix-core GEMM (gemm_big.hip) on the X and weight
 // images, for launches with at least one such tile per CU
 // (gemm_big_applies); use_big_tiles adds the dispatch setting

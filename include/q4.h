@@ -79,7 +79,8 @@ extern "C" {
 /* ---- formats and dispatch paths ------------------------------------------- */
 #define Q4_FMT_Q4_0     0
 #define Q4_FMT_AFFINE4  1
-#define Q4_FMT_AFFINE8  2  /* q4_dispatch_path only: the paths of affine8_gemm */
+#define Q4_FMT_AFFINE8  2  /* the paths and workspace of affine8_gemm, and the
+                              weight-image calls */
 
 #define Q4_PATH_GEMV          0  /* integer-dot GEMV on Q8_1 activations (q4_gemv)     */
 #define Q4_PATH_SKINNY        1  /* fused, weights streamed once, small M              */
@@ -98,8 +99,8 @@ extern "C" {
 #define Q4_KEY_TILE_ROWS       3  /* MFMA path: 128 = 128x256 output tiles (default),
                                      256 = 256x256 tiles where every CU gets at least one */
 #define Q4_KEY_AFFINE8_FUSED_MAX_M 4 /* affine8_gemm: M <= this (0..32) -> the fused
-                                     kernels (SKINNY), above -> DEQUANT_GEMM; f32 X
-                                     above 16 rows always takes DEQUANT_GEMM          */
+                                     kernels (SKINNY), above -> MFMA; f32 X above
+                                     16 rows always takes MFMA                        */
 
 /* Largest M that q4_gemv / q4_gemv_fused2 accept. */
 #define Q4_GEMV_MAX_M 16
@@ -347,7 +348,7 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
  * (quantized_matmul with transpose=True, bits=8, group_size=64).
  * Paths (q4_dispatch_path with Q4_FMT_AFFINE8): SKINNY up to
  * Q4_KEY_AFFINE8_FUSED_MAX_M rows (default 32: the fused kernels below),
- * DEQUANT_GEMM above it; Q4_KEY_FORCE_PATH = SKINNY or DEQUANT_GEMM forces
+ * MFMA above it; Q4_KEY_FORCE_PATH = SKINNY, MFMA or DEQUANT_GEMM forces
  * one of them, other forced values leave the automatic choice.  On SKINNY:
  *   M <= 4 (and M <= 16 on a Q4_F32 activation): one fused launch, no
  *     workspace: each weight is dequantised once in binary32 (q*s + b, one
@@ -356,11 +357,19 @@ int affine8_dequantize(const uint8_t* w_q, const uint16_t* scales, const uint16_
  *     the bf16 matrix cores multiply X with the raw codes (exact in
  *     bfloat16) per 64-weight group, and s and b scale the group's sums in
  *     binary32.  Both fused kernels sum in an order that depends on K only.
- *   Otherwise (and on DEQUANT_GEMM): dequantise-then-GEMM: the weights are dequantised to binary16
- *     in the workspace (at least N*K*2 bytes, 16-byte aligned; less:
- *     Q4_ERR_WORKSPACE), then the dense binary16 GEMM of dense_gemm runs on
- *     them.  affine8_gemm_workspace_size(M, N, K) is 0 for M <= 16 and N*K*2
- *     above (enough for either activation type).
+ *   Otherwise (and on MFMA): the matrix-core GEMM of q4_gemm's MFMA path
+ *     on a weight image of 17408 bytes per 256 columns and 64 K (the codes
+ *     and the group's s and b, dequantised in registers to binary16 as
+ *     (q + 1024 - 1024) * s + b with one rounding) and the X image, both
+ *     in the workspace: at least ceil(M/128)*128 * (K*2 + 1) +
+ *     ceil(N/256) * (K/64) * 17408 bytes, 16-byte aligned (less:
+ *     Q4_ERR_WORKSPACE), plus parts*M*N*4 for split-K partial results when
+ *     the tile count is small (without that room K is not split).
+ *   DEQUANT_GEMM (forced only): the weights are dequantised to binary16 in
+ *     the workspace (at least N*K*2 bytes), then the dense binary16 GEMM of
+ *     dense_gemm runs on them.
+ *   affine8_gemm_workspace_size(M, N, K) is 0 for M <= 16 and the size the
+ *   path needs above (enough for either activation type).
  *   x : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32); y : device out, [M][N]
  *   of y_dtype (Q4_BF16 RNE, or Q4_F32).  group_size 64 only, K % 64 == 0.
  *   Calls that share a workspace must not run concurrently.
@@ -380,7 +389,8 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
  * plus parts*M*N*4 for the K-split partial results when the tile count is
  * below half the device's CU count (parts: the most, up to 16, that divide
  * ceil(K/64), leave at least 4 K steps each and keep tiles*parts within the
- * CU count); for DEQUANT_GEMM N*K*2 (a dense binary16 W).
+ * CU count); for DEQUANT_GEMM N*K*2 (a dense binary16 W).  fmt
+ * Q4_FMT_AFFINE8: affine8_gemm_workspace_size(M, N, K).
  * Returns 0 for invalid arguments.
  */
 int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt);
@@ -393,14 +403,16 @@ int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt);
  * GEMM: the image holds the same 4.5 bits per weight as the planes.
  *
  * q4_weight_image_size -- bytes of the image of an [N][K] matrix,
- * ceil(N/256) * ceil(K/64) * 9216; 0 for invalid arguments.
+ * ceil(N/256) * ceil(K/64) * 9216 (Q4_0, affine 4-bit) or
+ * ceil(N/256) * (K/64) * 17408 (affine 8-bit); 0 for invalid arguments.
  */
 int64_t q4_weight_image_size(int64_t N, int64_t K, int fmt);
 
 /*
  * q4_pack_weight_image -- lay the weight planes out as that image.
- *   fmt   : Q4_FMT_Q4_0 (w_q = qs, w_s = d, w_b unused) or Q4_FMT_AFFINE4
- *           (w_q, w_s = scales, w_b = biases; group size 64)
+ *   fmt   : Q4_FMT_Q4_0 (w_q = qs, w_s = d, w_b unused), Q4_FMT_AFFINE4 or
+ *           Q4_FMT_AFFINE8 (w_q = codes, w_s = scales, w_b = biases, as
+ *           affine4_quantize / affine8_quantize write them; group size 64)
  *   image : device out, q4_weight_image_size(N, K, fmt) bytes, 16-byte aligned
  * K % 32 == 0 (Q4_0) or K % 64 == 0 (affine), else Q4_ERR_SHAPE.
  */
@@ -409,8 +421,8 @@ int q4_pack_weight_image(int fmt, const uint8_t* w_q, const uint16_t* w_s, const
 
 /*
  * q4_gemm_image -- Y = X . dequant(W)^T on the matrix-core path from a
- * weight image: the same results as q4_gemm / affine4_gemm on the MFMA path
- * with a workspace of the same size, for any M >= 1.
+ * weight image: the same results as q4_gemm / affine4_gemm / affine8_gemm
+ * on the MFMA path with a workspace of the same size, for any M >= 1.
  *   workspace : device scratch for the X image, at least
  *               q4_gemm_image_workspace_size(M, K) =
  *               ceil(M/128)*128 * (ceil(K/64)*64 * 2 + 1) bytes (else

@@ -163,14 +163,26 @@ def test_affine8_validation():
     assert g(P, P, P, 128, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 64, None, 0, None) == B.Q4_ERR_SHAPE
     assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 4, 8, 96, None, 0, None) == B.Q4_ERR_SHAPE
     assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 0, 8, 64, None, 0, None) == B.Q4_OK
-    # above the fused kernels (f32 X: M > 16, bf16 X: M > 32) the call dequantises
-    # into the workspace: N*K*2 bytes or Q4_ERR_WORKSPACE, checked before any launch
+    # above the fused kernels (f32 X: M > 16, bf16 X: M > 32) the matrix-core GEMM
+    # builds its X image (128-row tiles, K*2 + 1 bytes a row) and weight image
+    # (17408 bytes per 256 columns and 64 K) in the workspace: less room is
+    # Q4_ERR_WORKSPACE, checked before any launch
+    need = 128 * (64 * 2 + 1) + 17408
     assert g(P, P, P, 64, P, B.Q4_F32, P, B.Q4_BF16, 17, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
     assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, None, 0, None) == B.Q4_ERR_WORKSPACE
-    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, P, 8 * 64 * 2 - 1, None) == B.Q4_ERR_WORKSPACE
-    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, MIS, 8 * 64 * 2, None) == B.Q4_ERR_ALIGN
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, P, need - 1, None) == B.Q4_ERR_WORKSPACE
+    assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, MIS, need, None) == B.Q4_ERR_ALIGN
     ws = lib().affine8_gemm_workspace_size
-    assert ws(16, 12288, 4096) == 0 and ws(17, 12288, 4096) == 12288 * 4096 * 2 and ws(17, 8, 96) == 0
+    assert ws(16, 12288, 4096) == 0 and ws(17, 8, 96) == 0
+    assert ws(17, 12288, 4096) >= 128 * (4096 * 2 + 1) + 48 * 64 * 17408
+    # a forced dequantise-then-GEMM wants the binary16 weights
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+    try:
+        assert ws(17, 12288, 4096) == 12288 * 4096 * 2
+        assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, P, 8 * 64 * 2 - 1, None) == B.Q4_ERR_WORKSPACE
+        assert g(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 33, 8, 64, MIS, 8 * 64 * 2, None) == B.Q4_ERR_ALIGN
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
 
 
 def test_gemv_multi_validation():
@@ -201,6 +213,13 @@ def test_weight_image_validation_and_sizes():
     assert lib().q4_weight_image_size(300, 96, B.Q4_FMT_Q4_0) == 2 * 2 * 9216
     assert lib().q4_weight_image_size(300, 96, B.Q4_FMT_AFFINE4) == 0        # K % 64 != 0
     assert lib().q4_weight_image_size(300, 128, 5) == 0
+    # affine 8-bit: 17408-byte chunks (codes of 256 columns x 64 K, then s and b)
+    assert lib().q4_weight_image_size(12288, 4096, B.Q4_FMT_AFFINE8) == 48 * 64 * 17408
+    assert lib().q4_weight_image_size(300, 128, B.Q4_FMT_AFFINE8) == 2 * 2 * 17408
+    assert lib().q4_weight_image_size(300, 96, B.Q4_FMT_AFFINE8) == 0
+    for M in (1, 33, 2048):
+        assert lib().q4_gemm_workspace_size(M, 12288, 4096, B.Q4_FMT_AFFINE8) == \
+            lib().affine8_gemm_workspace_size(M, 12288, 4096)
     assert lib().q4_gemm_image_workspace_size(2048, 4096) == 2048 * (4096 * 2 + 1)
     assert lib().q4_gemm_image_workspace_size(129, 96) == 256 * (128 * 2 + 1)
     p = lib().q4_pack_weight_image
@@ -208,6 +227,8 @@ def test_weight_image_validation_and_sizes():
     assert p(B.Q4_FMT_Q4_0, P, P, None, 8, 48, P, None) == B.Q4_ERR_SHAPE
     assert p(B.Q4_FMT_AFFINE4, P, P, P, 8, 96, P, None) == B.Q4_ERR_SHAPE
     assert p(B.Q4_FMT_AFFINE4, P, P, None, 8, 128, P, None) == B.Q4_ERR_NULL   # affine needs biases
+    assert p(B.Q4_FMT_AFFINE8, P, P, None, 8, 128, P, None) == B.Q4_ERR_NULL
+    assert p(B.Q4_FMT_AFFINE8, P, P, P, 8, 96, P, None) == B.Q4_ERR_SHAPE
     assert p(B.Q4_FMT_Q4_0, P, P, None, 8, 64, MIS, None) == B.Q4_ERR_ALIGN
     assert p(B.Q4_FMT_Q4_0, P, P, None, 0, 64, P, None) == B.Q4_OK
     g = lib().q4_gemm_image
@@ -293,17 +314,17 @@ def test_dispatch_predicate_boundaries():
     with pytest.raises(B.Q4Error):
         B.q4_set_dispatch(77, 1)
     # affine 8-bit: fused kernels up to Q4_KEY_AFFINE8_FUSED_MAX_M (default 32),
-    # dequantise-then-GEMM above; only SKINNY and DEQUANT_GEMM can be forced
+    # the matrix-core GEMM above; SKINNY, MFMA and DEQUANT_GEMM can be forced
     A8 = B.Q4_FMT_AFFINE8
     assert B.q4_get_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M) == 32
     assert B.q4_dispatch_path(32, 4096, 4096, A8) == B.Q4_PATH_SKINNY
-    assert B.q4_dispatch_path(33, 4096, 4096, A8) == B.Q4_PATH_DEQUANT_GEMM
+    assert B.q4_dispatch_path(33, 4096, 4096, A8) == B.Q4_PATH_MFMA
     assert B.q4_dispatch_path(1, 4096, 4064, A8) == B.Q4_ERR_SHAPE     # K % 64
     ws8 = lib().affine8_gemm_workspace_size
     B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 4)
     try:
-        assert B.q4_dispatch_path(5, 4096, 4096, A8) == B.Q4_PATH_DEQUANT_GEMM
-        assert ws8(5, 4096, 4096) == 4096 * 4096 * 2 and ws8(4, 4096, 4096) == 0
+        assert B.q4_dispatch_path(5, 4096, 4096, A8) == B.Q4_PATH_MFMA
+        assert ws8(5, 4096, 4096) >= 128 * (4096 * 2 + 1) + 16 * 64 * 17408 and ws8(4, 4096, 4096) == 0
         assert lib().affine8_gemm(P, P, P, 64, P, B.Q4_BF16, P, B.Q4_BF16, 5, 8, 64, None, 0, None) == \
             B.Q4_ERR_WORKSPACE
         B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 1000)
@@ -312,8 +333,8 @@ def test_dispatch_predicate_boundaries():
         B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 32)
     for forced, want_small, want_big in ((B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM),
                                          (B.Q4_PATH_SKINNY, B.Q4_PATH_SKINNY, B.Q4_PATH_SKINNY),
-                                         (B.Q4_PATH_MFMA, B.Q4_PATH_SKINNY, B.Q4_PATH_DEQUANT_GEMM),
-                                         (B.Q4_PATH_INT8, B.Q4_PATH_SKINNY, B.Q4_PATH_DEQUANT_GEMM)):
+                                         (B.Q4_PATH_MFMA, B.Q4_PATH_MFMA, B.Q4_PATH_MFMA),
+                                         (B.Q4_PATH_INT8, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)):
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, forced)
         try:
             assert B.q4_dispatch_path(1, 64, 64, A8) == want_small
@@ -385,7 +406,7 @@ print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUA
     ({"Q4_FORCE_PATH": "17"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
     ({"Q4_FORCE_PATH": "-5"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
     ({"Q4_FORCE_PATH": "junk"}, (None, None, -1, None, None)),
-    ({"Q4_AFFINE8_FUSED_MAX_M": "16"}, (None, None, -1, None, None, None, 16, B.Q4_PATH_DEQUANT_GEMM)),
+    ({"Q4_AFFINE8_FUSED_MAX_M": "16"}, (None, None, -1, None, None, None, 16, B.Q4_PATH_MFMA)),
     ({"Q4_AFFINE8_FUSED_MAX_M": "99"}, (None, None, -1, None, None, None, 32, B.Q4_PATH_SKINNY)),
 ])
 def test_dispatch_environment_overrides(env, expect):

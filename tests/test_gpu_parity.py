@@ -425,11 +425,13 @@ def test_q4_gemm_every_path_boundary_m(M):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 160, 640, 1024), ("q4_0", 129, 300, 96), ("q4_0", 1, 257, 4096),
-                                       ("affine", 160, 640, 1024), ("affine", 129, 300, 128)])
+                                       ("affine", 160, 640, 1024), ("affine", 129, 300, 128),
+                                       ("affine8", 160, 640, 1024), ("affine8", 129, 300, 128),
+                                       ("affine8", 1, 257, 4096)])
 def test_gemm_image_equals_mfma_path(fmt, M, N, K):
-    """A prepacked weight image gives the bits of q4_gemm / affine4_gemm on the
-    matrix-core path with a workspace, call after call with new activations
-    (these shapes have few tiles, so both split K)."""
+    """A prepacked weight image gives the bits of q4_gemm / affine4_gemm /
+    affine8_gemm on the matrix-core path with a workspace, call after call
+    with new activations (these shapes have few tiles, so both split K)."""
     say(f"gemm_image {fmt} M={M} N={N} K={K}")
     rng = np.random.default_rng(M + N + K)
     W = synth.weights(rng, N, K)
@@ -437,10 +439,15 @@ def test_gemm_image_equals_mfma_path(fmt, M, N, K):
         planes = [dev(a) for a in oracle.q4_0_quantize(W)]
         run = lambda x, ws, ydt: B.q4_gemm(*planes, x, y_dtype=ydt, workspace=ws)
         f = B.Q4_FMT_Q4_0
-    else:
+    elif fmt == "affine":
         planes = [dev(a) for a in oracle.affine4_quantize(synth.bf16_bits(W), 64)]
         run = lambda x, ws, ydt: B.affine4_gemm(*planes, x, y_dtype=ydt, workspace=ws)
         f = B.Q4_FMT_AFFINE4
+    else:
+        planes = [dev(a) for a in oracle.affine8_quantize(synth.bf16_bits(W), 64)]
+        run = lambda x, ws, ydt: B.affine8_gemm(*planes, x, y_dtype=ydt, workspace=ws)
+        f = B.Q4_FMT_AFFINE8
+        assert B.q4_pack_weight_image(*planes).numel() == B.lib().q4_weight_image_size(N, K, f)   # format inferred
     image = B.q4_pack_weight_image(*planes, fmt=f)
     B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
     try:
@@ -668,7 +675,7 @@ def test_affine8_dequantize_bitexact(N, K):
     assert np.array_equal(got32, oracle.affine8_dequantize(q, s, b).astype(np.float32))
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16, 17, 32, 33, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16, 17, 32, 33, 130, 300])
 @pytest.mark.parametrize("N,K", [(257, 1024), (40, 64), (96, 4160)])
 def test_affine8_gemm_parity(M, N, K):
     say(f"affine8_gemm M={M} N={N} K={K}")
@@ -685,8 +692,8 @@ def test_affine8_gemm_parity(M, N, K):
         e = oracle.rel_frobenius(out_f64(y), ref)
         assert e <= BAR, (M, N, K, ydt, e)
         if ydt == torch.float32:
-            # fused (M <= 32 on bf16 X): exact products, binary32 sums; above:
-            # binary16 weights
+            # fused (M <= 32 on bf16 X): exact products, binary32 sums; above
+            # (the matrix-core GEMM): binary16 weights and X
             assert e <= (GEMV_TIGHT if M <= 32 else 1e-3), (M, N, K, e)
     if M <= 16:
         # a binary32 activation (the same values): binary32 weights times x
@@ -699,8 +706,9 @@ def test_affine8_gemm_parity(M, N, K):
 
 def test_affine8_dispatch_routes():
     """affine8_gemm follows q4_dispatch_path (Q4_FMT_AFFINE8): a forced
-    DEQUANT_GEMM, or Q4_KEY_AFFINE8_FUSED_MAX_M below M, gives the bits of
-    affine8_dequantize + dense_gemm; the default stays on the fused kernel;
+    DEQUANT_GEMM gives the bits of affine8_dequantize + dense_gemm; a forced
+    MFMA, or Q4_KEY_AFFINE8_FUSED_MAX_M below M, the matrix-core GEMM on
+    images (the same bits both ways); the default stays on the fused kernel;
     all within the bar of the binary64 oracle."""
     M, N, K = 8, 300, 256
     rng = np.random.default_rng(88)
@@ -714,25 +722,82 @@ def test_affine8_dispatch_routes():
     want_deq = B.dense_gemm(x, B.affine8_dequantize(*t, out_dtype=torch.float16), y_dtype=torch.float32)
     fused = B.affine8_gemm(*t, x, y_dtype=torch.float32)
     assert not torch.equal(fused, want_deq)          # a different path
-    for how in ("force", "key"):
-        if how == "force":
+    got = {}
+    for how in ("force_deq", "force_mfma", "key"):
+        if how == "force_deq":
             B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+        elif how == "force_mfma":
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
         else:
             B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 4)
         try:
-            assert B.affine8_gemm_workspace_size(M, N, K) == N * K * 2
-            y = B.affine8_gemm(*t, x, y_dtype=torch.float32)
+            wsb = B.affine8_gemm_workspace_size(M, N, K)
+            if how == "force_deq":
+                assert wsb == N * K * 2
+            else:
+                assert wsb >= 128 * (K * 2 + 1) + 2 * (K // 64) * 17408
+            got[how] = B.affine8_gemm(*t, x, y_dtype=torch.float32)
         finally:
             B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
             B.q4_set_dispatch(B.Q4_KEY_AFFINE8_FUSED_MAX_M, 32)
-        torch.cuda.synchronize()
-        assert torch.equal(y, want_deq), how
-    for y in (fused, want_deq):
+    torch.cuda.synchronize()
+    assert torch.equal(got["force_deq"], want_deq)
+    assert torch.equal(got["force_mfma"], got["key"])
+    assert not torch.equal(got["key"], want_deq)
+    for y in (fused, want_deq, got["key"]):
         assert rel(out_f64(y), ref) <= BAR
 
 
+@pytest.mark.parametrize("M", [33, 64, 130, 300])
+@pytest.mark.parametrize("N,K", [(300, 1024), (520, 4096), (1, 64)])
+def test_affine8_mfma_path(M, N, K):
+    """The matrix-core GEMM on affine 8-bit images against the binary64
+    oracle: bf16 and f32 X, bf16 and f32 Y, with the split-K partials room
+    (affine8_gemm_workspace_size) and without it (the two images only: K is
+    not split), ragged N and M; and against forced dequantise-then-GEMM."""
+    say(f"affine8 matrix-core path M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 13 + N * 5 + K)
+    W = synth.weights(rng, N, K)
+    X = synth.activations(rng, M, K)
+    q, s, b = oracle.affine8_quantize(synth.bf16_bits(W), 64)
+    t = [dev(a) for a in (q, s, b)]
+    xb = synth.bf16_bits(X)
+    xf = synth.bf16_bits_to_f32(xb)
+    ref = oracle.matmul_f64(xf.astype(np.float64), oracle.affine8_dequantize(q, s, b))
+    images = B.q4_gemm_image_workspace_size(M, K) + (N + 255) // 256 * (K // 64) * 17408
+    full = B.affine8_gemm_workspace_size(M, N, K)
+    assert full >= images
+    outs = {}
+    for xname, x in (("bf16", bf16_dev(X)), ("f32", dev(xf))):
+        for wsname, nbytes in (("split", full), ("images", images)):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            y32 = B.affine8_gemm(*t, x, y_dtype=torch.float32, workspace=ws)
+            y16 = B.affine8_gemm(*t, x, y_dtype=torch.bfloat16, workspace=ws)
+            torch.cuda.synchronize()
+            e = oracle.rel_frobenius(out_f64(y32), ref)
+            assert e <= 1e-3, (xname, wsname, e)
+            # bf16 Y: the same fp32 results rounded to nearest even (bf16
+            # rounding alone is up to 2^-9 of each output, so the Frobenius
+            # bar is checked only where there are enough outputs to average)
+            assert torch.equal(y16, y32.to(torch.bfloat16)), (xname, wsname)
+            if M * N >= 1024:
+                assert oracle.rel_frobenius(out_f64(y16), ref) <= BAR, (xname, wsname)
+            outs[(xname, wsname)] = y32
+    # the same values in bf16 and f32 X convert to the same binary16 image
+    assert torch.equal(outs[("bf16", "split")], outs[("f32", "split")])
+    assert torch.equal(outs[("bf16", "images")], outs[("f32", "images")])
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_DEQUANT_GEMM)
+    try:
+        yd = B.affine8_gemm(*t, bf16_dev(X), y_dtype=torch.float32)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+    torch.cuda.synchronize()
+    # both multiply the same binary16 weights and X: only the summation order differs
+    assert rel(out_f64(outs[("bf16", "images")]), out_f64(yd)) <= 1e-5
+
+
 def test_affine8_gemm_full_size_sampled():
-    """N=12288, K=4096 at M = 1, 16 and 32 (fused) and M = 64 (dequantise-then-GEMM): sampled outputs against binary64."""
+    """N=12288, K=4096 at M = 1, 16 and 32 (fused) and M = 64 (matrix-core GEMM): sampled outputs against binary64."""
     N, K = 12288, 4096
     rng = np.random.default_rng(2024)
     W = synth.weights(rng, N, K)
@@ -774,8 +839,8 @@ def test_affine8_gemm_edges_and_determinism(M, N, K):
 
 
 def test_affine8_graph_replays_match_eager():
-    """affine8_gemm on each of its three paths (vector kernel, bf16-MFMA kernel, dequantise-then-GEMM
-    with a caller workspace) captured in one graph: every replay, with eager work and synchronisations
+    """affine8_gemm on each of its three paths (vector kernel, bf16-MFMA kernel, matrix-core GEMM on
+    images in a caller workspace) captured in one graph: every replay, with eager work and synchronisations
     between replays, reproduces the eager results exactly."""
     rng = np.random.default_rng(77)
     N, K = 300, 1024

@@ -24,7 +24,10 @@ def _image(rng, fmt, N, K):
     if fmt == B.Q4_FMT_Q4_0:
         qs, d = B.q4_quantize(w)
         return B.q4_pack_weight_image(qs, d, fmt=fmt)
-    q, s, b = B.affine4_quantize(w.to(torch.bfloat16), 64)
+    if fmt == B.Q4_FMT_AFFINE8:
+        q, s, b = B.affine8_quantize(w.to(torch.bfloat16))
+    else:
+        q, s, b = B.affine4_quantize(w.to(torch.bfloat16), 64)
     return B.q4_pack_weight_image(q, s, b, fmt=fmt)
 
 
@@ -57,6 +60,7 @@ def _call_workspace(fmt, img, x, y, N, ws):
     # uses the split-K partial results after the X image
     (B.Q4_FMT_Q4_0, 12288, 4096, [(2048, torch.bfloat16, torch.bfloat16), (77, torch.bfloat16, torch.float32)]),
     (B.Q4_FMT_AFFINE4, 4160, 2048, [(1000, torch.float32, torch.float32), (33, torch.bfloat16, torch.bfloat16)]),
+    (B.Q4_FMT_AFFINE8, 2304, 1024, [(600, torch.bfloat16, torch.bfloat16), (40, torch.float32, torch.float32)]),
 ])
 def test_noalloc_matches_workspace_entry_point(fmt, N, K, calls):
     rng = np.random.default_rng(N + K)
