@@ -533,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 //    dequantising the weights of step k+1 into registers, interleaved
 //    instruction by instruction (one basic block per step);
 //  * waves 4-7 (producers, one per SIMD) copy the X tile and the raw weight
-//    blocks (and scales) of step k+5 into a 6-deep LDS ring with
+//    blocks (and scales) of step k+3 into a 4-deep LDS ring with
 //    direct-to-LDS loads and, before each barrier, wait until step k+2 has
 //    landed.  They issue no other memory operation, so the count in that
 //    wait is exact.  Their stream runs on across tile boundaries.
@@ -541,10 +541,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma(const GemmArgs a) {
 // output straight from the accumulators (pairs of columns per store) and
 // go on with the next tile, whose first steps are already in LDS.
 // ---------------------------------------------------------------------------
-// Ring depth: steps k..k+5 resident (k..k+3 for the 17 KiB affine 8-bit
-// chunks, which keeps the ring within LDS); producers request step
-// k + depth - 1 during step k.
-template <int WF> constexpr int pk_slots() { return WF == WF_AFFINE8 ? 4 : 6; }
+// Ring depth: steps k..k+3 resident (100 KiB; 132 KiB with the 17 KiB affine
+// 8-bit chunks); producers request step k + depth - 1 during step k.  A
+// 6-deep ring was slower: the slot of step k (k mod 6) costs address
+// arithmetic on every LDS read of the compute waves, k mod 4 almost none.
+template <int WF> constexpr int pk_slots() { return 4; }
 constexpr int kPkProducers = 4;          // producer waves, one per SIMD
 // X -> image (see above), one workgroup of 256 threads per image row.  The
 // workgroup first finds the row's largest |x|.  A row whose largest lies in
@@ -1122,7 +1123,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
         };
         // prologue: steps 0 .. kAhead-1 requested, steps 0 and 1 landed.
         // Steps k+3 .. k+kAhead may stay in flight: kAhead - 2 steps of this
-        // wave's copies (3 steps of 7 or 6; affine 8-bit 1 step of 9 or 8).
+        // wave's copies (one step: 7 or 6 copies; affine 8-bit 9 or 8).
         constexpr int kAhead = kSlots - 1;
         constexpr int kMaxC = (kCopies + kPkProducers - 1) / kPkProducers, kMinC = kCopies / kPkProducers;
         static_assert(kAhead >= 3 && (kAhead - 2) * kMaxC < 64, "wait counts below");
