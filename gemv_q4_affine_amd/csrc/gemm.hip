@@ -556,13 +556,14 @@ constexpr int kPkProducers = 4;          // producer waves, one per SIMD
 // to nearest even, and e to the exponent table.  For bfloat16 X of a scaled
 // row every value within 2^-31 of the row's largest converts exactly.  Rows
 // past M and steps past K are zero.
+// Workgroup blk of the packer (image row blk); wave_max: 4 floats of LDS.
 template <int WF, int XDT>
-__global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint16_t* __restrict__ img,
-                                                int8_t* __restrict__ xexp, int M, int K, int ksteps) {
+__device__ __forceinline__ void pack_x_body(int blk, float* wave_max, const void* __restrict__ x,
+                                            uint16_t* __restrict__ img, int8_t* __restrict__ xexp, int M, int K,
+                                            int ksteps) {
     constexpr int kBatch = 2;                   // chunks per thread held in registers (K <= 4096 in one batch)
     using Raw = RawX8<XDT>;
-    __shared__ float wave_max[4];
-    const int m = blockIdx.x;
+    const int m = blk;
     const int tid = threadIdx.x;
     const int nch = ksteps * 8;                 // 16-byte chunks of an image row
     const int kch = m < M ? K / 8 : 0;          // chunks holding X (K % 32 == 0)
@@ -648,20 +649,28 @@ __global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint
     if (tid == 0) xexp[xexp_pos(m)] = (int8_t)e;
 }
 
+template <int WF, int XDT>
+__global__ __launch_bounds__(256) void k_pack_x(const void* __restrict__ x, uint16_t* __restrict__ img,
+                                                int8_t* __restrict__ xexp, int M, int K, int ksteps) {
+    __shared__ float wave_max[4];
+    pack_x_body<WF, XDT>(blockIdx.x, wave_max, x, img, xexp, M, K, ksteps);
+}
+
 
 // planar weights -> image, one workgroup per (256-column tile, 4 K steps).
 // Loads go row by row (8 lanes read a row's 128 contiguous bytes of nibble
 // blocks) into an LDS tile swizzled by row; stores go plane by plane (each
 // thread writes one column's 16-byte block), so both sides are coalesced.
+// Workgroup blk of the packer; lq: 32 KiB of LDS, [column][8 blocks], block
+// slot b ^ (column & 7).
 template <int WF>
-__global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsc,
-                                                const uint16_t* __restrict__ wbias, uint8_t* __restrict__ img,
-                                                int N, int K, int n_tiles, int ksteps) {
-    __shared__ u32x4_t lq[256 * 8];            // [column][8 blocks], block slot b ^ (column & 7)
+__device__ __forceinline__ void pack_w_body(int blk, u32x4_t* lq, const uint8_t* __restrict__ wq,
+                                            const uint16_t* __restrict__ wsc, const uint16_t* __restrict__ wbias,
+                                            uint8_t* __restrict__ img, int N, int K, int ksteps) {
     const int tid = threadIdx.x;
     const int kq = (ksteps + 3) / 4;
-    const int grp = blockIdx.x % kq;
-    const int nt = blockIdx.x / kq;
+    const int grp = blk % kq;
+    const int nt = blk / kq;
     const int nb = K / 32;
     // nibble blocks 8*grp .. 8*grp+7 of the tile's columns
 #pragma unroll
@@ -740,20 +749,28 @@ __global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ wq, 
     }
 }
 
+template <int WF>
+__global__ __launch_bounds__(256) void k_pack_w(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsc,
+                                                const uint16_t* __restrict__ wbias, uint8_t* __restrict__ img,
+                                                int N, int K, int ksteps) {
+    __shared__ u32x4_t lq[256 * 8];
+    pack_w_body<WF>(blockIdx.x, lq, wq, wsc, wbias, img, N, K, ksteps);
+}
+
 // Affine 8-bit codes [N][K] with group-64 scales and biases [N][K/64] ->
 // image, one workgroup per (256-column tile, 2 K steps).  Loads go row by
 // row (8 lanes read a row's 128 contiguous code bytes, two groups) into an
 // LDS tile swizzled by row; stores go plane by plane (each thread writes one
 // column's 16 bytes), so both sides are coalesced.  Columns past N get zero
 // codes, scales and biases.
-__global__ __launch_bounds__(256) void k_pack_w8(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsc,
-                                                 const uint16_t* __restrict__ wbias, uint8_t* __restrict__ img, int N,
-                                                 int K, int ksteps) {
-    __shared__ u32x4_t lq[256 * 8];            // [column][8 chunks], chunk slot c ^ (column & 7)
+// lq: 32 KiB of LDS, [column][8 chunks], chunk slot c ^ (column & 7).
+__device__ __forceinline__ void pack_w8_body(int blk, u32x4_t* lq, const uint8_t* __restrict__ wq,
+                                             const uint16_t* __restrict__ wsc, const uint16_t* __restrict__ wbias,
+                                             uint8_t* __restrict__ img, int N, int K, int ksteps) {
     const int tid = threadIdx.x;
     const int kq = (ksteps + 1) / 2;
-    const int grp = blockIdx.x % kq;
-    const int nt = blockIdx.x / kq;
+    const int grp = blk % kq;
+    const int nt = blk / kq;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const int u = tid + 256 * i;
@@ -786,6 +803,36 @@ __global__ __launch_bounds__(256) void k_pack_w8(const uint8_t* __restrict__ wq,
         }
         reinterpret_cast<uint16_t*>(chunk + 16384)[tid] = sc[st];
         reinterpret_cast<uint16_t*>(chunk + 16896)[tid] = bi[st];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_pack_w8(const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wsc,
+                                                 const uint16_t* __restrict__ wbias, uint8_t* __restrict__ img, int N,
+                                                 int K, int ksteps) {
+    __shared__ u32x4_t lq[256 * 8];
+    pack_w8_body(blockIdx.x, lq, wq, wsc, wbias, img, N, K, ksteps);
+}
+
+// Workgroups per weight image: 4-bit formats one per (256-column tile, 4 K
+// steps), affine 8-bit one per (256-column tile, 2 K steps).
+template <int WF>
+constexpr int pack_w_steps() { return WF == WF_AFFINE8 ? 2 : 4; }
+
+// Both images of a per-call GEMM in one launch (they are independent HBM
+// streams; one launch saves the second launch and its ramp): workgroups
+// 0 .. nx-1 pack X rows, the rest the weight image.
+template <int WF, int XDT>
+__global__ __launch_bounds__(256) void k_pack_xw(int nx, const void* __restrict__ x, uint16_t* __restrict__ ximg,
+                                                 int8_t* __restrict__ xexp, int M, const uint8_t* __restrict__ wq,
+                                                 const uint16_t* __restrict__ wsc, const uint16_t* __restrict__ wbias,
+                                                 uint8_t* __restrict__ wimg, int N, int K, int ksteps) {
+    __shared__ u32x4_t lq[256 * 8];
+    const int b = blockIdx.x;
+    if (b < nx) {
+        pack_x_body<WF, XDT>(b, reinterpret_cast<float*>(lq), x, ximg, xexp, M, K, ksteps);
+    } else {
+        if constexpr (WF == WF_AFFINE8) pack_w8_body(b - nx, lq, wq, wsc, wbias, wimg, N, K, ksteps);
+        else pack_w_body<WF>(b - nx, lq, wq, wsc, wbias, wimg, N, K, ksteps);
     }
 }
 
@@ -1825,8 +1872,16 @@ static void launch_pack_w_t(const void* a, const void* b, const void* c, int N, 
     const int ksteps = (K + 63) / 64;
     const dim3 grid((unsigned)(n_tiles * ((ksteps + 3) / 4))), block(256);
     hipLaunchKernelGGL((k_pack_w<WF>), grid, block, 0, s, static_cast<const uint8_t*>(a),
-                       static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(c), wimg, N, K, n_tiles, ksteps);
+                       static_cast<const uint16_t*>(b), static_cast<const uint16_t*>(c), wimg, N, K, ksteps);
 }
+
+// The weight planes a per-call GEMM packs into its weight image.
+struct WPack {
+    const void* a;      // Q4_0 qs / affine codes
+    const void* b;      // Q4_0 d / affine scales
+    const void* c;      // affine biases
+    uint8_t* wimg;
+};
 
 // Y = the sum of the ksplit fp32 partial results, in part order; 4 outputs
 // per thread.
@@ -1878,24 +1933,43 @@ int64_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
     return d > 1 ? (int64_t)d * M * N * 4 : 0;
 }
 
+template <int WF, int XDT>
+static void launch_pack_xw_t(const GemmArgs& ga, uint16_t* ximg, const WPack& wp, hipStream_t s) {
+    const int ksteps = (ga.K + 63) / 64;
+    const int nx = ga.m_tiles * kImgRows;
+    const int nw = ga.n_tiles * ((ksteps + pack_w_steps<WF>() - 1) / pack_w_steps<WF>());
+    int8_t* xexp = const_cast<int8_t*>(x_image_exponents(ximg, ga.M, ga.K));
+    hipLaunchKernelGGL((k_pack_xw<WF, XDT>), dim3((unsigned)(nx + nw)), dim3(256), 0, s, nx, ga.x, ximg, xexp, ga.M,
+                       static_cast<const uint8_t*>(wp.a), static_cast<const uint16_t*>(wp.b),
+                       static_cast<const uint16_t*>(wp.c), wp.wimg, ga.N, ga.K, ksteps);
+}
+
 // X image into ximg, then the GEMM on it and the weight image ga.a; with a
 // partial buffer (splitk_bytes(M, N, K) bytes, or nullptr) small tile counts
-// are split along K.
+// are split along K.  With wp the weight image is packed too (into wp->wimg,
+// which ga.a points at), in the same launch as the X image.
 template <int WF>
-static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, float* part, hipStream_t s) {
+static void launch_on_images(GemmArgs ga, int xdt, int ydt, uint16_t* ximg, float* part, hipStream_t s,
+                             const WPack* wp = nullptr) {
     ga.m_tiles = (ga.M + kImgRows - 1) / kImgRows;
     ga.n_tiles = (ga.N + 255) / 256;
     if constexpr (WF != WF_AFFINE8) {
         if (use_big_tiles(ga.M, ga.N, ga.K)) {
             // 256 x 256 tiles (at least one per CU): no K split, no partials
+            if (wp != nullptr) launch_pack_w_t<WF>(wp->a, wp->b, wp->c, ga.N, ga.K, wp->wimg, s);
             if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
             else launch_pack_t<WF, DT_F32>(ga, ximg, s);
             launch_gemm_big(WF, ga.a, ximg, ga.y, ydt, ga.M, ga.N, ga.K, s);
             return;
         }
     }
-    if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
-    else launch_pack_t<WF, DT_F32>(ga, ximg, s);
+    if (wp != nullptr) {
+        if (xdt == DT_BF16) launch_pack_xw_t<WF, DT_BF16>(ga, ximg, *wp, s);
+        else launch_pack_xw_t<WF, DT_F32>(ga, ximg, *wp, s);
+    } else {
+        if (xdt == DT_BF16) launch_pack_t<WF, DT_BF16>(ga, ximg, s);
+        else launch_pack_t<WF, DT_F32>(ga, ximg, s);
+    }
     ga.x = ximg;
     ga.xexp = x_image_exponents(ximg, ga.M, ga.K);
     ga.ksplit = part != nullptr ? splitk_parts(ga.M, ga.N, ga.K) : 1;
@@ -1963,10 +2037,13 @@ hipError_t launch_affine8_gemm_packed(const uint8_t* wq, const uint16_t* scales,
                                       hipStream_t s) {
     uint8_t* wimg = static_cast<uint8_t*>(img) + x_image_bytes(M, K);
     float* part = reinterpret_cast<float*>(wimg + weight_image8_bytes(N, K));
-    hipError_t e = launch_pack_weight_image(WF_AFFINE8, wq, scales, biases, N, K, wimg, s);
-    if (e != hipSuccess) return e;
-    return launch_gemm_image(WF_AFFINE8, wimg, x, xdt, y, ydt, M, N, K, img,
-                             split && splitk_parts(M, N, K) > 1 ? part : nullptr, s);
+    GemmArgs ga{};
+    ga.a = wimg; ga.x = x; ga.y = y;
+    ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
+    const WPack wp{wq, scales, biases, wimg};
+    launch_on_images<WF_AFFINE8>(ga, xdt, ydt, static_cast<uint16_t*>(img),
+                                 split && splitk_parts(M, N, K) > 1 ? part : nullptr, s, &wp);
+    return hipGetLastError();
 }
 
 // One workspace: the X image, the weight image, then (with `split`) the
@@ -1975,11 +2052,15 @@ hipError_t launch_gemm_packed(int wfmt, const void* a, const void* b, const void
                               int ydt, int64_t M, int64_t N, int64_t K, void* img, bool split, hipStream_t s) {
     if (wfmt != WF_Q4_0 && wfmt != WF_AFFINE4) return hipErrorInvalidValue;
     uint8_t* wimg = static_cast<uint8_t*>(img) + x_image_bytes(M, K);
-    uint8_t* part = wimg + weight_image_bytes(N, K);
-    hipError_t e = launch_pack_weight_image(wfmt, a, b, c, N, K, wimg, s);
-    if (e != hipSuccess) return e;
-    return launch_gemm_image(wfmt, wimg, x, xdt, y, ydt, M, N, K, img,
-                             split && splitk_bytes(M, N, K) > 0 ? reinterpret_cast<float*>(part) : nullptr, s);
+    float* part = split && splitk_bytes(M, N, K) > 0 ? reinterpret_cast<float*>(wimg + weight_image_bytes(N, K))
+                                                     : nullptr;
+    GemmArgs ga{};
+    ga.a = wimg; ga.x = x; ga.y = y;
+    ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
+    const WPack wp{a, b, c, wimg};
+    if (wfmt == WF_Q4_0) launch_on_images<WF_Q4_0>(ga, xdt, ydt, static_cast<uint16_t*>(img), part, s, &wp);
+    else launch_on_images<WF_AFFINE4>(ga, xdt, ydt, static_cast<uint16_t*>(img), part, s, &wp);
+    return hipGetLastError();
 }
 
 template <int WF, int MT, int NT, int XDT, int YDT>
