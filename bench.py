@@ -788,6 +788,15 @@ def environment():
                                            timeout=10).stdout.strip() or None
     except (OSError, subprocess.SubprocessError):
         env["git_commit"] = None
+    if env["git_commit"] is None:
+        # a copy of the tree without git metadata: the commit the library was built from
+        try:
+            with open(os.path.join(ROOT, "gemv_q4_affine_amd", "build_info.json")) as f:
+                info = json.load(f)
+            env["git_commit"] = info.get("git_commit")
+            env["library_built_from_modified_tree"] = info.get("tree_modified")
+        except (OSError, ValueError):
+            pass
     env["device"] = torch.cuda.get_device_name(0)
     env["host_cpus_in_affinity"] = len(os.sched_getaffinity(0))
     return env

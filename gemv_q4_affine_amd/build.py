@@ -61,9 +61,33 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    _write_build_info()
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+BUILD_INFO = os.path.join(os.path.dirname(LIB), "build_info.json")
+
+
+def _write_build_info() -> None:
+    """Record the git commit the library was built from (and whether the tree
+    differed from it) beside the library: copies of the tree without git
+    metadata still name their source."""
+    import json
+    info = {"git_commit": None, "tree_modified": None}
+    try:
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        head = subprocess.run(["git", "-C", root, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        if head.returncode == 0:
+            info["git_commit"] = head.stdout.strip()
+            st = subprocess.run(["git", "-C", root, "status", "--porcelain", "--untracked-files=no"],
+                                capture_output=True, text=True, timeout=10)
+            info["tree_modified"] = bool(st.stdout.strip()) if st.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
 
 
 # ---- host-side AddressSanitizer / UndefinedBehaviorSanitizer build -------------
