@@ -754,7 +754,7 @@ def cpu_baseline_gemm(budget_s: float):
         "unit": "GFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"prefill GEMM M={M} N={N} K={K}: dequantise ({t_deq:.2f} s) + fp64 matmul on {rows} of "
+        "sample": f"prefill GEMM M={M} N={N} K={K}: dequantise ({t_deq * 1e3:.1f} ms) + fp64 matmul on {rows} of "
                   f"{M} X rows ({t_mm:.2f} s), matmul scaled linearly to {M} rows: {t_full:.1f} s per call",
     }
 
