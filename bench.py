@@ -20,7 +20,8 @@ TFLOP/s) against dequantise-then-GEMM, the affine-4 group-64 sweep over
 M in {1, 32, 512, 2048, 8192} with its crossover, the same sweep for affine
 8-bit weights, the small-M paths, and the Llama-3.2-1B-shaped
 16-layer stack (aggregate tokens/s).  The CPU oracle is timed on the host
-cores on a bounded sample of the decode workload (N=1 only).
+cores on bounded samples of the decode workload (`cpu_baseline`) and of the
+prefill GEMM (under `extra.gemm_roofline`), at N=1 only.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
