@@ -25,6 +25,11 @@ SOURCES = ["quant.hip", "gemv.hip", "gemm.hip", "gemm_big.hip", "gemm_q8.hip", "
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# Per-source flags.  The decode GEMVs are launch-latency bound: their leading
+# scalar and pointer arguments (what a one-matrix launch reads) are preloaded
+# into SGPRs at wave launch instead of being fetched from the argument block.
+SOURCE_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -44,7 +49,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -56,10 +56,14 @@ namespace q4 {
 //
 // Every dispatch's argument block is cold in the scalar cache, and a load
 // whose address depends on an earlier argument load pays that miss twice.
-// So the first 64 bytes (one cache line) hold everything a one-matrix launch
-// reads, and a several-matrix launch reads all its fields up front and picks
-// its matrix with selects, never with an index into the block.  The waves
-// per workgroup are passed, so the hidden block-size argument is not read.
+// So what a one-matrix launch reads comes first, as separate scalar and
+// pointer arguments that gfx950 preloads into SGPRs at wave launch (14
+// dwords with this source's -amdgpu-kernarg-preload-count: the weights, the
+// activation the variant reads, the sizes and the output); the
+// several-matrix fields follow in the argument block, read all up front,
+// and a workgroup picks its matrix with selects, never with an index into
+// the block.  The waves per workgroup are passed, so the hidden block-size
+// argument is not read.  The kernel rebuilds a GemvArgs from them.
 struct GemvMat {
     const uint8_t* qs;
     const uint16_t* d;
@@ -80,6 +84,12 @@ struct GemvArgs {
     GemvMat mr[kGemvMats - 1];      // matrices 1 ..
 };
 static_assert(offsetof(GemvArgs, wg0) == 64, "one-matrix fields in the first 64 bytes");
+// The several-matrix fields, passed after the one-matrix ones.
+struct GemvTail {
+    int wg0[kGemvMats - 1];
+    int nr[kGemvMats - 1];
+    GemvMat mr[kGemvMats - 1];
+};
 
 // The matrix of workgroup b (uniform across the workgroup): its pointers,
 // rows and first workgroup.
@@ -136,7 +146,22 @@ __device__ __forceinline__ float sum8(float v) {
 // (8 waves per SIMD) share a CU and twice the loads are in flight.
 template <int M, int RI, int NMAT, int U, int F, int XIN>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(M == 1 ? 8 : 1)))
-void k_q4_gemv(const GemvArgs args) {
+void k_q4_gemv(const uint8_t* qs0, const uint16_t* d0, const void* xa, const uint16_t* xds, int nb_, int nwp_,
+               int n0_, int K_, float* y0, const void* xb, const GemvTail tail) {
+    GemvArgs args;
+    args.m0.qs = qs0; args.m0.d = d0; args.m0.y = y0;
+    args.xqs = static_cast<const int8_t*>(XIN >= 0 ? xb : xa);
+    args.x = XIN >= 0 ? xa : xb;
+    args.xds = xds;
+    args.nb = nb_; args.nwp = nwp_; args.n0 = n0_; args.K = K_;
+    if constexpr (NMAT > 1) {
+#pragma unroll
+        for (int t = 0; t < kGemvMats - 1; t++) {
+            args.wg0[t] = tail.wg0[t];
+            args.nr[t] = tail.nr[t];
+            args.mr[t] = tail.mr[t];
+        }
+    }
     static_assert(RI * M * F <= 16, "partials per lane");
     static_assert(U % F == 0, "each iteration covers whole virtual-wave rounds");
     static_assert(U == 1 || M <= 4, "several columns in flight only for small M");
@@ -356,9 +381,19 @@ static GemvShape raw_shape(GemvShape g, int64_t rows, int64_t nb, int64_t M, boo
     return g;
 }
 
+static GemvTail tail_of(const GemvArgs& a) {
+    GemvTail t;
+    for (int k = 0; k < kGemvMats - 1; k++) {
+        t.wg0[k] = a.wg0[k];
+        t.nr[k] = a.nr[k];
+        t.mr[k] = a.mr[k];
+    }
+    return t;
+}
+
 #define Q4_LAUNCH(...)                                            \
     do {                                                          \
-        hipLaunchKernelGGL((__VA_ARGS__), grid, block, 0, s, a);  \
+        hipLaunchKernelGGL((__VA_ARGS__), grid, block, 0, s, a.m0.qs, a.m0.d, xa_, a.xds, a.nb, a.nwp, a.n0, a.K, a.m0.y, xb_, tail_of(a)); \
         return;                                                   \
     } while (0)
 
@@ -374,6 +409,9 @@ static int assign_workgroups(GemvArgs& a, int rows_per_wg) {
 
 template <int M, int NMAT, int XIN>
 static void launch_mx(GemvArgs a, const GemvShape& g, hipStream_t s) {
+    // the activation the variant reads first among the preloaded arguments
+    const void* xa_ = XIN >= 0 ? a.x : static_cast<const void*>(a.xqs);
+    const void* xb_ = XIN >= 0 ? static_cast<const void*>(a.xqs) : a.x;
     a.nwp = g.v / g.f;
     const dim3 block(a.nwp * kWave);
     const dim3 grid((unsigned)assign_workgroups(a, 8 * g.ri));
