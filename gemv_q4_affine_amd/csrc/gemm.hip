@@ -972,19 +972,36 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
         // sched_barrier, so that every LDS read is issued one segment ahead of
         // its use: the slice s+1 X fragments during slice s, the next step's
         // slice 0 during slice 3 (that tile landed one barrier ago), and the
-        // raw weights of step k+1 in segment 0 for the dequantisation, which
-        // runs word by word under the MFMAs of segments 1-3.  `a0` holds this
-        // step's slice 0 on entry and the next step's on return.  k is the
-        // global step; the next one may start the next tile.  Past the last
-        // step the k+1 slots hold older data that is never used.
-        auto body = [&](int k, const u32x4_t (&cur)[NT][4], u32x4_t (&nxt)[NT][4], u32x4_t (&a0)[MT]) {
+        // raw weights of step k+1 in segment 0.  The dequantisation is spread
+        // evenly, two 32-bit words of raw weights (a quarter of a step's) per
+        // segment, so that each segment issues about four VALU instructions
+        // per MFMA, what one wave hides under its MFMAs:
+        //   segment 0: words 2-3 of block 1 of step k (kept in `rb` from the
+        //              previous step): this step's slices that come from them
+        //              are used in segments 1-3
+        //   segment 1: words 0-1 of block 0 of step k+1
+        //   segment 2: words 0-1 of block 1 of step k+1
+        //   segment 3: words 2-3 of block 0 of step k+1
+        // Word w of a block feeds fragments w/2 and 2 + w/2 (Q4_0) or w
+        // (affine 4-bit and 8-bit), so every fragment of step k+1 that slice 0
+        // needs is complete at the end of step k.  `a0` holds this step's slice
+        // 0 on entry and the next step's on return; `rb` holds block 1 of step
+        // k on entry and of step k+1 on return.  k is the global step; the next
+        // one may start the next tile.  Past the last step the k+1 slots hold
+        // older data that is never used.
+        auto body = [&](int k, u32x4_t (&cur)[NT][4], u32x4_t (&nxt)[NT][4], u32x4_t (&a0)[MT], Blk& rb) {
             Blk r[NT];
             u32x4_t a1[MT], a2[MT], a3[MT];
             mfma_slice(0, a0, cur, true);
             read_a(k, 1, a1);
             read_w(k + 1, r);
             mfma_slice(0, a0, cur, false);
-            segment_order(std::integral_constant<int, kWReads + MT>{}, std::integral_constant<int, 2>{});
+            {
+                const BlkConst cb = blk_const<WF>(rb);
+                blk_fragment<WF>(rb, cb, 2, masks, cur[1]);
+                blk_fragment<WF>(rb, cb, 3, masks, cur[1]);
+            }
+            segment_order(std::integral_constant<int, kWReads + MT>{}, std::integral_constant<int, 4>{});
 
             mfma_slice(1, a1, cur, true);
             read_a(k, 2, a2);
@@ -992,30 +1009,29 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
             const BlkConst c0 = blk_const<WF>(r[0]);
             blk_fragment<WF>(r[0], c0, 0, masks, nxt[0]);
             blk_fragment<WF>(r[0], c0, 1, masks, nxt[0]);
-            blk_fragment<WF>(r[0], c0, 2, masks, nxt[0]);
-            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 7>{});
+            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 4>{});
 
             mfma_slice(2, a2, cur, true);
             read_a(k, 3, a3);
             mfma_slice(2, a2, cur, false);
             const BlkConst c1 = blk_const<WF>(r[1]);
-            blk_fragment<WF>(r[0], c0, 3, masks, nxt[0]);
             blk_fragment<WF>(r[1], c1, 0, masks, nxt[1]);
             blk_fragment<WF>(r[1], c1, 1, masks, nxt[1]);
-            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 7>{});
+            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 4>{});
 
             mfma_slice(3, a3, cur, true);
             read_a(k + 1, 0, a0);
             mfma_slice(3, a3, cur, false);
-            blk_fragment<WF>(r[1], c1, 2, masks, nxt[1]);
-            blk_fragment<WF>(r[1], c1, 3, masks, nxt[1]);
-            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 5>{});
+            blk_fragment<WF>(r[0], c0, 2, masks, nxt[0]);
+            blk_fragment<WF>(r[0], c0, 3, masks, nxt[0]);
+            segment_order(std::integral_constant<int, MT>{}, std::integral_constant<int, 4>{});
             // the fragments must be complete here: without this the compiler
             // may sink their dequantisation past the barrier into the next step
 #pragma unroll
             for (int ni = 0; ni < NT; ni++)
 #pragma unroll
                 for (int t = 0; t < 4; t++) asm volatile("" : "+v"(nxt[ni][t]));
+            rb = r[1];
         };
         static_assert(NT == 2, "the dequantisation split assumes two blocks per step");
 
@@ -1031,7 +1047,11 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
         auto swap_pair = [](float v) {
             return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
         };
-        auto epilogue = [&](int i) {
+        // A tile that lies wholly inside Y (with N even) takes a path with no
+        // bounds test: every pair store is in bounds and aligned, and each
+        // lane's stores advance by fixed multiples of N from one base address.
+        auto store_tile = [&](int i, auto whole_c) {
+            constexpr bool kWhole = decltype(whole_c)::value;
             const int m0 = tile_m0(i);
             const int nw0 = tile_n0(i) + wave * NT * 32;
 #pragma unroll
@@ -1047,9 +1067,11 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                 u32x2_t ex;
                 ex[0] = c == 0 ? w[0] : c == 1 ? w[2] : c == 2 ? w[4] : w[6];
                 ex[1] = c == 0 ? w[1] : c == 1 ? w[3] : c == 2 ? w[5] : w[7];
+                const int r0 = m0 + mi * 32 + 4 * g + (odd ? 1 : 0);
 #pragma unroll
                 for (int ni = 0; ni < NT; ni++) {
                     const int col = nw0 + ni * 32 + (j & ~1);    // even column of the pair
+                    const int64_t base = (int64_t)r0 * a.N + col;
 #pragma unroll
                     for (int v = 0; v < 16; v += 2) {
                         const float a0v = acc[mi][ni][v], a1v = acc[mi][ni][v + 1];
@@ -1058,12 +1080,14 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                         const int ue = -xexp_of(ex, v >> 2, (v >> 1) & 1);
                         const float lo = ldexpf(odd ? d1 : a0v, ue);   // column col
                         const float hi = ldexpf(odd ? a1v : d0, ue);   // column col + 1
-                        const int row = m0 + mi * 32 + 8 * (v >> 2) + 4 * g + (v & 3) + (odd ? 1 : 0);
-                        if (row >= a.M || col >= a.N) continue;
-                        const int64_t off = (int64_t)row * a.N + col;
+                        const int dr = 8 * (v >> 2) + (v & 3);
+                        const int row = r0 + dr;
+                        if (!kWhole && (row >= a.M || col >= a.N)) continue;
+                        const int64_t off = base + (int64_t)dr * a.N;
+                        const bool pair = kWhole || (pair_ok && col + 1 < a.N);
                         if constexpr (SPLIT) {
                             float* yp = a.part + (int64_t)part_of(i) * a.M * a.N + off;
-                            if (pair_ok && col + 1 < a.N) {
+                            if (pair) {
                                 *reinterpret_cast<f32x2_t*>(yp) = f32x2_t{lo, hi};
                             } else {
                                 yp[0] = lo;
@@ -1071,7 +1095,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                             }
                         } else if constexpr (YDT == DT_BF16) {
                             uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + off;
-                            if (pair_ok && col + 1 < a.N) {
+                            if (pair) {
                                 const f32x2_t f = {lo, hi};
                                 *reinterpret_cast<uint32_t*>(yp) =
                                     __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
@@ -1081,7 +1105,7 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                             }
                         } else {
                             float* yp = reinterpret_cast<float*>(a.y) + off;
-                            if (pair_ok && col + 1 < a.N) {
+                            if (pair) {
                                 *reinterpret_cast<f32x2_t*>(yp) = f32x2_t{lo, hi};
                             } else {
                                 yp[0] = lo;
@@ -1091,6 +1115,11 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
                     }
                 }
             }
+        };
+        auto epilogue = [&](int i) {
+            const bool whole = tile_m0(i) + kRows <= a.M && tile_n0(i) + kCols <= a.N && pair_ok;
+            if (whole) store_tile(i, std::true_type{});
+            else store_tile(i, std::false_type{});
 #pragma unroll
             for (int mi = 0; mi < MT; mi++)
 #pragma unroll
@@ -1101,11 +1130,13 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
 
         step_barrier<63>();                    // prologue: steps 0 and 1 landed
         u32x4_t a0[MT];
+        Blk rb;
         {
             Blk r[NT];
             read_w(0, r);
             dequant(0, r, bfA);
             read_a(0, 0, a0);
+            rb = r[1];
         }
         // kl: local index of the current step in its unit, ti: local unit
         int kl = 0, ti = 0;
@@ -1123,15 +1154,15 @@ __global__ __launch_bounds__(256 + 64 * kPkProducers, 1) void k_gemm_pk(const Ge
         // dequantisation out of the block it is meant to overlap
         int k = 0;
         for (; k + 1 < S; k += 2) {
-            body(k, bfA, bfB, a0);
+            body(k, bfA, bfB, a0, rb);
             step_barrier<63>();
             end_step();
-            body(k + 1, bfB, bfA, a0);
+            body(k + 1, bfB, bfA, a0, rb);
             step_barrier<63>();
             end_step();
         }
         if (k < S) {
-            body(k, bfA, bfB, a0);
+            body(k, bfA, bfB, a0, rb);
             step_barrier<63>();
             end_step();
         }
