@@ -425,6 +425,7 @@ def test_q4_gemm_every_path_boundary_m(M):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [("q4_0", 160, 640, 1024), ("q4_0", 129, 300, 96), ("q4_0", 1, 257, 4096),
+                                       ("q4_0", 300, 700, 2048), ("q4_0", 200, 1000, 320),
                                        ("affine", 160, 640, 1024), ("affine", 129, 300, 128),
                                        ("affine8", 160, 640, 1024), ("affine8", 129, 300, 128),
                                        ("affine8", 1, 257, 4096)])
@@ -470,6 +471,21 @@ def test_gemm_image_equals_mfma_path(fmt, M, N, K):
         assert torch.equal(got, want), (fmt, M, N, K, "unsplit")
     finally:
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+
+
+def test_q4_gemm_equals_image_at_prefill_size():
+    """q4_gemm with a workspace (the weight image built per call) gives the
+    bits of q4_gemm_image on a weight image prepared once, at the prefill
+    shape (M = 2048, N = 12288, K = 4096) and on a ragged one."""
+    rng = np.random.default_rng(11)
+    for M, N, K in ((2048, 12288, 4096), (2000, 12300, 4096)):
+        say(f"per-call vs prepared image M={M} N={N} K={K}")
+        qs, d = B.q4_quantize(torch.from_numpy(synth.weights(rng, N, K)).cuda())
+        x = bf16_dev(synth.activations(rng, M, K))
+        ws = torch.empty(B.q4_gemm_workspace_size(M, N, K), dtype=torch.uint8, device="cuda")
+        want = B.q4_gemm_image(B.q4_pack_weight_image(qs, d), x, N, workspace=ws)
+        got = B.q4_gemm(qs, d, x, workspace=ws)
+        assert torch.equal(got, want), (M, N, K)
 
 
 @pytest.mark.parametrize("M", [1, 17, 64, 65, 300])
