@@ -133,12 +133,37 @@ struct Q8Strided {
 // to nearest even), the same on all 8 lanes.  The standalone quantiser and
 // the GEMV that quantises its own activation both use it, so they give the
 // same bits.
+//
+// The two binary32 divisions it needs (amax / 127, then 1 / d8) are taken
+// through binary64, in a third of the instructions of a binary32 division
+// and with the same result for every binary32 input:
+//  * a / 127: a binary32 quotient a/127 lies at least 2^-32 (relative) from
+//    every binary32 rounding midpoint (a - 127 mid is an odd multiple of the
+//    midpoint spacing), and the binary64 product a * RN(1/127) is within
+//    2^-52 of it, so rounding that product to binary32 rounds the quotient;
+//  * 1 / d: 1/d lies at least about 2^-48 (relative) from every binary32
+//    midpoint, and the binary64 reciprocal (v_rcp_f64, within 2^-22) after
+//    two Newton steps is within about 2^-52 of it.
+// Both were also checked against binary32 division for every non-negative
+// finite binary32 input, the reciprocal with a start 2^-22 off in either
+// direction and no fused multiply-add (tests/test_q8_division_routes.py
+// runs a sample of that sweep).
+__device__ __forceinline__ float div127_rne(float a) { return (float)((double)a * (1.0 / 127.0)); }
+__device__ __forceinline__ float rcp_rne(float d) {
+    const double x = (double)d;
+    double r = __builtin_amdgcn_rcp(x);
+    double e = __builtin_fma(-x, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    e = __builtin_fma(-x, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    return (float)r;
+}
 template <class G, bool WANT_S>
 __device__ __forceinline__ uint32_t q8_1_block(const float (&v)[4], uint32_t& d16, uint32_t& s16) {
     float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
     amax = G::max8(amax);
-    const float dd = amax / 127.0f;
-    const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+    const float dd = div127_rne(amax);                 // amax / 127
+    const float id = (dd != 0.0f) ? rcp_rne(dd) : 0.0f;   // 1 / dd
     int q[4];
     int sum = 0;
 #pragma unroll
