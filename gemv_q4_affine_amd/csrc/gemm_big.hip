@@ -240,8 +240,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
     auto swap_pair = [](float x) __attribute__((always_inline)) {
         return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
     };
-    auto store_tile = [&](int m0, int nw0, auto ntc) __attribute__((always_inline)) {
+    // A tile wholly inside Y (with N even) takes a path with no bounds test:
+    // every pair store is in bounds and aligned, and a lane's stores advance
+    // by fixed multiples of N from one base address.
+    auto store_tile_w = [&](int m0, int nw0, auto ntc, auto whole_c) __attribute__((always_inline)) {
         constexpr int NT = decltype(ntc)::value;
+        constexpr bool kWhole = decltype(whole_c)::value;
         const int ln = big_lane_now();
         const int j = ln & 31, g = ln >> 5;
         const bool odd = (ln & 1) != 0;
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
             // the X image's exponents of sub-tile mi through the scalar cache
             // (the table covers 128-row tiles: a sub-tile wholly past M reads
             // none and stores nothing), then this lane's 8
-            if (m0 + mi * 32 >= a.M) continue;
+            if (!kWhole && m0 + mi * 32 >= a.M) continue;
             using const_u32 = __attribute__((address_space(4))) const uint32_t;
             const const_u32* sp = (const const_u32*)(a.xexp + m0 + mi * 32);
             uint32_t w[8];
@@ -260,9 +264,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
             u32x2_t ex;
             ex[0] = c == 0 ? w[0] : c == 1 ? w[2] : c == 2 ? w[4] : w[6];
             ex[1] = c == 0 ? w[1] : c == 1 ? w[3] : c == 2 ? w[5] : w[7];
+            const int r0 = m0 + mi * 32 + 4 * g + (odd ? 1 : 0);
 #pragma unroll
             for (int ni = 0; ni < NT; ni++) {
                 const int col = nw0 + ni * 32 + (j & ~1);
+                const int64_t base = (int64_t)r0 * a.N + col;
 #pragma unroll
                 for (int e = 0; e < 16; e += 2) {
                     const float a0v = acc[mi][ni][e], a1v = acc[mi][ni][e + 1];
@@ -271,12 +277,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
                     const int ue = -xexp_of(ex, e >> 2, (e >> 1) & 1);
                     const float lo_v = ldexpf(odd ? d1 : a0v, ue);
                     const float hi_v = ldexpf(odd ? a1v : d0, ue);
-                    const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3) + (odd ? 1 : 0);
-                    if (row >= a.M || col >= a.N) continue;
-                    const int64_t off = (int64_t)row * a.N + col;
+                    const int dr = 8 * (e >> 2) + (e & 3);
+                    if (!kWhole && (r0 + dr >= a.M || col >= a.N)) continue;
+                    const int64_t off = base + (int64_t)dr * a.N;
+                    const bool pair = kWhole || (pair_ok && col + 1 < a.N);
                     if constexpr (YDT == DT_BF16) {
                         uint16_t* yp = reinterpret_cast<uint16_t*>(a.y) + off;
-                        if (pair_ok && col + 1 < a.N) {
+                        if (pair) {
                             const f32x2_t f = {lo_v, hi_v};
                             *reinterpret_cast<uint32_t*>(yp) =
                                 __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
                         }
                     } else {
                         float* yp = reinterpret_cast<float*>(a.y) + off;
-                        if (pair_ok && col + 1 < a.N) {
+                        if (pair) {
                             *reinterpret_cast<f32x2_t*>(yp) = f32x2_t{lo_v, hi_v};
                         } else {
                             yp[0] = lo_v;
@@ -297,6 +304,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(const BigArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+    auto store_tile = [&](int m0, int nw0, auto ntc) __attribute__((always_inline)) {
+        constexpr int NT = decltype(ntc)::value;
+        const bool whole = m0 + kBigRows <= a.M && nw0 + 32 * NT <= a.N && pair_ok;   // this wave's columns
+        if (whole) store_tile_w(m0, nw0, ntc, std::true_type{});
+        else store_tile_w(m0, nw0, ntc, std::false_type{});
     };
 
     // ---- one unit: S steps of one tile, NT = 2 (whole) or 1 (column half) ------
