@@ -21,7 +21,11 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 // ---- dispatch settings -----------------------------------------------------
 // Defaults come from the measured crossovers of this library on MI355X.
 constexpr int64_t kSkinnyLimit = 64;          // the skinny kernel's largest M
-std::atomic<int64_t> g_skinny_max_m{32};
+std::atomic<int64_t> g_skinny_max_m{64};
+// binary32 activations: the small-M kernels take bfloat16 X, and the binary32
+// skinny kernel beats the matrix-core GEMM only up to this many rows, so an
+// automatic SKINNY choice above it runs the matrix-core GEMM
+constexpr int64_t kF32SkinnyMaxM = 16;
 std::atomic<int64_t> g_dequant_min_m{kMaxDim + 1};   // dequantise-then-GEMM never wins by default
 std::atomic<int64_t> g_force_path{-1};
 std::atomic<int64_t> g_tile_rows{128};
@@ -187,6 +191,9 @@ int64_t q4_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int fmt) {
     if (fmt == Q4_FMT_AFFINE8) return affine8_gemm_workspace_size(M, N, K);
     const int path = q4_dispatch_path(M, N, K, fmt, 1);
     if (path == Q4_PATH_MFMA) return q4::packed_x_bytes(M, N, K);
+    // an automatic SKINNY choice above kF32SkinnyMaxM rows runs the
+    // matrix-core GEMM for binary32 X: room for it (bfloat16 X uses none)
+    if (path == Q4_PATH_SKINNY && g_force_path < 0 && M > kF32SkinnyMaxM) return q4::packed_x_bytes(M, N, K);
     if (path == Q4_PATH_DEQUANT_GEMM) return N * K * 2;
     if (path == Q4_PATH_INT8 && fmt == Q4_FMT_Q4_0) return q8_planes_bytes(M, K);
     return 0;
@@ -350,9 +357,10 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
     const int fmt = (wf == q4::WF_Q4_0) ? Q4_FMT_Q4_0 : Q4_FMT_AFFINE4;
     // "have workspace" for the dispatch: enough for the dequantised weights
     const bool have_ws = workspace != nullptr && workspace_bytes >= N * K * 2;
-    const int path = q4_dispatch_path(M, N, K, fmt, have_ws ? 1 : 0);
+    int path = q4_dispatch_path(M, N, K, fmt, have_ws ? 1 : 0);
     if (path < 0) return path;
     if (M == 0 || N == 0) return Q4_OK;
+    if (path == Q4_PATH_SKINNY && g_force_path < 0 && x_dtype == Q4_F32 && M > kF32SkinnyMaxM) path = Q4_PATH_MFMA;
     hipStream_t s = as_stream(stream);
     switch (path) {
         case Q4_PATH_GEMV: {

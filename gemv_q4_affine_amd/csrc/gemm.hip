@@ -2396,7 +2396,7 @@ static void launch_small_w(GemmArgs ga, int ydt, hipStream_t s) {
     else launch_small_m<WF, DT_F32>(ga, s);
 }
 
-constexpr int kVecMaxM = 1;   // the skinny path's vector kernel serves M == 1 (MFMA beyond)
+constexpr int kVecMaxM = 1;   // the skinny path's vector kernel serves M == 1 (the small-M kernel beyond)
 
 hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
                               int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
@@ -2405,6 +2405,28 @@ hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void
     ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
     ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
     const bool small = xdt == DT_BF16 && M > kVecMaxM && M <= kSmMaxM;
+    if (xdt == DT_BF16 && M > kSmMaxM && (wfmt == WF_Q4_0 || wfmt == WF_AFFINE4)) {
+        // more rows than the small-M kernel takes: row chunks of at most
+        // kSmMaxM, each run as a call of that many rows would run (a last
+        // single row on the vector kernel) and each streaming the weights
+        // again (up to 64 rows that beats the matrix-core GEMM with its
+        // per-call images)
+        const int ysz = ydt == DT_BF16 ? 2 : 4;
+        for (int64_t r = 0; r < M; r += kSmMaxM) {
+            GemmArgs gc = ga;
+            gc.M = (int)(M - r < kSmMaxM ? M - r : kSmMaxM);
+            gc.x = static_cast<const uint16_t*>(x) + r * K;
+            gc.y = static_cast<uint8_t*>(y) + r * N * ysz;
+            if (gc.M <= kVecMaxM) {
+                if (wfmt == WF_Q4_0) launch_vec_w<WF_Q4_0>(gc, xdt, ydt, s);
+                else launch_vec_w<WF_AFFINE4>(gc, xdt, ydt, s);
+            } else {
+                if (wfmt == WF_Q4_0) launch_small_w<WF_Q4_0>(gc, ydt, s);
+                else launch_small_w<WF_AFFINE4>(gc, ydt, s);
+            }
+        }
+        return hipGetLastError();
+    }
     if (M <= kVecMaxM && wfmt == WF_Q4_0) launch_vec_w<WF_Q4_0>(ga, xdt, ydt, s);
     else if (M <= kVecMaxM && wfmt == WF_AFFINE4) launch_vec_w<WF_AFFINE4>(ga, xdt, ydt, s);
     else if (small && wfmt == WF_Q4_0) launch_small_w<WF_Q4_0>(ga, ydt, s);

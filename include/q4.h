@@ -89,7 +89,9 @@ extern "C" {
 #define Q4_PATH_INT8          4  /* X quantised to Q8_1, int8 MFMA GEMM (q4_gemm_q8)     */
 
 /* dispatch keys for q4_set_dispatch / q4_get_dispatch */
-#define Q4_KEY_SKINNY_MAX_M    0  /* q4_gemm/affine4_gemm: M <= this -> SKINNY          */
+#define Q4_KEY_SKINNY_MAX_M    0  /* q4_gemm/affine4_gemm: M <= this -> SKINNY (default
+                                     64; with binary32 X the automatic choice takes
+                                     MFMA above 16 rows)                               */
 #define Q4_KEY_DEQUANT_MIN_M   1  /* M >= this (and workspace given) -> DEQUANT_GEMM    */
 #define Q4_KEY_FORCE_PATH      2  /* -1 = automatic, else a Q4_PATH_* for q4_gemm etc.;
                                      GEMV and INT8 compute on X quantised to Q8_1 and
@@ -277,8 +279,8 @@ int q4_gemv_multi_act(int nmat, const uint8_t* const* w_qs, const uint16_t* cons
  *   - the paths without an X image (SKINNY with binary32 X, MFMA with too
  *     little workspace, DEQUANT_GEMM) convert X directly: exact for bfloat16
  *     values with 2^-17 <= |x| <= 65504; |x| > 65504 becomes +-inf.  The SKINNY
- *     path with bfloat16 X (2 <= M <= 32) multiplies in bfloat16 and has the
- *     whole range.
+ *     path with bfloat16 X (2 <= M <= 64; above 32 rows on row chunks of at
+ *     most 32) multiplies in bfloat16 and has the whole range.
  *   x         : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32)
  *   y         : device out, [M][N] of y_dtype (Q4_BF16 RNE, or Q4_F32)
  *   workspace : device scratch owned by the caller (16-byte aligned), or
@@ -382,7 +384,9 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
 
 /*
  * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
- * 0 for SKINNY and GEMV; M*K + M*(K/32)*4 (the Q8_1 planes of X) for INT8;
+ * 0 for SKINNY and GEMV (but an automatic SKINNY choice above 16 rows asks
+ * for the MFMA bytes below: binary32 X takes the MFMA path there; bfloat16 X
+ * uses none of them); M*K + M*(K/32)*4 (the Q8_1 planes of X) for INT8;
  * for MFMA the X and weight tile images,
  * ceil(M/128)*128 * (ceil(K/64)*64 * 2 + 1) + ceil(N/256) * ceil(K/64) * 9216
  * bytes (the X image holds one exponent byte per row after its tiles),

@@ -402,9 +402,11 @@ print(B.q4_get_dispatch(B.Q4_KEY_SKINNY_MAX_M), B.q4_get_dispatch(B.Q4_KEY_DEQUA
     ({"Q4_FORCE_PATH": "3"}, (None, None, 3, B.Q4_PATH_DEQUANT_GEMM, B.Q4_PATH_DEQUANT_GEMM)),
     ({"Q4_FORCE_PATH": "0"}, (None, None, 0, B.Q4_PATH_GEMV, B.Q4_PATH_GEMV, 0)),
     ({"Q4_FORCE_PATH": "4"}, (None, None, 4, B.Q4_PATH_INT8, B.Q4_PATH_INT8, 1)),
-    # values the setter rejects leave the automatic dispatch (17: no such path)
-    ({"Q4_FORCE_PATH": "17"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
-    ({"Q4_FORCE_PATH": "-5"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_MFMA)),
+    # values the setter rejects leave the automatic dispatch (17: no such path;
+    # SKINNY up to 64 rows, with room for the MFMA path that binary32 X takes
+    # above 16)
+    ({"Q4_FORCE_PATH": "17"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_SKINNY, 1)),
+    ({"Q4_FORCE_PATH": "-5"}, (None, None, -1, B.Q4_PATH_SKINNY, B.Q4_PATH_SKINNY, 1)),
     ({"Q4_FORCE_PATH": "junk"}, (None, None, -1, None, None)),
     ({"Q4_AFFINE8_FUSED_MAX_M": "16"}, (None, None, -1, None, None, None, 16, B.Q4_PATH_MFMA)),
     ({"Q4_AFFINE8_FUSED_MAX_M": "99"}, (None, None, -1, None, None, None, 32, B.Q4_PATH_SKINNY)),

@@ -473,6 +473,52 @@ def test_gemm_image_equals_mfma_path(fmt, M, N, K):
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
 
 
+@pytest.mark.parametrize("fmt", ["q4_0", "affine"])
+def test_small_m_row_chunks(fmt):
+    """Above 32 rows, bf16 X runs the small-M kernel on row chunks of at most
+    32: every chunk's rows are bit-identical to a call on those rows alone,
+    the whole result is within the bar of the oracle, and with binary32 X the
+    automatic choice above 16 rows is the matrix-core GEMM (bit-identical to
+    it forced, with the workspace the size query asks for)."""
+    rng = np.random.default_rng(21)
+    N, K = 700, 1024
+    W = synth.weights(rng, N, K)
+    if fmt == "q4_0":
+        qs, d = oracle.q4_0_quantize(W)
+        planes = [dev(qs), dev(d)]
+        ref_w = oracle.q4_0_dequantize(qs, d)
+        run = lambda x, **kw: B.q4_gemm(*planes, x, **kw)
+        f = B.Q4_FMT_Q4_0
+    else:
+        ap = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+        planes = [dev(a) for a in ap]
+        ref_w = oracle.affine4_dequantize(*ap, 64)
+        run = lambda x, **kw: B.affine4_gemm(*planes, x, **kw)
+        f = B.Q4_FMT_AFFINE4
+    assert B.q4_dispatch_path(64, N, K, f) == B.Q4_PATH_SKINNY
+    for M in (33, 40, 64):
+        say(f"small-M row chunks {fmt} M={M}")
+        X = synth.activations(rng, M, K)
+        x = bf16_dev(X)
+        for ydt in (torch.bfloat16, torch.float32):
+            y = run(x, y_dtype=ydt, workspace=None)
+            for r in range(0, M, 32):
+                part = run(x[r:r + 32].contiguous(), y_dtype=ydt, workspace=None)
+                assert torch.equal(y[r:r + 32], part), (fmt, M, r, ydt)
+            ref = oracle.matmul_f64(synth.bf16_bits_to_f32(synth.bf16_bits(X)).astype(np.float64), ref_w)
+            assert rel(out_f64(y), ref) <= BAR, (fmt, M, ydt)
+        # binary32 X above 16 rows: the matrix-core GEMM
+        xf = torch.from_numpy(X).cuda()
+        ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
+        auto = run(xf, y_dtype=torch.float32, workspace=ws)
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
+        try:
+            forced = run(xf, y_dtype=torch.float32, workspace=ws)
+        finally:
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+        assert torch.equal(auto, forced), (fmt, M)
+
+
 def test_q4_gemm_equals_image_at_prefill_size():
     """q4_gemm with a workspace (the weight image built per call) gives the
     bits of q4_gemm_image on a weight image prepared once, at the prefill
@@ -1040,19 +1086,23 @@ def test_splitk_odd_output_count():
     imgs = B.q4_gemm_image_workspace_size(M, K) + B.q4_weight_image_size(N, K)
     assert full > imgs, "this shape should split K"
     ys = {}
-    for name, nbytes in (("split", full), ("unsplit", imgs)):
-        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)       # warm
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        ys[name] = B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1)
-        say(f"  {name}: {ms:.3f} ms")
-        assert ms < 20.0, (name, ms)
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)     # 33 rows would run the small-M kernel
+    try:
+        for name, nbytes in (("split", full), ("unsplit", imgs)):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)       # warm
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            ys[name] = B.q4_gemm(tq, td, tx, y_dtype=torch.float32, workspace=ws)
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1)
+            say(f"  {name}: {ms:.3f} ms")
+            assert ms < 20.0, (name, ms)
+    finally:
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
     ref = _q4_gemm_ref(qs, d, synth.bf16_bits_to_f32(xb).astype(np.float64))
     for name, y in ys.items():
         assert rel(out_f64(y), ref) <= 1e-3, name
@@ -1255,6 +1305,7 @@ def test_wide_range_x_on_the_image_path(fmt, M, N, K, xdt, tile_rows):
     tp = [dev(a) for a in planes]
     ref = Xf64 @ What.T
     B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, tile_rows)
+    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)     # M = 64 would run the small-M kernel
     try:
         assert B.q4_dispatch_path(M, N, K, f, True) == B.Q4_PATH_MFMA
         ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
@@ -1267,6 +1318,7 @@ def test_wide_range_x_on_the_image_path(fmt, M, N, K, xdt, tile_rows):
         torch.cuda.synchronize()
     finally:
         B.q4_set_dispatch(B.Q4_KEY_TILE_ROWS, 128)
+        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
     got = out_f64(y)
     assert np.isfinite(got).all()
     e = _per_row_rel(got, ref)
