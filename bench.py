@@ -509,7 +509,7 @@ def affine8_section(iters: int):
 # small M: q4_gemm / affine4_gemm on the skinny paths
 # ---------------------------------------------------------------------------
 
-SMALL_MS = (1, 2, 4, 8, 16, 32)
+SMALL_MS = (1, 2, 4, 8, 16, 32, 48, 64)
 
 
 def small_section(iters: int):
