@@ -612,6 +612,44 @@ def test_affine4_gemm_sweep_sampled(M):
     assert e <= BAR
 
 
+
+_PREFILL_W = {}
+
+
+def _prefill_weights(fmt):
+    """The prefill shape's weights in one format, quantised by the oracle once."""
+    if fmt not in _PREFILL_W:
+        W, _ = synth.workload_inputs(synth.PREFILL, M=0)
+        if fmt == "q4_0":
+            planes = oracle.q4_0_quantize(W)
+            _PREFILL_W[fmt] = (planes, oracle.q4_0_dequantize(*planes))
+        else:
+            planes = oracle.affine4_quantize(synth.bf16_bits(W), 64)
+            _PREFILL_W[fmt] = (planes, oracle.affine4_dequantize(*planes, 64))
+    return _PREFILL_W[fmt]
+
+
+@pytest.mark.parametrize("fmt,M", [("q4_0", 2), ("q4_0", 16), ("q4_0", 48), ("q4_0", 64),
+                                   ("affine4", 16), ("affine4", 48), ("affine4", 64)])
+def test_small_m_prefill_shape_sampled(fmt, M):
+    """The small-M sweep at N = 12288, K = 4096 as it is timed (bf16 X and Y,
+    no workspace; 48 and 64 rows run as 32-row chunks): sampled outputs
+    against the binary64 product with the dequantised weights."""
+    wl = synth.PREFILL
+    say(f"small-M {fmt} M={M} N={wl.N} K={wl.K}")
+    planes, What = _prefill_weights(fmt)
+    f = B.Q4_FMT_Q4_0 if fmt == "q4_0" else B.Q4_FMT_AFFINE4
+    assert B.q4_dispatch_path(M, wl.N, wl.K, f) == B.Q4_PATH_SKINNY
+    X = synth.activations(np.random.default_rng(300 + M), M, wl.K)
+    xb = synth.bf16_bits(X)
+    tx = dev(xb).view(torch.bfloat16)
+    gemm = B.q4_gemm if fmt == "q4_0" else B.affine4_gemm
+    y = gemm(*[dev(a) for a in planes], tx, y_dtype=torch.bfloat16, workspace=None)
+    torch.cuda.synchronize()
+    e = _sampled_check(y, synth.bf16_bits_to_f32(xb).astype(np.float64), What, 100 + M)
+    say(f"  sampled rel err {e:.3e}")
+    assert e <= BAR
+
 def test_gemm_deterministic_and_row_permutation():
     M, N, K = 600, 512, 2048
     rng = np.random.default_rng(44)
