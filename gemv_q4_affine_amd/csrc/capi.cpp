@@ -23,9 +23,12 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int64_t kSkinnyLimit = 64;          // the skinny kernel's largest M
 std::atomic<int64_t> g_skinny_max_m{64};
 // binary32 activations: the small-M kernels take bfloat16 X, and the binary32
-// skinny kernel beats the matrix-core GEMM only up to this many rows, so an
-// automatic SKINNY choice above it runs the matrix-core GEMM
+// skinny kernel beats the matrix-core GEMM on its X and weight images only up
+// to kF32SkinnyMaxM rows (without room for the images, the GEMM converting X
+// in the kernel is slower than the skinny kernel up to kF32SkinnyNoImageMaxM
+// rows), so an automatic SKINNY choice above those runs the matrix-core GEMM
 constexpr int64_t kF32SkinnyMaxM = 16;
+constexpr int64_t kF32SkinnyNoImageMaxM = 32;
 std::atomic<int64_t> g_dequant_min_m{kMaxDim + 1};   // dequantise-then-GEMM never wins by default
 std::atomic<int64_t> g_force_path{-1};
 std::atomic<int64_t> g_tile_rows{128};
@@ -360,7 +363,11 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
     int path = q4_dispatch_path(M, N, K, fmt, have_ws ? 1 : 0);
     if (path < 0) return path;
     if (M == 0 || N == 0) return Q4_OK;
-    if (path == Q4_PATH_SKINNY && g_force_path < 0 && x_dtype == Q4_F32 && M > kF32SkinnyMaxM) path = Q4_PATH_MFMA;
+    if (path == Q4_PATH_SKINNY && g_force_path < 0 && x_dtype == Q4_F32 && M > kF32SkinnyMaxM) {
+        const bool have_images =
+            workspace != nullptr && workspace_bytes >= q4::x_image_bytes(M, K) + q4::weight_image_bytes(N, K);
+        if (have_images || M > kF32SkinnyNoImageMaxM) path = Q4_PATH_MFMA;
+    }
     hipStream_t s = as_stream(stream);
     switch (path) {
         case Q4_PATH_GEMV: {

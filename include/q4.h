@@ -91,7 +91,8 @@ extern "C" {
 /* dispatch keys for q4_set_dispatch / q4_get_dispatch */
 #define Q4_KEY_SKINNY_MAX_M    0  /* q4_gemm/affine4_gemm: M <= this -> SKINNY (default
                                      64; with binary32 X the automatic choice takes
-                                     MFMA above 16 rows)                               */
+                                     MFMA above 16 rows when the workspace holds the
+                                     MFMA images, above 32 rows otherwise)             */
 #define Q4_KEY_DEQUANT_MIN_M   1  /* M >= this (and workspace given) -> DEQUANT_GEMM    */
 #define Q4_KEY_FORCE_PATH      2  /* -1 = automatic, else a Q4_PATH_* for q4_gemm etc.;
                                      GEMV and INT8 compute on X quantised to Q8_1 and
@@ -385,8 +386,8 @@ int affine8_gemm(const uint8_t* w_q, const uint16_t* scales, const uint16_t* bia
 /*
  * Bytes of workspace for the path q4_dispatch_path(M, N, K, fmt, 1) picks:
  * 0 for SKINNY and GEMV (but an automatic SKINNY choice above 16 rows asks
- * for the MFMA bytes below: binary32 X takes the MFMA path there; bfloat16 X
- * uses none of them); M*K + M*(K/32)*4 (the Q8_1 planes of X) for INT8;
+ * for the MFMA bytes below: given them, binary32 X takes the MFMA path there;
+ * bfloat16 X uses none of them); M*K + M*(K/32)*4 (the Q8_1 planes of X) for INT8;
  * for MFMA the X and weight tile images,
  * ceil(M/128)*128 * (ceil(K/64)*64 * 2 + 1) + ceil(N/256) * ceil(K/64) * 9216
  * bytes (the X image holds one exponent byte per row after its tiles),

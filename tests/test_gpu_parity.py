@@ -479,7 +479,8 @@ def test_small_m_row_chunks(fmt):
     32: every chunk's rows are bit-identical to a call on those rows alone,
     the whole result is within the bar of the oracle, and with binary32 X the
     automatic choice above 16 rows is the matrix-core GEMM (bit-identical to
-    it forced, with the workspace the size query asks for)."""
+    it forced) with the workspace the size query asks for, and without a
+    workspace the skinny kernel up to 32 rows and the GEMM above."""
     rng = np.random.default_rng(21)
     N, K = 700, 1024
     W = synth.weights(rng, N, K)
@@ -507,16 +508,23 @@ def test_small_m_row_chunks(fmt):
                 assert torch.equal(y[r:r + 32], part), (fmt, M, r, ydt)
             ref = oracle.matmul_f64(synth.bf16_bits_to_f32(synth.bf16_bits(X)).astype(np.float64), ref_w)
             assert rel(out_f64(y), ref) <= BAR, (fmt, M, ydt)
-        # binary32 X above 16 rows: the matrix-core GEMM
-        xf = torch.from_numpy(X).cuda()
+    # binary32 X above 16 rows: the matrix-core GEMM when the workspace holds
+    # its images; without them the skinny kernel up to 32 rows, the GEMM above
+    for M in (24, 33, 64):
+        xf = torch.from_numpy(synth.activations(rng, M, K)).cuda()
         ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
         auto = run(xf, y_dtype=torch.float32, workspace=ws)
+        auto_none = run(xf, y_dtype=torch.float32, workspace=None)
         B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
         try:
             forced = run(xf, y_dtype=torch.float32, workspace=ws)
+            forced_none = run(xf, y_dtype=torch.float32, workspace=None)
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_SKINNY)
+            skinny = run(xf, y_dtype=torch.float32, workspace=None)
         finally:
             B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
         assert torch.equal(auto, forced), (fmt, M)
+        assert torch.equal(auto_none, skinny if M <= 32 else forced_none), (fmt, M)
 
 
 def test_q4_gemm_equals_image_at_prefill_size():
