@@ -1,6 +1,7 @@
 """Benchmark of the 4-bit GEMV / GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--sections decode,gemm,affine,affine8,small,llama,cpu]
+                    (also: crossover, calib; not in the default run)
 
 A step is one decode token through the decode-GEMV workload (Q4_0 W
 [12288, 4096], one bf16 activation [1, 4096] ~ N(0,1)): q4_gemv_act on W and
@@ -558,6 +559,61 @@ def small_section(iters: int):
     return {"N": N, "K": K, "copies": copies, "sweep": out}
 
 
+CROSS_MS = (16, 17, 24, 32, 33, 40, 48, 64, 65, 96, 128, 129)
+
+
+def crossover_section(iters: int):
+    """q4_gemm and affine4_gemm on N=12288, K=4096 around the skinny / matrix-core
+    crossover: the automatic choice and each path forced, on bf16 and binary32
+    X, with the workspace q4_gemm_workspace_size asks for and without one.
+    These are the measurements the default thresholds rest on (not a default
+    section: the bench line does not use them)."""
+    wl = synth.PREFILL
+    N, K = wl.N, wl.K
+    rng = np.random.default_rng(wl.seed)
+    wd = bf16_dev(synth.weights(rng, N, K))
+    copies = 10
+    fmts = {"q4_0": (B.Q4_FMT_Q4_0, B.q4_gemm, B.q4_quantize(wd)),
+            "affine4": (B.Q4_FMT_AFFINE4, B.affine4_gemm, B.affine4_quantize(wd))}
+    del wd
+    out = []
+    for M in CROSS_MS:
+        X = synth.activations(rng, M, K)
+        xs = {"bf16": bf16_dev(X), "f32": torch.from_numpy(X).cuda()}
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        for name, (f, gemm, planes) in fmts.items():
+            rot = [tuple(t.clone() for t in planes) for _ in range(copies)]
+            ws = torch.empty(max(16, B.q4_gemm_workspace_size(M, N, K, f)), dtype=torch.uint8, device="cuda")
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
+            try:
+                nm = B.q4_gemm_workspace_size(M, N, K, f)      # the matrix-core path's bytes
+            finally:
+                B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+            wsm = torch.empty(max(16, nm), dtype=torch.uint8, device="cuda")
+            for xn, x in xs.items():
+                rec = {"M": M, "format": name, "x": xn}
+
+                def t(force, w):
+                    B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, force)
+                    try:
+                        return round(min(region_us(lambda i: gemm(*rot[i % copies], x, y=y, workspace=w), iters)
+                                         for _ in range(2)), 2)
+                    finally:
+                        B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+
+                rec["auto_ws_us"] = t(-1, ws)
+                rec["auto_no_ws_us"] = t(-1, None)
+                rec["skinny_us"] = t(B.Q4_PATH_SKINNY, None) if M <= 64 else None
+                rec["mfma_images_us"] = t(B.Q4_PATH_MFMA, wsm)
+                rec["mfma_no_ws_us"] = t(B.Q4_PATH_MFMA, None)
+                out.append(rec)
+                log(f"[crossover] {name} {xn} M={M}: auto {rec['auto_ws_us']} (no workspace "
+                    f"{rec['auto_no_ws_us']}), skinny {rec['skinny_us']}, matrix-core on images "
+                    f"{rec['mfma_images_us']}, without {rec['mfma_no_ws_us']} us")
+            del rot
+    return {"N": N, "K": K, "copies": copies, "sweep": out}
+
+
 # ---------------------------------------------------------------------------
 # Llama-3.2-1B-shaped 16-layer stack
 # ---------------------------------------------------------------------------
@@ -834,6 +890,8 @@ def main():
         extra["small_m"] = small_section(100)
     if "llama" in sections:
         extra["llama1b_stack"] = llama_section(20)
+    if "crossover" in sections:
+        extra["small_m_crossover"] = crossover_section(40)
     if "calib" in sections:
         extra["counter_calibration"] = calib_section()
     cpu = cpu_baseline(args.cpu_seconds) if "cpu" in sections else None

@@ -29,6 +29,10 @@ std::atomic<int64_t> g_skinny_max_m{64};
 // rows), so an automatic SKINNY choice above those runs the matrix-core GEMM
 constexpr int64_t kF32SkinnyMaxM = 16;
 constexpr int64_t kF32SkinnyNoImageMaxM = 32;
+// bfloat16 activations with no room for the matrix-core GEMM's images: the
+// small-M kernel on 32-row chunks beats the GEMM converting X in the kernel
+// up to this many rows (while the skinny range is left at its full width)
+constexpr int64_t kBf16ChunkNoImageMaxM = 128;
 std::atomic<int64_t> g_dequant_min_m{kMaxDim + 1};   // dequantise-then-GEMM never wins by default
 std::atomic<int64_t> g_force_path{-1};
 std::atomic<int64_t> g_tile_rows{128};
@@ -363,11 +367,14 @@ static int gemm_common(int wf, const void* a, const void* b, const void* c, cons
     int path = q4_dispatch_path(M, N, K, fmt, have_ws ? 1 : 0);
     if (path < 0) return path;
     if (M == 0 || N == 0) return Q4_OK;
-    if (path == Q4_PATH_SKINNY && g_force_path < 0 && x_dtype == Q4_F32 && M > kF32SkinnyMaxM) {
-        const bool have_images =
-            workspace != nullptr && workspace_bytes >= q4::x_image_bytes(M, K) + q4::weight_image_bytes(N, K);
-        if (have_images || M > kF32SkinnyNoImageMaxM) path = Q4_PATH_MFMA;
-    }
+    const bool have_images =
+        workspace != nullptr && workspace_bytes >= q4::x_image_bytes(M, K) + q4::weight_image_bytes(N, K);
+    if (path == Q4_PATH_SKINNY && g_force_path < 0 && x_dtype == Q4_F32 && M > kF32SkinnyMaxM &&
+        (have_images || M > kF32SkinnyNoImageMaxM))
+        path = Q4_PATH_MFMA;
+    if (path == Q4_PATH_MFMA && g_force_path < 0 && x_dtype == Q4_BF16 && !have_images && M > kSkinnyLimit &&
+        M <= kBf16ChunkNoImageMaxM && g_skinny_max_m >= kSkinnyLimit)
+        return hip_status(q4::launch_gemm_skinny(wf, a, b, c, x, x_dtype, y, y_dtype, M, N, K, as_stream(stream)));
     hipStream_t s = as_stream(stream);
     switch (path) {
         case Q4_PATH_GEMV: {

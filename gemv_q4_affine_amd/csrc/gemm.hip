@@ -2396,16 +2396,18 @@ static void launch_small_w(GemmArgs ga, int ydt, hipStream_t s) {
     else launch_small_m<WF, DT_F32>(ga, s);
 }
 
+constexpr int kSmChunkMaxM = 128;   // most rows the skinny path takes as row chunks
 constexpr int kVecMaxM = 1;   // the skinny path's vector kernel serves M == 1 (the small-M kernel beyond)
 
 hipError_t launch_gemm_skinny(int wfmt, const void* a, const void* b, const void* c, const void* x, int xdt, void* y,
                               int ydt, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-    if (M > 64) return hipErrorInvalidValue;
+    const bool chunks = xdt == DT_BF16 && M > kSmMaxM && (wfmt == WF_Q4_0 || wfmt == WF_AFFINE4);
+    if (M > (chunks ? kSmChunkMaxM : 64)) return hipErrorInvalidValue;
     GemmArgs ga{};
     ga.a = a; ga.b = b; ga.c = c; ga.x = x; ga.y = y;
     ga.M = (int)M; ga.N = (int)N; ga.K = (int)K;
     const bool small = xdt == DT_BF16 && M > kVecMaxM && M <= kSmMaxM;
-    if (xdt == DT_BF16 && M > kSmMaxM && (wfmt == WF_Q4_0 || wfmt == WF_AFFINE4)) {
+    if (chunks) {
         // more rows than the small-M kernel takes: row chunks of at most
         // kSmMaxM, each run as a call of that many rows would run (a last
         // single row on the vector kernel) and each streaming the weights

@@ -92,7 +92,10 @@ extern "C" {
 #define Q4_KEY_SKINNY_MAX_M    0  /* q4_gemm/affine4_gemm: M <= this -> SKINNY (default
                                      64; with binary32 X the automatic choice takes
                                      MFMA above 16 rows when the workspace holds the
-                                     MFMA images, above 32 rows otherwise)             */
+                                     MFMA images, above 32 rows otherwise; with
+                                     bfloat16 X and no room for the images, an
+                                     automatic MFMA choice up to 128 rows runs the
+                                     SKINNY row chunks while this is 64)               */
 #define Q4_KEY_DEQUANT_MIN_M   1  /* M >= this (and workspace given) -> DEQUANT_GEMM    */
 #define Q4_KEY_FORCE_PATH      2  /* -1 = automatic, else a Q4_PATH_* for q4_gemm etc.;
                                      GEMV and INT8 compute on X quantised to Q8_1 and
@@ -281,7 +284,8 @@ int q4_gemv_multi_act(int nmat, const uint8_t* const* w_qs, const uint16_t* cons
  *     little workspace, DEQUANT_GEMM) convert X directly: exact for bfloat16
  *     values with 2^-17 <= |x| <= 65504; |x| > 65504 becomes +-inf.  The SKINNY
  *     path with bfloat16 X (2 <= M <= 64; above 32 rows on row chunks of at
- *     most 32) multiplies in bfloat16 and has the whole range.
+ *     most 32; up to 128 rows when the MFMA path has no room for its images)
+ *     multiplies in bfloat16 and has the whole range.
  *   x         : device, [M][K] of x_dtype (Q4_BF16 or Q4_F32)
  *   y         : device out, [M][N] of y_dtype (Q4_BF16 RNE, or Q4_F32)
  *   workspace : device scratch owned by the caller (16-byte aligned), or

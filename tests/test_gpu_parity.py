@@ -476,7 +476,9 @@ def test_gemm_image_equals_mfma_path(fmt, M, N, K):
 @pytest.mark.parametrize("fmt", ["q4_0", "affine"])
 def test_small_m_row_chunks(fmt):
     """Above 32 rows, bf16 X runs the small-M kernel on row chunks of at most
-    32: every chunk's rows are bit-identical to a call on those rows alone,
+    32 (up to 64 rows, and up to 128 when there is no room for the matrix-core
+    GEMM's images): every chunk's rows are bit-identical to a call on those
+    rows alone,
     the whole result is within the bar of the oracle, and with binary32 X the
     automatic choice above 16 rows is the matrix-core GEMM (bit-identical to
     it forced) with the workspace the size query asks for, and without a
@@ -497,7 +499,7 @@ def test_small_m_row_chunks(fmt):
         run = lambda x, **kw: B.affine4_gemm(*planes, x, **kw)
         f = B.Q4_FMT_AFFINE4
     assert B.q4_dispatch_path(64, N, K, f) == B.Q4_PATH_SKINNY
-    for M in (33, 40, 64):
+    for M in (33, 40, 64, 96, 128):
         say(f"small-M row chunks {fmt} M={M}")
         X = synth.activations(rng, M, K)
         x = bf16_dev(X)
@@ -508,6 +510,16 @@ def test_small_m_row_chunks(fmt):
                 assert torch.equal(y[r:r + 32], part), (fmt, M, r, ydt)
             ref = oracle.matmul_f64(synth.bf16_bits_to_f32(synth.bf16_bits(X)).astype(np.float64), ref_w)
             assert rel(out_f64(y), ref) <= BAR, (fmt, M, ydt)
+        if M > 64:
+            # with room for its images the matrix-core GEMM takes these rows
+            ws = torch.empty(B.q4_gemm_workspace_size(M, N, K, f), dtype=torch.uint8, device="cuda")
+            auto = run(x, y_dtype=torch.float32, workspace=ws)
+            B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, B.Q4_PATH_MFMA)
+            try:
+                forced = run(x, y_dtype=torch.float32, workspace=ws)
+            finally:
+                B.q4_set_dispatch(B.Q4_KEY_FORCE_PATH, -1)
+            assert torch.equal(auto, forced), (fmt, M)
     # binary32 X above 16 rows: the matrix-core GEMM when the workspace holds
     # its images; without them the skinny kernel up to 32 rows, the GEMM above
     for M in (24, 33, 64):
